@@ -1,0 +1,344 @@
+"""Plain float64 CPU oracle of the hybrid sparse attention forward pass.
+
+TEST INFRASTRUCTURE ONLY (tests, the smoke check and the CPU-baseline leg of the
+benchmark).  It never runs on the product path and shares no code with the HIP
+library.
+
+Pages cited (titles as published):
+  [Tiny-R2]  "Tiny-R2: A Hybrid Architecture Combining SWA, CSA, HCA, mHC and
+             DSMoE Under the DeepSeek V4 Design Paradigm" (project README).
+  [V4-blog]  "deepseek-v4" (astro-blog post), section "1. hybrid attn".
+  [V4-code]  CSDN article with example PyTorch code for CSA and HCA,
+             sections "1. HCA ... 机制实现" and "2. CSA ... 机制实现".
+  [V4-arch]  zwxr.cn article on the DeepSeek-V4 architecture figure,
+             section "4. SWA 滑动窗口注意力的边界处理".
+  [CS336]    CS336 course notes, "Attention Heads 变体" and
+             "Attention Alternatives".
+
+Storage convention (shared with the C interface only by specification, not by
+code): tensors are numpy arrays in their storage form, ``np.uint16`` holding
+bfloat16 bit patterns when ``dtype == DTYPE_BF16`` and ``np.float32`` when
+``dtype == DTYPE_F32``.  Logits, indexer weights and gates are float32 always.
+Every computation below decodes its inputs exactly to float64 and works in
+float64; results that mirror a stored tensor are rounded once, to nearest
+even, to the storage dtype.
+
+Readings taken where the pages are silent (each repeated at its function):
+  R1  Indexer score of query row t against CSA entry c is
+      sum_h w[t,h] * max(0, qI[t,h] . kI[c]), heads summed in order h = 0..Hi-1.
+  R2  A compressed entry c of ratio m covers raw positions [c*m, (c+1)*m);
+      N = floor(T/m), a trailing partial block is dropped.
+  R3  The window of the query at position t is the W positions t-W+1 .. t,
+      clipped at 0.  Compressed entries (CSA candidates and HCA entries) are
+      visible to t only when they lie wholly before that window:
+      (c+1)*m <= t-W+1.
+  R4  Top-k keeps the min(k, #visible) visible entries ordered by
+      (score descending, entry index ascending); output is ascending entry
+      index, padded with -1.  One selection per query row, shared by all
+      attention heads.
+  R5  Branch key sets: SWA = window; HCA = window + all visible HCA entries;
+      CSA = window + the selected CSA entries.  Each branch is one softmax
+      over its whole key set, scale 1/sqrt(d) unless given.
+  R6  out = g[h,0]*O_HCA + g[h,1]*O_CSA + g[h,2]*O_SWA with the per-head gates
+      as given (no renormalisation); an absent branch contributes nothing.
+  R7  KV head of query head h is h // (H // Hkv).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+__all__ = [
+    "DTYPE_BF16", "DTYPE_F32",
+    "bf16_bits_to_f64", "f64_to_bf16_bits", "to_f64", "to_storage",
+    "block_weights", "compress", "compress_kv",
+    "window_bounds", "visible_count",
+    "indexer_scores", "select_topk", "index_topk", "index_topk_row",
+    "attend", "attn_row", "hybrid_attn_fwd",
+    "score_key_order",
+]
+
+
+# --------------------------------------------------------------------------
+# Storage dtypes
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bfloat16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values once, to nearest even, to bfloat16 bit patterns.
+
+    Works from the float64 value directly (no detour through float32, which
+    could round twice).  Finite inputs only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                 # x = mant * 2**expo, |mant| in [0.5, 1)
+    # bfloat16 keeps 8 significant bits for normal numbers; below 2**-126 the
+    # spacing is fixed at 2**-133 (subnormals).
+    normal = expo >= -125
+    q_norm = np.ldexp(np.rint(mant * 256.0), expo - 8)
+    q_sub = np.ldexp(np.rint(np.ldexp(x, 133)), -133)
+    q = np.where(normal, q_norm, q_sub)
+    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def to_f64(a: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == DTYPE_BF16:
+        return bf16_bits_to_f64(a)
+    if dtype == DTYPE_F32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == DTYPE_BF16:
+        return f64_to_bf16_bits(x)
+    if dtype == DTYPE_F32:
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+# --------------------------------------------------------------------------
+# Step 1: block compression  ([V4-code] section 1, the block-merge method:
+# a learned [block_size, channels] parameter is softmaxed over the block
+# positions and used as per-channel weights of a sum over the block;
+# [V4-blog] "CSA" 4:1 diagram; m = 4 for CSA, m = 128 for HCA).
+# --------------------------------------------------------------------------
+def block_weights(z: np.ndarray) -> np.ndarray:
+    """Softmax of the logits z[i, g, ch] over the block position i (axis 0)."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=0, keepdims=True))
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def compress(x: np.ndarray, z: np.ndarray, m: int) -> np.ndarray:
+    """xc[b, c, g, ch] = sum_{i<m} P[i, g, ch] * x[b, c*m + i, g, ch] (float64).
+
+    x: [B, T, Hkv, d] float64; z: [m, Hkv, d] logits.  Reading R2: the number
+    of entries is floor(T / m); a trailing partial block is dropped.
+    """
+    B, T, Hkv, d = x.shape
+    if z.shape != (m, Hkv, d):
+        raise ValueError("logits must be [m, Hkv, d]")
+    n_blocks = T // m
+    p = block_weights(z)
+    blocks = x[:, : n_blocks * m].reshape(B, n_blocks, m, Hkv, d)
+    return (blocks * p[None, None]).sum(axis=2)
+
+
+def compress_kv(k, v, zk, zv, m: int, dtype: int):
+    """Compress K with zk and V with zv; return both in the storage dtype."""
+    kc = compress(to_f64(k, dtype), zk, m)
+    vc = compress(to_f64(v, dtype), zv, m)
+    return to_storage(kc, dtype), to_storage(vc, dtype)
+
+
+# --------------------------------------------------------------------------
+# Visibility (reading R3; [V4-blog] "SWA": recent raw tokens beside the
+# compressed history; [V4-arch] 4.4: out-of-range window positions at the
+# start of the sequence contribute nothing)
+# --------------------------------------------------------------------------
+def window_bounds(t: int, W: int):
+    """Absolute positions [lo, hi) of the window of the query at position t."""
+    return max(0, t - W + 1), t + 1
+
+
+def visible_count(t: int, W: int, m: int, n_entries: int) -> int:
+    """Number of entries c (a prefix 0..n-1) with (c+1)*m <= t - W + 1."""
+    start = t - W + 1
+    if start <= 0:
+        return 0
+    return min(n_entries, start // m)
+
+
+# --------------------------------------------------------------------------
+# Step 2: lightning-indexer scores ([V4-blog] "CSA": the indexer finds the
+# compressed entries most relevant to the current query; reading R1 gives the
+# score formula)
+# --------------------------------------------------------------------------
+def indexer_scores(q_row: np.ndarray, w_row: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """s[c] = sum_h w[h] * max(0, q[h] . keys[c]) in float64, h in order."""
+    s = np.zeros(keys.shape[0], dtype=np.float64)
+    for h in range(q_row.shape[0]):
+        dots = (keys * q_row[h][None, :]).sum(axis=1)
+        s = s + w_row[h] * np.maximum(dots, 0.0)
+    return s
+
+
+# --------------------------------------------------------------------------
+# Step 2b: per-query top-k (reading R4; [V4-blog] "CSA": Top-K compressed
+# entries for the current query)
+# --------------------------------------------------------------------------
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Ascending indices of the top min(k, n) of scores, -1 padded to k.
+
+    Order is (score descending, index ascending); -0.0 and +0.0 compare equal.
+    """
+    n = scores.shape[0]
+    k_eff = min(k, n)
+    order = np.lexsort((np.arange(n), -scores))
+    out = np.full(k, -1, dtype=np.int32)
+    out[:k_eff] = np.sort(order[:k_eff])
+    return out
+
+
+def index_topk_row(qI_row, w_row, kI_b, t: int, m: int, W: int, k: int):
+    """Selection for one query row at absolute position t (float64 inputs)."""
+    n_vis = visible_count(t, W, m, kI_b.shape[0])
+    scores = indexer_scores(qI_row, w_row, kI_b[:n_vis])
+    return select_topk(scores, k), scores
+
+
+def index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, dtype: int,
+               rows=None):
+    """Top-k CSA selection for every query row.
+
+    qI: [B, Tq, Hi, d_idx], kI: [B, N, d_idx] (storage dtype); w: [B, Tq, Hi]
+    float32.  Returns int32 [B, Tq, k] (or [len(rows), k] for a list of
+    (b, i) rows).
+    """
+    q = to_f64(qI, dtype)
+    kk = to_f64(kI, dtype)
+    ww = np.asarray(w, dtype=np.float32).astype(np.float64)
+    B, Tq = q.shape[:2]
+    if rows is None:
+        out = np.empty((B, Tq, k), dtype=np.int32)
+        for b in range(B):
+            for i in range(Tq):
+                out[b, i], _ = index_topk_row(q[b, i], ww[b, i], kk[b],
+                                              q_pos0 + i, m, W, k)
+        return out
+    out = np.empty((len(rows), k), dtype=np.int32)
+    for r, (b, i) in enumerate(rows):
+        out[r], _ = index_topk_row(q[b, i], ww[b, i], kk[b], q_pos0 + i, m, W, k)
+    return out
+
+
+def score_key_order(scores: np.ndarray) -> np.ndarray:
+    """Rank of each entry under (score desc, index asc); 0 is the best."""
+    order = np.lexsort((np.arange(scores.shape[0]), -scores))
+    rank = np.empty_like(order)
+    rank[order] = np.arange(order.shape[0])
+    return rank
+
+
+# --------------------------------------------------------------------------
+# Step 3: softmax attention over one key set ([V4-code] attention: scores
+# divided by sqrt(head_dim), softmax, weighted sum of values; [V4-blog] "SWA":
+# compressed and raw entries enter one attention together)
+# --------------------------------------------------------------------------
+def attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float):
+    """Textbook softmax attention of one query over n keys (float64).
+
+    Returns (output [d], weights [n]).
+    """
+    logits = scale * (keys * q[None, :]).sum(axis=1)
+    e = np.exp(logits - logits.max())
+    p = e / e.sum()
+    return (p[:, None] * vals).sum(axis=0), p
+
+
+def attn_row(q_row, t, *, W, raw_pos0, k_raw_b, v_raw_b, scale,
+             hca=None, csa=None, idx_row=None, want=("hca", "csa", "swa")):
+    """Per-branch outputs for one query row (all heads), float64.
+
+    q_row: [H, d]; k_raw_b/v_raw_b: [Tr, Hkv, d]; hca = (k_hca_b, v_hca_b, m)
+    with [N, Hkv, d] caches; csa = (k_csa_b, v_csa_b) with the row's selected
+    indices idx_row (-1 padded).  Returns dict branch -> (O [H, d], weights
+    list per head).
+    """
+    H, d = q_row.shape
+    Hkv = k_raw_b.shape[1]
+    G = H // Hkv
+    lo, hi = window_bounds(t, W)
+    r0, r1 = lo - raw_pos0, hi - raw_pos0
+    if r0 < 0 or r1 > k_raw_b.shape[0]:
+        raise ValueError("window rows fall outside the raw K/V rows given")
+    res = {}
+    for br in want:
+        out = np.zeros((H, d))
+        weights = []
+        for h in range(H):
+            g = h // G
+            ks = [k_raw_b[r0:r1, g]]
+            vs = [v_raw_b[r0:r1, g]]
+            if br == "hca":
+                k_h, v_h, m_h = hca
+                n_vis = visible_count(t, W, m_h, k_h.shape[0])
+                ks.append(k_h[:n_vis, g])
+                vs.append(v_h[:n_vis, g])
+            elif br == "csa":
+                k_c, v_c = csa
+                sel = idx_row[idx_row >= 0]
+                ks.append(k_c[sel, g])
+                vs.append(v_c[sel, g])
+            o, p = attend(q_row[h], np.concatenate(ks), np.concatenate(vs), scale)
+            out[h] = o
+            weights.append(p)
+        res[br] = (out, weights)
+    return res
+
+
+def hybrid_attn_fwd(q, k_raw, v_raw, gates, *, W, dtype, q_pos0=0, raw_pos0=0,
+                    hca=None, csa=None, scale=None, rows=None, branches=False):
+    """Gated hybrid attention output (reading R6, [Tiny-R2] 3.1.2 mode table
+    and 3.2 diagram: a per-branch gate and a weighted sum of the three
+    attentions, order [HCA, CSA, SWA]).
+
+    q: [B, Tq, H, d]; k_raw/v_raw: [B, Tr, Hkv, d]; gates: [H, 3] float32.
+    hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None
+    (idx int32 [B, Tq, k]).  A branch passed as None contributes nothing.
+    Returns the output in the storage dtype ([B, Tq, H, d], or [len(rows), H, d]
+    for a list of (b, i) rows); with branches=True also the float64 per-branch
+    outputs.
+    """
+    qf = to_f64(q, dtype)
+    kr = to_f64(k_raw, dtype)
+    vr = to_f64(v_raw, dtype)
+    g = np.asarray(gates, dtype=np.float32).astype(np.float64)
+    B, Tq, H, d = qf.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    hca_f = None
+    if hca is not None:
+        hca_f = (to_f64(hca[0], dtype), to_f64(hca[1], dtype), int(hca[2]))
+    csa_f = None
+    if csa is not None:
+        csa_f = (to_f64(csa[0], dtype), to_f64(csa[1], dtype), np.asarray(csa[2]))
+    want = ["swa"]
+    if hca_f is not None:
+        want.append("hca")
+    if csa_f is not None:
+        want.append("csa")
+    row_list = rows if rows is not None else [(b, i) for b in range(B) for i in range(Tq)]
+    out = np.zeros((len(row_list), H, d))
+    per_branch = {br: np.zeros((len(row_list), H, d)) for br in want}
+    for r, (b, i) in enumerate(row_list):
+        t = q_pos0 + i
+        res = attn_row(
+            qf[b, i], t, W=W, raw_pos0=raw_pos0, k_raw_b=kr[b], v_raw_b=vr[b],
+            scale=scale,
+            hca=None if hca_f is None else (hca_f[0][b], hca_f[1][b], hca_f[2]),
+            csa=None if csa_f is None else (csa_f[0][b], csa_f[1][b]),
+            idx_row=None if csa_f is None else csa_f[2][b, i],
+            want=want)
+        acc = np.zeros((H, d))
+        for col, br in ((0, "hca"), (1, "csa"), (2, "swa")):
+            if br in res:
+                acc = acc + g[:, col][:, None] * res[br][0]
+                per_branch[br][r] = res[br][0]
+        out[r] = acc
+    if rows is None:
+        out = out.reshape(B, Tq, H, d)
+        per_branch = {k: v.reshape(B, Tq, H, d) for k, v in per_branch.items()}
+    stored = to_storage(out, dtype)
+    if branches:
+        return stored, per_branch
+    return stored

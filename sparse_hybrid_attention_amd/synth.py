@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the hybrid sparse attention forward pass.
+
+This module only draws random numbers and packs them into the storage layout;
+it holds none of the method's arithmetic.  Tests feed the same arrays to the
+HIP library and to the CPU oracle, and the benchmark uses it for its inputs.
+
+Every array is drawn from ``numpy.random.Generator(PCG64(seed))`` in a fixed
+order, as float32, and bfloat16 tensors are produced from those draws by
+round-to-nearest-even on the float32 bit pattern (ties to even; finite values
+only).  Storage form: ``np.uint16`` bit patterns for bfloat16, ``np.float32``
+otherwise.
+
+Workloads (all sizes are the ones the method is quoted on):
+
+``tiny_fp32``       B1 T256 H=Hkv=4 d64 fp32; CSA m4 (64 entries) k8, indexer
+                    2 heads d_idx 64; HCA m32; W32; gates U(0,1).
+``tinyr2_bf16``     B8 T2048 H=Hkv=12 d128 bf16 (Tiny-R2 training shape);
+                    CSA m4 (512 entries) k64, indexer 4 heads d_idx 64;
+                    HCA m128 (16 entries); W128; gates U(0,1) or a one-hot mode.
+``hca_prefill_32k`` B1 T32768 H16 Hkv2 d128 bf16; Q ~ N(0,1)/sqrt(d); HCA m128
+                    (256 entries); W128; gates [1,0,0].
+``csa_prefill_128k`` B1 T131072 H32 Hkv4 d128 bf16; CSA m4 (32768 entries),
+                    indexer 4 heads d_idx 64, k512; W128; gates [0,1,0].
+``decode_1m``       B16 x 1 query at 1,048,576 tokens of context, H32 Hkv1 d128
+                    bf16; caches N(0,1): CSA 262,144 entries with indexer keys,
+                    k1024; HCA 8,192 entries; raw window 128; gates U(0,1).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+MODES = {
+    "hca": (1.0, 0.0, 0.0),
+    "csa": (0.0, 1.0, 0.0),
+    "swa": (0.0, 0.0, 1.0),
+}
+
+CONFIGS = {
+    "tiny_fp32": dict(kind="prefill", dtype=DTYPE_F32, B=1, T=256, H=4, Hkv=4, d=64,
+                      m_csa=4, k=8, Hi=2, d_idx=64, m_hca=32, W=32, gates="mix"),
+    "tinyr2_bf16": dict(kind="prefill", dtype=DTYPE_BF16, B=8, T=2048, H=12, Hkv=12,
+                        d=128, m_csa=4, k=64, Hi=4, d_idx=64, m_hca=128, W=128,
+                        gates="mix"),
+    "hca_prefill_32k": dict(kind="prefill", dtype=DTYPE_BF16, B=1, T=32768, H=16, Hkv=2,
+                            d=128, m_csa=None, m_hca=128, W=128, gates="hca",
+                            q_scale="rsqrt_d"),
+    "csa_prefill_128k": dict(kind="prefill", dtype=DTYPE_BF16, B=1, T=131072, H=32,
+                             Hkv=4, d=128, m_csa=4, k=512, Hi=4, d_idx=64, m_hca=None,
+                             W=128, gates="csa"),
+    "decode_1m": dict(kind="decode", dtype=DTYPE_BF16, B=16, H=32, Hkv=1, d=128,
+                      N_csa=262144, m_csa=4, k=1024, Hi=4, d_idx=64, N_hca=8192,
+                      m_hca=128, W=128, gates="mix"),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal(rng, shape, dtype, scale=1.0):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    if dtype == DTYPE_BF16:
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def _gates(rng, H, spec):
+    if spec == "mix":
+        return rng.random(size=(H, 3), dtype=np.float32)
+    if isinstance(spec, str):
+        return np.tile(np.asarray(MODES[spec], dtype=np.float32), (H, 1))
+    g = np.asarray(spec, dtype=np.float32)
+    return np.tile(g, (H, 1)) if g.ndim == 1 else g
+
+
+def config(name: str, **overrides) -> dict:
+    cfg = dict(CONFIGS[name])
+    cfg.update(overrides)
+    cfg["name"] = name
+    return cfg
+
+
+def make_prefill(cfg: dict, seed: int = 0) -> dict:
+    """Prefill inputs.  Draw order: Q, K, V, Zk_csa, Zv_csa, Zk_hca, Zv_hca, qI,
+    kI, w, gates (branches a workload lacks are skipped)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt, B, T, H, Hkv, d = cfg["dtype"], cfg["B"], cfg["T"], cfg["H"], cfg["Hkv"], cfg["d"]
+    q_scale = 1.0 / math.sqrt(d) if cfg.get("q_scale") == "rsqrt_d" else 1.0
+    out = dict(cfg=cfg)
+    out["q"] = _normal(rng, (B, T, H, d), dt, q_scale)
+    out["k"] = _normal(rng, (B, T, Hkv, d), dt)
+    out["v"] = _normal(rng, (B, T, Hkv, d), dt)
+    if cfg.get("m_csa"):
+        m = cfg["m_csa"]
+        out["zk_csa"] = rng.standard_normal((m, Hkv, d), dtype=np.float32) / np.float32(8)
+        out["zv_csa"] = rng.standard_normal((m, Hkv, d), dtype=np.float32) / np.float32(8)
+    if cfg.get("m_hca"):
+        m = cfg["m_hca"]
+        out["zk_hca"] = rng.standard_normal((m, Hkv, d), dtype=np.float32) / np.float32(8)
+        out["zv_hca"] = rng.standard_normal((m, Hkv, d), dtype=np.float32) / np.float32(8)
+    if cfg.get("m_csa"):
+        Hi, di = cfg["Hi"], cfg["d_idx"]
+        n_csa = T // cfg["m_csa"]
+        out["qI"] = _normal(rng, (B, T, Hi, di), dt)
+        out["kI"] = _normal(rng, (B, n_csa, di), dt)
+        w_h = rng.random(size=(Hi,), dtype=np.float32)
+        out["w"] = np.ascontiguousarray(np.broadcast_to(w_h, (B, T, Hi)))
+    out["gates"] = _gates(rng, H, cfg.get("gates", "mix"))
+    return out
+
+
+def make_decode(cfg: dict, seed: int = 0) -> dict:
+    """Decode inputs.  Draw order: Q, window K, window V, Kc_csa, Vc_csa, kI,
+    Kc_hca, Vc_hca, qI, w, gates.  The query sits at the last position of a raw
+    window that follows N_csa * m_csa tokens of compressed history."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt, B, H, Hkv, d, W = cfg["dtype"], cfg["B"], cfg["H"], cfg["Hkv"], cfg["d"], cfg["W"]
+    Nc, Nh, Hi, di = cfg["N_csa"], cfg["N_hca"], cfg["Hi"], cfg["d_idx"]
+    out = dict(cfg=cfg)
+    out["q"] = _normal(rng, (B, 1, H, d), dt)
+    out["k_win"] = _normal(rng, (B, W, Hkv, d), dt)
+    out["v_win"] = _normal(rng, (B, W, Hkv, d), dt)
+    out["k_csa"] = _normal(rng, (B, Nc, Hkv, d), dt)
+    out["v_csa"] = _normal(rng, (B, Nc, Hkv, d), dt)
+    out["kI"] = _normal(rng, (B, Nc, di), dt)
+    out["k_hca"] = _normal(rng, (B, Nh, Hkv, d), dt)
+    out["v_hca"] = _normal(rng, (B, Nh, Hkv, d), dt)
+    out["qI"] = _normal(rng, (B, 1, Hi, di), dt)
+    w_h = rng.random(size=(Hi,), dtype=np.float32)
+    out["w"] = np.ascontiguousarray(np.broadcast_to(w_h, (B, 1, Hi)))
+    out["gates"] = _gates(rng, H, cfg.get("gates", "mix"))
+    out["raw_pos0"] = Nc * cfg["m_csa"]
+    out["q_pos0"] = Nc * cfg["m_csa"] + W - 1
+    return out
+
+
+def make_inputs(name: str, seed: int = 0, **overrides) -> dict:
+    cfg = config(name, **overrides)
+    if cfg["kind"] == "decode":
+        return make_decode(cfg, seed)
+    return make_prefill(cfg, seed)

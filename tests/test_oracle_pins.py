@@ -1,0 +1,340 @@
+"""Pins of the CPU oracle against things other than itself: numbers the pages
+print, closed forms, textbook special cases computed by library routines, and
+brute force on tiny inputs.  Each test is chosen so that a plausible slip in the
+oracle (a dropped term, a wrong sign or index, a transposed operand, an
+off-by-one in the window or visibility rule) fails it."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_hybrid_attention_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- dtypes
+def test_bf16_rounding_known_patterns():
+    # bfloat16 patterns: 1.0 = 0x3F80, one ulp at 1 is 2**-7, subnormal spacing 2**-133.
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.0, 0.0, 1.0 + 2**-8 + 2**-30,
+                  3.140625, 2.0**-130])
+    want = np.array([0x3F80, 0x3F80, 0x3F82, 0xC000, 0x0000, 0x3F81, 0x4049, 0x0008],
+                    dtype=np.uint16)
+    assert np.array_equal(O.f64_to_bf16_bits(x), want)
+    assert np.array_equal(O.bf16_bits_to_f64(want)[:5], [1.0, 1.0, 1.0 + 2**-6, -2.0, 0.0])
+
+
+def test_bf16_rounding_matches_independent_f32_path():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(100000) * 10.0).astype(np.float32)
+    a = O.f64_to_bf16_bits(x.astype(np.float64))
+    b = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------ compression
+def _rand(shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_compress_m1_is_identity():
+    x = _rand((2, 7, 3, 5))
+    z = _rand((1, 3, 5), 1) * 3
+    assert np.array_equal(O.compress(x, z, 1), x)
+
+
+def test_compress_zero_logits_is_block_mean():
+    x = _rand((2, 12, 2, 4))
+    y = O.compress(x, np.zeros((4, 2, 4)), 4)
+    want = x.reshape(2, 3, 4, 2, 4).mean(axis=2)
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-15)
+
+
+def test_compress_constant_block_and_dominant_logit():
+    x = np.repeat(_rand((1, 3, 2, 4)), 8, axis=1)       # every block constant
+    z = _rand((8, 2, 4), 2)
+    np.testing.assert_allclose(O.compress(x, z, 8), x[:, ::8], rtol=1e-14, atol=0)
+    x2 = _rand((1, 16, 2, 4), 3)
+    z2 = np.zeros((8, 2, 4))
+    z2[5] = 60.0                                         # position 5 dominates
+    np.testing.assert_allclose(O.compress(x2, z2, 8), x2[:, 5::8], rtol=1e-20, atol=1e-24)
+
+
+def test_compress_brute_force_and_partial_block():
+    B, T, Hkv, d, m = 2, 11, 2, 3, 4
+    x = _rand((B, T, Hkv, d), 4)
+    z = _rand((m, Hkv, d), 5)
+    y = O.compress(x, z, m)
+    assert y.shape == (B, 2, Hkv, d)                       # 11 // 4, tail dropped
+    for b in range(B):
+        for c in range(2):
+            for g in range(Hkv):
+                for ch in range(d):
+                    ex = [math.exp(z[i, g, ch]) for i in range(m)]
+                    tot = sum(ex)
+                    val = sum(ex[i] / tot * x[b, c * m + i, g, ch] for i in range(m))
+                    assert abs(val - y[b, c, g, ch]) < 1e-13
+
+
+def test_block_counts_match_pages():
+    g = golden()
+    for key in ("csa_entries_at_1M", "hca_entries_at_1M"):
+        e = g[key]
+        x_len = e["context_tokens"]
+        # entries = floor(T / m), computed through the oracle's own shapes
+        z = np.zeros((e["m"], 1, 1))
+        x = np.zeros((1, x_len, 1, 1), dtype=np.float32)
+        n = O.compress(x.astype(np.float64), z, e["m"]).shape[1]
+        assert n == e["exact"]
+    assert abs(g["csa_entries_at_1M"]["exact"] - 250_000) / 250_000 < 0.05
+    assert abs(g["hca_entries_at_1M"]["exact"] - 8_000) / 8_000 < 0.05
+
+
+# ------------------------------------------------------- window / visibility
+def _brute_window(t, W):
+    return [j for j in range(0, t + 1) if t - j < W]
+
+
+def _brute_visible(t, W, m, N):
+    win = _brute_window(t, W)
+    start = win[0]
+    return [c for c in range(N) if all(p < start for p in range(c * m, (c + 1) * m))]
+
+
+@pytest.mark.parametrize("W,m,N", [(4, 2, 20), (32, 4, 64), (7, 3, 30), (1, 1, 40), (5, 8, 6)])
+def test_window_and_visibility_brute_force(W, m, N):
+    for t in range(0, 70):
+        lo, hi = O.window_bounds(t, W)
+        assert list(range(lo, hi)) == _brute_window(t, W)
+        vis = _brute_visible(t, W, m, N)
+        assert vis == list(range(O.visible_count(t, W, m, N)))
+
+
+def test_window_boundaries():
+    W, m = 128, 4
+    assert O.window_bounds(0, W) == (0, 1)
+    assert O.window_bounds(127, W) == (0, 128)
+    assert O.window_bounds(128, W) == (1, 129)
+    assert O.visible_count(127 + 3, W, m, 10) == 0       # window starts at 3: block 0 spans 0..3
+    assert O.visible_count(127 + 4, W, m, 10) == 1       # starts at 4: block 0 wholly before
+    assert O.visible_count(10**6, W, m, 10) == 10
+
+
+def test_window_score_count_matches_pages():
+    g = golden()["swa_score_count"]
+    n, w = g["n"], g["w"]
+    # unclipped band cost n*w; clipping removes exactly w(w-1)/2 pairs at the start
+    clipped = sum(O.window_bounds(t, w)[1] - O.window_bounds(t, w)[0] for t in range(n))
+    assert clipped + w * (w - 1) // 2 == g["exact_window"]
+    assert g["exact_full"] == n * n
+    assert g["exact_full"] // g["exact_window"] == g["ratio"]
+    assert g["exact_full"] // (n * 512) == g["ratio_w512"]
+    assert abs(g["exact_window"] / 1e6 - 8.4) < 0.05 and abs(g["exact_full"] / 1e6 - 67) < 0.5
+
+
+# ------------------------------------------------------------------ indexer
+def test_indexer_brute_force():
+    rng = np.random.default_rng(7)
+    Hi, di, n = 3, 5, 9
+    q = rng.standard_normal((Hi, di))
+    k = rng.standard_normal((n, di))
+    w = rng.random(Hi)
+    s = O.indexer_scores(q, w, k)
+    for c in range(n):
+        tot = 0.0
+        for h in range(Hi):
+            dot = 0.0
+            for e in range(di):
+                dot += q[h, e] * k[c, e]
+            tot += w[h] * (dot if dot > 0 else 0.0)
+        assert abs(tot - s[c]) < 1e-12
+
+
+def test_indexer_single_head_ranking_is_library_sort():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 16))
+    k = rng.standard_normal((300, 16))
+    dots = np.maximum(np.dot(k, q[0]), 0.0)
+    order = np.lexsort((np.arange(300), -dots))
+    want = np.sort(order[:40])
+    got = O.select_topk(O.indexer_scores(q, np.ones(1), k), 40)
+    assert np.array_equal(got, want)
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(9)
+    for trial in range(50):
+        n = int(rng.integers(1, 40))
+        k = int(rng.integers(1, 50))
+        s = rng.integers(0, 5, n).astype(np.float64)       # many ties
+        got = O.select_topk(s, k)
+        ranked = sorted(range(n), key=lambda c: (-s[c], c))[: min(k, n)]
+        want = sorted(ranked) + [-1] * (k - min(k, n))
+        assert got.tolist() == want
+
+
+def test_all_negative_dots_select_lowest_visible():
+    B, T, Hi, di, m, W, k = 1, 64, 2, 8, 4, 8, 5
+    qI = -np.abs(_rand((B, T, Hi, di), 10)).astype(np.float32)
+    kI = np.abs(_rand((B, T // m, di), 11)).astype(np.float32)
+    w = np.ones((B, T, Hi), np.float32)
+    idx = O.index_topk(qI, kI, w, 0, m, W, k, O.DTYPE_F32)
+    for i in range(T):
+        nv = O.visible_count(i, W, m, T // m)
+        want = list(range(min(k, nv))) + [-1] * (k - min(k, nv))
+        assert idx[0, i].tolist() == want
+
+
+def test_k_at_least_visible_selects_all():
+    B, T, Hi, di, m, W = 1, 48, 2, 8, 2, 4
+    qI = _rand((B, T, Hi, di), 12).astype(np.float32)
+    kI = _rand((B, T // m, di), 13).astype(np.float32)
+    w = np.ones((B, T, Hi), np.float32)
+    idx = O.index_topk(qI, kI, w, 0, m, W, T, O.DTYPE_F32)
+    for i in range(T):
+        nv = O.visible_count(i, W, m, T // m)
+        assert idx[0, i, :nv].tolist() == list(range(nv))
+        assert (idx[0, i, nv:] == -1).all()
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch CPU float64 scaled_dot_product_attention; q [T,H,d], k/v [T,H,d]."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2)
+    tv = torch.from_numpy(v).permute(1, 0, 2)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, is_causal=causal)
+    return o.permute(1, 0, 2).numpy()
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def test_swa_with_wide_window_is_dense_causal():
+    T, H, d = 40, 2, 16
+    q, k, v = (_f32(_rand((1, T, H, d), s)) for s in (20, 21, 22))
+    g = np.tile(np.array([0, 0, 1], np.float32), (H, 1))
+    out = O.hybrid_attn_fwd(q, k, v, g, W=T, dtype=O.DTYPE_F32)
+    want = _sdpa(q[0].astype(np.float64), k[0].astype(np.float64), v[0].astype(np.float64), causal=True)
+    np.testing.assert_allclose(out[0], want, rtol=1e-6, atol=1e-6)
+
+
+def test_swa_is_banded_attention():
+    T, H, d, W = 50, 2, 8, 7
+    q, k, v = (_rand((1, T, H, d), s).astype(np.float32) for s in (23, 24, 25))
+    g = np.tile(np.array([0, 0, 1], np.float32), (H, 1))
+    _, br = O.hybrid_attn_fwd(q, k, v, g, W=W, dtype=O.DTYPE_F32, branches=True)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    band = (j <= i) & (j > i - W)
+    want = _sdpa(q[0].astype(np.float64), k[0].astype(np.float64), v[0].astype(np.float64), mask=band)
+    np.testing.assert_allclose(br["swa"][0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_csa_m1_all_selected_is_dense_causal():
+    T, H, d, W, Hi, di = 36, 2, 8, 5, 2, 4
+    q, k, v = (_rand((1, T, H, d), s).astype(np.float32) for s in (26, 27, 28))
+    z = _rand((1, H, d), 29).astype(np.float32)
+    kc, vc = O.compress_kv(k, v, z, z, 1, O.DTYPE_F32)
+    qI = _rand((1, T, Hi, di), 30).astype(np.float32)
+    kI = _rand((1, T, di), 31).astype(np.float32)
+    w = np.ones((1, T, Hi), np.float32)
+    idx = O.index_topk(qI, kI, w, 0, 1, W, T, O.DTYPE_F32)
+    g = np.tile(np.array([0, 1, 0], np.float32), (H, 1))
+    _, br = O.hybrid_attn_fwd(q, k, v, g, W=W, dtype=O.DTYPE_F32, csa=(kc, vc, idx), branches=True)
+    want = _sdpa(q[0].astype(np.float64), k[0].astype(np.float64), v[0].astype(np.float64), causal=True)
+    np.testing.assert_allclose(br["csa"][0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_hca_two_windows_reduces_to_window_plus_one_entry():
+    W = 16
+    T, H, d = 2 * W, 2, 8
+    q, k, v = (_rand((1, T, H, d), s).astype(np.float32) for s in (32, 33, 34))
+    z = np.zeros((W, H, d), np.float32)
+    kc, vc = O.compress_kv(k, v, z, z, W, O.DTYPE_F32)
+    g = np.tile(np.array([1, 0, 0], np.float32), (H, 1))
+    _, br = O.hybrid_attn_fwd(q, k, v, g, W=W, dtype=O.DTYPE_F32, hca=(kc, vc, W), branches=True)
+    np.testing.assert_allclose(br["hca"][0, : T - 1], br["swa"][0, : T - 1], rtol=0, atol=0)
+    # last row: window T-W..T-1 plus one entry = mean of rows 0..W-1 (zero logits)
+    t = T - 1
+    q64, k64, v64 = (a[0].astype(np.float64) for a in (q, k, v))
+    for h in range(H):
+        keys = np.vstack([k64[t - W + 1:, h], k64[:W, h].mean(axis=0)])
+        vals = np.vstack([v64[t - W + 1:, h], v64[:W, h].mean(axis=0)])
+        logit = keys @ q64[t, h] / math.sqrt(d)
+        p = np.exp(logit - logit.max())
+        p /= p.sum()
+        np.testing.assert_allclose(br["hca"][0, t, h], p @ vals, rtol=1e-7, atol=1e-6)
+
+
+def test_attention_weights_are_convex():
+    rng = np.random.default_rng(35)
+    q = rng.standard_normal(8)
+    keys = rng.standard_normal((20, 8)) * 3
+    vals = rng.standard_normal((20, 8))
+    o, p = O.attend(q, keys, vals, 0.5)
+    assert (p >= 0).all() and abs(p.sum() - 1) < 1e-14
+    np.testing.assert_allclose(o, np.einsum("n,nd->d", p, vals), rtol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv_and_gate_linearity():
+    B, T, H, Hkv, d, W = 1, 40, 4, 2, 8, 6
+    inp = synth.make_inputs("tiny_fp32", B=B, T=T, H=H, Hkv=Hkv, d=d, W=W, m_csa=2, k=4,
+                            Hi=2, d_idx=8, m_hca=4)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    kh, vh = O.compress_kv(k, v, inp["zk_hca"], inp["zv_hca"], 4, O.DTYPE_F32)
+    kc, vc = O.compress_kv(k, v, inp["zk_csa"], inp["zv_csa"], 2, O.DTYPE_F32)
+    idx = O.index_topk(inp["qI"], inp["kI"], inp["w"], 0, 2, W, 4, O.DTYPE_F32)
+    g = inp["gates"]
+    out = O.hybrid_attn_fwd(q, k, v, g, W=W, dtype=O.DTYPE_F32, hca=(kh, vh, 4), csa=(kc, vc, idx))
+    rep = lambda a: np.repeat(a, H // Hkv, axis=2)
+    out_mha = O.hybrid_attn_fwd(q, rep(k), rep(v), g, W=W, dtype=O.DTYPE_F32,
+                                hca=(rep(kh), rep(vh), 4), csa=(rep(kc), rep(vc), idx))
+    np.testing.assert_array_equal(out, out_mha)
+    parts = []
+    for col in range(3):
+        one = np.zeros_like(g)
+        one[:, col] = 1
+        parts.append(O.hybrid_attn_fwd(q, k, v, one, W=W, dtype=O.DTYPE_F32,
+                                       hca=(kh, vh, 4), csa=(kc, vc, idx)).astype(np.float64))
+    lin = sum(g[:, c][None, None, :, None].astype(np.float64) * parts[c] for c in range(3))
+    np.testing.assert_allclose(out, lin, rtol=1e-6, atol=1e-6)
+
+
+def test_constant_values_give_gate_sum():
+    T, H, d, W = 30, 3, 8, 5
+    q = _rand((1, T, H, d), 36).astype(np.float32)
+    k = _rand((1, T, H, d), 37).astype(np.float32)
+    row = _rand((d,), 38)
+    v = np.broadcast_to(row, (1, T, H, d)).astype(np.float32)
+    z = _rand((4, H, d), 39).astype(np.float32)
+    kh, vh = O.compress_kv(k, v, z, z, 4, O.DTYPE_F32)
+    g = np.random.default_rng(40).random((H, 3)).astype(np.float32)
+    out = O.hybrid_attn_fwd(q, k, v, g, W=W, dtype=O.DTYPE_F32, hca=(kh, vh, 4))
+    want = (g[:, 0] + g[:, 2])[:, None] * row.astype(np.float32)[None, :]
+    np.testing.assert_allclose(out[0], np.broadcast_to(want, (T, H, d)), rtol=1e-6, atol=1e-6)
+
+
+def test_modes_table_matches_pages():
+    g = golden()["modes"]
+    assert [list(synth.MODES[m]) for m in ("hca", "csa", "swa")] == [g["HCA"], g["CSA"], g["SWA"]]
+
+
+def test_decode_query_sees_all_cache_entries():
+    cfg = synth.CONFIGS["decode_1m"]
+    t = cfg["N_csa"] * cfg["m_csa"] + cfg["W"] - 1
+    assert O.visible_count(t, cfg["W"], cfg["m_csa"], cfg["N_csa"]) == 262144
+    assert O.visible_count(t, cfg["W"], cfg["m_hca"], cfg["N_hca"]) == 8192
+    lo, hi = O.window_bounds(t, cfg["W"])
+    assert lo == cfg["N_csa"] * cfg["m_csa"] and hi - lo == cfg["W"]
