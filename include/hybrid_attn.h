@@ -1,0 +1,172 @@
+/*
+ * hybrid_attn.h -- C interface of the MI355X (gfx950) hybrid sparse attention
+ * forward pass: HCA (heavily compressed), CSA (compressed + sparse-selected) and
+ * SWA (sliding window) branches mixed by per-head gates.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [V4-blog] "deepseek-v4" (astro-blog post), section "1. hybrid attn":
+ *             CSA = 4:1 compression + lightning indexer top-K + sparse attention;
+ *             HCA = ratio 128, dense attention over the compressed entries;
+ *             SWA = the most recent 128 raw tokens, attended together with the
+ *             compressed history in one attention; the caches are kept apart.
+ *   [V4-code] CSDN article with CSA/HCA example code, section "1. HCA":
+ *             block merge = softmax over block positions of a learned
+ *             [block_size, channels] parameter, weighted sum over the block;
+ *             attention scale 1/sqrt(head_dim).
+ *   [Tiny-R2] Tiny-R2 README, sections 3.1.2 (modes HCA [1,0,0], CSA [0,1,0],
+ *             SWA [0,0,1]) and 3.2 (branch gate + weighted sum, config fields
+ *             block_size / window_size / num_tokens_to_keep).
+ *   [CS336]   CS336 notes, "Attention Heads 变体" (MQA / GQA head sharing).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer allocated and owned by the caller.
+ *    The library never allocates or frees device memory and keeps no state
+ *    between calls (apart from the thread-local error string).
+ *  - dtype: SHATTN_DTYPE_BF16 (bfloat16) or SHATTN_DTYPE_F32 applies to every
+ *    tensor operand except logits, indexer weights and gates, which are always
+ *    float32.  Accumulation is float32; stored results are rounded once to
+ *    nearest even.
+ *  - Layouts are dense row-major with the shapes given below; pointers must be
+ *    16-byte aligned.
+ *  - Positions: query row i has absolute position q_pos0 + i.  A compressed
+ *    entry c of ratio m covers raw positions [c*m, (c+1)*m).  The window of the
+ *    query at t is positions max(0, t-W+1) .. t.  A compressed entry is visible
+ *    to t only when it lies wholly before that window: (c+1)*m <= t-W+1.
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work; they never synchronise the device.  Calls are reentrant.
+ *  - Return value: SHATTN_OK (0) or a negative error code.  Every argument is
+ *    validated on the host before any HIP call, so an invalid call enqueues
+ *    nothing.  shattn_last_error() returns a message for the calling thread's
+ *    last failure.
+ *  - Identical inputs give bitwise identical outputs (no floating-point
+ *    atomics in any reduction).
+ */
+#ifndef HYBRID_ATTN_H
+#define HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SHATTN_API __attribute__((visibility("default")))
+#else
+#define SHATTN_API
+#endif
+
+#define SHATTN_DTYPE_BF16 0
+#define SHATTN_DTYPE_F32 1
+
+#define SHATTN_OK 0
+#define SHATTN_EINVAL (-1)       /* invalid argument (null pointer, bad shape) */
+#define SHATTN_EUNSUPPORTED (-2) /* valid but outside what the kernels support */
+#define SHATTN_EWORKSPACE (-3)   /* workspace missing or too small */
+#define SHATTN_EHIP (-4)         /* a HIP launch failed; message has the reason */
+
+/*
+ * Block compression of K and V ([V4-code] section 1, block merge; [V4-blog]
+ * "CSA" 4:1 diagram; m = 4 for CSA and m = 128 for HCA).
+ *
+ *   P[i,g,ch]      = softmax over i < m of z[i,g,ch]         (float32)
+ *   kc[b,c,g,ch]   = sum_{i<m} Pk[i,g,ch] * k[b, c*m+i, g, ch]
+ *   vc[b,c,g,ch]   = sum_{i<m} Pv[i,g,ch] * v[b, c*m+i, g, ch]
+ *
+ *   k, v   : [B, T, Hkv, d]          dtype
+ *   zk, zv : [m, Hkv, d]             float32 logits (may be the same pointer)
+ *   kc, vc : [B, floor(T/m), Hkv, d] dtype, written; a trailing partial block
+ *            of T % m rows is not compressed.
+ * Supported: d in {64, 128}; 1 <= m <= 1024; Hkv >= 1; B, T >= 0.
+ */
+SHATTN_API int hca_compress_kv(const void* k, const void* v, const float* zk, const float* zv,
+                    void* kc, void* vc, int B, int T, int Hkv, int d, int m, int dtype,
+                    void* stream);
+
+/*
+ * Lightning indexer + per-query top-k over the CSA entries ([V4-blog] "CSA":
+ * the indexer finds, for the current query, the Top-K most relevant
+ * compressed entries; [Tiny-R2] 3.2 importance_score / topk selection).
+ *
+ *   score[b,i,c] = sum_{h<Hi} w[b,i,h] * max(0, qI[b,i,h,:] . kI[b,c,:])
+ *
+ * for the entries c visible to query row i (position q_pos0 + i; visibility
+ * uses ratio m and window W as above).  idx[b,i,:] receives the
+ * k_eff = min(k, #visible) visible entries ranked first by (score descending,
+ * entry index ascending), written in ascending entry index and padded with -1.
+ * The ranking is decided on exact scores: a float32 MFMA pass screens the
+ * candidates and every candidate within the float32 error bound of the k-th
+ * score is re-scored in float64, so the selected set equals the one a float64
+ * evaluation of the formula selects.
+ *
+ *   qI  : [B, Tq, Hi, d_idx] dtype      kI : [B, N, d_idx] dtype
+ *   w   : [B, Tq, Hi]        float32    idx: [B, Tq, k] int32, written
+ *   ws  : device workspace of at least csa_index_topk_workspace_size() bytes
+ *         (may be NULL when that size is 0); its contents are scratch.
+ * Supported: Hi in {1, 2, 4, 8, 16}; d_idx in {64, 128}; 1 <= k <= 2048;
+ *            m >= 1; W >= 1; N >= 0.
+ */
+SHATTN_API size_t csa_index_topk_workspace_size(int B, int Tq, int N, int Hi, int d_idx, int k);
+SHATTN_API int csa_index_topk(const void* qI, const void* kI, const float* w, int32_t* idx, int B,
+                   int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k,
+                   int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Gated hybrid attention forward ([V4-blog] "SWA": the raw window and the
+ * compressed history enter one attention; [Tiny-R2] 3.1.2 / 3.2: three
+ * branches mixed by a per-head gate, order [HCA, CSA, SWA]).
+ *
+ * For query row i (position t) and head h (KV head g = h / (H/Hkv)), with
+ * logits sm_scale * q.k and one softmax per key set:
+ *   O_SWA = attention over the window rows of k_raw / v_raw
+ *   O_HCA = attention over the window rows + every visible HCA entry
+ *   O_CSA = attention over the window rows + the entries idx[b,i,:] (those
+ *           with 0 <= idx < N_csa; -1 marks padding)
+ *   out   = gates[h,0]*O_HCA + gates[h,1]*O_CSA + gates[h,2]*O_SWA
+ * A branch whose cache pointers are NULL is absent and contributes nothing.
+ * Raw K/V row r holds absolute position raw_pos0 + r; every window row the
+ * queries need must lie in [raw_pos0, raw_pos0 + Tr).
+ */
+typedef struct shattn_fwd_args {
+    int32_t struct_size; /* must equal sizeof(shattn_fwd_args) */
+    int32_t dtype;
+    int32_t B, Tq, H, Hkv, d, W;
+    float sm_scale;      /* 0 -> 1/sqrt(d) */
+    int32_t reserved0;   /* must be 0 */
+    int64_t q_pos0;
+    const void* q;       /* [B, Tq, H, d] */
+    void* out;           /* [B, Tq, H, d], written */
+    int64_t raw_pos0;
+    int32_t Tr;
+    int32_t m_hca;
+    const void* k_raw;   /* [B, Tr, Hkv, d] */
+    const void* v_raw;   /* [B, Tr, Hkv, d] */
+    int32_t N_hca;
+    int32_t N_csa;
+    const void* k_hca;   /* [B, N_hca, Hkv, d] or NULL (branch absent) */
+    const void* v_hca;
+    int32_t m_csa;       /* informational; selection already encodes visibility */
+    int32_t k;           /* entries per row in idx */
+    const void* k_csa;   /* [B, N_csa, Hkv, d] or NULL (branch absent) */
+    const void* v_csa;
+    const int32_t* idx;  /* [B, Tq, k] */
+    const float* gates;  /* [H, 3] float32 */
+} shattn_fwd_args;
+
+/* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the
+ * launch needs none). */
+SHATTN_API size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a);
+/* Supported: d in {64, 128}; H % Hkv == 0 with H/Hkv <= 64; W >= 1;
+ *            k <= 4096. */
+SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Message describing the calling thread's last failure ("" if none). */
+SHATTN_API const char* shattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYBRID_ATTN_H */

@@ -1,0 +1,252 @@
+"""Thin ctypes binding of libhybridattn.so (the C interface in include/hybrid_attn.h).
+
+Argument marshalling only: validate torch tensors, allocate outputs and
+workspace with torch on the caller's device, pass raw device pointers and the
+current HIP stream.  Every step of the computation runs in the HIP kernels;
+there is no fallback.  Importing this module does not load the library; the
+first call does, and raises if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+SHATTN_OK = 0
+SHATTN_EINVAL = -1
+SHATTN_EUNSUPPORTED = -2
+SHATTN_EWORKSPACE = -3
+SHATTN_EHIP = -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybridattn.so")
+
+EXPORTED = (
+    "hca_compress_kv",
+    "csa_index_topk_workspace_size",
+    "csa_index_topk",
+    "hybrid_sparse_attn_fwd_workspace_size",
+    "hybrid_sparse_attn_fwd",
+    "shattn_last_error",
+)
+
+
+class ShattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of shattn_fwd_args (same field order; C alignment rules)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("reserved0", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("q", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("raw_pos0", ctypes.c_int64),
+        ("Tr", ctypes.c_int32),
+        ("m_hca", ctypes.c_int32),
+        ("k_raw", ctypes.c_void_p),
+        ("v_raw", ctypes.c_void_p),
+        ("N_hca", ctypes.c_int32),
+        ("N_csa", ctypes.c_int32),
+        ("k_hca", ctypes.c_void_p),
+        ("v_hca", ctypes.c_void_p),
+        ("m_csa", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("k_csa", ctypes.c_void_p),
+        ("v_csa", ctypes.c_void_p),
+        ("idx", ctypes.c_void_p),
+        ("gates", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhybridattn.so and declare its signatures (raises if missing)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; run `python -m sparse_hybrid_attention_amd.build_lib` "
+                "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        lib.hca_compress_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.hca_compress_kv.restype = i32
+        lib.csa_index_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        lib.csa_index_topk_workspace_size.restype = sz
+        lib.csa_index_topk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32,
+                                       i32, i32, vp, sz, vp]
+        lib.csa_index_topk.restype = i32
+        lib.hybrid_sparse_attn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+        lib.hybrid_sparse_attn_fwd_workspace_size.restype = sz
+        lib.hybrid_sparse_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp, sz, vp]
+        lib.hybrid_sparse_attn_fwd.restype = i32
+        lib.shattn_last_error.argtypes = []
+        lib.shattn_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != SHATTN_OK:
+        msg = _lib.shattn_last_error().decode(errors="replace")
+        raise ShattnError(rc, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+# ---------------------------------------------------------------------------
+def hca_compress_kv(k, v, zk, zv, m: int, out=None):
+    """Block compression of K and V; returns (kc, vc) of shape [B, T//m, Hkv, d]."""
+    lib = load_library()
+    _need(k, "k")
+    _need(v, "v", k.dtype, k.device)
+    _need(zk, "zk", torch.float32, k.device)
+    _need(zv, "zv", torch.float32, k.device)
+    B, T, Hkv, d = k.shape
+    if v.shape != k.shape:
+        raise ValueError("k and v shapes differ")
+    N = T // m if m > 0 else 0
+    if out is None:
+        kc = torch.empty((B, N, Hkv, d), dtype=k.dtype, device=k.device)
+        vc = torch.empty((B, N, Hkv, d), dtype=k.dtype, device=k.device)
+    else:
+        kc, vc = out
+    _check(lib.hca_compress_kv(_ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(kc), _ptr(vc),
+                               B, T, Hkv, d, m, _dtype_code(k), _stream(k)))
+    return kc, vc
+
+
+def csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k) -> int:
+    return int(load_library().csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k))
+
+
+def csa_index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, out=None, ws=None):
+    """Per-query top-k CSA entries; returns int32 [B, Tq, k] (ascending, -1 padded)."""
+    lib = load_library()
+    _need(qI, "qI")
+    _need(kI, "kI", qI.dtype, qI.device)
+    _need(w, "w", torch.float32, qI.device)
+    B, Tq, Hi, d_idx = qI.shape
+    N = kI.shape[1]
+    if kI.shape[0] != B or kI.shape[2] != d_idx or tuple(w.shape) != (B, Tq, Hi):
+        raise ValueError("indexer shapes disagree")
+    idx = out if out is not None else torch.empty((B, Tq, k), dtype=torch.int32, device=qI.device)
+    nbytes = int(lib.csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k))
+    if ws is None and nbytes > 0:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=qI.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.csa_index_topk(_ptr(qI), _ptr(kI), _ptr(w), _ptr(idx), B, Tq, N, Hi, d_idx,
+                              int(q_pos0), m, W, k, _dtype_code(qI), _ptr(ws), ws_bytes,
+                              _stream(qI)))
+    return idx
+
+
+def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
+                  sm_scale=0.0, out=None):
+    """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
+
+    hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
+    Returns (FwdArgs, out, keepalive tuple)."""
+    _need(q, "q")
+    dev = q.device
+    _need(k_raw, "k_raw", q.dtype, dev)
+    _need(v_raw, "v_raw", q.dtype, dev)
+    _need(gates, "gates", torch.float32, dev)
+    B, Tq, H, d = q.shape
+    Tr, Hkv = k_raw.shape[1], k_raw.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    a = FwdArgs()
+    a.struct_size = ctypes.sizeof(FwdArgs)
+    a.dtype = _dtype_code(q)
+    a.B, a.Tq, a.H, a.Hkv, a.d, a.W = B, Tq, H, Hkv, d, W
+    a.sm_scale = sm_scale
+    a.q_pos0 = int(q_pos0)
+    a.q = q.data_ptr()
+    a.out = out.data_ptr()
+    a.raw_pos0 = int(raw_pos0)
+    a.Tr = Tr
+    a.k_raw, a.v_raw = k_raw.data_ptr(), v_raw.data_ptr()
+    keep = [q, k_raw, v_raw, gates, out]
+    if hca is not None:
+        kh, vh, mh = hca
+        _need(kh, "k_hca", q.dtype, dev)
+        _need(vh, "v_hca", q.dtype, dev)
+        a.k_hca, a.v_hca, a.m_hca, a.N_hca = kh.data_ptr(), vh.data_ptr(), int(mh), kh.shape[1]
+        keep += [kh, vh]
+    if csa is not None:
+        kc, vc, idx = csa
+        _need(kc, "k_csa", q.dtype, dev)
+        _need(vc, "v_csa", q.dtype, dev)
+        _need(idx, "idx", torch.int32, dev)
+        a.k_csa, a.v_csa, a.idx = kc.data_ptr(), vc.data_ptr(), idx.data_ptr()
+        a.N_csa, a.k = kc.shape[1], idx.shape[-1]
+        keep += [kc, vc, idx]
+    a.gates = gates.data_ptr()
+    return a, out, tuple(keep)
+
+
+def hybrid_sparse_attn_fwd_workspace_size(args: FwdArgs) -> int:
+    return int(load_library().hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(args)))
+
+
+def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None,
+                           csa=None, sm_scale=0.0, out=None, ws=None):
+    """Gated hybrid attention forward; returns out [B, Tq, H, d]."""
+    lib = load_library()
+    a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
+                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out)
+    nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
+    if ws is None and nbytes > 0:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.hybrid_sparse_attn_fwd(ctypes.byref(a), _ptr(ws), ws_bytes, _stream(q)))
+    return out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
