@@ -125,7 +125,10 @@ SHATTN_API int csa_index_topk(const void* qI, const void* kI, const float* w, in
  *   O_CSA = attention over the window rows + the entries idx[b,i,:] (those
  *           with 0 <= idx < N_csa; -1 marks padding)
  *   out   = gates[h,0]*O_HCA + gates[h,1]*O_CSA + gates[h,2]*O_SWA
- * A branch whose cache pointers are NULL is absent and contributes nothing.
+ * The HCA branch is present iff m_hca > 0 and the CSA branch iff k > 0; an
+ * absent branch contributes nothing (its gate column is ignored).  A present
+ * branch with no entries (N = 0, pointers may then be NULL) still contributes
+ * its window-only attention.  idx rows list distinct entries.
  * Raw K/V row r holds absolute position raw_pos0 + r; every window row the
  * queries need must lie in [raw_pos0, raw_pos0 + Tr).
  */
@@ -140,16 +143,16 @@ typedef struct shattn_fwd_args {
     void* out;           /* [B, Tq, H, d], written */
     int64_t raw_pos0;
     int32_t Tr;
-    int32_t m_hca;
+    int32_t m_hca;       /* HCA ratio; 0 = HCA branch absent */
     const void* k_raw;   /* [B, Tr, Hkv, d] */
     const void* v_raw;   /* [B, Tr, Hkv, d] */
     int32_t N_hca;
     int32_t N_csa;
-    const void* k_hca;   /* [B, N_hca, Hkv, d] or NULL (branch absent) */
+    const void* k_hca;   /* [B, N_hca, Hkv, d] */
     const void* v_hca;
     int32_t m_csa;       /* informational; selection already encodes visibility */
-    int32_t k;           /* entries per row in idx */
-    const void* k_csa;   /* [B, N_csa, Hkv, d] or NULL (branch absent) */
+    int32_t k;           /* entries per row in idx; 0 = CSA branch absent */
+    const void* k_csa;   /* [B, N_csa, Hkv, d] */
     const void* v_csa;
     const int32_t* idx;  /* [B, Tq, k] */
     const float* gates;  /* [H, 3] float32 */

@@ -1,0 +1,866 @@
+// Gated hybrid (HCA / CSA / SWA) attention forward on gfx950.
+//
+// Method ([V4-blog] "SWA": the recent raw window and the compressed history
+// enter one attention; [V4-blog] "HCA" / "CSA": all compressed entries vs the
+// top-k selected ones; [Tiny-R2] 3.1.2 / 3.2: three branches mixed by a
+// per-head gate; [V4-code] attention scale 1/sqrt(head_dim); [CS336] GQA/MQA
+// head sharing; FlashAttention-style online softmax).
+//
+// Design:
+//  * One workgroup = (sequence b, KV head g, a tile of QW query rows) with the
+//    G = H/Hkv query heads of that KV head: 16..64 "columns" (query, head),
+//    16 per wave.  All columns of a workgroup share the window and HCA keys,
+//    so those K/V tiles are staged once in LDS and read by every wave.
+//  * Transposed MFMA formulation: S^T = K Q^T (rows = 32 keys per chunk,
+//    columns = the wave's 16 (query, head) pairs) and O^T = V^T P^T.  The key
+//    rows of the two 16-row S^T tiles are interleaved so that the C layout of
+//    S^T is already the B-operand layout of P^T: no LDS round trip for P.
+//    V is stored transposed in LDS (written transposed while staging).
+//  * Three online-softmax states per column (window, HCA part, CSA part) in
+//    registers; the window state is shared by all branches and merged with
+//    the HCA / CSA states in the epilogue:
+//       O_SWA = win, O_HCA = merge(win, hca), O_CSA = merge(win, csa),
+//       out   = g0 O_HCA + g1 O_CSA + g2 O_SWA  (float32, rounded once).
+//  * CSA keys: when the selections of a tile's queries cover most visible
+//    entries (small N, G < 8) the CSA entries are attended densely with a
+//    per-(query, entry) selection bitmap in LDS ("dense-masked"); otherwise
+//    each wave gathers the selected rows of its queries into its own LDS
+//    tile ("gather").  Both give the same mathematical result.
+//  * A branch whose gate is 0 for every head of the workgroup is skipped.
+//  * Long key lists with few workgroups (decode) are split along the key
+//    list; each split writes (m, l, acc) partial states to the workspace and a
+//    combine kernel merges them in split order (deterministic).
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+
+namespace shattn {
+
+long long n_visible_host(long long t, int W, int m, int N) {
+    const long long s = t - W + 1;
+    if (s <= 0) return 0;
+    const long long n = s / m;
+    return n < N ? n : N;
+}
+
+namespace {
+
+constexpr int KT = 64;  // keys per shared LDS tile
+constexpr int KC = 32;  // keys per MFMA chunk
+constexpr int MAX_WAVES = 4;
+
+enum CsaMode { CSA_NONE = 0, CSA_DENSE = 1, CSA_GATHER = 2 };
+
+struct AttnParams {
+    const void* q;
+    void* out;
+    const void* k_raw;
+    const void* v_raw;
+    const void* k_hca;
+    const void* v_hca;
+    const void* k_csa;
+    const void* v_csa;
+    const int32_t* idx;
+    const float* gates;
+    float* ws;  // split partial states (split mode only)
+    long long q_pos0, raw_pos0;
+    int B, Tq, H, Hkv, G, W, Tr;
+    int m_hca, N_hca, N_csa, k;
+    float scale_log2;
+    int QW;        // query rows per workgroup
+    int nqt;       // query tiles per (b, g)
+    int csa_mode;
+    int bm_words;  // bitmap words per query (dense mode)
+    int lds_bm;    // byte offsets in dynamic LDS
+    int lds_gather;
+    int lds_gather_stride;
+    // split mode (0 = off): work item list over [window | HCA | CSA] keys
+    int nsplit;
+    int split_keys;
+    int n_win_items, n_hca_items;
+    int has_hca, has_csa;  // branch present (its gate column is used)
+};
+
+// ---------------------------------------------------------------- per-dtype MFMA
+template <typename T, int D> struct Tr;
+
+template <int D> struct Tr<bf16_t, D> {
+    static constexpr int KS = D / 32;     // S^T k-steps
+    static constexpr int DT = D / 16;     // O^T dim tiles
+    static constexpr int KPAD = D + 8;    // K tile row stride (elements)
+    static constexpr int VST = KT + 8;    // shared V^T row stride (elements)
+    static constexpr int GVST = KC + 8;   // gather V^T row stride
+    static constexpr int VEC = 8;
+    typedef bf16x8_t QF;
+
+    __device__ static void load_q(const bf16_t* qrow, int q4, bool ok, QF* qf) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ok) {
+                qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks + 8 * q4);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qf[ks][j] = (__bf16)0.0f;
+            }
+        }
+    }
+    // key offset (within the 32-key chunk) of this lane's score j
+    __device__ static int key_of(int q4, int j) { return 8 * q4 + j; }
+
+    // S^T for keys [c, c+32) of a K tile (row stride KPAD).  s[j] <-> key_of(q4, j).
+    __device__ static void scores(const bf16_t* Ks, int c, int lane, const QF* qf, float* s) {
+        const int rho = lane & 15, q4 = lane >> 4;
+        const int key0 = c + 8 * (rho >> 2) + (rho & 3);
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(Ks + key0 * KPAD + 32 * ks + 8 * q4);
+            const bf16x8_t a1 =
+                *reinterpret_cast<const bf16x8_t*>(Ks + (key0 + 4) * KPAD + 32 * ks + 8 * q4);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = s0[r];
+            s[4 + r] = s1[r];
+        }
+    }
+    // acc += V^T P^T for keys [c, c+32) of a V^T tile with row stride vst.
+    __device__ static void pv(const bf16_t* Vt, int vst, int c, int lane, const float* p,
+                              f32x4_t* acc) {
+        const int rho = lane & 15, q4 = lane >> 4;
+        bf16x8_t b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (__bf16)p[j];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Vt + (16 * dt + rho) * vst + c + 8 * q4);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[dt], 0, 0, 0);
+        }
+    }
+    // Stage rows into LDS: K row-major (stride KPAD), V transposed (stride vst).
+    // rows[kk] = element offset of key kk's row in k / v, or -1 (zero row).
+    __device__ static void stage(bf16_t* Ks, bf16_t* Vt, int vst, const bf16_t* __restrict__ kg,
+                                 const bf16_t* __restrict__ vg, const long long* rows, int nkeys,
+                                 int tid, int nthr) {
+        constexpr int PIECES = D / 8;
+        for (int u = tid; u < nkeys * PIECES; u += nthr) {
+            const int kk = u / PIECES, pc = u - kk * PIECES;
+            const long long r = rows[kk];
+            const uint4 val = r >= 0 ? ld16(kg + r + pc * 8) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(Ks + kk * KPAD + pc * 8) = val;
+        }
+        // V: units of 4 keys x 8 dims, written as 8 rows of 4 keys (8 bytes)
+        const int nquads = nkeys / 4;
+        for (int u = tid; u < nquads * PIECES; u += nthr) {
+            const int kq = u / PIECES, oc = u - kq * PIECES;
+            uint4 x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const long long r = rows[4 * kq + e];
+                x[e] = r >= 0 ? ld16(vg + r + oc * 8) : make_uint4(0, 0, 0, 0);
+            }
+            const uint32_t w[4][4] = {{x[0].x, x[0].y, x[0].z, x[0].w},
+                                      {x[1].x, x[1].y, x[1].z, x[1].w},
+                                      {x[2].x, x[2].y, x[2].z, x[2].w},
+                                      {x[3].x, x[3].y, x[3].z, x[3].w}};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int wi = j >> 1;
+                uint32_t lo, hi;
+                if ((j & 1) == 0) {
+                    lo = (w[0][wi] & 0xFFFFu) | (w[1][wi] << 16);
+                    hi = (w[2][wi] & 0xFFFFu) | (w[3][wi] << 16);
+                } else {
+                    lo = (w[0][wi] >> 16) | (w[1][wi] & 0xFFFF0000u);
+                    hi = (w[2][wi] >> 16) | (w[3][wi] & 0xFFFF0000u);
+                }
+                *reinterpret_cast<uint2*>(Vt + (oc * 8 + j) * vst + 4 * kq) = make_uint2(lo, hi);
+            }
+        }
+    }
+    __device__ static void store_out(bf16_t* o, const float* v4) {
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+    }
+    static constexpr int shared_bytes() { return (KT * KPAD + D * VST) * 2; }
+    static constexpr int gather_bytes() { return (KC * KPAD + D * GVST) * 2 + KC * 8; }
+};
+
+template <int D> struct Tr<float, D> {
+    static constexpr int KS = D / 4;
+    static constexpr int DT = D / 16;
+    static constexpr int KPAD = D + 4;
+    static constexpr int VST = KPAD;   // V kept row-major for fp32
+    static constexpr int GVST = KPAD;
+    static constexpr int VEC = 4;
+    typedef float QF;
+
+    __device__ static void load_q(const float* qrow, int q4, bool ok, QF* qf) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = ok ? qrow[4 * ks + q4] : 0.f;
+    }
+    __device__ static int key_of(int q4, int j) { return 16 * (j >> 2) + 4 * (j & 3) + q4; }
+
+    __device__ static void scores(const float* Ks, int c, int lane, const QF* qf, float* s) {
+        const int rho = lane & 15, q4 = lane >> 4;
+        const int key0 = c + 4 * (rho & 3) + (rho >> 2);
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[key0 * KPAD + 4 * ks + q4], qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(key0 + 16) * KPAD + 4 * ks + q4], qf[ks], s1,
+                                                      0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = s0[r];
+            s[4 + r] = s1[r];
+        }
+    }
+    __device__ static void pv(const float* Vs, int vst, int c, int lane, const float* p,
+                              f32x4_t* acc) {
+        const int rho = lane & 15, q4 = lane >> 4;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const float a = Vs[(c + 4 * st + q4) * vst + 16 * dt + rho];
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[st], acc[dt], 0, 0, 0);
+            }
+        }
+    }
+    __device__ static void stage(float* Ks, float* Vs, int vst, const float* __restrict__ kg,
+                                 const float* __restrict__ vg, const long long* rows, int nkeys,
+                                 int tid, int nthr) {
+        constexpr int PIECES = D / 4;
+        for (int u = tid; u < nkeys * PIECES; u += nthr) {
+            const int kk = u / PIECES, pc = u - kk * PIECES;
+            const long long r = rows[kk];
+            const uint4 a = r >= 0 ? ld16(kg + r + pc * 4) : make_uint4(0, 0, 0, 0);
+            const uint4 b = r >= 0 ? ld16(vg + r + pc * 4) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(Ks + kk * KPAD + pc * 4) = a;
+            *reinterpret_cast<uint4*>(Vs + kk * vst + pc * 4) = b;
+        }
+    }
+    __device__ static void store_out(float* o, const float* v4) {
+        *reinterpret_cast<float4*>(o) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+    }
+    static constexpr int shared_bytes() { return (KT * KPAD + KT * VST) * 4; }
+    static constexpr int gather_bytes() { return (KC * KPAD + KC * GVST) * 4 + KC * 8; }
+};
+
+// ---------------------------------------------------------------- online softmax
+template <int DT> struct State {
+    float m;  // running max (log2 domain), identical across the 4 lane groups of a column
+    float l;  // this lane's partial sum of weights
+    f32x4_t acc[DT];
+    __device__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+__device__ __forceinline__ float col_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float col_sum(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// One 32-key chunk: x[j] are log2-domain logits (-inf when masked).
+template <typename T, int D>
+__device__ __forceinline__ void softmax_pv(State<D / 16>& st, float* x, const T* Vt, int vst, int c,
+                                           int lane) {
+    float mloc = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, x[j]);
+    mloc = col_max(mloc);
+    const float mnew = fmaxf(st.m, mloc);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(x[j] - muse);
+        ps += p[j];
+    }
+    st.l = st.l * alpha + ps;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.acc[dt][r] *= alpha;
+    }
+    st.m = mnew;
+    Tr<T, D>::pv(Vt, vst, c, lane, p, st.acc);
+}
+
+__device__ __forceinline__ long long n_visible(long long t, int W, int m, int N) {
+    const long long s = t - W + 1;
+    if (s <= 0) return 0;
+    const long long n = s / m;
+    return n < N ? n : N;
+}
+
+// ---------------------------------------------------------------- main kernel
+template <typename T, int D>
+__global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) {
+    typedef Tr<T, D> TR;
+    constexpr int DT = D / 16;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* Ks = reinterpret_cast<T*>(smem);
+    T* Vs = Ks + KT * TR::KPAD;
+    __shared__ long long rows[KT];
+    __shared__ int sflag[4];
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, q4 = lane >> 4;
+
+    // work decomposition: (b, g, query tile) [, split item]
+    long long wg = blockIdx.x;
+    int item = 0;
+    if (p.nsplit) {
+        item = (int)(wg % p.nsplit);
+        wg /= p.nsplit;
+    }
+    const int qt = (int)(wg % p.nqt);
+    const long long bg = wg / p.nqt;
+    const int g = (int)(bg % p.Hkv);
+    const int b = (int)(bg / p.Hkv);
+    const int i0 = qt * p.QW;
+    const int nq = min(p.QW, p.Tq - i0);
+
+    const int col = wave * 16 + n;
+    const int ql = col / p.G;
+    const int hl = col - ql * p.G;
+    const bool valid = (ql < nq);
+    const int h = g * p.G + hl;
+    const int qi = i0 + (valid ? ql : 0);
+    const long long t = p.q_pos0 + qi;
+
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (((long long)b * p.Tq + qi) * p.H + (valid ? h : 0)) * D;
+    typename TR::QF qf[TR::KS];
+    TR::load_q(qrow, q4, valid, qf);
+
+    float gate[3] = {0.f, 0.f, 0.f};
+    if (valid) {
+        gate[0] = p.gates[h * 3 + 0];
+        gate[1] = p.gates[h * 3 + 1];
+        gate[2] = p.gates[h * 3 + 2];
+    }
+    if (tid < 4) sflag[tid] = 0;
+    __syncthreads();
+    if (valid && gate[0] != 0.f) sflag[0] = 1;
+    if (valid && gate[1] != 0.f) sflag[1] = 1;
+    __syncthreads();
+    const bool use_hca = p.has_hca && sflag[0] != 0;
+    const bool use_csa = p.has_csa && sflag[1] != 0;
+
+    const long long t_first = p.q_pos0 + i0;
+    const long long t_last = p.q_pos0 + i0 + nq - 1;
+    const long long win_lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;  // this column's window start
+    const T* kraw = reinterpret_cast<const T*>(p.k_raw);
+    const T* vraw = reinterpret_cast<const T*>(p.v_raw);
+
+    State<DT> sw, sh, sc;
+    sw.init();
+    sh.init();
+    sc.init();
+
+    // which key ranges this workgroup covers (split mode: one item)
+    bool do_win = true, do_hca = use_hca, do_csa = use_csa;
+    long long hca_lo = 0, hca_hi = -1, csa_lo = 0, csa_hi = -1;
+    if (p.nsplit) {
+        do_win = item < p.n_win_items;
+        do_hca = use_hca && item >= p.n_win_items && item < p.n_win_items + p.n_hca_items;
+        do_csa = use_csa && item >= p.n_win_items + p.n_hca_items;
+        if (do_hca) {
+            hca_lo = (long long)(item - p.n_win_items) * p.split_keys;
+            hca_hi = hca_lo + p.split_keys;
+        }
+        if (do_csa) {
+            csa_lo = (long long)(item - p.n_win_items - p.n_hca_items) * p.split_keys;
+            csa_hi = csa_lo + p.split_keys;
+        }
+    }
+
+    // ------------------------------------------------------------ window
+    if (do_win) {
+        const long long pos_lo = t_first - p.W + 1 > 0 ? t_first - p.W + 1 : 0;
+        const long long pos_hi = t_last + 1;
+        for (long long tp = pos_lo; tp < pos_hi; tp += KT) {
+            if (tid < KT) {
+                const long long pos = tp + tid;
+                const long long r = pos - p.raw_pos0;
+                rows[tid] = (pos < pos_hi && r >= 0 && r < p.Tr)
+                                ? ((((long long)b * p.Tr + r) * p.Hkv + g) * D)
+                                : -1;
+            }
+            __syncthreads();
+            TR::stage(Ks, Vs, TR::VST, kraw, vraw, rows, KT, tid, nthr);
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < KT; c += KC) {
+                float x[8];
+                bool any = false;
+                float s[8];
+                // visibility first: skip chunks no column of the wave can see
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const long long pos = tp + c + TR::key_of(q4, j);
+                    const bool vis = valid && pos >= win_lo && pos <= t;
+                    x[j] = vis ? 0.f : -INFINITY;
+                    any |= vis;
+                }
+                if (!__any(any)) continue;
+                TR::scores(Ks, c, lane, qf, s);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (x[j] == 0.f) ? s[j] * p.scale_log2 : -INFINITY;
+                softmax_pv<T, D>(sw, x, Vs, TR::VST, c, lane);
+            }
+            __syncthreads();
+        }
+    }
+
+    // ------------------------------------------------------------ HCA (dense)
+    if (do_hca) {
+        const long long nv = valid ? n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
+        long long e_hi = n_visible(t_last, p.W, p.m_hca, p.N_hca);
+        long long e_lo = 0;
+        if (p.nsplit) {
+            e_lo = hca_lo;
+            if (e_hi > hca_hi) e_hi = hca_hi;
+        }
+        const T* kh = reinterpret_cast<const T*>(p.k_hca);
+        const T* vh = reinterpret_cast<const T*>(p.v_hca);
+        for (long long e0 = e_lo; e0 < e_hi; e0 += KT) {
+            if (tid < KT) {
+                const long long e = e0 + tid;
+                rows[tid] = e < e_hi ? ((((long long)b * p.N_hca + e) * p.Hkv + g) * D) : -1;
+            }
+            __syncthreads();
+            TR::stage(Ks, Vs, TR::VST, kh, vh, rows, KT, tid, nthr);
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < KT; c += KC) {
+                float x[8], s[8];
+                bool any = false;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const long long e = e0 + c + TR::key_of(q4, j);
+                    const bool vis = e < nv && e < e_hi;
+                    x[j] = vis ? 0.f : -INFINITY;
+                    any |= vis;
+                }
+                if (!__any(any)) continue;
+                TR::scores(Ks, c, lane, qf, s);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (x[j] == 0.f) ? s[j] * p.scale_log2 : -INFINITY;
+                softmax_pv<T, D>(sh, x, Vs, TR::VST, c, lane);
+            }
+            __syncthreads();
+        }
+    }
+
+    // ------------------------------------------------------------ CSA
+    if (do_csa && p.csa_mode == CSA_DENSE) {
+        uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
+        __shared__ int emax_s;
+        for (int u = tid; u < p.QW * p.bm_words; u += nthr) bm[u] = 0u;
+        if (tid == 0) emax_s = -1;
+        __syncthreads();
+        for (int u = tid; u < nq * p.k; u += nthr) {
+            const int qq = u / p.k, j = u - qq * p.k;
+            const int e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
+            if (e >= 0 && e < p.N_csa) {
+                atomicOr(&bm[qq * p.bm_words + (e >> 5)], 1u << (e & 31));
+                atomicMax(&emax_s, e);
+            }
+        }
+        __syncthreads();
+        const long long e_hi = (long long)emax_s + 1;
+        const T* kc = reinterpret_cast<const T*>(p.k_csa);
+        const T* vc = reinterpret_cast<const T*>(p.v_csa);
+        for (long long e0 = 0; e0 < e_hi; e0 += KT) {
+            if (tid < KT) {
+                const long long e = e0 + tid;
+                rows[tid] = e < e_hi ? ((((long long)b * p.N_csa + e) * p.Hkv + g) * D) : -1;
+            }
+            __syncthreads();
+            TR::stage(Ks, Vs, TR::VST, kc, vc, rows, KT, tid, nthr);
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < KT; c += KC) {
+                if (e0 + c >= e_hi) break;
+                // the 32 entries [e0+c, e0+c+32) are one bitmap word
+                const uint32_t word = valid ? bm[ql * p.bm_words + (int)((e0 + c) >> 5)] : 0u;
+                if (!__any(word != 0u)) continue;
+                float x[8], s[8];
+                TR::scores(Ks, c, lane, qf, s);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool vis = (word >> TR::key_of(q4, j)) & 1u;
+                    x[j] = vis ? s[j] * p.scale_log2 : -INFINITY;
+                }
+                softmax_pv<T, D>(sc, x, Vs, TR::VST, c, lane);
+            }
+            __syncthreads();
+        }
+    } else if (do_csa && p.csa_mode == CSA_GATHER) {
+        // per-wave private tiles (aliasing the shared tiles, which are no longer used)
+        char* gbase = smem + p.lds_gather + wave * p.lds_gather_stride;
+        T* gK = reinterpret_cast<T*>(gbase);
+        T* gV = gK + KC * TR::KPAD;
+        long long* grows = reinterpret_cast<long long*>(gbase + p.lds_gather_stride - KC * 8);
+        const T* kc = reinterpret_cast<const T*>(p.k_csa);
+        const T* vc = reinterpret_cast<const T*>(p.v_csa);
+        const int c_first = wave * 16, c_last = wave * 16 + 15;
+        const int ql_a = c_first / p.G;
+        int ql_b = c_last / p.G;
+        if (ql_b > nq - 1) ql_b = nq - 1;
+        long long j_lo = 0, j_hi = p.k;
+        if (p.nsplit) {
+            j_lo = csa_lo;
+            j_hi = csa_hi < p.k ? csa_hi : p.k;
+        }
+        for (int qq = ql_a; qq <= ql_b; ++qq) {
+            const int32_t* sel = p.idx + ((long long)b * p.Tq + i0 + qq) * p.k;
+            for (long long j0 = j_lo; j0 < j_hi; j0 += KC) {
+                if (lane < KC) {
+                    const long long j = j0 + lane;
+                    const int e = j < j_hi ? sel[j] : -1;
+                    grows[lane] = (e >= 0 && e < p.N_csa) ? ((((long long)b * p.N_csa + e) * p.Hkv + g) * D) : -1;
+                }
+                wave_lds_sync();
+                bool anyv = lane < KC ? grows[lane] >= 0 : false;
+                if (!__any(anyv)) {
+                    wave_lds_sync();
+                    continue;
+                }
+                TR::stage(gK, gV, TR::GVST, kc, vc, grows, KC, lane, 64);
+                wave_lds_sync();
+                float x[8], s[8];
+                TR::scores(gK, 0, lane, qf, s);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bool vis = valid && ql == qq && grows[TR::key_of(q4, j)] >= 0;
+                    x[j] = vis ? s[j] * p.scale_log2 : -INFINITY;
+                }
+                softmax_pv<T, D>(sc, x, gV, TR::GVST, 0, lane);
+                wave_lds_sync();
+            }
+        }
+    }
+
+    // ------------------------------------------------------------ epilogue
+    if (p.nsplit) {
+        // partial state of this item for the wave's columns: [m, l, -, -, acc[D]] per column
+        // layout: ws[((wg * nsplit + item) * (MAX_WAVES*16) + col) * (D + 4) + ...]
+        State<DT>& st = do_win ? sw : (do_hca ? sh : sc);
+        const float ltot = col_sum(st.l);
+        float* dst = p.ws + (((long long)blockIdx.x) * (MAX_WAVES * 16) + col) * (D + 4);
+        if (q4 == 0) {
+            dst[0] = st.m;
+            dst[1] = ltot;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<float4*>(dst + 4 + 16 * dt + 4 * q4) =
+                make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+        return;
+    }
+    if (!valid) return;
+    const float lw = col_sum(sw.l);
+    const float lh = col_sum(sh.l);
+    const float lc = col_sum(sc.l);
+    float ah = 0.f, bh = 0.f, ac = 0.f, bc = 0.f;
+    if (use_hca) {
+        const float m = fmaxf(sw.m, sh.m);
+        const float wa = __builtin_amdgcn_exp2f(sw.m - m), wb = __builtin_amdgcn_exp2f(sh.m - m);
+        const float den = wa * lw + wb * lh;
+        ah = gate[0] * wa / den;
+        bh = gate[0] * wb / den;
+    }
+    if (use_csa) {
+        const float m = fmaxf(sw.m, sc.m);
+        const float wa = __builtin_amdgcn_exp2f(sw.m - m), wb = __builtin_amdgcn_exp2f(sc.m - m);
+        const float den = wa * lw + wb * lc;
+        ac = gate[1] * wa / den;
+        bc = gate[1] * wb / den;
+    }
+    const float aw = gate[2] / lw + ah + ac;  // coefficient of the window accumulator
+    T* orow = reinterpret_cast<T*>(p.out) + (((long long)b * p.Tq + qi) * p.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        float v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = aw * sw.acc[dt][r] + bh * sh.acc[dt][r] + bc * sc.acc[dt][r];
+        TR::store_out(orow + 16 * dt + 4 * q4, v4);
+    }
+}
+
+// Merge the split partial states: one thread per (column, 4 dims).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int DQ = D / 4;
+    const long long ncols_total = (long long)p.B * p.Hkv * p.nqt * (MAX_WAVES * 16);
+    if (gid >= ncols_total * DQ) return;
+    const int dq = (int)(gid % DQ);
+    const long long cg = gid / DQ;           // global column
+    const int col = (int)(cg % (MAX_WAVES * 16));
+    const long long wg = cg / (MAX_WAVES * 16);
+    const int qt = (int)(wg % p.nqt);
+    const long long bg = wg / p.nqt;
+    const int g = (int)(bg % p.Hkv);
+    const int b = (int)(bg / p.Hkv);
+    const int i0 = qt * p.QW;
+    const int nq = min(p.QW, p.Tq - i0);
+    const int ql = col / p.G, hl = col - (col / p.G) * p.G;
+    if (ql >= nq) return;
+    const int h = g * p.G + hl;
+    const int qi = i0 + ql;
+    const float g0 = p.gates[h * 3 + 0], g1 = p.gates[h * 3 + 1], g2 = p.gates[h * 3 + 2];
+    const bool use_hca = p.has_hca && p.n_hca_items > 0;
+    const bool use_csa = p.has_csa && p.nsplit > p.n_win_items + p.n_hca_items;
+    auto part = [&](int item) -> const float* {
+        return p.ws + ((wg * p.nsplit + item) * (MAX_WAVES * 16) + col) * (D + 4);
+    };
+    // merge a range of items into (m, l, acc4)
+    auto merge = [&](int it0, int it1, float& m, float& l, float* a) {
+        for (int it = it0; it < it1; ++it) {
+            const float* s = part(it);
+            const float mi = s[0], li = s[1];
+            if (mi == -INFINITY) continue;
+            const float4 ai = *reinterpret_cast<const float4*>(s + 4 + 4 * dq);
+            const float mn = fmaxf(m, mi);
+            const float x = __builtin_amdgcn_exp2f(m - mn), y = __builtin_amdgcn_exp2f(mi - mn);
+            l = l * x + li * y;
+            a[0] = a[0] * x + ai.x * y;
+            a[1] = a[1] * x + ai.y * y;
+            a[2] = a[2] * x + ai.z * y;
+            a[3] = a[3] * x + ai.w * y;
+            m = mn;
+        }
+    };
+    float mw = -INFINITY, lw = 0.f, aw[4] = {0.f, 0.f, 0.f, 0.f};
+    merge(0, p.n_win_items, mw, lw, aw);
+    float o[4];
+    for (int r = 0; r < 4; ++r) o[r] = g2 * aw[r] / lw;
+    if (use_hca && g0 != 0.f) {
+        float m = mw, l = lw, a[4] = {aw[0], aw[1], aw[2], aw[3]};
+        merge(p.n_win_items, p.n_win_items + p.n_hca_items, m, l, a);
+        for (int r = 0; r < 4; ++r) o[r] += g0 * a[r] / l;
+    }
+    if (use_csa && g1 != 0.f) {
+        float m = mw, l = lw, a[4] = {aw[0], aw[1], aw[2], aw[3]};
+        merge(p.n_win_items + p.n_hca_items, p.nsplit, m, l, a);
+        for (int r = 0; r < 4; ++r) o[r] += g1 * a[r] / l;
+    }
+    T* orow = reinterpret_cast<T*>(p.out) + (((long long)b * p.Tq + qi) * p.H + h) * D;
+    Tr<T, D>::store_out(orow + 4 * dq, o);
+}
+
+struct Plan {
+    AttnParams p;
+    int waves;
+    size_t lds;
+    long long grid;
+    size_t ws_bytes;
+};
+
+int make_plan(const shattn_fwd_args* a, Plan& pl) {
+    if (!a) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: null args");
+    if (a->struct_size != (int)sizeof(shattn_fwd_args))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: struct_size %d != %d", a->struct_size,
+                    (int)sizeof(shattn_fwd_args));
+    if (a->reserved0 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved0 must be 0");
+    if (a->dtype != SHATTN_DTYPE_BF16 && a->dtype != SHATTN_DTYPE_F32)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: unknown dtype %d", a->dtype);
+    if (a->B < 0 || a->Tq < 0 || a->H < 1 || a->Hkv < 1 || a->W < 1 || a->Tr < 0)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: bad sizes B=%d Tq=%d H=%d Hkv=%d W=%d Tr=%d",
+                    a->B, a->Tq, a->H, a->Hkv, a->W, a->Tr);
+    if (a->H % a->Hkv != 0)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: H=%d not a multiple of Hkv=%d", a->H, a->Hkv);
+    if (a->d != 64 && a->d != 128)
+        return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: d=%d (supported: 64, 128)", a->d);
+    const int G = a->H / a->Hkv;
+    if (G > 64) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: H/Hkv=%d > 64", G);
+    if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: sm_scale must be finite and >= 0");
+    if (a->q_pos0 < 0 || a->raw_pos0 < 0)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: negative position");
+    // a branch is present iff its ratio (HCA) / row width k (CSA) is positive
+    const bool has_hca = a->m_hca > 0;
+    const bool has_csa = a->k > 0;
+    if (a->m_hca < 0 || a->k < 0 || a->N_hca < 0 || a->N_csa < 0)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: negative m_hca / k / N_hca / N_csa");
+    if (has_hca && a->N_hca > 0 && (!a->k_hca || !a->v_hca))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: HCA branch needs k_hca and v_hca");
+    if (has_csa && ((a->N_csa > 0 && (!a->k_csa || !a->v_csa)) || (a->B > 0 && a->Tq > 0 && !a->idx)))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: CSA branch needs k_csa, v_csa and idx");
+    if (has_csa && a->k > 4096) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: k=%d > 4096", a->k);
+    AttnParams& p = pl.p;
+    p = AttnParams{};
+    p.B = a->B;
+    p.Tq = a->Tq;
+    p.H = a->H;
+    p.Hkv = a->Hkv;
+    p.G = G;
+    p.W = a->W;
+    p.Tr = a->Tr;
+    pl.ws_bytes = 0;
+    pl.grid = 0;
+    if (a->B == 0 || a->Tq == 0) return SHATTN_OK;
+    if (!a->q || !a->out || !a->k_raw || !a->v_raw || !a->gates)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: null q/out/k_raw/v_raw/gates");
+    if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->k_raw) || !aligned16(a->v_raw) ||
+        (has_hca && (!aligned16(a->k_hca) || !aligned16(a->v_hca))) ||
+        (has_csa && (!aligned16(a->k_csa) || !aligned16(a->v_csa) || (reinterpret_cast<uintptr_t>(a->idx) & 3))))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: tensors must be 16-byte aligned");
+    // every window row the queries need must be present
+    const long long lo_need = a->q_pos0 - a->W + 1 > 0 ? a->q_pos0 - a->W + 1 : 0;
+    const long long hi_need = a->q_pos0 + a->Tq;  // exclusive
+    if (lo_need < a->raw_pos0 || hi_need > a->raw_pos0 + a->Tr)
+        return fail(SHATTN_EINVAL,
+                    "hybrid_sparse_attn_fwd: window rows [%lld, %lld) not inside raw rows [%lld, %lld)",
+                    lo_need, hi_need, (long long)a->raw_pos0, (long long)a->raw_pos0 + a->Tr);
+    p.q = a->q;
+    p.out = a->out;
+    p.k_raw = a->k_raw;
+    p.v_raw = a->v_raw;
+    p.k_hca = has_hca ? a->k_hca : nullptr;
+    p.v_hca = has_hca ? a->v_hca : nullptr;
+    p.k_csa = has_csa ? a->k_csa : nullptr;
+    p.v_csa = has_csa ? a->v_csa : nullptr;
+    p.idx = has_csa ? a->idx : nullptr;
+    p.gates = a->gates;
+    p.q_pos0 = a->q_pos0;
+    p.raw_pos0 = a->raw_pos0;
+    p.has_hca = has_hca;
+    p.has_csa = has_csa;
+    p.m_hca = has_hca ? a->m_hca : 1;
+    p.N_hca = has_hca ? a->N_hca : 0;
+    p.N_csa = has_csa ? a->N_csa : 0;
+    p.k = has_csa ? a->k : 0;
+    const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.QW = G >= 64 ? 1 : 64 / G;
+    p.nqt = (a->Tq + p.QW - 1) / p.QW;
+    const int cols = std::min(p.QW, a->Tq) * G;
+    pl.waves = (cols + 15) / 16;
+    if (pl.waves > MAX_WAVES) pl.waves = MAX_WAVES;
+
+    const long long nwg = (long long)a->B * a->Hkv * p.nqt;
+    // split the key list when there are too few workgroups to fill the chip
+    long long keys = (long long)a->W;
+    long long nh_max = 0;
+    if (has_hca) nh_max = n_visible_host(a->q_pos0 + a->Tq - 1, a->W, a->m_hca, a->N_hca);
+    keys += nh_max;
+    if (has_csa) keys += a->k;
+    p.nsplit = 0;
+    if (nwg < 128 && keys > 1024) {
+        p.split_keys = 256;
+        p.n_win_items = 1;
+        p.n_hca_items = (int)((nh_max + p.split_keys - 1) / p.split_keys);
+        const int n_csa_items = has_csa ? (a->k + p.split_keys - 1) / p.split_keys : 0;
+        p.nsplit = p.n_win_items + p.n_hca_items + n_csa_items;
+        pl.ws_bytes = (size_t)nwg * p.nsplit * (MAX_WAVES * 16) * (a->d + 4) * sizeof(float);
+        pl.grid = nwg * p.nsplit;
+    } else {
+        pl.grid = nwg;
+    }
+
+    const bool bf = a->dtype == SHATTN_DTYPE_BF16;
+    const int esz = bf ? 2 : 4;
+    const int kpad = bf ? a->d + 8 : a->d + 4;
+    const size_t shared_b = bf ? (size_t)(KT * kpad + a->d * (KT + 8)) * esz
+                               : (size_t)(2 * KT * kpad) * esz;
+    const size_t gather_b = bf ? (size_t)(KC * kpad + a->d * (KC + 8)) * esz + KC * 8
+                               : (size_t)(2 * KC * kpad) * esz + KC * 8;
+    p.csa_mode = CSA_NONE;
+    size_t lds = shared_b;
+    if (has_csa) {
+        // dense-masked when the union of a tile's selections is likely dense
+        const long long span_q = (long long)std::min(p.QW, a->Tq);
+        const bool dense = p.nsplit == 0 && G < 8 && a->N_csa <= 4096 &&
+                           span_q * a->k >= a->N_csa / 2;
+        if (dense) {
+            p.csa_mode = CSA_DENSE;
+            p.bm_words = (a->N_csa + 31) / 32;
+            p.lds_bm = (int)shared_b;
+            lds = shared_b + (size_t)p.QW * p.bm_words * 4;
+        } else {
+            p.csa_mode = CSA_GATHER;
+            p.lds_gather = 0;
+            p.lds_gather_stride = (int)((gather_b + 15) / 16 * 16);
+            lds = std::max(lds, (size_t)p.lds_gather_stride * pl.waves);
+        }
+    }
+    pl.lds = lds;
+    return SHATTN_OK;
+}
+
+}  // namespace
+}  // namespace shattn
+
+using namespace shattn;
+
+extern "C" size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a) {
+    Plan pl;
+    if (make_plan(a, pl) != SHATTN_OK) return 0;
+    return pl.ws_bytes;
+}
+
+template <typename T, int D>
+static int launch_attn(Plan& pl, hipStream_t s) {
+    if (pl.lds > 64 * 1024) {
+        // dynamic LDS beyond 64 KiB must be opted into per kernel
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: %zu bytes of LDS not available: %s",
+                        pl.lds, hipGetErrorString(e));
+        }
+    }
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3((unsigned)pl.grid), dim3(pl.waves * 64), pl.lds, s,
+                       pl.p);
+    hipError_t le = hipGetLastError();
+    if (le != hipSuccess)
+        return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
+                    pl.grid, pl.waves * 64, pl.lds, hipGetErrorString(le));
+    if (!pl.p.nsplit) return SHATTN_OK;
+    const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * (MAX_WAVES * 16) * (D / 4);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       pl.p);
+    return check_launch("hybrid_sparse_attn_fwd (combine)");
+}
+
+extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+    Plan pl;
+    int rc = make_plan(a, pl);
+    if (rc != SHATTN_OK) return rc;
+    if (pl.grid == 0) return SHATTN_OK;
+    if (pl.ws_bytes > 0) {
+        if (!ws || ws_bytes < pl.ws_bytes)
+            return fail(SHATTN_EWORKSPACE, "hybrid_sparse_attn_fwd: workspace of %zu bytes needed, %zu given",
+                        pl.ws_bytes, ws ? ws_bytes : (size_t)0);
+        if (!aligned16(ws)) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: workspace must be 16-byte aligned");
+        pl.p.ws = reinterpret_cast<float*>(ws);
+    }
+    if (pl.grid > 2147483647LL) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: problem too large");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (a->dtype == SHATTN_DTYPE_BF16)
+        return a->d == 128 ? launch_attn<bf16_t, 128>(pl, s) : launch_attn<bf16_t, 64>(pl, s);
+    return a->d == 128 ? launch_attn<float, 128>(pl, s) : launch_attn<float, 64>(pl, s);
+}

@@ -1,0 +1,174 @@
+"""GPU parity of hybrid_sparse_attn_fwd against the oracle's gated attention.
+
+Compressed caches and CSA selections fed to the kernel come from the oracle
+(never from the HIP path), so this isolates the attention kernel."""
+import numpy as np
+import pytest
+
+import oracle as O
+from sparse_hybrid_attention_amd import binding, synth
+from gpu_util import assert_close, dev, host, lib
+
+pytestmark = pytest.mark.gpu
+
+
+def prefill_case(name, seed=0, gates=None, branches=("hca", "csa"), **over):
+    inp = synth.make_inputs(name, seed=seed, **over)
+    cfg = inp["cfg"]
+    dt = cfg["dtype"]
+    if gates is not None:
+        inp["gates"] = np.tile(np.asarray(gates, np.float32), (cfg["H"], 1))
+    hca = csa = None
+    if "hca" in branches and cfg.get("m_hca"):
+        kh, vh = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"], dt)
+        hca = (kh, vh, cfg["m_hca"])
+    if "csa" in branches and cfg.get("m_csa"):
+        kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"], dt)
+        idx = O.index_topk(inp["qI"], inp["kI"], inp["w"], 0, cfg["m_csa"], cfg["W"], cfg["k"], dt)
+        csa = (kc, vc, idx)
+    return inp, hca, csa
+
+
+def gpu_attn(inp, hca, csa, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v"):
+    cfg = inp["cfg"]
+    hca_d = None if hca is None else (dev(hca[0]), dev(hca[1]), hca[2])
+    csa_d = None if csa is None else (dev(csa[0]), dev(csa[1]), dev(csa[2]))
+    out = binding.hybrid_sparse_attn_fwd(dev(inp["q"]), dev(inp[k_raw]), dev(inp[v_raw]),
+                                         dev(inp["gates"]), cfg["W"], q_pos0=q_pos0,
+                                         raw_pos0=raw_pos0, hca=hca_d, csa=csa_d)
+    return host(out)
+
+
+def sample_rows(B, T, W, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, W - 2, W - 1, W, W + 1, 2 * W - 1, 2 * W, 63, 64, 65, T - 1, T - 2}
+    rows = set()
+    for b in range(B):
+        for t in fixed:
+            if 0 <= t < T:
+                rows.add((b, t))
+    while len(rows) < min(n + len(fixed) * B, B * T):
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, T))))
+    return sorted(rows)
+
+
+def check(inp, hca, csa, got, rows=None, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v", what=""):
+    cfg = inp["cfg"]
+    want = O.hybrid_attn_fwd(inp["q"], inp[k_raw], inp[v_raw], inp["gates"], W=cfg["W"],
+                             dtype=cfg["dtype"], q_pos0=q_pos0, raw_pos0=raw_pos0, hca=hca,
+                             csa=csa, rows=rows)
+    if rows is not None:
+        got = np.stack([got[b, i] for b, i in rows])
+    return assert_close(got, want, what)
+
+
+@pytest.mark.parametrize("gates", [[1, 0, 0], [0, 1, 0], [0, 0, 1], None])
+def test_tiny_fp32_all_rows(gates):
+    lib()
+    inp, hca, csa = prefill_case("tiny_fp32", gates=gates)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, what=f"tiny gates={gates}")
+
+
+@pytest.mark.parametrize("gates", [[1, 0, 0], [0, 1, 0], [0, 0, 1], None])
+def test_tinyr2_reduced(gates):
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", gates=gates, seed=1, B=2, T=640)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(2, 640, 128), what=f"tinyr2 gates={gates}")
+
+
+def test_gqa_hca_prefill_reduced():
+    lib()
+    inp, hca, csa = prefill_case("hca_prefill_32k", seed=2, T=2048)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(1, 2048, 128, n=64), what="hca gqa")
+
+
+def test_gqa_csa_gather_reduced():
+    lib()
+    inp, hca, csa = prefill_case("csa_prefill_128k", seed=3, T=4096, k=96)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(1, 4096, 128, n=64), what="csa gqa gather")
+
+
+def test_all_branches_gqa_ragged():
+    # G = 3 (non power of two), T not a multiple of any tile, small window
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=4, B=1, T=333, H=6, Hkv=2, d=64, W=16,
+                                 m_hca=8, k=12)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, what="ragged G=3")
+
+
+def test_short_sequence_and_window_one():
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=5, B=2, T=40, W=1, m_hca=4, k=3)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, what="W=1")
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=6, B=1, T=100, W=128)   # T < W
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, what="T<W")
+
+
+def test_csa_gather_many_heads_per_group():
+    # G = 16: one query per wave in the gather path
+    lib()
+    inp, hca, csa = prefill_case("csa_prefill_128k", seed=7, T=1024, H=32, Hkv=2, k=40)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(1, 1024, 128, n=48), what="G=16 gather")
+
+
+def decode_case(seed=0, **over):
+    inp = synth.make_inputs("decode_1m", seed=seed, **over)
+    cfg = inp["cfg"]
+    # selections from the oracle indexer over the whole cache
+    idx = O.index_topk(inp["qI"], inp["kI"], inp["w"], inp["q_pos0"], cfg["m_csa"], cfg["W"],
+                       cfg["k"], cfg["dtype"])
+    hca = (inp["k_hca"], inp["v_hca"], cfg["m_hca"])
+    csa = (inp["k_csa"], inp["v_csa"], idx)
+    return inp, hca, csa
+
+
+def test_decode_split_reduced():
+    lib()
+    inp, hca, csa = decode_case(seed=8, B=3, N_csa=4096, N_hca=2048, k=300)
+    got = gpu_attn(inp, hca, csa, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
+                   k_raw="k_win", v_raw="v_win")
+    check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+          v_raw="v_win", what="decode split")
+
+
+def test_decode_full_size():
+    lib()
+    inp, hca, csa = decode_case(seed=0)
+    got = gpu_attn(inp, hca, csa, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
+                   k_raw="k_win", v_raw="v_win")
+    check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+          v_raw="v_win", what="decode 1M")
+
+
+def test_attention_deterministic_and_constant_values():
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=9, B=1, T=512)
+    a = gpu_attn(inp, hca, csa)
+    b = gpu_attn(inp, hca, csa)
+    assert np.array_equal(a, b)
+    # V = constant row everywhere => out = (sum of gates) * row
+    row = synth.f32_to_bf16_bits(np.linspace(-1, 1, 128).astype(np.float32))
+    inp["v"] = np.ascontiguousarray(np.broadcast_to(row, inp["v"].shape))
+    cfg = inp["cfg"]
+    kh, vh = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"], cfg["dtype"])
+    kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"], cfg["dtype"])
+    got = gpu_attn(inp, (kh, vh, cfg["m_hca"]), (kc, vc, csa[2]))
+    vrow = O.bf16_bits_to_f64(row)
+    g = inp["gates"].astype(np.float64)
+    for b_, i in [(0, 0), (0, 200), (0, 511)]:
+        t = i
+        gsum = g[:, 2].copy()
+        if O.visible_count(t, cfg["W"], cfg["m_hca"], kh.shape[1]) >= 0:
+            gsum += g[:, 0]
+        gsum += g[:, 1]
+        want = gsum[:, None] * vrow[None, :]
+        # compressed constant rows round to the same bf16 value, so every branch averages `row`
+        np.testing.assert_allclose(O.bf16_bits_to_f64(got[b_, i]), want, rtol=2e-2, atol=2e-2)
