@@ -1,0 +1,991 @@
+// Lightning indexer + exact per-query top-k over the CSA entries on gfx950.
+//
+// Method ([V4-blog] "CSA": a lightning indexer scores the current query
+// against the compressed entries and the Top-K most relevant are kept;
+// [Tiny-R2] 3.2 importance_score / topk selection; [CS336] "Attention
+// Alternatives": DSA's lightning indexer):
+//     score(q, c) = sum_h w[q,h] * max(0, qI[q,h,:] . kI[c,:])
+// keep the k_eff = min(k, #visible) visible entries ranked by
+// (score descending, entry index ascending), output in ascending index.
+//
+// Design:
+//  * Scores are a dense contraction: MFMA with rows = (query, head) pairs and
+//    columns = 16 candidate entries per tile; the head sum (ReLU, w) happens in
+//    registers (for Hi = 4 a lane's four accumulator rows are exactly the four
+//    heads of one query).  Scores are never written to memory in prefill.
+//  * Each wave owns QPW queries and streams their visible entries in index
+//    order.  Per query an LDS buffer holds the candidates that can still be
+//    in the top-k; a candidate enters when its float32 score is >= tau.  When a
+//    buffer fills it is compacted (wave-level): an LDS radix select finds the
+//    k-th key, and everything below (k-th score - 2 delta) is dropped, where
+//    delta bounds |float32 score - exact score| for that query (MFMA
+//    accumulation error bound from the norms of the operands).  Ballot /
+//    popcount prefix sums keep every buffer in index order.
+//  * Final decision (exact): with T the float32 k-th score, entries above
+//    T + 2 delta are certainly selected, entries below T - 2 delta certainly
+//    not; the few in between are re-scored in float64 (products of the
+//    inputs are exact in float64) and ranked by (score desc, index asc).  The
+//    selected set therefore equals the float64 evaluation of the formula.
+//  * Decode (few query rows, long N): scoring is split over many workgroups,
+//    each writes its float32 scores and a lower bound on the global k-th
+//    score (its local ceil(k/chunks)-th score); a collect pass keeps the
+//    entries that can reach the top-k into per-chunk lists, and one wave per
+//    query runs the same buffer / exact-final logic over those lists.
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+
+namespace shattn {
+namespace {
+
+constexpr int WAVES = 4;
+constexpr int TILE = 16;  // candidate entries per MFMA tile
+constexpr int MAX_RT = 4; // row tiles per wave
+
+struct IdxParams {
+    const void* qI;
+    const void* kI;
+    const float* w;
+    int32_t* idx;
+    long long q_pos0;
+    int B, Tq, N, k, m, W;
+    int cap;   // candidate buffer entries per query
+    int mcap;  // band list capacity
+    int qpw;   // queries per wave
+    int nqt;   // query tiles (of WAVES*qpw queries) per sequence
+    int wave_stride;  // LDS bytes per wave (prefill), multiple of 16
+    float err_c;  // delta = err_c * sum_h |w_h| ||q_h|| * max ||k||
+    // split (decode) pipeline workspace
+    float* scores;      // [rows, N] float32 scores
+    float* chunk_lb;    // [rows, nchunks] chunk_k-th largest score of the chunk
+    float* chunk_kmax;  // [rows, nchunks] max ||k||^2 over the chunk
+    float* row_qn;      // [rows] sum_h |w_h| ||q_h||
+    uint32_t* lists;    // [rows, nchunks, list_cap] keys
+    int32_t* list_idx;  // [rows, nchunks, list_cap] entries
+    int32_t* list_cnt;  // [rows, nchunks] (may exceed list_cap: then the
+                        //  chunk is re-read from `scores`)
+    int nchunks, chunk, list_cap, chunk_k;
+};
+
+// ----------------------------------------------------------- key encoding
+// order-preserving map float32 -> uint32 (-0.0 and +0.0 share one key)
+__device__ __forceinline__ uint32_t fkey(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f(uint32_t k) {
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+    const int l = __lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ long long n_visible(long long t, int W, int m, int N) {
+    const long long s = t - W + 1;
+    if (s <= 0) return 0;
+    const long long n = s / m;
+    return n < N ? n : N;
+}
+
+// ----------------------------------------------------------- wave selection
+struct WaveBuf {
+    uint32_t* keys;  // [cap]
+    int32_t* ids;    // [cap]
+    uint32_t* hist;  // [256]
+    int32_t* mpos;   // [mcap]
+    double* mex;     // [mcap]
+};
+
+// k-th largest key among keys[0..cnt), 1 <= kk <= cnt.  *n_gt = #keys > result.
+__device__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
+    const int lane = __lane_id();
+    uint32_t prefix = 0u, pmask = 0u;
+    int want = kk;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+        wave_lds_sync();
+        for (int e = lane; e < cnt; e += 64) {
+            const uint32_t key = keys[e];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        wave_lds_sync();
+        const uint32_t c0 = hist[lane * 4 + 0], c1 = hist[lane * 4 + 1];
+        const uint32_t c2 = hist[lane * 4 + 2], c3 = hist[lane * 4 + 3];
+        const int mine = (int)(c0 + c1 + c2 + c3);
+        int suf = mine;  // sum over lanes >= this lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_down(suf, off);
+            if (lane + off < 64) suf += o;
+        }
+        const int above = suf - mine;  // sum over bins of higher lanes
+        int bin = -1, cnt_above = 0;
+        if (above < want && want <= suf) {
+            int acc = above;
+            if (acc + (int)c3 >= want) { bin = lane * 4 + 3; cnt_above = acc; }
+            else {
+                acc += c3;
+                if (acc + (int)c2 >= want) { bin = lane * 4 + 2; cnt_above = acc; }
+                else {
+                    acc += c2;
+                    if (acc + (int)c1 >= want) { bin = lane * 4 + 1; cnt_above = acc; }
+                    else { acc += c1; bin = lane * 4 + 0; cnt_above = acc; }
+                }
+            }
+        }
+        const unsigned long long who = __ballot(bin >= 0);
+        const int src = __ffsll((long long)who) - 1;
+        const int b = __shfl(bin, src);
+        const int ca = __shfl(cnt_above, src);
+        prefix |= ((uint32_t)b) << shift;
+        pmask |= 255u << shift;
+        want -= ca;
+        wave_lds_sync();
+    }
+    *n_gt = kk - want;
+    return prefix;
+}
+
+// Stable in-place compaction: keep entries with key >= lo.  Returns new count.
+__device__ int compact_ge(uint32_t* keys, int32_t* ids, int cnt, uint32_t lo) {
+    const int lane = __lane_id();
+    int out = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int e = base + lane;
+        uint32_t key = 0u;
+        int32_t id = 0;
+        bool keep = false;
+        if (e < cnt) {
+            key = keys[e];
+            id = ids[e];
+            keep = key >= lo;
+        }
+        const unsigned long long msk = __ballot(keep);
+        wave_lds_sync();
+        if (keep) {
+            const int pos = out + __popcll(msk & lanemask_lt());
+            keys[pos] = key;
+            ids[pos] = id;
+        }
+        out += __popcll(msk);
+        wave_lds_sync();
+    }
+    return out;
+}
+
+// Stable: keep entries with key > kth and the first `need` entries with key == kth.
+__device__ int compact_topk(uint32_t* keys, int32_t* ids, int cnt, uint32_t kth, int need) {
+    const int lane = __lane_id();
+    int out = 0, eq_seen = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int e = base + lane;
+        uint32_t key = 0u;
+        int32_t id = 0;
+        bool gt = false, eq = false;
+        if (e < cnt) {
+            key = keys[e];
+            id = ids[e];
+            gt = key > kth;
+            eq = key == kth;
+        }
+        const unsigned long long meq = __ballot(eq);
+        const bool keep = gt || (eq && eq_seen + __popcll(meq & lanemask_lt()) < need);
+        const unsigned long long msk = __ballot(keep);
+        wave_lds_sync();
+        if (keep) {
+            const int pos = out + __popcll(msk & lanemask_lt());
+            keys[pos] = key;
+            ids[pos] = id;
+        }
+        out += __popcll(msk);
+        eq_seen += __popcll(meq);
+        wave_lds_sync();
+    }
+    return out;
+}
+
+// Streaming compaction of a full buffer.  Returns the new count; *tau_key is the
+// new insertion threshold (keys >= tau_key may enter).
+__device__ int compact_stream(WaveBuf& wb, int cnt, int kk, float delta, int cap, int slack,
+                              uint32_t* tau_key) {
+    int n_gt;
+    const uint32_t kth = radix_kth(wb.keys, cnt, kk, wb.hist, &n_gt);
+    const float T = key_f(kth);
+    const uint32_t lo = fkey(T - 2.0f * delta);
+    int n = compact_ge(wb.keys, wb.ids, cnt, lo);
+    if (n > cap - slack) {
+        // more near-ties than the buffer holds: fall back to the float32 order
+        n = compact_topk(wb.keys, wb.ids, n, kth, kk - n_gt);
+        *tau_key = kth == 0xFFFFFFFFu ? kth : kth + 1u;
+        return n;
+    }
+    *tau_key = lo;
+    return n;
+}
+
+// Exact (float64) score of entry c for query row (b, i).
+template <typename T, int HI, int DI>
+__device__ double exact_score(const T* __restrict__ qrow /* [HI][DI] */, const T* __restrict__ krow,
+                              const float* __restrict__ wrow) {
+    double s = 0.0;
+    for (int h = 0; h < HI; ++h) {
+        double dot = 0.0;
+        for (int e = 0; e < DI; e += 16 / (int)sizeof(T)) {
+            float qa[8], ka[8];
+            Elem<T>::unpack(ld16(qrow + h * DI + e), qa);
+            Elem<T>::unpack(ld16(krow + e), ka);
+#pragma unroll
+            for (int j = 0; j < 16 / (int)sizeof(T); ++j) dot += (double)qa[j] * (double)ka[j];
+        }
+        s += (double)wrow[h] * (dot > 0.0 ? dot : 0.0);
+    }
+    return s;
+}
+
+// Final exact selection of one query and output of its idx row.
+template <typename T, int HI, int DI>
+__device__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k, float delta, int mcap,
+                             const T* __restrict__ qrow, const T* __restrict__ kI_b,
+                             const float* __restrict__ wrow, int32_t* __restrict__ out_row) {
+    const int lane = __lane_id();
+    if (cnt > k_eff) {
+        int n_gt;
+        const uint32_t kth = radix_kth(wb.keys, cnt, k_eff, wb.hist, &n_gt);
+        const float Tf = key_f(kth);
+        const uint32_t hi = fkey(Tf + 2.0f * delta);
+        const uint32_t lo = fkey(Tf - 2.0f * delta);
+        // D = key > hi (certain), M = lo <= key <= hi (band)
+        int nD = 0, nM = 0;
+        for (int base = 0; base < cnt; base += 64) {
+            const int e = base + lane;
+            const uint32_t key = e < cnt ? wb.keys[e] : 0u;
+            const bool inD = e < cnt && key > hi;
+            const bool inM = e < cnt && key >= lo && key <= hi;
+            const unsigned long long mm = __ballot(inM);
+            if (inM) {
+                const int pos = nM + __popcll(mm & lanemask_lt());
+                if (pos < mcap) wb.mpos[pos] = e;
+            }
+            nD += __popcll(__ballot(inD));
+            nM += __popcll(mm);
+        }
+        wave_lds_sync();
+        const int need = k_eff - nD;
+        if (nM <= mcap) {
+            for (int j = lane; j < nM; j += 64) {
+                const int e = wb.mpos[j];
+                wb.mex[j] = exact_score<T, HI, DI>(qrow, kI_b + (long long)wb.ids[e] * DI, wrow);
+            }
+            wave_lds_sync();
+            // rank within M by (exact desc, index asc); keep the first `need`
+            for (int j = lane; j < nM; j += 64) {
+                const double ex = wb.mex[j];
+                const int id = wb.ids[wb.mpos[j]];
+                int rank = 0;
+                for (int y = 0; y < nM; ++y) {
+                    const double ey = wb.mex[y];
+                    rank += (ey > ex) || (ey == ex && wb.ids[wb.mpos[y]] < id);
+                }
+                wb.keys[wb.mpos[j]] = rank < need ? 0xFFFFFFFFu : 0u;
+            }
+            wave_lds_sync();
+            cnt = compact_ge(wb.keys, wb.ids, cnt, hi == 0xFFFFFFFFu ? hi : hi + 1u);
+        } else {
+            // more entries in the error band than the band list holds: decide
+            // on float32 scores (index tie-break)
+            cnt = compact_topk(wb.keys, wb.ids, cnt, kth, k_eff - n_gt);
+        }
+    }
+    // buffer is in ascending entry order: write it, pad with -1
+    for (int j = lane; j < k; j += 64) out_row[j] = j < cnt ? wb.ids[j] : -1;
+    wave_lds_sync();
+}
+
+// ----------------------------------------------------------- MFMA scoring
+template <typename T, int DI> struct IdxMma;
+template <int DI> struct IdxMma<bf16_t, DI> {
+    static constexpr int KS = DI / 32;
+    typedef bf16x8_t F;
+    __device__ static void load_a(const bf16_t* row, bool ok, int q4, F* a) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ok) a[ks] = *reinterpret_cast<const bf16x8_t*>(row + 32 * ks + 8 * q4);
+            else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a[ks][j] = (__bf16)0.0f;
+            }
+        }
+    }
+    // partial squared norm of this lane's slice
+    __device__ static float sq(const F* a) {
+        float s = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = (float)a[ks][j];
+                s = fmaf(x, x, s);
+            }
+        return s;
+    }
+    __device__ static f32x4_t mma(const F* a, const F* b) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b[ks], c, 0, 0, 0);
+        return c;
+    }
+};
+template <int DI> struct IdxMma<float, DI> {
+    static constexpr int KS = DI / 4;
+    typedef float F;
+    __device__ static void load_a(const float* row, bool ok, int q4, F* a) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = ok ? row[4 * ks + q4] : 0.f;
+    }
+    __device__ static float sq(const F* a) {
+        float s = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = fmaf(a[ks], a[ks], s);
+        return s;
+    }
+    __device__ static f32x4_t mma(const F* a, const F* b) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], b[ks], c, 0, 0, 0);
+        return c;
+    }
+};
+
+// Scores of the lane's query slots from one 16-row accumulator tile.
+// Returns the number of slots; s[j], qs[j] = query index within the tile, own[j].
+template <int HI>
+__device__ __forceinline__ int tile_scores(const f32x4_t& c, const float* wr, int q4, float* s, int* qs,
+                                           bool* own) {
+    if constexpr (HI == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = wr[r] * fmaxf(c[r], 0.f);
+            qs[r] = 4 * q4 + r;
+            own[r] = true;
+        }
+        return 4;
+    } else if constexpr (HI == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            s[j] = wr[2 * j] * fmaxf(c[2 * j], 0.f) + wr[2 * j + 1] * fmaxf(c[2 * j + 1], 0.f);
+            qs[j] = 2 * q4 + j;
+            own[j] = true;
+        }
+        return 2;
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += wr[r] * fmaxf(c[r], 0.f);
+        if constexpr (HI == 4) {
+            s[0] = part;
+            qs[0] = q4;
+            own[0] = true;
+        } else if constexpr (HI == 8) {
+            const float other = __shfl_xor(part, 16);
+            s[0] = (q4 & 1) ? other + part : part + other;
+            qs[0] = q4 >> 1;
+            own[0] = (q4 & 1) == 0;
+        } else {
+            const int base = __lane_id() & 15;
+            const float p0 = __shfl(part, base), p1 = __shfl(part, base + 16);
+            const float p2 = __shfl(part, base + 32), p3 = __shfl(part, base + 48);
+            s[0] = (p0 + p1) + (p2 + p3);
+            qs[0] = 0;
+            own[0] = q4 == 0;
+        }
+        return 1;
+    }
+}
+
+// ----------------------------------------------------------- prefill kernel
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) {
+    typedef IdxMma<T, DI> MM;
+    constexpr int QPT = 16 / HI;  // queries per row tile
+    constexpr int SLOTS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4;
+    const int qpw = p.qpw, cap = p.cap, mcap = p.mcap;
+    const int RT = qpw / QPT;
+
+    // per-wave LDS: keys[qpw][cap] ids[qpw][cap] hist[256] mpos[mcap] mex[mcap] qn[qpw]
+    char* base = smem + (size_t)wave * p.wave_stride;
+    uint32_t* keys_all = reinterpret_cast<uint32_t*>(base);
+    int32_t* ids_all = reinterpret_cast<int32_t*>(base + 4ull * qpw * cap);
+    WaveBuf wb;
+    wb.hist = reinterpret_cast<uint32_t*>(base + 8ull * qpw * cap);
+    wb.mex = reinterpret_cast<double*>(base + 8ull * qpw * cap + 1024);
+    wb.mpos = reinterpret_cast<int32_t*>(base + 8ull * qpw * cap + 1024 + 8ull * mcap);
+    float* qn = reinterpret_cast<float*>(base + 8ull * qpw * cap + 1024 + 12ull * mcap);
+
+    const int qt = blockIdx.x % p.nqt;
+    const int b = blockIdx.x / p.nqt;
+    const int q0 = (qt * WAVES + wave) * qpw;  // first query row of this wave
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
+
+    // ---- A fragments (rows = (query, head)), weights, norms
+    typename MM::F a[MAX_RT][MM::KS];
+    float wr[MAX_RT][4];
+    const int rho = lane & 15;
+#pragma unroll
+    for (int rt = 0; rt < MAX_RT; ++rt) {
+        const int qw = rt * QPT + rho / HI, hh = rho % HI;
+        const int i = q0 + qw;
+        const bool ok = rt < RT && qw < qpw && i < p.Tq;
+        MM::load_a(qI + (((long long)b * p.Tq + (ok ? i : 0)) * HI + hh) * DI, ok, q4, a[rt]);
+        // weights of this lane's accumulator rows 4*q4 + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * q4 + r;
+            const int qr = rt * QPT + row / HI, hr = row % HI;
+            const int ir = q0 + qr;
+            wr[rt][r] = (rt < RT && qr < qpw && ir < p.Tq) ? p.w[((long long)b * p.Tq + ir) * HI + hr] : 0.f;
+        }
+        // sum_h |w_h| ||q_h|| per query (row norms combined in fixed head order)
+        float n2 = MM::sq(a[rt]);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        if (rt < RT) {
+            // lane rho (q4 == 0) holds ||row rho||^2; gather the HI rows of each query
+            const int qsl = lane < QPT ? lane : 0;  // lane j < QPT finishes query slot j
+            float acc = 0.f;
+            for (int h = 0; h < HI; ++h) {
+                const float nr = __shfl(n2, qsl * HI + h);
+                const int ir = q0 + rt * QPT + qsl;
+                const float wv = (ir < p.Tq && rt * QPT + qsl < qpw)
+                                     ? p.w[((long long)b * p.Tq + ir) * HI + h] : 0.f;
+                acc += fabsf(wv) * sqrtf(nr);
+            }
+            if (lane < QPT && rt * QPT + lane < qpw) qn[rt * QPT + lane] = acc;
+        }
+    }
+
+    // ---- per (row tile, slot) state of the lane's queries
+    int cnt[MAX_RT][4];
+    uint32_t tau[MAX_RT][4];
+    long long nv[MAX_RT][4];
+    long long nv_max = 0;
+#pragma unroll
+    for (int rt = 0; rt < MAX_RT; ++rt)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            cnt[rt][sl] = 0;
+            tau[rt][sl] = 0u;
+            int qw;
+            if (HI == 1) qw = 4 * q4 + sl;
+            else if (HI == 2) qw = 2 * q4 + sl;
+            else if (HI == 4) qw = q4;
+            else if (HI == 8) qw = q4 >> 1;
+            else qw = 0;
+            qw += rt * QPT;
+            const int i = q0 + qw;
+            const bool ok = rt < RT && sl < SLOTS && qw < qpw && i < p.Tq;
+            nv[rt][sl] = ok ? n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
+            nv_max = nv[rt][sl] > nv_max ? nv[rt][sl] : nv_max;
+        }
+    // wave-wide maximum of visible entries
+    {
+        long long v = nv_max;
+        for (int off = 32; off > 0; off >>= 1) {
+            const long long o = __shfl_xor(v, off);
+            v = o > v ? o : v;
+        }
+        nv_max = v;
+    }
+    float kmax2 = 0.f;
+    wave_lds_sync();
+
+    // ---- stream the candidates in index order
+    for (long long c0 = 0; c0 < nv_max; c0 += TILE) {
+        const long long c = c0 + rho;
+        typename MM::F bf[MM::KS];
+        MM::load_a(kI_b + (c < p.N ? c : 0) * DI, c < p.N, q4, bf);
+        float n2 = MM::sq(bf);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        kmax2 = fmaxf(kmax2, n2);
+#pragma unroll
+        for (int rt = 0; rt < MAX_RT; ++rt) {
+            if (rt >= RT) break;
+            const f32x4_t acc = MM::mma(a[rt], bf);
+            float s[4];
+            int qs[4];
+            bool own[4];
+            const int ns = tile_scores<HI>(acc, wr[rt], q4, s, qs, own);
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                if (sl >= ns) break;
+                const uint32_t key = fkey(s[sl]);
+                const bool ins = own[sl] && c < nv[rt][sl] && key >= tau[rt][sl];
+                const unsigned long long msk = __ballot(ins);
+                const unsigned long long gm = msk & (0xFFFFull << (16 * q4));
+                const int qw = rt * QPT + qs[sl];
+                if (ins) {
+                    const int pos = cnt[rt][sl] + __popcll(gm & lanemask_lt());
+                    keys_all[qw * cap + pos] = key;
+                    ids_all[qw * cap + pos] = (int32_t)c;
+                }
+                cnt[rt][sl] += __popcll(gm);
+            }
+        }
+        // compaction of full buffers
+#pragma unroll
+        for (int rt = 0; rt < MAX_RT; ++rt) {
+            if (rt >= RT) break;
+#pragma unroll
+            for (int sl = 0; sl < SLOTS; ++sl) {
+                int qw_l;
+                if (HI == 1) qw_l = 4 * q4 + sl;
+                else if (HI == 2) qw_l = 2 * q4 + sl;
+                else if (HI == 4) qw_l = q4;
+                else if (HI == 8) qw_l = q4 >> 1;
+                else qw_l = 0;
+                const bool owner = (HI <= 4) || (HI == 8 ? (q4 & 1) == 0 : q4 == 0);
+                const bool full = owner && cnt[rt][sl] > cap - TILE;
+                unsigned long long fm = __ballot(full);
+                if (fm == 0ull) continue;
+                wave_lds_sync();
+                const float delta = p.err_c * sqrtf(kmax2);
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    if (((fm >> (16 * g4)) & 0xFFFFull) == 0ull) continue;
+                    const int src = 16 * g4;
+                    const int qw = rt * QPT + __shfl(qw_l, src);
+                    const int cq = __shfl(cnt[rt][sl], src);
+                    const long long nvq = __shfl(nv[rt][sl], src);
+                    WaveBuf q = wb;
+                    q.keys = keys_all + qw * cap;
+                    q.ids = ids_all + qw * cap;
+                    const int kk = (int)std::min<long long>(p.k, nvq);
+                    uint32_t tk;
+                    const int nc = compact_stream(q, cq, kk, delta * qn[qw], cap, TILE, &tk);
+                    if (q4 == g4) {
+                        cnt[rt][sl] = nc;
+                        tau[rt][sl] = tk;
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- final exact selection per query, output
+    const float delta0 = p.err_c * sqrtf(kmax2);
+#pragma unroll
+    for (int rt = 0; rt < MAX_RT; ++rt) {
+        if (rt >= RT) break;
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            for (int g4 = 0; g4 < 4; ++g4) {
+                if (HI == 8 && (g4 & 1)) continue;
+                if (HI == 16 && g4 != 0) continue;
+                int qw_l;
+                if (HI == 1) qw_l = 4 * g4 + sl;
+                else if (HI == 2) qw_l = 2 * g4 + sl;
+                else if (HI == 4) qw_l = g4;
+                else if (HI == 8) qw_l = g4 >> 1;
+                else qw_l = 0;
+                const int qw = rt * QPT + qw_l;
+                const int i = q0 + qw;
+                if (qw >= qpw || i >= p.Tq) continue;
+                const int src = 16 * g4;
+                const int cq = __shfl(cnt[rt][sl], src);
+                const long long nvq = __shfl(nv[rt][sl], src);
+                WaveBuf q = wb;
+                q.keys = keys_all + qw * cap;
+                q.ids = ids_all + qw * cap;
+                const int k_eff = (int)std::min<long long>(p.k, nvq);
+                const long long row = (long long)b * p.Tq + i;
+                final_select<T, HI, DI>(q, cq, k_eff, p.k, delta0 * qn[qw], mcap, qI + row * HI * DI, kI_b,
+                                        p.w + row * HI, p.idx + row * p.k);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- split pipeline
+// S1: one wave per (query row, chunk of entries): float32 scores of the row
+// against the chunk (written to the workspace), the chunk's chunk_k-th largest
+// score and the chunk's max ||k||^2.  If every chunk holds >= chunk_k visible
+// entries and nchunks * chunk_k >= k, the minimum over chunks of those scores
+// is a lower bound of the row's float32 k-th score.
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
+    typedef IdxMma<T, DI> MM;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t* skeys = reinterpret_cast<uint32_t*>(smem);          // [chunk]
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + 4ull * p.chunk);
+    const int lane = threadIdx.x, q4 = lane >> 4, rho = lane & 15;
+    const int chunk_id = blockIdx.x % p.nchunks;
+    const long long row = blockIdx.x / p.nchunks;
+    const long long b = row / p.Tq, i = row % p.Tq;
+    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const long long c_lo = (long long)chunk_id * p.chunk;
+    const long long c_hi = std::min<long long>(c_lo + p.chunk, nvq);
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
+
+    // A rows: the HI heads of this query (rows >= HI are zero)
+    typename MM::F a[MM::KS];
+    MM::load_a(qI + (row * HI + (rho < HI ? rho : 0)) * DI, rho < HI, q4, a);
+    float wr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int rr = 4 * q4 + r;
+        wr[r] = rr < HI ? p.w[row * HI + rr] : 0.f;
+    }
+    if (chunk_id == 0) {
+        float n2 = MM::sq(a);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        float acc = 0.f;
+        for (int h = 0; h < HI; ++h) acc += fabsf(p.w[row * HI + h]) * sqrtf(__shfl(n2, h));
+        if (lane == 0) p.row_qn[row] = acc;
+    }
+    float kmax2 = 0.f;
+    for (long long c0 = c_lo; c0 < c_hi; c0 += TILE) {
+        const long long c = c0 + rho;
+        const bool cok = c < c_hi;
+        typename MM::F bf[MM::KS];
+        MM::load_a(kI_b + (cok ? c : 0) * DI, cok, q4, bf);
+        float n2 = MM::sq(bf);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        kmax2 = fmaxf(kmax2, n2);
+        const f32x4_t acc = MM::mma(a, bf);
+        float s[4];
+        int qs[4];
+        bool own[4];
+        tile_scores<HI>(acc, wr, q4, s, qs, own);
+        // the row is query 0 of the tile; its owning lanes hold s[0]
+        if (own[0] && qs[0] == 0 && cok) {
+            p.scores[row * p.N + c] = s[0];
+            skeys[c - c_lo] = fkey(s[0]);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+    wave_lds_sync();
+    const int n = c_hi > c_lo ? (int)(c_hi - c_lo) : 0;
+    float lb = -INFINITY;
+    if (n >= p.chunk_k) {
+        int n_gt;
+        lb = key_f(radix_kth(skeys, n, p.chunk_k, hist, &n_gt));
+    }
+    if (lane == 0) {
+        p.chunk_lb[row * p.nchunks + chunk_id] = lb;
+        p.chunk_kmax[row * p.nchunks + chunk_id] = kmax2;
+    }
+}
+
+__device__ __forceinline__ void row_bound(const IdxParams& p, long long row, float* lb_out, float* delta_out) {
+    const int lane = __lane_id();
+    float lb = INFINITY, km = 0.f;
+    for (int j = lane; j < p.nchunks; j += 64) {
+        lb = fminf(lb, p.chunk_lb[row * p.nchunks + j]);
+        km = fmaxf(km, p.chunk_kmax[row * p.nchunks + j]);
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        lb = fminf(lb, __shfl_xor(lb, off));
+        km = fmaxf(km, __shfl_xor(km, off));
+    }
+    *lb_out = lb;
+    *delta_out = p.err_c * p.row_qn[row] * sqrtf(km);
+}
+
+// S2: one wave per (row, chunk): keep, in index order, the chunk's entries whose
+// float32 score can still reach the row's top-k (>= lower bound - 2 delta).
+__global__ __launch_bounds__(64) void index_split_collect_kernel(IdxParams p) {
+    const int lane = threadIdx.x;
+    const int chunk_id = blockIdx.x % p.nchunks;
+    const long long row = blockIdx.x / p.nchunks;
+    const long long i = row % p.Tq;
+    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    float lb, delta;
+    row_bound(p, row, &lb, &delta);
+    const uint32_t lo = lb == -INFINITY ? 0u : fkey(lb - 2.0f * delta);
+    const long long c_lo = (long long)chunk_id * p.chunk;
+    const long long c_hi = std::min<long long>(c_lo + p.chunk, nvq);
+    uint32_t* lk = p.lists + (row * p.nchunks + chunk_id) * (long long)p.list_cap;
+    int32_t* li = p.list_idx + (row * p.nchunks + chunk_id) * (long long)p.list_cap;
+    int out = 0;
+    for (long long base = c_lo; base < c_hi; base += 64) {
+        const long long c = base + lane;
+        uint32_t key = 0u;
+        bool keep = false;
+        if (c < c_hi) {
+            key = fkey(p.scores[row * p.N + c]);
+            keep = key >= lo;
+        }
+        const unsigned long long msk = __ballot(keep);
+        const int pos = out + __popcll(msk & lanemask_lt());
+        if (keep && pos < p.list_cap) {
+            lk[pos] = key;
+            li[pos] = (int32_t)c;
+        }
+        out += __popcll(msk);
+    }
+    if (lane == 0) p.list_cnt[row * p.nchunks + chunk_id] = out;
+}
+
+// S3: one wave per row: stream the chunk lists in entry order through the
+// candidate buffer, then the exact final selection.
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(64) void index_split_final_kernel(IdxParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x;
+    const long long row = blockIdx.x;
+    const long long b = row / p.Tq, i = row % p.Tq;
+    const int cap = p.cap;
+    WaveBuf wb;
+    wb.keys = reinterpret_cast<uint32_t*>(smem);
+    wb.ids = reinterpret_cast<int32_t*>(smem + 4ull * cap);
+    wb.hist = reinterpret_cast<uint32_t*>(smem + 8ull * cap);
+    wb.mex = reinterpret_cast<double*>(smem + 8ull * cap + 1024);
+    wb.mpos = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 8ull * p.mcap);
+    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const int k_eff = (int)std::min<long long>(p.k, nvq);
+    float lb, delta;
+    row_bound(p, row, &lb, &delta);
+    uint32_t tau = lb == -INFINITY ? 0u : fkey(lb - 2.0f * delta);
+    int cnt = 0;
+    for (int j = 0; j < p.nchunks; ++j) {
+        const int lc = p.list_cnt[row * p.nchunks + j];
+        const bool from_list = lc <= p.list_cap;
+        const long long c_lo = (long long)j * p.chunk;
+        const long long c_hi = std::min<long long>(c_lo + p.chunk, nvq);
+        const long long n = from_list ? lc : (c_hi > c_lo ? c_hi - c_lo : 0);
+        const uint32_t* lk = p.lists + (row * p.nchunks + j) * (long long)p.list_cap;
+        const int32_t* li = p.list_idx + (row * p.nchunks + j) * (long long)p.list_cap;
+        for (long long base = 0; base < n; base += 64) {
+            const long long e = base + lane;
+            uint32_t key = 0u;
+            int32_t id = 0;
+            bool ins = false;
+            if (e < n) {
+                if (from_list) {
+                    key = lk[e];
+                    id = li[e];
+                } else {
+                    id = (int32_t)(c_lo + e);
+                    key = fkey(p.scores[row * p.N + id]);
+                }
+                ins = key >= tau;
+            }
+            const unsigned long long msk = __ballot(ins);
+            if (ins) {
+                const int pos = cnt + __popcll(msk & lanemask_lt());
+                wb.keys[pos] = key;
+                wb.ids[pos] = id;
+            }
+            cnt += __popcll(msk);
+            if (cnt > cap - 64) {
+                wave_lds_sync();
+                cnt = compact_stream(wb, cnt, k_eff, delta, cap, 64, &tau);
+            }
+        }
+    }
+    wave_lds_sync();
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
+    final_select<T, HI, DI>(wb, cnt, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b, p.w + row * HI,
+                            p.idx + row * p.k);
+}
+
+// ----------------------------------------------------------- host planning
+struct IdxPlan {
+    IdxParams p;
+    bool split;
+    size_t lds;  // prefill: per workgroup; split: final kernel
+    size_t lds_score;
+    long long grid;
+    size_t ws_bytes;
+};
+
+constexpr int kMaxLds = 160 * 1024;
+
+int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k,
+                  int dtype, IdxPlan& pl) {
+    if (dtype != SHATTN_DTYPE_BF16 && dtype != SHATTN_DTYPE_F32)
+        return fail(SHATTN_EINVAL, "csa_index_topk: unknown dtype %d", dtype);
+    if (B < 0 || Tq < 0 || N < 0 || Hi < 1 || d_idx < 1 || m < 1 || W < 1 || k < 1 || q_pos0 < 0)
+        return fail(SHATTN_EINVAL, "csa_index_topk: bad sizes B=%d Tq=%d N=%d Hi=%d d_idx=%d m=%d W=%d k=%d",
+                    B, Tq, N, Hi, d_idx, m, W, k);
+    if (Hi != 1 && Hi != 2 && Hi != 4 && Hi != 8 && Hi != 16)
+        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: Hi=%d (supported: 1, 2, 4, 8, 16)", Hi);
+    if (d_idx != 64 && d_idx != 128)
+        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: d_idx=%d (supported: 64, 128)", d_idx);
+    if (k > 2048) return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: k=%d > 2048", k);
+    IdxParams& p = pl.p;
+    p = IdxParams{};
+    p.B = B;
+    p.Tq = Tq;
+    p.N = N;
+    p.k = k;
+    p.m = m;
+    p.W = W;
+    p.q_pos0 = q_pos0;
+    p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
+    p.mcap = std::min(p.cap, 256);
+    // |float32 score - exact| <= err_c * sum_h |w_h| ||q_h|| * max ||k||:
+    // 2*d_idx*u for the dot products (any summation order, rounding or
+    // truncation inside the MFMA), Hi + 2 roundings of the weighted head sum,
+    // and a factor 2 of margin.
+    p.err_c = 2.0f * (2.0f * d_idx + Hi + 4.0f) * 5.9604645e-8f;
+    pl.ws_bytes = 0;
+    pl.grid = 0;
+    const long long rows = (long long)B * Tq;
+    pl.split = rows > 0 && rows <= 64 && N >= 8192;
+    if (pl.split) {
+        p.chunk = 4096;
+        p.nchunks = (N + p.chunk - 1) / p.chunk;
+        p.chunk_k = (k + p.nchunks - 1) / p.nchunks;
+        p.list_cap = 256;
+        size_t off = 0;
+        auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
+        const size_t o_scores = take((size_t)rows * N * 4);
+        const size_t o_lb = take((size_t)rows * p.nchunks * 4);
+        const size_t o_km = take((size_t)rows * p.nchunks * 4);
+        const size_t o_qn = take((size_t)rows * 4);
+        const size_t o_lk = take((size_t)rows * p.nchunks * p.list_cap * 4);
+        const size_t o_li = take((size_t)rows * p.nchunks * p.list_cap * 4);
+        const size_t o_lc = take((size_t)rows * p.nchunks * 4);
+        pl.ws_bytes = off;
+        // offsets are stored in the pointers until the workspace is known
+        p.scores = reinterpret_cast<float*>(o_scores);
+        p.chunk_lb = reinterpret_cast<float*>(o_lb);
+        p.chunk_kmax = reinterpret_cast<float*>(o_km);
+        p.row_qn = reinterpret_cast<float*>(o_qn);
+        p.lists = reinterpret_cast<uint32_t*>(o_lk);
+        p.list_idx = reinterpret_cast<int32_t*>(o_li);
+        p.list_cnt = reinterpret_cast<int32_t*>(o_lc);
+        pl.lds_score = 4ull * p.chunk + 1024;
+        pl.lds = 8ull * p.cap + 1024 + 12ull * p.mcap;
+        pl.grid = rows;
+        return SHATTN_OK;
+    }
+    // prefill: choose queries per wave so that 4 waves fit the LDS budget
+    const int qpt = 16 / Hi;
+    int qpw = std::max(16, qpt);
+    if (qpw > 4 * qpt) qpw = 4 * qpt;
+    auto per_wave = [&](int q) { return (8ull * q * p.cap + 1024 + 12ull * p.mcap + 4ull * q + 31) / 16 * 16; };
+    while (qpw > qpt && WAVES * per_wave(qpw) > (size_t)kMaxLds) qpw -= qpt;
+    if (WAVES * per_wave(qpw) > (size_t)kMaxLds)
+        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: k=%d needs more LDS than available", k);
+    // fewer queries per wave when the batch is small (more waves in flight)
+    while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 512) qpw -= qpt;
+    p.qpw = qpw;
+    p.wave_stride = (int)per_wave(qpw);
+    p.nqt = (Tq + WAVES * qpw - 1) / (WAVES * qpw);
+    pl.lds = WAVES * per_wave(qpw);
+    pl.grid = (long long)B * p.nqt;
+    return SHATTN_OK;
+}
+
+template <typename T, int HI, int DI>
+int launch_idx(IdxPlan& pl, hipStream_t s) {
+    if (!pl.split) {
+        if (pl.lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_prefill_kernel<T, HI, DI>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
+            }
+        }
+        hipLaunchKernelGGL((index_prefill_kernel<T, HI, DI>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds,
+                           s, pl.p);
+        return check_launch("csa_index_topk");
+    }
+    const long long rows = pl.grid;
+    hipLaunchKernelGGL((index_split_score_kernel<T, HI, DI>), dim3((unsigned)(rows * pl.p.nchunks)), dim3(64),
+                       pl.lds_score, s, pl.p);
+    int rc = check_launch("csa_index_topk (score)");
+    if (rc) return rc;
+    hipLaunchKernelGGL(index_split_collect_kernel, dim3((unsigned)(rows * pl.p.nchunks)), dim3(64), 0, s, pl.p);
+    rc = check_launch("csa_index_topk (collect)");
+    if (rc) return rc;
+    if (pl.lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_split_final_kernel<T, HI, DI>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
+        }
+    }
+    hipLaunchKernelGGL((index_split_final_kernel<T, HI, DI>), dim3((unsigned)rows), dim3(64), pl.lds, s, pl.p);
+    return check_launch("csa_index_topk (final)");
+}
+
+template <typename T, int HI>
+int launch_idx_di(IdxPlan& pl, int d_idx, hipStream_t s) {
+    return d_idx == 128 ? launch_idx<T, HI, 128>(pl, s) : launch_idx<T, HI, 64>(pl, s);
+}
+template <typename T>
+int launch_idx_hi(IdxPlan& pl, int Hi, int d_idx, hipStream_t s) {
+    switch (Hi) {
+        case 1: return launch_idx_di<T, 1>(pl, d_idx, s);
+        case 2: return launch_idx_di<T, 2>(pl, d_idx, s);
+        case 4: return launch_idx_di<T, 4>(pl, d_idx, s);
+        case 8: return launch_idx_di<T, 8>(pl, d_idx, s);
+        default: return launch_idx_di<T, 16>(pl, d_idx, s);
+    }
+}
+
+}  // namespace
+}  // namespace shattn
+
+using namespace shattn;
+
+extern "C" size_t csa_index_topk_workspace_size(int B, int Tq, int N, int Hi, int d_idx, int k) {
+    IdxPlan pl;
+    // positions and ratio do not change the workspace size
+    if (make_idx_plan(B, Tq, N, Hi, d_idx, 0, 1, 1, k, SHATTN_DTYPE_BF16, pl) != SHATTN_OK) return 0;
+    return pl.ws_bytes;
+}
+
+extern "C" int csa_index_topk(const void* qI, const void* kI, const float* w, int32_t* idx, int B, int Tq,
+                              int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k, int dtype,
+                              void* ws, size_t ws_bytes, void* stream) {
+    IdxPlan pl;
+    int rc = make_idx_plan(B, Tq, N, Hi, d_idx, q_pos0, m, W, k, dtype, pl);
+    if (rc != SHATTN_OK) return rc;
+    if (B == 0 || Tq == 0) return SHATTN_OK;
+    if (!qI || !w || !idx || (N > 0 && !kI)) return fail(SHATTN_EINVAL, "csa_index_topk: null pointer");
+    if (!aligned16(qI) || (N > 0 && !aligned16(kI)) || (reinterpret_cast<uintptr_t>(w) & 3) ||
+        (reinterpret_cast<uintptr_t>(idx) & 3))
+        return fail(SHATTN_EINVAL, "csa_index_topk: qI/kI must be 16-byte aligned, w/idx 4-byte aligned");
+    if (pl.ws_bytes > 0) {
+        if (!ws || ws_bytes < pl.ws_bytes)
+            return fail(SHATTN_EWORKSPACE, "csa_index_topk: workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                        ws ? ws_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(ws) & 255)
+            return fail(SHATTN_EINVAL, "csa_index_topk: workspace must be 256-byte aligned");
+        char* base = reinterpret_cast<char*>(ws);
+        IdxParams& p = pl.p;
+        p.scores = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.scores));
+        p.chunk_lb = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.chunk_lb));
+        p.chunk_kmax = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.chunk_kmax));
+        p.row_qn = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.row_qn));
+        p.lists = reinterpret_cast<uint32_t*>(base + reinterpret_cast<size_t>(p.lists));
+        p.list_idx = reinterpret_cast<int32_t*>(base + reinterpret_cast<size_t>(p.list_idx));
+        p.list_cnt = reinterpret_cast<int32_t*>(base + reinterpret_cast<size_t>(p.list_cnt));
+    }
+    pl.p.qI = qI;
+    pl.p.kI = kI;
+    pl.p.w = w;
+    pl.p.idx = idx;
+    if (pl.grid > 2147483647LL / 64) return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: problem too large");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dtype == SHATTN_DTYPE_BF16 ? launch_idx_hi<bf16_t>(pl, Hi, d_idx, s)
+                                      : launch_idx_hi<float>(pl, Hi, d_idx, s);
+}
