@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid sparse attention forward hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs that
+are already resident in HBM: block compression of K/V for CSA (m=4) and HCA
+(m=128), lightning-indexer scoring + exact top-k, and the gated window + HCA
++ CSA attention.  Default workload: the Tiny-R2 training shape (B8 T2048
+H=Hkv=12 d128 bf16, CSA k64 with 4 indexer heads, HCA m128, W128, all three
+branches mixed with U(0,1) gates).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hybrid sparse attn fwd queries/s + % HBM/MFMA roofline at 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense, published
+KERNEL_SOURCES = {
+    "compress_csa": "compress.hip", "compress_hca": "compress.hip",
+    "index_topk": "indexer.hip", "attention": "attention.hip",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workload
+def build_inputs(name, seed=0):
+    from sparse_hybrid_attention_amd import synth
+    return synth.make_inputs(name, seed=seed)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def make_pipeline(inp):
+    from sparse_hybrid_attention_amd.binding import HybridPipeline
+    cfg = inp["cfg"]
+    if cfg["kind"] == "decode":
+        return HybridPipeline(q=to_dev(inp["q"]), gates=to_dev(inp["gates"]), W=cfg["W"],
+                              k_raw=to_dev(inp["k_win"]), v_raw=to_dev(inp["v_win"]),
+                              q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
+                              qI=to_dev(inp["qI"]), kI=to_dev(inp["kI"]), w=to_dev(inp["w"]),
+                              k=cfg["k"], m_csa=cfg["m_csa"], m_hca=cfg["m_hca"],
+                              k_csa=to_dev(inp["k_csa"]), v_csa=to_dev(inp["v_csa"]),
+                              k_hca=to_dev(inp["k_hca"]), v_hca=to_dev(inp["v_hca"]))
+    kw = {}
+    if cfg.get("m_csa"):
+        kw.update(zk_csa=to_dev(inp["zk_csa"]), zv_csa=to_dev(inp["zv_csa"]), m_csa=cfg["m_csa"],
+                  qI=to_dev(inp["qI"]), kI=to_dev(inp["kI"]), w=to_dev(inp["w"]), k=cfg["k"])
+    if cfg.get("m_hca"):
+        kw.update(zk_hca=to_dev(inp["zk_hca"]), zv_hca=to_dev(inp["zv_hca"]), m_hca=cfg["m_hca"])
+    return HybridPipeline(q=to_dev(inp["q"]), gates=to_dev(inp["gates"]), W=cfg["W"],
+                          k_raw=to_dev(inp["k"]), v_raw=to_dev(inp["v"]), **kw)
+
+
+def n_visible(t, W, m, N):
+    s = t - W + 1
+    return 0 if s <= 0 else min(N, s // m)
+
+
+def algorithmic(inp, pipe):
+    """Algorithmic (compulsory) HBM bytes and MFMA flops per launch of each kernel."""
+    import torch
+    cfg = inp["cfg"]
+    esz = 2 if cfg["dtype"] == 0 else 4
+    B, H, Hkv, d, W = cfg["B"], cfg["H"], cfg["Hkv"], cfg["d"], cfg["W"]
+    g = inp["gates"]
+    out = {}
+    if cfg["kind"] == "decode":
+        Tq, Tr = 1, W
+        q_pos0, raw_pos0 = inp["q_pos0"], inp["raw_pos0"]
+        Nc, Nh = cfg["N_csa"], cfg["N_hca"]
+    else:
+        Tq = Tr = cfg["T"]
+        q_pos0 = raw_pos0 = 0
+        Nc = Tr // cfg["m_csa"] if cfg.get("m_csa") else 0
+        Nh = Tr // cfg["m_hca"] if cfg.get("m_hca") else 0
+    t = np.arange(Tq, dtype=np.int64) + q_pos0
+    win = np.minimum(t + 1, W).astype(np.float64)                 # window keys per query
+    for name, m in (("compress_csa", cfg.get("m_csa")), ("compress_hca", cfg.get("m_hca"))):
+        if name in pipe.names():
+            N = Tr // m
+            out[name] = dict(bytes=2 * B * N * m * Hkv * d * esz + 2 * B * N * Hkv * d * esz
+                             + 2 * m * Hkv * d * 4, flops=0.0, units=B * N, unit="entries")
+    if "index_topk" in pipe.names():
+        Hi, di, k = cfg["Hi"], cfg["d_idx"], cfg["k"]
+        vis = np.array([n_visible(x, W, cfg["m_csa"], Nc) for x in t], dtype=np.float64)
+        pairs = B * vis.sum()
+        out["index_topk"] = dict(bytes=B * Tq * Hi * di * esz + B * Nc * di * esz + B * Tq * Hi * 4
+                                 + B * Tq * k * 4, flops=2.0 * di * Hi * pairs, units=pairs,
+                                 unit="scored pairs")
+    # attention: each tensor once; the CSA cache counts the entries selected by anyone
+    use_hca = pipe.k_hca is not None and (g[:, 0] != 0).any()
+    use_csa = pipe.idx is not None and (g[:, 1] != 0).any()
+    keys = win.copy()
+    byt = 2 * B * Tq * H * d * esz + 2 * B * Tr * Hkv * d * esz + H * 3 * 4
+    if use_hca:
+        vis_h = np.array([n_visible(x, W, cfg["m_hca"], Nh) for x in t], dtype=np.float64)
+        keys += vis_h
+        byt += 2 * B * int(vis_h.max()) * Hkv * d * esz
+    if use_csa:
+        idx = pipe.idx
+        sel = (idx >= 0).sum(dim=-1).to(torch.float64).mean(dim=0).cpu().numpy()
+        keys += sel
+        used = 0
+        for b in range(B):
+            used += int(torch.unique(idx[b]).numel()) - int((idx[b] < 0).any().item())
+        byt += 2 * used * Hkv * d * esz + B * Tq * cfg["k"] * 4
+    pairs = B * H * keys.sum()
+    out["attention"] = dict(bytes=float(byt), flops=4.0 * d * pairs, units=B * keys.sum(),
+                            unit="attended (query, key) pairs")
+    return out
+
+
+def source_hash(fname):
+    p = os.path.join(ROOT, "sparse_hybrid_attention_amd", "csrc", fname)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        e = data.get(workload, {}).get(kernel)
+        if not e or e.get("source_sha") != source_hash(KERNEL_SOURCES[kernel]):
+            return None
+        return float(e["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(inp, budget_rows):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle as O
+    cfg = inp["cfg"]
+    dt = cfg["dtype"]
+    t0 = time.perf_counter()
+    B = cfg["B"]
+    if cfg["kind"] == "decode":
+        Tq = 1
+        q_pos0, raw_pos0 = inp["q_pos0"], inp["raw_pos0"]
+        rows = [(b, 0) for b in range(min(B, 2))]
+        t_comp = 0.0
+        hca = (inp["k_hca"], inp["v_hca"], cfg["m_hca"])
+        kc, vc = inp["k_csa"], inp["v_csa"]
+        kr, vr = inp["k_win"], inp["v_win"]
+        total_q = B
+    else:
+        Tq = cfg["T"]
+        q_pos0 = raw_pos0 = 0
+        rng = np.random.default_rng(1)
+        rows = sorted({(int(rng.integers(0, B)), int(rng.integers(0, Tq))) for _ in range(budget_rows)})
+        hca = None
+        kc = vc = None
+        if cfg.get("m_hca"):
+            kh, vh = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"], dt)
+            hca = (kh, vh, cfg["m_hca"])
+        if cfg.get("m_csa"):
+            kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"], dt)
+        t_comp = time.perf_counter() - t0
+        kr, vr = inp["k"], inp["v"]
+        total_q = B * Tq
+    t1 = time.perf_counter()
+    csa = None
+    if cfg.get("m_csa"):
+        sel = O.index_topk(inp["qI"], inp["kI"], inp["w"], q_pos0, cfg["m_csa"], cfg["W"], cfg["k"], dt,
+                           rows=rows)
+        idx = np.full((B, Tq, cfg["k"]), -1, dtype=np.int32)
+        for r, (b, i) in enumerate(rows):
+            idx[b, i] = sel[r]
+        csa = (kc, vc, idx)
+    O.hybrid_attn_fwd(inp["q"], kr, vr, inp["gates"], W=cfg["W"], dtype=dt, q_pos0=q_pos0,
+                      raw_pos0=raw_pos0, hca=hca, csa=csa, rows=rows)
+    t_rows = time.perf_counter() - t1
+    per_query = t_comp / total_q + t_rows / len(rows)
+    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} query rows (all heads, all branches, indexer + attention) "
+                      f"plus the full K/V compression of the batch ({t_comp:.1f} s, charged "
+                      f"per query); float64 NumPy, single thread; {t_comp + t_rows:.1f} s total"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tinyr2_bf16",
+                    help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="query rows of the CPU-baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter scaling for rocprofv3)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; the path's multi-GPU sharding is a "
+              "design note (see the sharding paragraph of the design document). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 3}))
+        return
+
+    from sparse_hybrid_attention_amd import binding
+    binding.load_library()
+    log(f"[bench] building inputs for {args.workload}")
+    inp = build_inputs(args.workload)
+    cfg = inp["cfg"]
+    pipe = make_pipeline(inp)
+    names = pipe.names()
+    stream = pipe.stream
+    log(f"[bench] kernels per step: {names}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        pipe.run()
+    torch.cuda.synchronize()
+    alg = algorithmic(inp, pipe)
+
+    # timed region: K steps, per-kernel HIP events on the pipeline's stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        pipe.run(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms")
+    ktime = {n: 0.0 for n in names}
+    for s in range(args.steps):
+        for j, n in enumerate(names):
+            ktime[n] += evs[s][j].elapsed_time(evs[s][j + 1])
+    ktime = {n: v / args.steps for n, v in ktime.items()}   # ms per launch
+    gpu_ms = sum(evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    if cfg["kind"] == "decode":
+        queries = cfg["B"]
+    else:
+        queries = cfg["B"] * cfg["T"]
+    value = queries * args.steps / wall
+    dtype = "bf16" if cfg["dtype"] == 0 else "f32"
+
+    kernels = {}
+    for n in names:
+        a = alg.get(n)
+        ms = ktime[n]
+        e = {"ms": round(ms, 5)}
+        if a:
+            e["GB/s"] = round(a["bytes"] / (ms * 1e-3) / 1e9, 1)
+            e["TFLOP/s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 2)
+            e[a["unit"] + "/s"] = a["units"] / (ms * 1e-3)
+            e["alg_bytes"] = a["bytes"]
+            e["alg_flops"] = a["flops"]
+        kernels[n] = e
+    dom = max(names, key=lambda n: ktime[n])
+    a = alg[dom]
+    t_hbm = a["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = a["flops"] / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
+    ms = ktime[dom]
+    if t_mfma > t_hbm:
+        ach = a["flops"] / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS[dtype],
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[dtype], 4)}
+    else:
+        ach = a["bytes"] / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic_for(dom, args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inp, args.cpu_rows)
+        log(f"[bench] cpu baseline {cpu['value']:.1f} queries/s")
+
+    desc = {
+        "tinyr2_bf16": "Tiny-R2 training-shape forward, B8 T2048 H=Hkv=12 d128 bf16, CSA m4 k64 "
+                       "(indexer 4 heads d_idx 64), HCA m128, W128, gates U(0,1) (all branches)",
+        "tiny_fp32": "tiny fp32 forward, B1 T256 H=Hkv=4 d64, CSA m4 k8 (indexer 2 heads), HCA m32, W32",
+        "hca_prefill_32k": "HCA-only prefill, B1 T32768 H16 Hkv2 d128 bf16, m128, W128, gates [1,0,0]",
+        "csa_prefill_128k": "CSA-only prefill, B1 T131072 H32 Hkv4 d128 bf16, m4, k512 (4 indexer heads), "
+                            "W128, gates [0,1,0]",
+        "decode_1m": "decode, B16 x 1 query at 1,048,576 context, H32 Hkv1 d128 bf16, CSA 262144 entries "
+                     "k1024, HCA 8192 entries, W128, gates U(0,1)",
+    }[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
+        "config": {"workload": desc, "name": args.workload, "batch": cfg["B"],
+                   "query_rows": queries, "gpu_ms_per_step_events": round(gpu_ms, 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -250,3 +250,86 @@ def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, h
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+class HybridPipeline:
+    """One pass of the forward hot path with every buffer allocated up front.
+
+    Prefill: compress K/V for CSA (m_csa) and HCA (m_hca), score + select the
+    CSA entries, gated attention.  Decode: the caches are given; select, then
+    attend.  `run()` only enqueues the kernels (C calls with prepared
+    arguments) on the current stream; it allocates nothing.
+    """
+
+    def __init__(self, *, q, gates, W, k_raw, v_raw, q_pos0=0, raw_pos0=0,
+                 zk_csa=None, zv_csa=None, m_csa=None, zk_hca=None, zv_hca=None, m_hca=None,
+                 qI=None, kI=None, w=None, k=None,
+                 k_csa=None, v_csa=None, k_hca=None, v_hca=None):
+        lib = load_library()
+        self.lib = lib
+        dev = q.device
+        self.stream = torch.cuda.current_stream(dev)
+        self.calls = []      # (name, function, args)
+        self.keep = [q, gates, k_raw, v_raw, qI, kI, w]
+        dt = _dtype_code(q)
+        B, Tq, H, d = q.shape
+        Tr, Hkv = k_raw.shape[1], k_raw.shape[2]
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        # compression (prefill): caches are produced from the raw K/V
+        if zk_csa is not None:
+            N = Tr // m_csa
+            k_csa = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=dev)
+            v_csa = torch.empty_like(k_csa)
+            self.calls.append(("compress_csa", lib.hca_compress_kv,
+                               (_ptr(k_raw), _ptr(v_raw), _ptr(zk_csa), _ptr(zv_csa), _ptr(k_csa),
+                                _ptr(v_csa), B, Tr, Hkv, d, m_csa, dt, s)))
+            self.keep += [zk_csa, zv_csa]
+        if zk_hca is not None:
+            N = Tr // m_hca
+            k_hca = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=dev)
+            v_hca = torch.empty_like(k_hca)
+            self.calls.append(("compress_hca", lib.hca_compress_kv,
+                               (_ptr(k_raw), _ptr(v_raw), _ptr(zk_hca), _ptr(zv_hca), _ptr(k_hca),
+                                _ptr(v_hca), B, Tr, Hkv, d, m_hca, dt, s)))
+            self.keep += [zk_hca, zv_hca]
+        self.k_csa, self.v_csa, self.k_hca, self.v_hca = k_csa, v_csa, k_hca, v_hca
+        idx = None
+        if qI is not None:
+            Bq, Tq_i, Hi, d_idx = qI.shape
+            N = kI.shape[1]
+            idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+            nbytes = int(lib.csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k))
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+            self.keep.append(ws)
+            self.calls.append(("index_topk", lib.csa_index_topk,
+                               (_ptr(qI), _ptr(kI), _ptr(w), _ptr(idx), B, Tq, N, Hi, d_idx,
+                                int(q_pos0), m_csa, W, k, _dtype_code(qI), _ptr(ws) if nbytes else None,
+                                nbytes, s)))
+        self.idx = idx
+        hca = None if k_hca is None else (k_hca, v_hca, m_hca)
+        csa = None if idx is None else (k_csa, v_csa, idx)
+        a, out, keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
+                                     hca=hca, csa=csa)
+        self.args = a
+        self.out = out
+        self.keep += list(keep)
+        nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
+        self.attn_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.calls.append(("attention", lib.hybrid_sparse_attn_fwd,
+                           (ctypes.byref(a), _ptr(self.attn_ws) if nbytes else None, nbytes, s)))
+
+    def names(self):
+        return [c[0] for c in self.calls]
+
+    def run(self, events=None):
+        """Enqueue one pass.  events: optional list of len(calls)+1 torch events
+        recorded around the calls on the pipeline's stream."""
+        if events is not None:
+            events[0].record(self.stream)
+        for j, (name, fn, args) in enumerate(self.calls):
+            rc = fn(*args)
+            if rc != SHATTN_OK:
+                raise ShattnError(rc, f"{name}: " + self.lib.shattn_last_error().decode(errors="replace"))
+            if events is not None:
+                events[j + 1].record(self.stream)
+        return self.out

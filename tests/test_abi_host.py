@@ -1,0 +1,152 @@
+"""Host-side checks of the C interface (no GPU needed): the library loads and
+exports every symbol include/hybrid_attn.h declares, the ctypes struct mirrors
+the C layout, and every invalid call returns its documented error code before
+touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from sparse_hybrid_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hybrid_attn.h")
+
+# fake, 256-byte aligned device addresses: never dereferenced because every
+# call below fails validation on the host
+P = ctypes.c_void_p(0x7F0000000000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sparse_hybrid_attention_amd import build_lib
+        build_lib.build()
+    return binding.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SHATTN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == set(binding.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for s in syms:
+        assert s in exported, s
+        assert getattr(lib, s) is not None
+    # nothing else leaks out of the library
+    assert exported == set(syms)
+
+
+def test_struct_layout_matches_c(lib, tmp_path):
+    fields = [f for f, _ in binding.FwdArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'printf("{f} %zu\\n", offsetof(shattn_fwd_args, {f}));' for f in fields)
+    src.write_text(f"""#include <stdio.h>
+#include <stddef.h>
+#include "hybrid_attn.h"
+int main(void) {{ printf("size %zu\\n", sizeof(shattn_fwd_args)); {body} return 0; }}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(binding.FwdArgs)
+    for f in fields:
+        assert int(out[f]) == getattr(binding.FwdArgs, f).offset, f
+
+
+def err(lib):
+    return lib.shattn_last_error().decode()
+
+
+def test_compress_errors(lib):
+    f = lib.hca_compress_kv
+    assert f(P, P, P, P, P, P, 1, 64, 2, 128, 4, 7, None) == binding.SHATTN_EINVAL
+    assert "dtype" in err(lib)
+    assert f(P, P, P, P, P, P, 1, 64, 2, 96, 4, 0, None) == binding.SHATTN_EUNSUPPORTED
+    assert f(P, P, P, P, P, P, 1, 64, 2, 128, 0, 0, None) == binding.SHATTN_EINVAL
+    assert f(P, P, P, P, P, P, 1, 64, 2, 128, 2000, 0, None) == binding.SHATTN_EUNSUPPORTED
+    assert f(None, P, P, P, P, P, 1, 64, 2, 128, 4, 0, None) == binding.SHATTN_EINVAL
+    assert f(ctypes.c_void_p(0x7F0000000008), P, P, P, P, P, 1, 64, 2, 128, 4, 0, None) == binding.SHATTN_EINVAL
+    assert "aligned" in err(lib)
+    # nothing to do: T < m is a successful no-op
+    assert f(None, None, None, None, None, None, 1, 3, 2, 128, 4, 0, None) == binding.SHATTN_OK
+
+
+def test_index_errors(lib):
+    f = lib.csa_index_topk
+    ok = dict(B=1, Tq=16, N=64, Hi=4, d_idx=64, q_pos0=0, m=4, W=8, k=8, dtype=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(P, P, P, P, a["B"], a["Tq"], a["N"], a["Hi"], a["d_idx"], a["q_pos0"], a["m"], a["W"],
+                 a["k"], a["dtype"], None, 0, None)
+    assert call(Hi=3) == binding.SHATTN_EUNSUPPORTED
+    assert call(d_idx=32) == binding.SHATTN_EUNSUPPORTED
+    assert call(k=0) == binding.SHATTN_EINVAL
+    assert call(k=5000) == binding.SHATTN_EUNSUPPORTED
+    assert call(m=0) == binding.SHATTN_EINVAL
+    assert call(dtype=3) == binding.SHATTN_EINVAL
+    assert call(q_pos0=-1) == binding.SHATTN_EINVAL
+    # decode-shaped call needs a workspace
+    assert lib.csa_index_topk_workspace_size(16, 1, 262144, 4, 64, 1024) > 0
+    assert call(B=16, Tq=1, N=262144, k=1024) == binding.SHATTN_EWORKSPACE
+    assert "workspace" in err(lib)
+    assert f(None, P, P, P, 1, 16, 64, 4, 64, 0, 4, 8, 8, 0, None, 0, None) == binding.SHATTN_EINVAL
+
+
+def fwd(**kw):
+    a = binding.FwdArgs()
+    a.struct_size = ctypes.sizeof(binding.FwdArgs)
+    a.dtype, a.B, a.Tq, a.H, a.Hkv, a.d, a.W = 0, 1, 16, 4, 2, 128, 8
+    a.q = a.out = a.k_raw = a.v_raw = a.gates = P.value
+    a.Tr = 16
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_attention_errors(lib):
+    f = lib.hybrid_sparse_attn_fwd
+
+    def call(**kw):
+        return f(ctypes.byref(fwd(**kw)), None, 0, None)
+    assert call(struct_size=8) == binding.SHATTN_EINVAL
+    assert call(H=5) == binding.SHATTN_EINVAL
+    assert "multiple" in err(lib)
+    assert call(d=80) == binding.SHATTN_EUNSUPPORTED
+    assert call(H=130, Hkv=1) == binding.SHATTN_EUNSUPPORTED
+    assert call(dtype=9) == binding.SHATTN_EINVAL
+    assert call(W=0) == binding.SHATTN_EINVAL
+    assert call(reserved0=1) == binding.SHATTN_EINVAL
+    assert call(Tr=10) == binding.SHATTN_EINVAL          # window rows missing
+    assert "window rows" in err(lib)
+    assert call(raw_pos0=4) == binding.SHATTN_EINVAL     # first rows missing
+    assert call(k=8, N_csa=100) == binding.SHATTN_EINVAL  # CSA without caches / idx
+    assert call(k=5000, N_csa=0, idx=P.value) == binding.SHATTN_EUNSUPPORTED
+    assert call(m_hca=4, N_hca=10) == binding.SHATTN_EINVAL
+    assert call(q=0x7F0000000004) == binding.SHATTN_EINVAL
+    assert call(sm_scale=float("nan")) == binding.SHATTN_EINVAL
+    # decode-shaped split launch needs a workspace
+    a = fwd(B=1, Tq=1, H=32, Hkv=1, W=128, Tr=128, q_pos0=1048703, raw_pos0=1048576, m_hca=128, N_hca=8192,
+            k_hca=P.value, v_hca=P.value)
+    assert lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)) > 0
+    assert f(ctypes.byref(a), None, 0, None) == binding.SHATTN_EWORKSPACE
+    # empty problem is a no-op
+    assert call(B=0) == binding.SHATTN_OK
+
+
+def test_library_refuses_to_fall_back(tmp_path, monkeypatch):
+    # a missing library is an error, never a silent CPU path
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library(str(tmp_path / "missing.so"))

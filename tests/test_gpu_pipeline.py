@@ -1,0 +1,115 @@
+"""End-to-end GPU path (compress -> index -> attention, in the launch
+configuration the benchmark times) against the oracle run end to end on the
+same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_hybrid_attention_amd import binding, synth
+from gpu_util import assert_close, dev, host, lib
+
+pytestmark = pytest.mark.gpu
+
+
+def pipeline(inp):
+    cfg = inp["cfg"]
+    kw = {}
+    if cfg.get("m_csa"):
+        kw.update(zk_csa=dev(inp["zk_csa"]), zv_csa=dev(inp["zv_csa"]), m_csa=cfg["m_csa"],
+                  qI=dev(inp["qI"]), kI=dev(inp["kI"]), w=dev(inp["w"]), k=cfg["k"])
+    if cfg.get("m_hca"):
+        kw.update(zk_hca=dev(inp["zk_hca"]), zv_hca=dev(inp["zv_hca"]), m_hca=cfg["m_hca"])
+    return binding.HybridPipeline(q=dev(inp["q"]), gates=dev(inp["gates"]), W=cfg["W"],
+                                  k_raw=dev(inp["k"]), v_raw=dev(inp["v"]), **kw)
+
+
+def oracle_pipeline(inp, rows):
+    cfg = inp["cfg"]
+    dt = cfg["dtype"]
+    hca = csa = None
+    if cfg.get("m_hca"):
+        kh, vh = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"], dt)
+        hca = (kh, vh, cfg["m_hca"])
+    if cfg.get("m_csa"):
+        kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"], dt)
+        B, T = inp["qI"].shape[:2]
+        sel = O.index_topk(inp["qI"], inp["kI"], inp["w"], 0, cfg["m_csa"], cfg["W"], cfg["k"], dt, rows=rows)
+        idx = np.full((B, T, cfg["k"]), -1, np.int32)
+        for r, (b, i) in enumerate(rows):
+            idx[b, i] = sel[r]
+        csa = (kc, vc, idx)
+    out = O.hybrid_attn_fwd(inp["q"], inp["k"], inp["v"], inp["gates"], W=cfg["W"], dtype=dt,
+                            hca=hca, csa=csa, rows=rows)
+    return out, (None if csa is None else sel)
+
+
+def rows_for(B, T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(b, t) for b in range(B) for t in (0, 127, 128, 131, 255, 1000, T - 1) if t < T}
+    while len(rows) < n:
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, T))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("gates", ["mix", "hca", "csa", "swa"])
+def test_tinyr2_full_pipeline(gates):
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=0, gates=gates)
+    pipe = pipeline(inp)
+    out = pipe.run()
+    torch.cuda.synchronize()
+    got = host(out)
+    idx = host(pipe.idx)
+    rows = rows_for(8, 2048, 160, 1)
+    want, sel = oracle_pipeline(inp, rows)
+    for r, (b, i) in enumerate(rows):
+        assert np.array_equal(idx[b, i], sel[r]), f"idx row {(b, i)}"
+    assert_close(np.stack([got[b, i] for b, i in rows]), want, f"tinyr2 {gates}")
+    # compressed caches produced on the GPU match the oracle's
+    kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], 4, O.DTYPE_BF16)
+    assert_close(host(pipe.k_csa), kc, "k_csa")
+    assert_close(host(pipe.v_csa), vc, "v_csa")
+
+
+def test_tiny_fp32_pipeline_all_rows():
+    lib()
+    inp = synth.make_inputs("tiny_fp32", seed=0)
+    pipe = pipeline(inp)
+    got = host(pipe.run())
+    rows = [(0, i) for i in range(256)]
+    want, sel = oracle_pipeline(inp, rows)
+    assert np.array_equal(host(pipe.idx)[0], np.stack(sel))
+    assert_close(got[0], want, "tiny fp32 pipeline")
+
+
+def test_hca_prefill_pipeline_reduced():
+    lib()
+    inp = synth.make_inputs("hca_prefill_32k", seed=0, T=8192)
+    pipe = pipeline(inp)
+    got = host(pipe.run())
+    rows = rows_for(1, 8192, 64, 2)
+    want, _ = oracle_pipeline(inp, rows)
+    assert_close(np.stack([got[b, i] for b, i in rows]), want, "hca prefill")
+
+
+def test_csa_prefill_pipeline_reduced():
+    lib()
+    inp = synth.make_inputs("csa_prefill_128k", seed=0, T=16384)
+    pipe = pipeline(inp)
+    got = host(pipe.run())
+    idx = host(pipe.idx)
+    rows = rows_for(1, 16384, 48, 3)
+    want, sel = oracle_pipeline(inp, rows)
+    for r, (b, i) in enumerate(rows):
+        assert np.array_equal(idx[b, i], sel[r]), f"idx row {(b, i)}"
+    assert_close(np.stack([got[b, i] for b, i in rows]), want, "csa prefill")
+
+
+def test_pipeline_repeat_is_bitwise_stable():
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=4, B=2, T=1024)
+    pipe = pipeline(inp)
+    a = host(pipe.run()).copy()
+    b = host(pipe.run()).copy()
+    assert np.array_equal(a, b)
