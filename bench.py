@@ -30,7 +30,7 @@ METRIC = "hybrid sparse attn fwd queries/s + % HBM/MFMA roofline at 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense, published
 KERNEL_SOURCES = {
-    "compress_csa": "compress.hip", "compress_hca": "compress.hip",
+    "compress_csa": "compress.hip", "compress_hca": "compress.hip", "compress_dual": "compress.hip",
     "index_topk": "indexer.hip", "attention": "attention.hip",
 }
 
@@ -40,9 +40,10 @@ def log(msg):
 
 
 # ------------------------------------------------------------------ workload
-def build_inputs(name, seed=0):
+def build_inputs(name, seed=0, gates=None):
     from sparse_hybrid_attention_amd import synth
-    return synth.make_inputs(name, seed=seed)
+    over = {} if gates is None else {"gates": gates}
+    return synth.make_inputs(name, seed=seed, **over)
 
 
 def to_dev(a):
@@ -103,6 +104,12 @@ def algorithmic(inp, pipe):
             N = Tr // m
             out[name] = dict(bytes=2 * B * N * m * Hkv * d * esz + 2 * B * N * Hkv * d * esz
                              + 2 * m * Hkv * d * 4, flops=0.0, units=B * N, unit="entries")
+    if "compress_dual" in pipe.names():
+        m1, m2 = cfg["m_csa"], cfg["m_hca"]
+        N1, N2 = Tr // m1, Tr // m2
+        out["compress_dual"] = dict(bytes=2 * B * Tr * Hkv * d * esz + 2 * B * (N1 + N2) * Hkv * d * esz
+                                    + 2 * (m1 + m2) * Hkv * d * 4, flops=0.0, units=B * (N1 + N2),
+                                    unit="entries")
     if "index_topk" in pipe.names():
         Hi, di, k = cfg["Hi"], cfg["d_idx"], cfg["k"]
         vis = np.array([n_visible(x, W, cfg["m_csa"], Nc) for x in t], dtype=np.float64)
@@ -215,6 +222,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyr2_bf16",
                     help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m")
+    ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
+                    help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768, help="query rows of the CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -248,7 +257,7 @@ def main():
     from sparse_hybrid_attention_amd import binding
     binding.load_library()
     log(f"[bench] building inputs for {args.workload}")
-    inp = build_inputs(args.workload)
+    inp = build_inputs(args.workload, gates=args.gates)
     cfg = inp["cfg"]
     pipe = make_pipeline(inp)
     names = pipe.names()
@@ -339,7 +348,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
-        "config": {"workload": desc, "name": args.workload, "batch": cfg["B"],
+        "config": {"workload": desc + ("" if args.gates is None else f" [gates: {args.gates}]"),
+                   "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],
                    "query_rows": queries, "gpu_ms_per_step_events": round(gpu_ms, 5)},
         "roofline": roof,
         "cpu_baseline": cpu,

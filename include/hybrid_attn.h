@@ -86,6 +86,20 @@ SHATTN_API int hca_compress_kv(const void* k, const void* v, const float* zk, co
                     void* stream);
 
 /*
+ * The same block compression for two ratios in one pass over K and V (each raw
+ * row is read once): ratio m1 into kc1/vc1 ([B, floor(T/m1), Hkv, d], logits
+ * zk1/zv1 [m1, Hkv, d]) and ratio m2 into kc2/vc2 ([B, floor(T/m2), Hkv, d],
+ * logits zk2/zv2 [m2, Hkv, d]).  Results equal two hca_compress_kv calls.
+ * Supported: m1 in {1, 2, 4, 8}; m2 a multiple of 8, at most 1024; d in {64, 128}.
+ * Rows past the last full m2-block are compressed for ratio m1 only, with
+ * extra launches (one per sequence).
+ */
+SHATTN_API int hca_compress_kv_dual(const void* k, const void* v, const float* zk1, const float* zv1,
+                                    void* kc1, void* vc1, int m1, const float* zk2, const float* zv2,
+                                    void* kc2, void* vc2, int m2, int B, int T, int Hkv, int d, int dtype,
+                                    void* stream);
+
+/*
  * Lightning indexer + per-query top-k over the CSA entries ([V4-blog] "CSA":
  * the indexer finds, for the current query, the Top-K most relevant
  * compressed entries; [Tiny-R2] 3.2 importance_score / topk selection).

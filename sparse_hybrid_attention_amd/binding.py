@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhybridat
 
 EXPORTED = (
     "hca_compress_kv",
+    "hca_compress_kv_dual",
     "csa_index_topk_workspace_size",
     "csa_index_topk",
     "hybrid_sparse_attn_fwd_workspace_size",
@@ -90,6 +91,9 @@ def load_library(path: str = LIB_PATH):
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         lib.hca_compress_kv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.hca_compress_kv.restype = i32
+        lib.hca_compress_kv_dual.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                             i32, i32, vp]
+        lib.hca_compress_kv_dual.restype = i32
         lib.csa_index_topk_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
         lib.csa_index_topk_workspace_size.restype = sz
         lib.csa_index_topk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32,
@@ -158,6 +162,24 @@ def hca_compress_kv(k, v, zk, zv, m: int, out=None):
     _check(lib.hca_compress_kv(_ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(kc), _ptr(vc),
                                B, T, Hkv, d, m, _dtype_code(k), _stream(k)))
     return kc, vc
+
+
+def hca_compress_kv_dual(k, v, zk1, zv1, m1: int, zk2, zv2, m2: int):
+    """Both ratios in one pass; returns ((kc1, vc1), (kc2, vc2))."""
+    lib = load_library()
+    _need(k, "k")
+    _need(v, "v", k.dtype, k.device)
+    for name, z in (("zk1", zk1), ("zv1", zv1), ("zk2", zk2), ("zv2", zv2)):
+        _need(z, name, torch.float32, k.device)
+    B, T, Hkv, d = k.shape
+    kc1 = torch.empty((B, T // m1, Hkv, d), dtype=k.dtype, device=k.device)
+    vc1 = torch.empty_like(kc1)
+    kc2 = torch.empty((B, T // m2, Hkv, d), dtype=k.dtype, device=k.device)
+    vc2 = torch.empty_like(kc2)
+    _check(lib.hca_compress_kv_dual(_ptr(k), _ptr(v), _ptr(zk1), _ptr(zv1), _ptr(kc1), _ptr(vc1), m1,
+                                    _ptr(zk2), _ptr(zv2), _ptr(kc2), _ptr(vc2), m2, B, T, Hkv, d,
+                                    _dtype_code(k), _stream(k)))
+    return (kc1, vc1), (kc2, vc2)
 
 
 def csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k) -> int:
@@ -275,23 +297,30 @@ class HybridPipeline:
         B, Tq, H, d = q.shape
         Tr, Hkv = k_raw.shape[1], k_raw.shape[2]
         s = ctypes.c_void_p(self.stream.cuda_stream)
-        # compression (prefill): caches are produced from the raw K/V
+        # compression (prefill): caches are produced from the raw K/V, both
+        # ratios in one pass when the fused kernel supports them
         if zk_csa is not None:
-            N = Tr // m_csa
-            k_csa = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=dev)
+            k_csa = torch.empty((B, Tr // m_csa, Hkv, d), dtype=q.dtype, device=dev)
             v_csa = torch.empty_like(k_csa)
-            self.calls.append(("compress_csa", lib.hca_compress_kv,
-                               (_ptr(k_raw), _ptr(v_raw), _ptr(zk_csa), _ptr(zv_csa), _ptr(k_csa),
-                                _ptr(v_csa), B, Tr, Hkv, d, m_csa, dt, s)))
             self.keep += [zk_csa, zv_csa]
         if zk_hca is not None:
-            N = Tr // m_hca
-            k_hca = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=dev)
+            k_hca = torch.empty((B, Tr // m_hca, Hkv, d), dtype=q.dtype, device=dev)
             v_hca = torch.empty_like(k_hca)
-            self.calls.append(("compress_hca", lib.hca_compress_kv,
-                               (_ptr(k_raw), _ptr(v_raw), _ptr(zk_hca), _ptr(zv_hca), _ptr(k_hca),
-                                _ptr(v_hca), B, Tr, Hkv, d, m_hca, dt, s)))
             self.keep += [zk_hca, zv_hca]
+        if zk_csa is not None and zk_hca is not None and 8 % m_csa == 0 and m_hca % 8 == 0 and m_hca <= 1024:
+            self.calls.append(("compress_dual", lib.hca_compress_kv_dual,
+                               (_ptr(k_raw), _ptr(v_raw), _ptr(zk_csa), _ptr(zv_csa), _ptr(k_csa), _ptr(v_csa),
+                                m_csa, _ptr(zk_hca), _ptr(zv_hca), _ptr(k_hca), _ptr(v_hca), m_hca, B, Tr, Hkv,
+                                d, dt, s)))
+        else:
+            if zk_csa is not None:
+                self.calls.append(("compress_csa", lib.hca_compress_kv,
+                                   (_ptr(k_raw), _ptr(v_raw), _ptr(zk_csa), _ptr(zv_csa), _ptr(k_csa),
+                                    _ptr(v_csa), B, Tr, Hkv, d, m_csa, dt, s)))
+            if zk_hca is not None:
+                self.calls.append(("compress_hca", lib.hca_compress_kv,
+                                   (_ptr(k_raw), _ptr(v_raw), _ptr(zk_hca), _ptr(zv_hca), _ptr(k_hca),
+                                    _ptr(v_hca), B, Tr, Hkv, d, m_hca, dt, s)))
         self.k_csa, self.v_csa, self.k_hca, self.v_hca = k_csa, v_csa, k_hca, v_hca
         idx = None
         if qI is not None:

@@ -48,7 +48,6 @@ namespace {
 
 constexpr int KT = 64;  // keys per shared LDS tile
 constexpr int KC = 32;  // keys per MFMA chunk
-constexpr int MAX_WAVES = 4;
 
 enum CsaMode { CSA_NONE = 0, CSA_DENSE = 1, CSA_GATHER = 2 };
 
@@ -80,6 +79,7 @@ struct AttnParams {
     int split_keys;
     int n_win_items, n_hca_items;
     int has_hca, has_csa;  // branch present (its gate column is used)
+    int ncol;              // columns (query, head) per workgroup = 16 * waves
 };
 
 // ---------------------------------------------------------------- per-dtype MFMA
@@ -107,6 +107,8 @@ template <int D> struct Tr<bf16_t, D> {
     }
     // key offset (within the 32-key chunk) of this lane's score j
     __device__ static int key_of(int q4, int j) { return 8 * q4 + j; }
+    // bit j = visibility of key_of(q4, j), from a chunk mask over its 32 keys
+    __device__ static uint32_t lane_bits(uint32_t m, int q4) { return (m >> (8 * q4)) & 0xFFu; }
 
     // S^T for keys [c, c+32) of a K tile (row stride KPAD).  s[j] <-> key_of(q4, j).
     __device__ static void scores(const bf16_t* Ks, int c, int lane, const QF* qf, float* s) {
@@ -202,6 +204,12 @@ template <int D> struct Tr<float, D> {
         for (int ks = 0; ks < KS; ++ks) qf[ks] = ok ? qrow[4 * ks + q4] : 0.f;
     }
     __device__ static int key_of(int q4, int j) { return 16 * (j >> 2) + 4 * (j & 3) + q4; }
+    __device__ static uint32_t lane_bits(uint32_t m, int q4) {
+        uint32_t r = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r |= ((m >> key_of(q4, j)) & 1u) << j;
+        return r;
+    }
 
     __device__ static void scores(const float* Ks, int c, int lane, const QF* qf, float* s) {
         const int rho = lane & 15, q4 = lane >> 4;
@@ -310,18 +318,130 @@ __device__ __forceinline__ long long n_visible(long long t, int W, int m, int N)
     return n < N ? n : N;
 }
 
+// ---------------------------------------------------------------- tile staging
+// Register staging of one KT-key tile (global -> registers -> LDS), so the next
+// tile's loads are in flight while the current tile is computed.
+template <typename T, int D, int NT> struct Stage;
+
+template <int D, int NT> struct Stage<bf16_t, D, NT> {
+    static constexpr int PIECES = D / 8;                          // 16-byte pieces per row
+    static constexpr int KU = KT * PIECES;                        // K pieces per tile
+    static constexpr int VUN = (KT / 2) * PIECES;                 // V units (2 keys x 8 dims)
+    static constexpr int KP = (KU + NT - 1) / NT;
+    static constexpr int VU = (VUN + NT - 1) / NT;
+    uint4 k[KP];
+    uint4 v[VU][2];
+    // rows [0, nvalid) of the tile start at kb / vb, rs elements apart; rows
+    // past nvalid are zero.  Branch-free: out-of-range lanes load row 0.
+    __device__ void load(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, int rs, int nvalid,
+                         int tid) {
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            const int u = tid + j * NT;
+            const int kk = u / PIECES, pc = u % PIECES;
+            const bool ok = kk < nvalid && (KU % NT == 0 || u < KU);
+            const uint4 x = ld16(kb + (ok ? kk : 0) * rs + pc * 8);
+            k[j] = ok ? x : make_uint4(0, 0, 0, 0);
+        }
+        // V: key pairs fastest across lanes (conflict-free transposed LDS writes)
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = tid + j * NT;
+            const int kp = u % (KT / 2), oc = u / (KT / 2);
+            const bool in = VUN % NT == 0 || u < VUN;
+            const bool ok0 = in && 2 * kp < nvalid, ok1 = in && 2 * kp + 1 < nvalid;
+            const uint4 x0 = ld16(vb + (ok0 ? 2 * kp : 0) * rs + (in ? oc : 0) * 8);
+            const uint4 x1 = ld16(vb + (ok1 ? 2 * kp + 1 : 0) * rs + (in ? oc : 0) * 8);
+            v[j][0] = ok0 ? x0 : make_uint4(0, 0, 0, 0);
+            v[j][1] = ok1 ? x1 : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ void store(bf16_t* Ks, bf16_t* Vt, int tid) const {
+        constexpr int KPAD = D + 8, VST = KT + 8;
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            const int u = tid + j * NT;
+            if (KU % NT == 0 || u < KU) {
+                const int kk = u / PIECES, pc = u % PIECES;
+                *reinterpret_cast<uint4*>(Ks + kk * KPAD + pc * 8) = k[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = tid + j * NT;
+            const int kp = u % (KT / 2), oc = u / (KT / 2);
+            if (VUN % NT == 0 || u < VUN) {
+                const uint32_t a[4] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w};
+                const uint32_t c[4] = {v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd) {
+                    const uint32_t lo = (dd & 1) ? (a[dd >> 1] >> 16) : (a[dd >> 1] & 0xFFFFu);
+                    const uint32_t hi = (dd & 1) ? (c[dd >> 1] & 0xFFFF0000u) : (c[dd >> 1] << 16);
+                    *reinterpret_cast<uint32_t*>(Vt + (oc * 8 + dd) * VST + 2 * kp) = lo | hi;
+                }
+            }
+        }
+    }
+};
+
+template <int D, int NT> struct Stage<float, D, NT> {
+    static constexpr int PIECES = D / 4;
+    static constexpr int KU = KT * PIECES;
+    static constexpr int KP = (KU + NT - 1) / NT;
+    uint4 k[KP], v[KP];
+    __device__ void load(const float* __restrict__ kb, const float* __restrict__ vb, int rs, int nvalid, int tid) {
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            const int u = tid + j * NT;
+            const int kk = u / PIECES, pc = u % PIECES;
+            const bool ok = kk < nvalid && (KU % NT == 0 || u < KU);
+            const int off = (ok ? kk : 0) * rs + pc * 4;
+            const uint4 x = ld16(kb + off), y = ld16(vb + off);
+            k[j] = ok ? x : make_uint4(0, 0, 0, 0);
+            v[j] = ok ? y : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ void store(float* Ks, float* Vs, int tid) const {
+        constexpr int KPAD = D + 4;
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            const int u = tid + j * NT;
+            if (KU % NT == 0 || u < KU) {
+                const int kk = u / PIECES, pc = u % PIECES;
+                *reinterpret_cast<uint4*>(Ks + kk * KPAD + pc * 4) = k[j];
+                *reinterpret_cast<uint4*>(Vs + kk * KPAD + pc * 4) = v[j];
+            }
+        }
+    }
+};
+
+// bits [a, b] of a 32-bit mask (empty when b < a or the range misses [0, 31])
+__device__ __forceinline__ uint32_t range_mask(int a, int b) {
+    a = a < 0 ? 0 : a;
+    b = b > 31 ? 31 : b;
+    if (b < a) return 0u;
+    const uint32_t hi = b == 31 ? 0xFFFFFFFFu : ((2u << b) - 1u);
+    return hi & ~((1u << a) - 1u);
+}
+
 // ---------------------------------------------------------------- main kernel
-template <typename T, int D>
-__global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) {
+enum { ITEM_WIN = 0, ITEM_HCA = 1, ITEM_CSA = 2 };
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     typedef Tr<T, D> TR;
     constexpr int DT = D / 16;
+    constexpr int NT = NW * 64;
+    constexpr int TILE_ELEMS = KT * TR::KPAD + (sizeof(T) == 2 ? D * TR::VST : KT * TR::VST);
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T* Ks = reinterpret_cast<T*>(smem);
-    T* Vs = Ks + KT * TR::KPAD;
-    __shared__ long long rows[KT];
+    T* Kb0 = reinterpret_cast<T*>(smem);
+    T* Vb0 = Kb0 + KT * TR::KPAD;
+    T* Kb1 = Kb0 + TILE_ELEMS;
+    T* Vb1 = Kb1 + KT * TR::KPAD;
     __shared__ int sflag[4];
+    __shared__ int emax_s;
 
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, q4 = lane >> 4;
 
@@ -358,6 +478,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) 
         gate[2] = p.gates[h * 3 + 2];
     }
     if (tid < 4) sflag[tid] = 0;
+    if (tid == 0) emax_s = -1;
     __syncthreads();
     if (valid && gate[0] != 0.f) sflag[0] = 1;
     if (valid && gate[1] != 0.f) sflag[1] = 1;
@@ -368,17 +489,30 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) 
     const long long t_first = p.q_pos0 + i0;
     const long long t_last = p.q_pos0 + i0 + nq - 1;
     const long long win_lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;  // this column's window start
-    const T* kraw = reinterpret_cast<const T*>(p.k_raw);
-    const T* vraw = reinterpret_cast<const T*>(p.v_raw);
 
-    State<DT> sw, sh, sc;
-    sw.init();
-    sh.init();
-    sc.init();
+    // One running online-softmax state S and one output accumulator oacc per
+    // column.  Branches are folded into oacc (normalised and gated) as soon as
+    // they are complete:  S = window -> fold g2 (SWA);  S continues with the
+    // CSA entries -> fold g1;  S restarts, window again + HCA entries -> fold
+    // g0.  The window is recomputed only when both HCA and CSA are active;
+    // this keeps two accumulator arrays live instead of three.
+    State<DT> S;
+    S.init();
+    f32x4_t oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](float gcoef) {   // oacc += gcoef * S / sum(S)
+        const float l = col_sum(S.l);
+        const float c = valid ? gcoef / l : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dt][r] = fmaf(c, S.acc[dt][r], oacc[dt][r]);
+    };
 
     // which key ranges this workgroup covers (split mode: one item)
     bool do_win = true, do_hca = use_hca, do_csa = use_csa;
-    long long hca_lo = 0, hca_hi = -1, csa_lo = 0, csa_hi = -1;
+    long long hca_lo = 0, hca_hi = 0x7FFFFFFFFFFFLL, csa_lo = 0, csa_hi = -1;
     if (p.nsplit) {
         do_win = item < p.n_win_items;
         do_hca = use_hca && item >= p.n_win_items && item < p.n_win_items + p.n_hca_items;
@@ -393,130 +527,91 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) 
         }
     }
 
-    // ------------------------------------------------------------ window
-    if (do_win) {
-        const long long pos_lo = t_first - p.W + 1 > 0 ? t_first - p.W + 1 : 0;
-        const long long pos_hi = t_last + 1;
-        for (long long tp = pos_lo; tp < pos_hi; tp += KT) {
-            if (tid < KT) {
-                const long long pos = tp + tid;
-                const long long r = pos - p.raw_pos0;
-                rows[tid] = (pos < pos_hi && r >= 0 && r < p.Tr)
-                                ? ((((long long)b * p.Tr + r) * p.Hkv + g) * D)
-                                : -1;
-            }
-            __syncthreads();
-            TR::stage(Ks, Vs, TR::VST, kraw, vraw, rows, KT, tid, nthr);
-            __syncthreads();
-#pragma unroll
-            for (int c = 0; c < KT; c += KC) {
-                float x[8];
-                bool any = false;
-                float s[8];
-                // visibility first: skip chunks no column of the wave can see
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const long long pos = tp + c + TR::key_of(q4, j);
-                    const bool vis = valid && pos >= win_lo && pos <= t;
-                    x[j] = vis ? 0.f : -INFINITY;
-                    any |= vis;
-                }
-                if (!__any(any)) continue;
-                TR::scores(Ks, c, lane, qf, s);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (x[j] == 0.f) ? s[j] * p.scale_log2 : -INFINITY;
-                softmax_pv<T, D>(sw, x, Vs, TR::VST, c, lane);
-            }
-            __syncthreads();
-        }
-    }
-
-    // ------------------------------------------------------------ HCA (dense)
-    if (do_hca) {
-        const long long nv = valid ? n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
-        long long e_hi = n_visible(t_last, p.W, p.m_hca, p.N_hca);
-        long long e_lo = 0;
-        if (p.nsplit) {
-            e_lo = hca_lo;
-            if (e_hi > hca_hi) e_hi = hca_hi;
-        }
-        const T* kh = reinterpret_cast<const T*>(p.k_hca);
-        const T* vh = reinterpret_cast<const T*>(p.v_hca);
-        for (long long e0 = e_lo; e0 < e_hi; e0 += KT) {
-            if (tid < KT) {
-                const long long e = e0 + tid;
-                rows[tid] = e < e_hi ? ((((long long)b * p.N_hca + e) * p.Hkv + g) * D) : -1;
-            }
-            __syncthreads();
-            TR::stage(Ks, Vs, TR::VST, kh, vh, rows, KT, tid, nthr);
-            __syncthreads();
-#pragma unroll
-            for (int c = 0; c < KT; c += KC) {
-                float x[8], s[8];
-                bool any = false;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const long long e = e0 + c + TR::key_of(q4, j);
-                    const bool vis = e < nv && e < e_hi;
-                    x[j] = vis ? 0.f : -INFINITY;
-                    any |= vis;
-                }
-                if (!__any(any)) continue;
-                TR::scores(Ks, c, lane, qf, s);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (x[j] == 0.f) ? s[j] * p.scale_log2 : -INFINITY;
-                softmax_pv<T, D>(sh, x, Vs, TR::VST, c, lane);
-            }
-            __syncthreads();
-        }
-    }
-
-    // ------------------------------------------------------------ CSA
-    if (do_csa && p.csa_mode == CSA_DENSE) {
-        uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
-        __shared__ int emax_s;
-        for (int u = tid; u < p.QW * p.bm_words; u += nthr) bm[u] = 0u;
-        if (tid == 0) emax_s = -1;
+    // ---- CSA selection bitmap (dense-masked mode)
+    const bool dense_csa = do_csa && p.csa_mode == CSA_DENSE;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
+    if (dense_csa) {
+        for (int u = tid; u < p.QW * p.bm_words; u += NT) bm[u] = 0u;
         __syncthreads();
-        for (int u = tid; u < nq * p.k; u += nthr) {
+        int emax = -1;
+        for (int u = tid; u < nq * p.k; u += NT) {
             const int qq = u / p.k, j = u - qq * p.k;
             const int e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
             if (e >= 0 && e < p.N_csa) {
                 atomicOr(&bm[qq * p.bm_words + (e >> 5)], 1u << (e & 31));
-                atomicMax(&emax_s, e);
+                emax = e > emax ? e : emax;
             }
         }
+        for (int off = 32; off > 0; off >>= 1) {
+            const int o = __shfl_xor(emax, off);
+            emax = o > emax ? o : emax;
+        }
+        if (lane == 0) atomicMax(&emax_s, emax);
         __syncthreads();
-        const long long e_hi = (long long)emax_s + 1;
-        const T* kc = reinterpret_cast<const T*>(p.k_csa);
-        const T* vc = reinterpret_cast<const T*>(p.v_csa);
-        for (long long e0 = 0; e0 < e_hi; e0 += KT) {
-            if (tid < KT) {
-                const long long e = e0 + tid;
-                rows[tid] = e < e_hi ? ((((long long)b * p.N_csa + e) * p.Hkv + g) * D) : -1;
+    }
+
+    // ---- geometry: every index inside a stream is a 32-bit offset from the
+    // workgroup's window start (window) or from entry 0 (HCA, CSA)
+    const long long w_lo = t_first - p.W + 1 > 0 ? t_first - p.W + 1 : 0;
+    const int wlen = (int)(t_last + 1 - w_lo);
+    int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
+    if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
+    const int h_lo = do_hca ? (int)hca_lo : 0;
+    const int c_hi = dense_csa ? emax_s + 1 : 0;
+    const int wv_lo = valid ? (int)(win_lo - w_lo) : 1;  // column's window [wv_lo, wv_hi]
+    const int wv_hi = valid ? (int)(t - w_lo) : 0;
+    int hv = (valid && do_hca) ? (int)n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
+    if (hv > h_hi) hv = h_hi;
+    const int rs = p.Hkv * D;  // row stride of every K/V tensor (elements)
+    const long long hoff = (long long)g * D;
+    const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * rs + hoff;
+    const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * rs + hoff;
+    const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * rs + hoff;
+    const T* vcsa = reinterpret_cast<const T*>(p.v_csa) + (long long)b * p.N_csa * rs + hoff;
+
+    // ---- a pipelined stream of KT-key tiles of one source into S: tile i+1 is
+    // loaded into registers while tile i is computed from LDS (double buffer)
+    Stage<T, D, NT> stg;
+    int parity = 0;
+    auto stream = [&](const T* kb, const T* vb, int k_begin, int k_end, int type) {
+        const int n = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
+        if (n == 0) return;
+        stg.load(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, rs, min(KT, k_end - k_begin), tid);
+        stg.store(parity ? Kb1 : Kb0, parity ? Vb1 : Vb0, tid);
+        __syncthreads();
+        for (int i = 0; i < n; ++i) {
+            const int k0 = k_begin + i * KT;
+            const T* Ks = parity ? Kb1 : Kb0;
+            const T* Vs = parity ? Vb1 : Vb0;
+            if (i + 1 < n) {
+                const int k1 = k0 + KT;
+                stg.load(kb + (long long)k1 * rs, vb + (long long)k1 * rs, rs, min(KT, k_end - k1), tid);
             }
-            __syncthreads();
-            TR::stage(Ks, Vs, TR::VST, kc, vc, rows, KT, tid, nthr);
-            __syncthreads();
 #pragma unroll
             for (int c = 0; c < KT; c += KC) {
-                if (e0 + c >= e_hi) break;
-                // the 32 entries [e0+c, e0+c+32) are one bitmap word
-                const uint32_t word = valid ? bm[ql * p.bm_words + (int)((e0 + c) >> 5)] : 0u;
-                if (!__any(word != 0u)) continue;
-                float x[8], s[8];
-                TR::scores(Ks, c, lane, qf, s);
+                const int kc0 = k0 + c;
+                uint32_t m;
+                if (type == ITEM_WIN) m = range_mask(wv_lo - kc0, wv_hi - kc0);
+                else if (type == ITEM_HCA) m = range_mask(0, hv - kc0 - 1);
+                else m = (valid && kc0 < c_hi) ? bm[ql * p.bm_words + (kc0 >> 5)] : 0u;
+                const uint32_t mb = TR::lane_bits(m, q4);
+                if (!__any(mb != 0u)) continue;
+                float sc[8], x[8];
+                TR::scores(Ks, c, lane, qf, sc);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const bool vis = (word >> TR::key_of(q4, j)) & 1u;
-                    x[j] = vis ? s[j] * p.scale_log2 : -INFINITY;
-                }
-                softmax_pv<T, D>(sc, x, Vs, TR::VST, c, lane);
+                for (int j = 0; j < 8; ++j) x[j] = ((mb >> j) & 1u) ? sc[j] * p.scale_log2 : -INFINITY;
+                softmax_pv<T, D>(S, x, Vs, TR::VST, c, lane);
             }
+            parity ^= 1;
+            if (i + 1 < n) stg.store(parity ? Kb1 : Kb0, parity ? Vb1 : Vb0, tid);
             __syncthreads();
         }
-    } else if (do_csa && p.csa_mode == CSA_GATHER) {
-        // per-wave private tiles (aliasing the shared tiles, which are no longer used)
+    };
+
+    // ---- CSA gather (per wave, private LDS tiles aliasing the stream buffers)
+    auto gather = [&]() {
         char* gbase = smem + p.lds_gather + wave * p.lds_gather_stride;
         T* gK = reinterpret_cast<T*>(gbase);
         T* gV = gK + KC * TR::KPAD;
@@ -541,69 +636,72 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void attn_fwd_kernel(AttnParams p) 
                     grows[lane] = (e >= 0 && e < p.N_csa) ? ((((long long)b * p.N_csa + e) * p.Hkv + g) * D) : -1;
                 }
                 wave_lds_sync();
-                bool anyv = lane < KC ? grows[lane] >= 0 : false;
+                const bool anyv = lane < KC ? grows[lane] >= 0 : false;
                 if (!__any(anyv)) {
                     wave_lds_sync();
                     continue;
                 }
                 TR::stage(gK, gV, TR::GVST, kc, vc, grows, KC, lane, 64);
                 wave_lds_sync();
-                float x[8], s[8];
-                TR::scores(gK, 0, lane, qf, s);
+                float x[8], sc[8];
+                TR::scores(gK, 0, lane, qf, sc);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const bool vis = valid && ql == qq && grows[TR::key_of(q4, j)] >= 0;
-                    x[j] = vis ? s[j] * p.scale_log2 : -INFINITY;
+                    x[j] = vis ? sc[j] * p.scale_log2 : -INFINITY;
                 }
-                softmax_pv<T, D>(sc, x, gV, TR::GVST, 0, lane);
+                softmax_pv<T, D>(S, x, gV, TR::GVST, 0, lane);
                 wave_lds_sync();
             }
         }
+    };
+
+    // ---- the branch schedule
+    if (do_win) {
+        stream(kraw, vraw, 0, wlen, ITEM_WIN);
+        if (!p.nsplit) fold(gate[2]);
+    }
+    if (do_csa) {
+        if (dense_csa) stream(kcsa, vcsa, 0, c_hi, ITEM_CSA);
+        else {
+            __syncthreads();  // the stream buffers become the per-wave gather tiles
+            gather();
+            __syncthreads();
+        }
+        if (!p.nsplit) {
+            fold(gate[1]);
+            if (do_hca) {
+                S.init();
+                stream(kraw, vraw, 0, wlen, ITEM_WIN);
+            }
+        }
+    }
+    if (do_hca) {
+        stream(khca, vhca, h_lo, h_hi, ITEM_HCA);
+        if (!p.nsplit) fold(gate[0]);
     }
 
     // ------------------------------------------------------------ epilogue
     if (p.nsplit) {
-        // partial state of this item for the wave's columns: [m, l, -, -, acc[D]] per column
-        // layout: ws[((wg * nsplit + item) * (MAX_WAVES*16) + col) * (D + 4) + ...]
-        State<DT>& st = do_win ? sw : (do_hca ? sh : sc);
-        const float ltot = col_sum(st.l);
-        float* dst = p.ws + (((long long)blockIdx.x) * (MAX_WAVES * 16) + col) * (D + 4);
+        // partial state of this item: [m, l, -, -, acc[D]] per column at
+        // ws[((wg * nsplit + item) * ncol + col) * (D + 4)]
+        const float ltot = col_sum(S.l);
+        float* dst = p.ws + (((long long)blockIdx.x) * p.ncol + col) * (D + 4);
         if (q4 == 0) {
-            dst[0] = st.m;
+            dst[0] = S.m;
             dst[1] = ltot;
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             *reinterpret_cast<float4*>(dst + 4 + 16 * dt + 4 * q4) =
-                make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+                make_float4(S.acc[dt][0], S.acc[dt][1], S.acc[dt][2], S.acc[dt][3]);
         return;
     }
     if (!valid) return;
-    const float lw = col_sum(sw.l);
-    const float lh = col_sum(sh.l);
-    const float lc = col_sum(sc.l);
-    float ah = 0.f, bh = 0.f, ac = 0.f, bc = 0.f;
-    if (use_hca) {
-        const float m = fmaxf(sw.m, sh.m);
-        const float wa = __builtin_amdgcn_exp2f(sw.m - m), wb = __builtin_amdgcn_exp2f(sh.m - m);
-        const float den = wa * lw + wb * lh;
-        ah = gate[0] * wa / den;
-        bh = gate[0] * wb / den;
-    }
-    if (use_csa) {
-        const float m = fmaxf(sw.m, sc.m);
-        const float wa = __builtin_amdgcn_exp2f(sw.m - m), wb = __builtin_amdgcn_exp2f(sc.m - m);
-        const float den = wa * lw + wb * lc;
-        ac = gate[1] * wa / den;
-        bc = gate[1] * wb / den;
-    }
-    const float aw = gate[2] / lw + ah + ac;  // coefficient of the window accumulator
     T* orow = reinterpret_cast<T*>(p.out) + (((long long)b * p.Tq + qi) * p.H + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        float v4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = aw * sw.acc[dt][r] + bh * sh.acc[dt][r] + bc * sc.acc[dt][r];
+        float v4[4] = {oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]};
         TR::store_out(orow + 16 * dt + 4 * q4, v4);
     }
 }
@@ -613,12 +711,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     constexpr int DQ = D / 4;
-    const long long ncols_total = (long long)p.B * p.Hkv * p.nqt * (MAX_WAVES * 16);
+    const long long ncols_total = (long long)p.B * p.Hkv * p.nqt * p.ncol;
     if (gid >= ncols_total * DQ) return;
     const int dq = (int)(gid % DQ);
     const long long cg = gid / DQ;           // global column
-    const int col = (int)(cg % (MAX_WAVES * 16));
-    const long long wg = cg / (MAX_WAVES * 16);
+    const int col = (int)(cg % p.ncol);
+    const long long wg = cg / p.ncol;
     const int qt = (int)(wg % p.nqt);
     const long long bg = wg / p.nqt;
     const int g = (int)(bg % p.Hkv);
@@ -633,7 +731,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const bool use_hca = p.has_hca && p.n_hca_items > 0;
     const bool use_csa = p.has_csa && p.nsplit > p.n_win_items + p.n_hca_items;
     auto part = [&](int item) -> const float* {
-        return p.ws + ((wg * p.nsplit + item) * (MAX_WAVES * 16) + col) * (D + 4);
+        return p.ws + ((wg * p.nsplit + item) * p.ncol + col) * (D + 4);
     };
     // merge a range of items into (m, l, acc4)
     auto merge = [&](int it0, int it1, float& m, float& l, float* a) {
@@ -754,11 +852,18 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.k = has_csa ? a->k : 0;
     const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.QW = G >= 64 ? 1 : 64 / G;
+    // 8 waves (128 columns) per workgroup for prefill: every staged K/V tile is
+    // shared by twice as many (query, head) columns; 4 waves for short launches.
+    const bool small = (long long)a->B * a->Hkv * ((long long)a->Tq * G) < 128LL * 1024;
+    // the CSA gather path keeps per-wave gather tiles: 4 waves keep LDS in budget
+    const bool gather_likely = has_csa && !(G < 8 && a->N_csa <= 4096);
+    (void)small;
+    (void)gather_likely;
+    pl.waves = 4;
+    p.ncol = pl.waves * 16;
+    p.QW = G >= p.ncol ? 1 : p.ncol / G;
+    if (G > p.ncol) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: H/Hkv=%d too large", G);
     p.nqt = (a->Tq + p.QW - 1) / p.QW;
-    const int cols = std::min(p.QW, a->Tq) * G;
-    pl.waves = (cols + 15) / 16;
-    if (pl.waves > MAX_WAVES) pl.waves = MAX_WAVES;
 
     const long long nwg = (long long)a->B * a->Hkv * p.nqt;
     // split the key list when there are too few workgroups to fill the chip
@@ -774,7 +879,7 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
         p.n_hca_items = (int)((nh_max + p.split_keys - 1) / p.split_keys);
         const int n_csa_items = has_csa ? (a->k + p.split_keys - 1) / p.split_keys : 0;
         p.nsplit = p.n_win_items + p.n_hca_items + n_csa_items;
-        pl.ws_bytes = (size_t)nwg * p.nsplit * (MAX_WAVES * 16) * (a->d + 4) * sizeof(float);
+        pl.ws_bytes = (size_t)nwg * p.nsplit * p.ncol * (a->d + 4) * sizeof(float);
         pl.grid = nwg * p.nsplit;
     } else {
         pl.grid = nwg;
@@ -783,8 +888,9 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     const bool bf = a->dtype == SHATTN_DTYPE_BF16;
     const int esz = bf ? 2 : 4;
     const int kpad = bf ? a->d + 8 : a->d + 4;
-    const size_t shared_b = bf ? (size_t)(KT * kpad + a->d * (KT + 8)) * esz
-                               : (size_t)(2 * KT * kpad) * esz;
+    // two staged tiles (double buffer)
+    const size_t tile_b = bf ? (size_t)(KT * kpad + a->d * (KT + 8)) * esz : (size_t)(2 * KT * kpad) * esz;
+    const size_t shared_b = 2 * tile_b;
     const size_t gather_b = bf ? (size_t)(KC * kpad + a->d * (KC + 8)) * esz + KC * 8
                                : (size_t)(2 * KC * kpad) * esz + KC * 8;
     p.csa_mode = CSA_NONE;
@@ -806,6 +912,7 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
             lds = std::max(lds, (size_t)p.lds_gather_stride * pl.waves);
         }
     }
+    if (lds > 160 * 1024) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: LDS budget exceeded");
     pl.lds = lds;
     return SHATTN_OK;
 }
@@ -821,11 +928,11 @@ extern "C" size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
     return pl.ws_bytes;
 }
 
-template <typename T, int D>
-static int launch_attn(Plan& pl, hipStream_t s) {
+template <typename T, int D, int NW>
+static int launch_attn_nw(Plan& pl, hipStream_t s) {
     if (pl.lds > 64 * 1024) {
         // dynamic LDS beyond 64 KiB must be opted into per kernel
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D, NW>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -833,17 +940,21 @@ static int launch_attn(Plan& pl, hipStream_t s) {
                         pl.lds, hipGetErrorString(e));
         }
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3((unsigned)pl.grid), dim3(pl.waves * 64), pl.lds, s,
-                       pl.p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s, pl.p);
     hipError_t le = hipGetLastError();
     if (le != hipSuccess)
         return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
-                    pl.grid, pl.waves * 64, pl.lds, hipGetErrorString(le));
+                    pl.grid, NW * 64, pl.lds, hipGetErrorString(le));
     if (!pl.p.nsplit) return SHATTN_OK;
-    const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * (MAX_WAVES * 16) * (D / 4);
+    const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * pl.p.ncol * (D / 4);
     hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        pl.p);
     return check_launch("hybrid_sparse_attn_fwd (combine)");
+}
+
+template <typename T, int D>
+static int launch_attn(Plan& pl, hipStream_t s) {
+    return pl.waves == 8 ? launch_attn_nw<T, D, 8>(pl, s) : launch_attn_nw<T, D, 4>(pl, s);
 }
 
 extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {

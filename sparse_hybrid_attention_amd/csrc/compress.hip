@@ -214,3 +214,245 @@ extern "C" int hca_compress_kv(const void* k, const void* v, const float* zk, co
     }
     return check_launch("hca_compress_kv");
 }
+
+// ---------------------------------------------------------------------------
+// Both ratios in one pass: every raw row is read once and feeds the CSA entry
+// (ratio m1 <= 8, m1 | 8) and the HCA entry (ratio m2, 8 | m2) it belongs to.
+// Thread = (channel group j, 8 consecutive rows s of an m2-block).  The m1
+// entries are complete inside the thread; the m2 partial sums of the R = m2/8
+// threads of a channel group are combined in LDS in a fixed order.
+namespace shattn {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void compress_dual_kernel(
+    const T* __restrict__ x0, const T* __restrict__ x1,
+    const float* __restrict__ za0, const float* __restrict__ za1, T* __restrict__ ya0, T* __restrict__ ya1, int m1,
+    const float* __restrict__ zb0, const float* __restrict__ zb1, T* __restrict__ yb0, T* __restrict__ yb1, int m2,
+    int T_len, int C, int N1, int N2, int R, int NGt, long long total_blocks, int blocks_per_wg) {
+    constexpr int VW = Elem<T>::kVec;
+    const bool second = blockIdx.z != 0;
+    const T* __restrict__ x = second ? x1 : x0;
+    const float* __restrict__ za = second ? za1 : za0;
+    const float* __restrict__ zb = second ? zb1 : zb0;
+    T* __restrict__ ya = second ? ya1 : ya0;
+    T* __restrict__ yb = second ? yb1 : yb0;
+
+    __shared__ float red[2][kThreads * VW];
+
+    const int NG = C / VW;
+    const int tid = threadIdx.x;
+    const int s = tid / NGt;
+    const int jl = tid - s * NGt;
+    const int j = blockIdx.x * NGt + jl;
+    const bool active = (s < R) && (j < NG);
+
+    // ---- m2 weights of this thread's 8 positions (softmax over all m2 positions)
+    float pb[kPPT][VW];
+    float mx[VW];
+#pragma unroll
+    for (int v = 0; v < VW; ++v) mx[v] = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kPPT; ++q) {
+        const int i = s * kPPT + q;
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            pb[q][v] = active ? zb[(size_t)i * C + (size_t)j * VW + v] : -INFINITY;
+            mx[v] = fmaxf(mx[v], pb[q][v]);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < VW; ++v) red[0][tid * VW + v] = mx[v];
+    __syncthreads();
+    if (active) {
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            float a = -INFINITY;
+            for (int r = 0; r < R; ++r) a = fmaxf(a, red[0][(r * NGt + jl) * VW + v]);
+            mx[v] = a;
+        }
+    }
+    float sum[VW];
+#pragma unroll
+    for (int v = 0; v < VW; ++v) sum[v] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kPPT; ++q)
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            const float e = active ? __expf(pb[q][v] - mx[v]) : 0.f;
+            pb[q][v] = e;
+            sum[v] += e;
+        }
+#pragma unroll
+    for (int v = 0; v < VW; ++v) red[1][tid * VW + v] = sum[v];
+    __syncthreads();
+    if (active) {
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            float a = 0.f;
+            for (int r = 0; r < R; ++r) a += red[1][(r * NGt + jl) * VW + v];
+            const float inv = 1.0f / a;
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q) pb[q][v] *= inv;
+        }
+    }
+    // ---- m1 weights (the thread sees whole m1-blocks)
+    float pa[kPPT][VW];   // pa[q] = weight of row q of the thread's 8 rows in its m1-block
+    {
+        float am[VW], as[VW];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) { am[v] = -INFINITY; as[v] = 0.f; }
+#pragma unroll
+        for (int q = 0; q < kPPT; ++q) {
+            if (q < m1) {
+#pragma unroll
+                for (int v = 0; v < VW; ++v) {
+                    pa[q][v] = active ? za[(size_t)q * C + (size_t)j * VW + v] : 0.f;
+                    am[v] = fmaxf(am[v], pa[q][v]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kPPT; ++q)
+            if (q < m1)
+#pragma unroll
+                for (int v = 0; v < VW; ++v) {
+                    pa[q][v] = __expf(pa[q][v] - am[v]);
+                    as[v] += pa[q][v];
+                }
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            const float inv = 1.0f / as[v];
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q) pa[q][v] = q < m1 ? pa[q][v] * inv : pa[q % m1][v];
+        }
+    }
+    __syncthreads();
+
+    const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
+    long long bc1 = bc0 + blocks_per_wg;
+    if (bc1 > total_blocks) bc1 = total_blocks;
+    int buf = 0;
+    for (long long bc = bc0; bc < bc1; ++bc) {
+        const long long b = bc / N2;
+        const long long c = bc - b * N2;
+        float acc[VW];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) acc[v] = 0.f;
+        if (active) {
+            const long long row0 = (long long)c * m2 + (long long)s * kPPT;  // first row in the sequence
+            const T* __restrict__ src = x + ((size_t)b * T_len + row0) * C + (size_t)j * VW;
+            uint4 raw[kPPT];
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q) raw[q] = ld16_stream(src + (size_t)q * C);
+            float f[kPPT][VW];
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q) Elem<T>::unpack(raw[q], f[q]);
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q)
+#pragma unroll
+                for (int v = 0; v < VW; ++v) acc[v] = fmaf(pb[q][v], f[q][v], acc[v]);
+            // the 8 / m1 entries of ratio m1 covered by these rows
+#pragma unroll
+            for (int a0 = 0; a0 < kPPT; a0 += 1) {
+                if (a0 % m1 != 0) continue;
+                float o[VW];
+#pragma unroll
+                for (int v = 0; v < VW; ++v) o[v] = 0.f;
+#pragma unroll
+                for (int q = 0; q < kPPT; ++q)
+                    if (q >= a0 && q < a0 + m1)
+#pragma unroll
+                        for (int v = 0; v < VW; ++v) o[v] = fmaf(pa[q - a0][v], f[q][v], o[v]);
+                const long long e1 = (row0 + a0) / m1;   // entry index of ratio m1
+                if (e1 < N1)
+                    *reinterpret_cast<uint4*>(ya + ((size_t)b * N1 + e1) * C + (size_t)j * VW) = Elem<T>::pack(o);
+            }
+        }
+        float* r = red[buf];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) r[tid * VW + v] = acc[v];
+        __syncthreads();
+        T* __restrict__ dst = yb + (size_t)bc * C;
+        const int nch = NGt * VW;
+        for (int t = tid; t < nch; t += kThreads) {
+            const int jl2 = t / VW, v2 = t - jl2 * VW;
+            const int j2 = blockIdx.x * NGt + jl2;
+            if (j2 < NG) {
+                float a = 0.f;
+                for (int rr = 0; rr < R; ++rr) a += r[(rr * NGt + jl2) * VW + v2];
+                Elem<T>::store1(dst + (size_t)j2 * VW + v2, a);
+            }
+        }
+        buf ^= 1;   // next block writes the other buffer: one barrier per block
+    }
+}
+
+}  // namespace
+}  // namespace shattn
+
+extern "C" int hca_compress_kv_dual(const void* k, const void* v, const float* zk1, const float* zv1, void* kc1,
+                                    void* vc1, int m1, const float* zk2, const float* zv2, void* kc2, void* vc2,
+                                    int m2, int B, int T, int Hkv, int d, int dtype, void* stream) {
+    if (dtype != SHATTN_DTYPE_BF16 && dtype != SHATTN_DTYPE_F32)
+        return fail(SHATTN_EINVAL, "hca_compress_kv_dual: unknown dtype %d", dtype);
+    if (B < 0 || T < 0 || Hkv < 1 || d < 1 || m1 < 1 || m2 < 1)
+        return fail(SHATTN_EINVAL, "hca_compress_kv_dual: bad sizes B=%d T=%d Hkv=%d d=%d m1=%d m2=%d", B, T,
+                    Hkv, d, m1, m2);
+    if (d != 64 && d != 128)
+        return fail(SHATTN_EUNSUPPORTED, "hca_compress_kv_dual: d=%d (supported: 64, 128)", d);
+    if (8 % m1 != 0 || m2 % 8 != 0 || m2 > 1024)
+        return fail(SHATTN_EUNSUPPORTED,
+                    "hca_compress_kv_dual: needs m1 in {1,2,4,8} and m2 a multiple of 8 up to 1024 (m1=%d m2=%d)",
+                    m1, m2);
+    const int N1 = T / m1, N2 = T / m2;
+    if (B == 0 || N1 == 0) return SHATTN_OK;
+    if (!k || !v || !zk1 || !zv1 || !kc1 || !vc1 || !zk2 || !zv2 || (N2 > 0 && (!kc2 || !vc2)))
+        return fail(SHATTN_EINVAL, "hca_compress_kv_dual: null pointer");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(kc1) || !aligned16(vc1) ||
+        (N2 > 0 && (!aligned16(kc2) || !aligned16(vc2))))
+        return fail(SHATTN_EINVAL, "hca_compress_kv_dual: tensors must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the rows past the last full m2-block only feed ratio m1: compress them on their own
+    const int tail_rows = T - N2 * m2;
+    if (N2 > 0) {
+        const int C = Hkv * d;
+        const int VW = dtype == SHATTN_DTYPE_BF16 ? 8 : 4;
+        const int NG = C / VW;
+        const int R = m2 / kPPT;
+        int NGt = kThreads / R;
+        if (NGt > NG) NGt = NG;
+        const int tiles = (NG + NGt - 1) / NGt;
+        const long long total = (long long)B * N2;
+        long long per = (total * tiles + 1023) / 1024;
+        if (per < 1) per = 1;
+        if (per > 64) per = 64;
+        const long long ywgs = (total + per - 1) / per;
+        dim3 grid(tiles, (unsigned)ywgs, 2);
+        if (dtype == SHATTN_DTYPE_BF16)
+            hipLaunchKernelGGL(compress_dual_kernel<bf16_t>, grid, dim3(kThreads), 0, s, (const bf16_t*)k,
+                               (const bf16_t*)v, zk1, zv1, (bf16_t*)kc1, (bf16_t*)vc1, m1, zk2, zv2, (bf16_t*)kc2,
+                               (bf16_t*)vc2, m2, T, C, N1, N2, R, NGt, total, (int)per);
+        else
+            hipLaunchKernelGGL(compress_dual_kernel<float>, grid, dim3(kThreads), 0, s, (const float*)k,
+                               (const float*)v, zk1, zv1, (float*)kc1, (float*)vc1, m1, zk2, zv2, (float*)kc2,
+                               (float*)vc2, m2, T, C, N1, N2, R, NGt, total, (int)per);
+        const int rc = check_launch("hca_compress_kv_dual");
+        if (rc) return rc;
+    }
+    if (tail_rows >= m1) {
+        // entries of ratio m1 past the last m2-block: [N2*m2/m1, N1)
+        const long long e0 = (long long)N2 * m2 / m1;
+        const size_t esz = dtype == SHATTN_DTYPE_BF16 ? 2 : 4;
+        const size_t C = (size_t)Hkv * d;
+        for (int b = 0; b < B; ++b) {
+            const char* kb = (const char*)k + ((size_t)b * T + (size_t)N2 * m2) * C * esz;
+            const char* vb = (const char*)v + ((size_t)b * T + (size_t)N2 * m2) * C * esz;
+            char* kcb = (char*)kc1 + ((size_t)b * N1 + e0) * C * esz;
+            char* vcb = (char*)vc1 + ((size_t)b * N1 + e0) * C * esz;
+            const int rc = hca_compress_kv(kb, vb, zk1, zv1, kcb, vcb, 1, tail_rows, Hkv, d, m1, dtype, stream);
+            if (rc) return rc;
+        }
+    }
+    return SHATTN_OK;
+}

@@ -102,7 +102,7 @@ struct WaveBuf {
 };
 
 // k-th largest key among keys[0..cnt), 1 <= kk <= cnt.  *n_gt = #keys > result.
-__device__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
+__device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
     const int lane = __lane_id();
     uint32_t prefix = 0u, pmask = 0u;
     int want = kk;
@@ -153,7 +153,7 @@ __device__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* h
 }
 
 // Stable in-place compaction: keep entries with key >= lo.  Returns new count.
-__device__ int compact_ge(uint32_t* keys, int32_t* ids, int cnt, uint32_t lo) {
+__device__ __noinline__ int compact_ge(uint32_t* keys, int32_t* ids, int cnt, uint32_t lo) {
     const int lane = __lane_id();
     int out = 0;
     for (int base = 0; base < cnt; base += 64) {
@@ -180,7 +180,7 @@ __device__ int compact_ge(uint32_t* keys, int32_t* ids, int cnt, uint32_t lo) {
 }
 
 // Stable: keep entries with key > kth and the first `need` entries with key == kth.
-__device__ int compact_topk(uint32_t* keys, int32_t* ids, int cnt, uint32_t kth, int need) {
+__device__ __noinline__ int compact_topk(uint32_t* keys, int32_t* ids, int cnt, uint32_t kth, int need) {
     const int lane = __lane_id();
     int out = 0, eq_seen = 0;
     for (int base = 0; base < cnt; base += 64) {
@@ -212,7 +212,7 @@ __device__ int compact_topk(uint32_t* keys, int32_t* ids, int cnt, uint32_t kth,
 
 // Streaming compaction of a full buffer.  Returns the new count; *tau_key is the
 // new insertion threshold (keys >= tau_key may enter).
-__device__ int compact_stream(WaveBuf& wb, int cnt, int kk, float delta, int cap, int slack,
+__device__ __noinline__ int compact_stream(WaveBuf& wb, int cnt, int kk, float delta, int cap, int slack,
                               uint32_t* tau_key) {
     int n_gt;
     const uint32_t kth = radix_kth(wb.keys, cnt, kk, wb.hist, &n_gt);
@@ -234,8 +234,10 @@ template <typename T, int HI, int DI>
 __device__ double exact_score(const T* __restrict__ qrow /* [HI][DI] */, const T* __restrict__ krow,
                               const float* __restrict__ wrow) {
     double s = 0.0;
+#pragma unroll 1
     for (int h = 0; h < HI; ++h) {
         double dot = 0.0;
+#pragma unroll 1
         for (int e = 0; e < DI; e += 16 / (int)sizeof(T)) {
             float qa[8], ka[8];
             Elem<T>::unpack(ld16(qrow + h * DI + e), qa);
@@ -250,7 +252,7 @@ __device__ double exact_score(const T* __restrict__ qrow /* [HI][DI] */, const T
 
 // Final exact selection of one query and output of its idx row.
 template <typename T, int HI, int DI>
-__device__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k, float delta, int mcap,
+__device__ __noinline__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k, float delta, int mcap,
                              const T* __restrict__ qrow, const T* __restrict__ kI_b,
                              const float* __restrict__ wrow, int32_t* __restrict__ out_row) {
     const int lane = __lane_id();
@@ -473,14 +475,14 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     }
 
     // ---- per (row tile, slot) state of the lane's queries
-    int cnt[MAX_RT][4];
-    uint32_t tau[MAX_RT][4];
-    long long nv[MAX_RT][4];
-    long long nv_max = 0;
+    int cnt[MAX_RT][SLOTS];
+    uint32_t tau[MAX_RT][SLOTS];
+    int nv[MAX_RT][SLOTS];
+    int nv_max = 0;
 #pragma unroll
     for (int rt = 0; rt < MAX_RT; ++rt)
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
+        for (int sl = 0; sl < SLOTS; ++sl) {
             cnt[rt][sl] = 0;
             tau[rt][sl] = 0u;
             int qw;
@@ -492,26 +494,25 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
             qw += rt * QPT;
             const int i = q0 + qw;
             const bool ok = rt < RT && sl < SLOTS && qw < qpw && i < p.Tq;
-            nv[rt][sl] = ok ? n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
+            nv[rt][sl] = ok ? (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
             nv_max = nv[rt][sl] > nv_max ? nv[rt][sl] : nv_max;
         }
     // wave-wide maximum of visible entries
-    {
-        long long v = nv_max;
-        for (int off = 32; off > 0; off >>= 1) {
-            const long long o = __shfl_xor(v, off);
-            v = o > v ? o : v;
-        }
-        nv_max = v;
+    for (int off = 32; off > 0; off >>= 1) {
+        const int o = __shfl_xor(nv_max, off);
+        nv_max = o > nv_max ? o : nv_max;
     }
     float kmax2 = 0.f;
     wave_lds_sync();
 
-    // ---- stream the candidates in index order
-    for (long long c0 = 0; c0 < nv_max; c0 += TILE) {
+    // ---- stream the candidates in index order; B fragments of the next PF
+    // tiles are loaded while the current PF tiles are scored
+    auto load_b = [&](long long c0, typename MM::F* bf) {
         const long long c = c0 + rho;
-        typename MM::F bf[MM::KS];
         MM::load_a(kI_b + (c < p.N ? c : 0) * DI, c < p.N, q4, bf);
+    };
+    auto process_tile = [&](long long c0, const typename MM::F* bf) {
+        const long long c = c0 + rho;
         float n2 = MM::sq(bf);
         n2 += __shfl_xor(n2, 16);
         n2 += __shfl_xor(n2, 32);
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
             bool own[4];
             const int ns = tile_scores<HI>(acc, wr[rt], q4, s, qs, own);
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
+            for (int sl = 0; sl < SLOTS; ++sl) {
                 if (sl >= ns) break;
                 const uint32_t key = fkey(s[sl]);
                 const bool ins = own[sl] && c < nv[rt][sl] && key >= tau[rt][sl];
@@ -563,11 +564,11 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                     const int src = 16 * g4;
                     const int qw = rt * QPT + __shfl(qw_l, src);
                     const int cq = __shfl(cnt[rt][sl], src);
-                    const long long nvq = __shfl(nv[rt][sl], src);
+                    const int nvq = __shfl(nv[rt][sl], src);
                     WaveBuf q = wb;
                     q.keys = keys_all + qw * cap;
                     q.ids = ids_all + qw * cap;
-                    const int kk = (int)std::min<long long>(p.k, nvq);
+                    const int kk = min(p.k, nvq);
                     uint32_t tk;
                     const int nc = compact_stream(q, cq, kk, delta * qn[qw], cap, TILE, &tk);
                     if (q4 == g4) {
@@ -577,6 +578,26 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                 }
             }
         }
+    };
+    constexpr int PF = 2;
+    typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
+    auto group = [&](long long g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+        const long long g1 = g0 + PF * TILE;
+        if (g1 < nv_max) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+            if (g0 + t * TILE < nv_max) process_tile(g0 + t * TILE, cur[t]);
+    };
+    if (nv_max > 0) {
+#pragma unroll
+        for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
+    }
+    for (long long g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
+        group(g0, bq0, bq1);
+        if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
     }
 
     // ---- final exact selection per query, output
@@ -600,11 +621,11 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                 if (qw >= qpw || i >= p.Tq) continue;
                 const int src = 16 * g4;
                 const int cq = __shfl(cnt[rt][sl], src);
-                const long long nvq = __shfl(nv[rt][sl], src);
+                const int nvq = __shfl(nv[rt][sl], src);
                 WaveBuf q = wb;
                 q.keys = keys_all + qw * cap;
                 q.ids = ids_all + qw * cap;
-                const int k_eff = (int)std::min<long long>(p.k, nvq);
+                const int k_eff = min(p.k, nvq);
                 const long long row = (long long)b * p.Tq + i;
                 final_select<T, HI, DI>(q, cq, k_eff, p.k, delta0 * qn[qw], mcap, qI + row * HI * DI, kI_b,
                                         p.w + row * HI, p.idx + row * p.k);
@@ -834,7 +855,7 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     p.m = m;
     p.W = W;
     p.q_pos0 = q_pos0;
-    p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
+    p.cap = ((k + std::max(192, k / 2)) + 63) / 64 * 64;
     p.mcap = std::min(p.cap, 256);
     // |float32 score - exact| <= err_c * sum_h |w_h| ||q_h|| * max ||k||:
     // 2*d_idx*u for the dot products (any summation order, rounding or
