@@ -41,11 +41,13 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 
     const int NG = C / VW;
     const int tid = threadIdx.x;
-    const int s = tid / NGt;          // position subset
+    const int s = tid / NGt;          // position subset (R > 1) or block lane (R == 1)
     const int jl = tid - s * NGt;     // channel group within the tile
     const int j = blockIdx.x * NGt + jl;
-    const bool active = (s < R) && (j < NG);
+    const int nsub = kThreads / NGt;  // threads per channel group in the workgroup
+    const bool active = (R == 1 ? s < nsub : s < R) && (j < NG);
     const int ppt = (m < kPPT) ? m : kPPT;
+    const int spos = R == 1 ? 0 : s;  // which positions of the block this thread owns
 
     // ---- softmax weights of this thread's positions and channels
     float p[kPPT][VW];
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     for (int v = 0; v < VW; ++v) mx[v] = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kPPT; ++q) {
-        const int i = s * ppt + q;
+        const int i = spos * ppt + q;
         const bool ok = active && q < ppt && i < m;
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
@@ -113,6 +115,42 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
     long long bc1 = bc0 + blocks_per_wg;
     if (bc1 > total_blocks) bc1 = total_blocks;
+    if (R == 1) {
+        // whole blocks per thread: thread s of a channel group takes blocks
+        // bc0 + s, bc0 + s + nsub, ...; two blocks' loads are in flight at once
+        auto load_block = [&](long long bc, uint4* raw) {
+            const long long b = bc / N;
+            const long long c = bc - b * N;
+            const T* __restrict__ src = x + ((size_t)b * T_len + (size_t)c * m) * C + (size_t)j * VW;
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q)
+                raw[q] = q < ppt ? ld16_stream(src + (size_t)q * C) : make_uint4(0, 0, 0, 0);
+        };
+        auto finish_block = [&](long long bc, const uint4* raw) {
+            float acc[VW];
+#pragma unroll
+            for (int v = 0; v < VW; ++v) acc[v] = 0.f;
+#pragma unroll
+            for (int q = 0; q < kPPT; ++q) {
+                if (q >= ppt) break;
+                float f[VW];
+                Elem<T>::unpack(raw[q], f);
+#pragma unroll
+                for (int v = 0; v < VW; ++v) acc[v] = fmaf(p[q][v], f[v], acc[v]);
+            }
+            *reinterpret_cast<uint4*>(y + (size_t)bc * C + (size_t)j * VW) = Elem<T>::pack(acc);
+        };
+        if (!active) return;
+        for (long long bc = bc0 + s; bc < bc1; bc += 2 * nsub) {
+            uint4 r0[kPPT], r1[kPPT];
+            const bool two = bc + nsub < bc1;
+            load_block(bc, r0);
+            if (two) load_block(bc + nsub, r1);
+            finish_block(bc, r0);
+            if (two) finish_block(bc + nsub, r1);
+        }
+        return;
+    }
     for (long long bc = bc0; bc < bc1; ++bc) {
         const long long b = bc / N;
         const long long c = bc - b * N;
@@ -139,26 +177,21 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             }
         }
         T* __restrict__ dst = y + (size_t)bc * C;
-        if (R == 1) {
-            if (active)
-                *reinterpret_cast<uint4*>(dst + (size_t)j * VW) = Elem<T>::pack(acc);
-        } else {
 #pragma unroll
-            for (int v = 0; v < VW; ++v) red[tid * VW + v] = acc[v];
-            __syncthreads();
-            // thread t finishes channel t of the tile: sum of R partials in order
-            const int nch = NGt * VW;
-            for (int t = tid; t < nch; t += kThreads) {
-                const int jl2 = t / VW, v2 = t - jl2 * VW;
-                const int j2 = blockIdx.x * NGt + jl2;
-                if (j2 < NG) {
-                    float a = 0.f;
-                    for (int r = 0; r < R; ++r) a += red[(r * NGt + jl2) * VW + v2];
-                    Elem<T>::store1(dst + (size_t)j2 * VW + v2, a);
-                }
+        for (int v = 0; v < VW; ++v) red[tid * VW + v] = acc[v];
+        __syncthreads();
+        // thread t finishes channel t of the tile: sum of R partials in order
+        const int nch = NGt * VW;
+        for (int t = tid; t < nch; t += kThreads) {
+            const int jl2 = t / VW, v2 = t - jl2 * VW;
+            const int j2 = blockIdx.x * NGt + jl2;
+            if (j2 < NG) {
+                float a = 0.f;
+                for (int r = 0; r < R; ++r) a += red[(r * NGt + jl2) * VW + v2];
+                Elem<T>::store1(dst + (size_t)j2 * VW + v2, a);
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
@@ -195,10 +228,13 @@ extern "C" int hca_compress_kv(const void* k, const void* v, const float* zk, co
     if (NGt > NG) NGt = NG;
     const int tiles = (NG + NGt - 1) / NGt;
     const long long total = (long long)B * N;
-    // aim at ~2048 workgroups (8 per CU) per slice
-    long long per = (total * tiles + 2047) / 2048;
+    // aim at ~1024 workgroups per slice; whole-block threads (R == 1) take
+    // several blocks each
+    const int nsub = kThreads / NGt;
+    long long per = (total * tiles + 1023) / 1024;
+    if (R == 1) per = ((per + 2 * nsub - 1) / (2 * nsub)) * (2 * nsub);
     if (per < 1) per = 1;
-    if (per > 64) per = 64;
+    if (per > 4096) per = 4096;
     const long long ywgs = (total + per - 1) / per;
     if (ywgs > 2147483647LL) return fail(SHATTN_EUNSUPPORTED, "hca_compress_kv: too many blocks");
     dim3 grid(tiles, (unsigned)ywgs, 2);
@@ -224,13 +260,14 @@ extern "C" int hca_compress_kv(const void* k, const void* v, const float* zk, co
 namespace shattn {
 namespace {
 
-template <typename T>
+template <typename T, int M1, int PPT>
 __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
     const T* __restrict__ x0, const T* __restrict__ x1,
-    const float* __restrict__ za0, const float* __restrict__ za1, T* __restrict__ ya0, T* __restrict__ ya1, int m1,
+    const float* __restrict__ za0, const float* __restrict__ za1, T* __restrict__ ya0, T* __restrict__ ya1,
     const float* __restrict__ zb0, const float* __restrict__ zb1, T* __restrict__ yb0, T* __restrict__ yb1, int m2,
     int T_len, int C, int N1, int N2, int R, int NGt, long long total_blocks, int blocks_per_wg) {
     constexpr int VW = Elem<T>::kVec;
+    static_assert(PPT % M1 == 0, "a thread must cover whole m1-blocks");
     const bool second = blockIdx.z != 0;
     const T* __restrict__ x = second ? x1 : x0;
     const float* __restrict__ za = second ? za1 : za0;
@@ -247,14 +284,27 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
     const int j = blockIdx.x * NGt + jl;
     const bool active = (s < R) && (j < NG);
 
-    // ---- m2 weights of this thread's 8 positions (softmax over all m2 positions)
-    float pb[kPPT][VW];
+    const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
+    long long bc1 = bc0 + blocks_per_wg;
+    if (bc1 > total_blocks) bc1 = total_blocks;
+    auto load_rows = [&](long long bc, uint4* raw) {
+        const long long b = bc / N2;
+        const long long c = bc - b * N2;
+        const T* __restrict__ src = x + ((size_t)b * T_len + (size_t)c * m2 + (size_t)s * PPT) * C + (size_t)j * VW;
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) raw[q] = ld16_stream(src + (size_t)q * C);
+    };
+    uint4 nxt[PPT];
+    if (active && bc0 < bc1) load_rows(bc0, nxt);   // first block in flight during the setup
+
+    // ---- m2 weights of this thread's PPT positions (softmax over all m2 positions)
+    float pb[PPT][VW];
     float mx[VW];
 #pragma unroll
     for (int v = 0; v < VW; ++v) mx[v] = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kPPT; ++q) {
-        const int i = s * kPPT + q;
+    for (int q = 0; q < PPT; ++q) {
+        const int i = s * PPT + q;
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
             pb[q][v] = active ? zb[(size_t)i * C + (size_t)j * VW + v] : -INFINITY;
@@ -276,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
 #pragma unroll
     for (int v = 0; v < VW; ++v) sum[v] = 0.f;
 #pragma unroll
-    for (int q = 0; q < kPPT; ++q)
+    for (int q = 0; q < PPT; ++q)
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
             const float e = active ? __expf(pb[q][v] - mx[v]) : 0.f;
@@ -293,45 +343,38 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
             for (int r = 0; r < R; ++r) a += red[1][(r * NGt + jl) * VW + v];
             const float inv = 1.0f / a;
 #pragma unroll
-            for (int q = 0; q < kPPT; ++q) pb[q][v] *= inv;
+            for (int q = 0; q < PPT; ++q) pb[q][v] *= inv;
         }
     }
     // ---- m1 weights (the thread sees whole m1-blocks)
-    float pa[kPPT][VW];   // pa[q] = weight of row q of the thread's 8 rows in its m1-block
+    float pa[M1][VW];
     {
         float am[VW], as[VW];
 #pragma unroll
         for (int v = 0; v < VW; ++v) { am[v] = -INFINITY; as[v] = 0.f; }
 #pragma unroll
-        for (int q = 0; q < kPPT; ++q) {
-            if (q < m1) {
+        for (int q = 0; q < M1; ++q)
 #pragma unroll
-                for (int v = 0; v < VW; ++v) {
-                    pa[q][v] = active ? za[(size_t)q * C + (size_t)j * VW + v] : 0.f;
-                    am[v] = fmaxf(am[v], pa[q][v]);
-                }
+            for (int v = 0; v < VW; ++v) {
+                pa[q][v] = active ? za[(size_t)q * C + (size_t)j * VW + v] : 0.f;
+                am[v] = fmaxf(am[v], pa[q][v]);
             }
-        }
 #pragma unroll
-        for (int q = 0; q < kPPT; ++q)
-            if (q < m1)
+        for (int q = 0; q < M1; ++q)
 #pragma unroll
-                for (int v = 0; v < VW; ++v) {
-                    pa[q][v] = __expf(pa[q][v] - am[v]);
-                    as[v] += pa[q][v];
-                }
+            for (int v = 0; v < VW; ++v) {
+                pa[q][v] = __expf(pa[q][v] - am[v]);
+                as[v] += pa[q][v];
+            }
 #pragma unroll
         for (int v = 0; v < VW; ++v) {
             const float inv = 1.0f / as[v];
 #pragma unroll
-            for (int q = 0; q < kPPT; ++q) pa[q][v] = q < m1 ? pa[q][v] * inv : pa[q % m1][v];
+            for (int q = 0; q < M1; ++q) pa[q][v] *= inv;
         }
     }
     __syncthreads();
 
-    const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
-    long long bc1 = bc0 + blocks_per_wg;
-    if (bc1 > total_blocks) bc1 = total_blocks;
     int buf = 0;
     for (long long bc = bc0; bc < bc1; ++bc) {
         const long long b = bc / N2;
@@ -340,33 +383,29 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
 #pragma unroll
         for (int v = 0; v < VW; ++v) acc[v] = 0.f;
         if (active) {
-            const long long row0 = (long long)c * m2 + (long long)s * kPPT;  // first row in the sequence
-            const T* __restrict__ src = x + ((size_t)b * T_len + row0) * C + (size_t)j * VW;
-            uint4 raw[kPPT];
+            const long long row0 = (long long)c * m2 + (long long)s * PPT;  // first row in the sequence
+            uint4 raw[PPT];
 #pragma unroll
-            for (int q = 0; q < kPPT; ++q) raw[q] = ld16_stream(src + (size_t)q * C);
-            float f[kPPT][VW];
+            for (int q = 0; q < PPT; ++q) raw[q] = nxt[q];
+            if (bc + 1 < bc1) load_rows(bc + 1, nxt);   // next block's rows in flight
+            float o[VW];
 #pragma unroll
-            for (int q = 0; q < kPPT; ++q) Elem<T>::unpack(raw[q], f[q]);
+            for (int q = 0; q < PPT; ++q) {
+                float f[VW];
+                Elem<T>::unpack(raw[q], f);
+                if (q % M1 == 0) {
 #pragma unroll
-            for (int q = 0; q < kPPT; ++q)
+                    for (int v = 0; v < VW; ++v) o[v] = 0.f;
+                }
 #pragma unroll
-                for (int v = 0; v < VW; ++v) acc[v] = fmaf(pb[q][v], f[q][v], acc[v]);
-            // the 8 / m1 entries of ratio m1 covered by these rows
-#pragma unroll
-            for (int a0 = 0; a0 < kPPT; a0 += 1) {
-                if (a0 % m1 != 0) continue;
-                float o[VW];
-#pragma unroll
-                for (int v = 0; v < VW; ++v) o[v] = 0.f;
-#pragma unroll
-                for (int q = 0; q < kPPT; ++q)
-                    if (q >= a0 && q < a0 + m1)
-#pragma unroll
-                        for (int v = 0; v < VW; ++v) o[v] = fmaf(pa[q - a0][v], f[q][v], o[v]);
-                const long long e1 = (row0 + a0) / m1;   // entry index of ratio m1
-                if (e1 < N1)
+                for (int v = 0; v < VW; ++v) {
+                    acc[v] = fmaf(pb[q][v], f[v], acc[v]);
+                    o[v] = fmaf(pa[q % M1][v], f[v], o[v]);
+                }
+                if (q % M1 == M1 - 1) {
+                    const long long e1 = (row0 + q) / M1;   // entry index of ratio m1
                     *reinterpret_cast<uint4*>(ya + ((size_t)b * N1 + e1) * C + (size_t)j * VW) = Elem<T>::pack(o);
+                }
             }
         }
         float* r = red[buf];
@@ -374,18 +413,55 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
         for (int v = 0; v < VW; ++v) r[tid * VW + v] = acc[v];
         __syncthreads();
         T* __restrict__ dst = yb + (size_t)bc * C;
+        // channel ch of the tile is summed by 4 consecutive threads (R/4 partials
+        // each), then combined in a fixed order across those 4 lanes
         const int nch = NGt * VW;
-        for (int t = tid; t < nch; t += kThreads) {
-            const int jl2 = t / VW, v2 = t - jl2 * VW;
-            const int j2 = blockIdx.x * NGt + jl2;
-            if (j2 < NG) {
-                float a = 0.f;
-                for (int rr = 0; rr < R; ++rr) a += r[(rr * NGt + jl2) * VW + v2];
-                Elem<T>::store1(dst + (size_t)j2 * VW + v2, a);
+        const int quarter = (R + 3) / 4;
+        for (int t0 = 0; t0 < 4 * nch; t0 += kThreads) {
+            const int t = t0 + tid;
+            const int ch = t >> 2, part = t & 3;
+            float a = 0.f;
+            if (ch < nch) {
+                const int jl2 = ch / VW, v2 = ch - jl2 * VW;
+                const int r0 = part * quarter, r1 = min(R, r0 + quarter);
+                for (int rr = r0; rr < r1; ++rr) a += r[(rr * NGt + jl2) * VW + v2];
+            }
+            const float a1 = __shfl_xor(a, 1);
+            const float lo = (part & 1) ? a1 + a : a + a1;          // (p0+p1) or (p2+p3)
+            const float hi = __shfl_xor(lo, 2);
+            const float tot = (part & 2) ? hi + lo : lo + hi;       // (p0+p1)+(p2+p3)
+            if (ch < nch && part == 0) {
+                const int jl2 = ch / VW, v2 = ch - jl2 * VW;
+                const int j2 = blockIdx.x * NGt + jl2;
+                if (j2 < NG) Elem<T>::store1(dst + (size_t)j2 * VW + v2, tot);
             }
         }
         buf ^= 1;   // next block writes the other buffer: one barrier per block
     }
+}
+
+template <typename E, int M1, int PPT>
+void launch_dual(dim3 grid, hipStream_t st, const void* k, const void* v, const float* zk1, const float* zv1,
+                 void* kc1, void* vc1, const float* zk2, const float* zv2, void* kc2, void* vc2, int m2, int Tl,
+                 int C, int N1, int N2, int R, int NGt, long long total, int per) {
+    hipLaunchKernelGGL((compress_dual_kernel<E, M1, PPT>), grid, dim3(kThreads), 0, st, (const E*)k, (const E*)v,
+                       zk1, zv1, (E*)kc1, (E*)vc1, zk2, zv2, (E*)kc2, (E*)vc2, m2, Tl, C, N1, N2, R, NGt, total,
+                       per);
+}
+
+template <typename E>
+void launch_dual_m1(int m1, dim3 grid, hipStream_t st, const void* k, const void* v, const float* zk1,
+                    const float* zv1, void* kc1, void* vc1, const float* zk2, const float* zv2, void* kc2, void* vc2,
+                    int m2, int Tl, int C, int N1, int N2, int R, int NGt, long long total, int per) {
+#define SHATTN_DUAL(M1, P) launch_dual<E, M1, P>(grid, st, k, v, zk1, zv1, kc1, vc1, zk2, zv2, kc2, vc2, m2, Tl, C, \
+                                                 N1, N2, R, NGt, total, per)
+    switch (m1) {
+        case 1: SHATTN_DUAL(1, 4); break;
+        case 2: SHATTN_DUAL(2, 4); break;
+        case 4: SHATTN_DUAL(4, 4); break;
+        default: SHATTN_DUAL(8, 8); break;
+    }
+#undef SHATTN_DUAL
 }
 
 }  // namespace
@@ -419,24 +495,25 @@ extern "C" int hca_compress_kv_dual(const void* k, const void* v, const float* z
         const int C = Hkv * d;
         const int VW = dtype == SHATTN_DTYPE_BF16 ? 8 : 4;
         const int NG = C / VW;
-        const int R = m2 / kPPT;
+        const int ppt = m1 == 8 ? 8 : 4;
+        const int R = m2 / ppt;
+        if (R > kThreads) return fail(SHATTN_EUNSUPPORTED, "hca_compress_kv_dual: m2=%d too large", m2);
         int NGt = kThreads / R;
         if (NGt > NG) NGt = NG;
         const int tiles = (NG + NGt - 1) / NGt;
         const long long total = (long long)B * N2;
-        long long per = (total * tiles + 1023) / 1024;
-        if (per < 1) per = 1;
+        // about one resident round of workgroups (4 per CU, K and V slices)
+        long long per = (total * tiles * 2 + 1023) / 1024;
+        if (per < 2) per = 2;
         if (per > 64) per = 64;
         const long long ywgs = (total + per - 1) / per;
         dim3 grid(tiles, (unsigned)ywgs, 2);
         if (dtype == SHATTN_DTYPE_BF16)
-            hipLaunchKernelGGL(compress_dual_kernel<bf16_t>, grid, dim3(kThreads), 0, s, (const bf16_t*)k,
-                               (const bf16_t*)v, zk1, zv1, (bf16_t*)kc1, (bf16_t*)vc1, m1, zk2, zv2, (bf16_t*)kc2,
-                               (bf16_t*)vc2, m2, T, C, N1, N2, R, NGt, total, (int)per);
+            launch_dual_m1<bf16_t>(m1, grid, s, k, v, zk1, zv1, kc1, vc1, zk2, zv2, kc2, vc2, m2, T, C, N1, N2, R,
+                                   NGt, total, (int)per);
         else
-            hipLaunchKernelGGL(compress_dual_kernel<float>, grid, dim3(kThreads), 0, s, (const float*)k,
-                               (const float*)v, zk1, zv1, (float*)kc1, (float*)vc1, m1, zk2, zv2, (float*)kc2,
-                               (float*)vc2, m2, T, C, N1, N2, R, NGt, total, (int)per);
+            launch_dual_m1<float>(m1, grid, s, k, v, zk1, zv1, kc1, vc1, zk2, zv2, kc2, vc2, m2, T, C, N1, N2, R,
+                                  NGt, total, (int)per);
         const int rc = check_launch("hca_compress_kv_dual");
         if (rc) return rc;
     }

@@ -229,25 +229,44 @@ __device__ __noinline__ int compact_stream(WaveBuf& wb, int cnt, int kk, float d
     return n;
 }
 
-// Exact (float64) score of entry c for query row (b, i).
+// Exact (float64) scores of the band candidates, 4 per pass: 16 lanes per
+// candidate, each holding DI/16 dims of the query's HI heads and of the
+// candidate's key; products of the inputs are exact in float64 and the 16
+// partial dot products are combined in a fixed order.
 template <typename T, int HI, int DI>
-__device__ double exact_score(const T* __restrict__ qrow /* [HI][DI] */, const T* __restrict__ krow,
-                              const float* __restrict__ wrow) {
-    double s = 0.0;
-#pragma unroll 1
-    for (int h = 0; h < HI; ++h) {
-        double dot = 0.0;
-#pragma unroll 1
-        for (int e = 0; e < DI; e += 16 / (int)sizeof(T)) {
-            float qa[8], ka[8];
-            Elem<T>::unpack(ld16(qrow + h * DI + e), qa);
-            Elem<T>::unpack(ld16(krow + e), ka);
+__device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T* __restrict__ kI_b,
+                             const float* __restrict__ wrow, const int32_t* ids, const int32_t* mpos, int nM,
+                             double* mex) {
+    constexpr int PER = DI / 16;  // dims per lane (4 or 8)
+    const int lane = __lane_id();
+    const int slot = lane >> 4, dl = lane & 15;
+    float q[HI][PER];
 #pragma unroll
-            for (int j = 0; j < 16 / (int)sizeof(T); ++j) dot += (double)qa[j] * (double)ka[j];
+    for (int h = 0; h < HI; ++h)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) q[h][u] = Elem<T>::load1(qrow + h * DI + dl * PER + u);
+    for (int j0 = 0; j0 < nM; j0 += 4) {
+        const int j = j0 + slot;
+        const bool ok = j < nM;
+        const int c = ok ? ids[mpos[j]] : 0;
+        float kv[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) kv[u] = Elem<T>::load1(kI_b + (long long)c * DI + dl * PER + u);
+        double s = 0.0;
+#pragma unroll
+        for (int h = 0; h < HI; ++h) {
+            double d = 0.0;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) d += (double)q[h][u] * (double)kv[u];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const double o = __shfl_xor(d, off);
+                d = (dl & off) ? o + d : d + o;
+            }
+            s += (double)wrow[h] * (d > 0.0 ? d : 0.0);
         }
-        s += (double)wrow[h] * (dot > 0.0 ? dot : 0.0);
+        if (ok && dl == 0) mex[j] = s;
     }
-    return s;
 }
 
 // Final exact selection of one query and output of its idx row.
@@ -280,10 +299,7 @@ __device__ __noinline__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k
         wave_lds_sync();
         const int need = k_eff - nD;
         if (nM <= mcap) {
-            for (int j = lane; j < nM; j += 64) {
-                const int e = wb.mpos[j];
-                wb.mex[j] = exact_score<T, HI, DI>(qrow, kI_b + (long long)wb.ids[e] * DI, wrow);
-            }
+            exact_scores<T, HI, DI>(qrow, kI_b, wrow, wb.ids, wb.mpos, nM, wb.mex);
             wave_lds_sync();
             // rank within M by (exact desc, index asc); keep the first `need`
             for (int j = lane; j < nM; j += 64) {
@@ -855,7 +871,7 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     p.m = m;
     p.W = W;
     p.q_pos0 = q_pos0;
-    p.cap = ((k + std::max(192, k / 2)) + 63) / 64 * 64;
+    p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
     p.mcap = std::min(p.cap, 256);
     // |float32 score - exact| <= err_c * sum_h |w_h| ||q_h|| * max ||k||:
     // 2*d_idx*u for the dot products (any summation order, rounding or
