@@ -104,9 +104,28 @@ struct WaveBuf {
 // k-th largest key among keys[0..cnt), 1 <= kk <= cnt.  *n_gt = #keys > result.
 __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
     const int lane = __lane_id();
-    uint32_t prefix = 0u, pmask = 0u;
+    // bytes shared by every key need no histogram pass
+    uint32_t andv = 0xFFFFFFFFu, orv = 0u;
+    for (int e = lane; e < cnt; e += 64) {
+        const uint32_t key = keys[e];
+        andv &= key;
+        orv |= key;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        andv &= __shfl_xor(andv, off);
+        orv |= __shfl_xor(orv, off);
+    }
+    const uint32_t diff = andv ^ orv;
+    if (diff == 0u) {
+        *n_gt = 0;
+        return andv;
+    }
+    const int top_byte = (31 - __clz(diff)) >> 3;
+    uint32_t pmask = top_byte == 3 ? 0u : (0xFFFFFFFFu << (8 * (top_byte + 1)));
+    uint32_t prefix = andv & pmask;
     int want = kk;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 8 * top_byte; shift >= 0; shift -= 8) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
         wave_lds_sync();
@@ -229,7 +248,8 @@ __device__ __noinline__ int compact_stream(WaveBuf& wb, int cnt, int kk, float d
     return n;
 }
 
-// Exact (float64) scores of the band candidates, 4 per pass: 16 lanes per
+// Exact (float64) scores of the band candidates, 4 per pass (candidate j is
+// entry ids[mpos[j]], or mpos[j] itself when ids is null): 16 lanes per
 // candidate, each holding DI/16 dims of the query's HI heads and of the
 // candidate's key; products of the inputs are exact in float64 and the 16
 // partial dot products are combined in a fixed order.
@@ -248,7 +268,7 @@ __device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T*
     for (int j0 = 0; j0 < nM; j0 += 4) {
         const int j = j0 + slot;
         const bool ok = j < nM;
-        const int c = ok ? ids[mpos[j]] : 0;
+        const int c = ok ? (ids ? ids[mpos[j]] : mpos[j]) : 0;
         float kv[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u) kv[u] = Elem<T>::load1(kI_b + (long long)c * DI + dl * PER + u);
@@ -650,6 +670,202 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     }
 }
 
+// ----------------------------------------------------------- dense prefill
+// Small candidate sets (N <= 2048): every visible score of a query is written
+// to LDS once as an order-preserving key, then one exact selection per query
+// (no streaming compactions).  Same scoring tiles and the same exact decision
+// rule as the streaming kernel.
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
+    typedef IdxMma<T, DI> MM;
+    constexpr int QPT = 16 / HI;
+    constexpr int SLOTS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4;
+    const int qpw = p.qpw, np = p.cap, mcap = p.mcap;   // cap = keys per query (>= N)
+    const int RT = qpw / QPT;
+    char* base = smem + (size_t)wave * p.wave_stride;
+    uint32_t* keys_all = reinterpret_cast<uint32_t*>(base);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(base + 4ull * qpw * np);
+    double* mex = reinterpret_cast<double*>(base + 4ull * qpw * np + 1024);
+    int32_t* mpos = reinterpret_cast<int32_t*>(base + 4ull * qpw * np + 1024 + 8ull * mcap);
+    float* qn = reinterpret_cast<float*>(base + 4ull * qpw * np + 1024 + 12ull * mcap);
+
+    const int qt = blockIdx.x % p.nqt;
+    const int b = blockIdx.x / p.nqt;
+    const int q0 = (qt * WAVES + wave) * qpw;
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
+
+    typename MM::F a[MAX_RT][MM::KS];
+    float wr[MAX_RT][4];
+    const int rho = lane & 15;
+#pragma unroll
+    for (int rt = 0; rt < MAX_RT; ++rt) {
+        const int qw = rt * QPT + rho / HI, hh = rho % HI;
+        const int i = q0 + qw;
+        const bool ok = rt < RT && qw < qpw && i < p.Tq;
+        MM::load_a(qI + (((long long)b * p.Tq + (ok ? i : 0)) * HI + hh) * DI, ok, q4, a[rt]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * q4 + r;
+            const int qr = rt * QPT + row / HI, hr = row % HI;
+            const int ir = q0 + qr;
+            wr[rt][r] = (rt < RT && qr < qpw && ir < p.Tq) ? p.w[((long long)b * p.Tq + ir) * HI + hr] : 0.f;
+        }
+        float n2 = MM::sq(a[rt]);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        if (rt < RT) {
+            const int qsl = lane < QPT ? lane : 0;
+            float acc = 0.f;
+            for (int h = 0; h < HI; ++h) {
+                const float nr = __shfl(n2, qsl * HI + h);
+                const int ir = q0 + rt * QPT + qsl;
+                const float wv = (ir < p.Tq && rt * QPT + qsl < qpw) ? p.w[((long long)b * p.Tq + ir) * HI + h] : 0.f;
+                acc += fabsf(wv) * sqrtf(nr);
+            }
+            if (lane < QPT && rt * QPT + lane < qpw) qn[rt * QPT + lane] = acc;
+        }
+    }
+    // visible entries of the wave's queries
+    int nv_max = 0;
+    for (int qw = 0; qw < qpw; ++qw) {
+        const int i = q0 + qw;
+        if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N));
+    }
+    float kmax2 = 0.f;
+    // ---- all scores -> LDS keys
+    auto score_tile = [&](int c0, const typename MM::F* bf) {
+        const int c = c0 + rho;
+        float n2 = MM::sq(bf);
+        n2 += __shfl_xor(n2, 16);
+        n2 += __shfl_xor(n2, 32);
+        kmax2 = fmaxf(kmax2, n2);
+#pragma unroll
+        for (int rt = 0; rt < MAX_RT; ++rt) {
+            if (rt >= RT) break;
+            const f32x4_t acc = MM::mma(a[rt], bf);
+            float sc[4];
+            int qs[4];
+            bool own[4];
+            const int ns = tile_scores<HI>(acc, wr[rt], q4, sc, qs, own);
+#pragma unroll
+            for (int sl = 0; sl < SLOTS; ++sl) {
+                if (sl >= ns) break;
+                const int qw = rt * QPT + qs[sl];
+                if (own[sl] && qw < qpw && c < np) keys_all[qw * np + c] = fkey(sc[sl]);
+            }
+        }
+    };
+    auto load_b = [&](int c0, typename MM::F* bf) {
+        const int c = c0 + rho;
+        MM::load_a(kI_b + (long long)(c < p.N ? c : 0) * DI, c < p.N, q4, bf);
+    };
+    constexpr int PF = 2;
+    typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
+    auto group = [&](int g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+        const int g1 = g0 + PF * TILE;
+        if (g1 < nv_max) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+            if (g0 + t * TILE < nv_max) score_tile(g0 + t * TILE, cur[t]);
+    };
+    if (nv_max > 0) {
+#pragma unroll
+        for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
+    }
+    for (int g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
+        group(g0, bq0, bq1);
+        if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
+    }
+    for (int off = 32; off > 0; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+    wave_lds_sync();
+
+    // ---- one exact selection per query
+    const float kmax = sqrtf(kmax2);
+    for (int qw = 0; qw < qpw; ++qw) {
+        const int i = q0 + qw;
+        if (i >= p.Tq) break;
+        const long long row = (long long)b * p.Tq + i;
+        int32_t* out_row = p.idx + row * p.k;
+        const int n = (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+        const int k_eff = min(p.k, n);
+        uint32_t* keys = keys_all + qw * np;
+        uint32_t hi = 0u;  // entries with key > hi are kept
+        if (n > k_eff) {
+            const float delta = p.err_c * qn[qw] * kmax;
+            int n_gt;
+            const uint32_t kth = radix_kth(keys, n, k_eff, hist, &n_gt);
+            const float Tf = key_f(kth);
+            hi = fkey(Tf + 2.0f * delta);
+            const uint32_t lo = fkey(Tf - 2.0f * delta);
+            int nD = 0, nM = 0;
+            for (int base0 = 0; base0 < n; base0 += 64) {
+                const int e = base0 + lane;
+                const uint32_t key = e < n ? keys[e] : 0u;
+                const bool inD = e < n && key > hi;
+                const bool inM = e < n && key >= lo && key <= hi;
+                const unsigned long long mm = __ballot(inM);
+                if (inM) {
+                    const int pos = nM + __popcll(mm & lanemask_lt());
+                    if (pos < mcap) mpos[pos] = e;
+                }
+                nD += __popcll(__ballot(inD));
+                nM += __popcll(mm);
+            }
+            wave_lds_sync();
+            const int need = k_eff - nD;
+            if (nM <= mcap) {
+                exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, nullptr, mpos, nM, mex);
+                wave_lds_sync();
+                for (int j = lane; j < nM; j += 64) {
+                    const double ex = mex[j];
+                    const int id = mpos[j];
+                    int rank = 0;
+                    for (int y = 0; y < nM; ++y) {
+                        const double ey = mex[y];
+                        rank += (ey > ex) || (ey == ex && mpos[y] < id);
+                    }
+                    keys[id] = rank < need ? 0xFFFFFFFFu : 0u;
+                }
+            } else {
+                // band larger than the band list: decide on float32 keys (index tie-break)
+                int eq_seen = 0;
+                for (int base0 = 0; base0 < n; base0 += 64) {
+                    const int e = base0 + lane;
+                    const uint32_t key = e < n ? keys[e] : 0u;
+                    const bool inM = e < n && key >= lo && key <= hi;
+                    const unsigned long long meq = __ballot(inM && key == kth);
+                    const bool keq = inM && key == kth && eq_seen + __popcll(meq & lanemask_lt()) < k_eff - n_gt;
+                    if (inM) keys[e] = (key > kth || keq) ? 0xFFFFFFFFu : 0u;
+                    eq_seen += __popcll(meq);
+                }
+            }
+            wave_lds_sync();
+            if (hi == 0xFFFFFFFFu) hi = 0xFFFFFFFEu;
+        } else {
+            hi = 0u;   // keep every visible entry (keys are never 0 for finite scores)
+            for (int e = lane; e < n; e += 64) keys[e] = 0xFFFFFFFFu;
+            wave_lds_sync();
+        }
+        // ascending entry order: stable pass over the visible entries
+        int out = 0;
+        for (int base0 = 0; base0 < n; base0 += 64) {
+            const int e = base0 + lane;
+            const bool keep = e < n && keys[e] > hi;
+            const unsigned long long msk = __ballot(keep);
+            if (keep) out_row[out + __popcll(msk & lanemask_lt())] = e;
+            out += __popcll(msk);
+        }
+        for (int j = out + lane; j < p.k; j += 64) out_row[j] = -1;
+        wave_lds_sync();
+    }
+}
+
 // ----------------------------------------------------------- split pipeline
 // S1: one wave per (query row, chunk of entries): float32 scores of the row
 // against the chunk (written to the workspace), the chunk's chunk_k-th largest
@@ -842,6 +1058,7 @@ __global__ __launch_bounds__(64) void index_split_final_kernel(IdxParams p) {
 struct IdxPlan {
     IdxParams p;
     bool split;
+    bool dense;  // small N: all scores of a query in LDS, one exact select
     size_t lds;  // prefill: per workgroup; split: final kernel
     size_t lds_score;
     long long grid;
@@ -849,6 +1066,7 @@ struct IdxPlan {
 };
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kDenseMaxN = 2048;
 
 int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k,
                   int dtype, IdxPlan& pl) {
@@ -880,6 +1098,7 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     p.err_c = 2.0f * (2.0f * d_idx + Hi + 4.0f) * 5.9604645e-8f;
     pl.ws_bytes = 0;
     pl.grid = 0;
+    pl.dense = false;
     const long long rows = (long long)B * Tq;
     pl.split = rows > 0 && rows <= 64 && N >= 8192;
     if (pl.split) {
@@ -910,8 +1129,27 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
         pl.grid = rows;
         return SHATTN_OK;
     }
-    // prefill: choose queries per wave so that 4 waves fit the LDS budget
     const int qpt = 16 / Hi;
+    pl.dense = N > 0 && N <= kDenseMaxN;
+    if (pl.dense) {
+        // p.cap = per-query key slots (N rounded up to a tile)
+        p.cap = (N + TILE - 1) / TILE * TILE;
+        auto dense_wave = [&](int q) { return (4ull * q * p.cap + 1024 + 12ull * p.mcap + 4ull * q + 15) / 16 * 16; };
+        int qpw = 4 * qpt;
+        while (qpw > qpt && WAVES * dense_wave(qpw) > (size_t)kMaxLds) qpw -= qpt;
+        while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 1024) qpw -= qpt;
+        if (WAVES * dense_wave(qpw) > (size_t)kMaxLds) pl.dense = false;
+        else {
+            p.qpw = qpw;
+            p.wave_stride = (int)dense_wave(qpw);
+            p.nqt = (Tq + WAVES * qpw - 1) / (WAVES * qpw);
+            pl.lds = WAVES * dense_wave(qpw);
+            pl.grid = (long long)B * p.nqt;
+            return SHATTN_OK;
+        }
+        p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
+    }
+    // prefill: choose queries per wave so that 4 waves fit the LDS budget
     int qpw = std::max(16, qpt);
     if (qpw > 4 * qpt) qpw = 4 * qpt;
     auto per_wave = [&](int q) { return (8ull * q * p.cap + 1024 + 12ull * p.mcap + 4ull * q + 31) / 16 * 16; };
@@ -930,6 +1168,19 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
 
 template <typename T, int HI, int DI>
 int launch_idx(IdxPlan& pl, hipStream_t s) {
+    if (pl.dense) {
+        if (pl.lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
+            }
+        }
+        hipLaunchKernelGGL((index_dense_kernel<T, HI, DI>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds, s,
+                           pl.p);
+        return check_launch("csa_index_topk");
+    }
     if (!pl.split) {
         if (pl.lds > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_prefill_kernel<T, HI, DI>),

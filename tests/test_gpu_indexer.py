@@ -101,6 +101,42 @@ def test_k_at_least_visible():
     run_case(inp, what="k >= visible")
 
 
+def sampled_rows(B, T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(b, t) for b in range(B) for t in (0, 127, 128, 131, T // 2, T - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(0, B)), int(rng.integers(0, T))))
+    return sorted(rows)
+
+
+# Above 2048 entries the kernel streams candidates through bounded per-query
+# buffers with compactions instead of holding every score; the cases below
+# repeat the small-N checks on that path (N = T / 4 > 2048).
+@pytest.mark.parametrize("Hi,d_idx", [(2, 128), (4, 64), (16, 128)])
+def test_streaming_head_counts(Hi, d_idx):
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=30 + Hi, B=2, T=8500, Hi=Hi, d_idx=d_idx, k=64)
+    run_case(inp, rows=sampled_rows(2, 8500, 200, Hi), what=f"streaming Hi={Hi} d_idx={d_idx}")
+
+
+def test_streaming_fp32_ragged():
+    lib()
+    inp = synth.make_inputs("tiny_fp32", seed=34, T=8403, k=37, W=9, m_hca=8)
+    run_case(inp, rows=sampled_rows(1, 8403, 200, 34), what="streaming fp32 ragged")
+
+
+def test_streaming_duplicate_and_identical_keys():
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=35, B=1, T=9000, k=20)
+    kI = inp["kI"].copy()
+    kI[:, 1::3] = kI[:, 0:-1:3][:, : kI[:, 1::3].shape[1]]
+    inp["kI"] = kI
+    run_case(inp, rows=sampled_rows(1, 9000, 150, 35), what="streaming duplicate keys")
+    inp["kI"] = np.ascontiguousarray(np.broadcast_to(inp["kI"][:, :1], inp["kI"].shape))
+    got = run_case(inp, rows=sampled_rows(1, 9000, 150, 36), what="streaming identical keys")
+    assert got[0, 8999, :20].tolist() == list(range(20))
+
+
 def test_csa_prefill_reduced_all_rows():
     lib()
     inp = synth.make_inputs("csa_prefill_128k", seed=16, T=8192)
