@@ -225,7 +225,8 @@ def main():
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="query rows of the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=10000,
+                    help="query rows of the CPU-baseline sample (about 10-15 s of oracle work at the default workload)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scaling for rocprofv3)")
     args = ap.parse_args()
@@ -322,7 +323,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(inp, args.cpu_rows)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):   # the oracle runs on exactly one host thread
+            cpu = cpu_baseline(inp, args.cpu_rows)
         log(f"[bench] cpu baseline {cpu['value']:.1f} queries/s")
 
     desc = {

@@ -445,8 +445,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, q4 = lane >> 4;
 
-    // work decomposition: (b, g, query tile) [, split item]
-    long long wg = blockIdx.x;
+    // work decomposition: (b, g, query tile) [, split item].  Workgroups are
+    // dealt round-robin to the 8 XCDs (each with its own L2); the work id is
+    // remapped so that every XCD runs a contiguous range of work ids: the
+    // query tiles of one (b, g), which share window rows and compressed
+    // entries, then meet in one L2.
+    const long long wid = xcd_work_id(blockIdx.x, gridDim.x);
+    long long wg = wid;
     int item = 0;
     if (p.nsplit) {
         item = (int)(wg % p.nsplit);
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         // partial state of this item: [m, l, -, -, acc[D]] per column at
         // ws[((wg * nsplit + item) * ncol + col) * (D + 4)]
         const float ltot = col_sum(S.l);
-        float* dst = p.ws + (((long long)blockIdx.x) * p.ncol + col) * (D + 4);
+        float* dst = p.ws + (wid * p.ncol + col) * (D + 4);
         if (q4 == 0) {
             dst[0] = S.m;
             dst[1] = ltot;

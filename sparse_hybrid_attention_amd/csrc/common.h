@@ -99,4 +99,16 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+
+// Workgroup -> work id remap for the 8 XCDs of MI355X.  The dispatcher deals
+// workgroup i to XCD i % 8; XCD x receives ceil/floor(n / 8) workgroups and the
+// j-th of them (i = x + 8 j) gets work id start(x) + j, so each XCD covers one
+// contiguous range of work ids.  A bijection of [0, n) for every n.
+__device__ __forceinline__ long long xcd_work_id(long long i, long long n) {
+    constexpr int kXcds = 8;
+    const long long q = n / kXcds, r = n % kXcds;
+    const long long x = i % kXcds, j = i / kXcds;
+    return x * q + (x < r ? x : r) + j;
+}
+
 }  // namespace shattn
