@@ -272,43 +272,59 @@ template <int DT> struct State {
     }
 };
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one column.
+// v_permlane16_swap / v_permlane32_swap exchange rows of 16 / halves of 32
+// lanes in registers: swapping a value with itself leaves lane l holding the
+// values of lanes l and l^16 (resp. l^32) in the two results.
 __device__ __forceinline__ float col_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// fixed order: (l0 + l16) + (l32 + l48) on every lane of the column
 __device__ __forceinline__ float col_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One 32-key chunk: x[j] are log2-domain logits (-inf when masked).
-template <typename T, int D>
-__device__ __forceinline__ void softmax_pv(State<D / 16>& st, float* x, const T* Vt, int vst, int c,
-                                           int lane) {
+// One online-softmax step over NCH 32-key chunks (keys [c, c + 32 NCH) of a
+// tile).  s[8 ch + j] is this lane's raw score of key key_of(q4, j) of chunk
+// ch; bit 8 ch + j of mb says whether that key is attended (FULL: every key
+// of the step is attended by every column of the wave); scale = softmax
+// scale * log2(e) > 0.  The scale is applied inside the exponent's FMA and to
+// the (monotone) column max.
+template <int D, int NCH, bool FULL, typename PV>
+__device__ __forceinline__ void softmax_pv(State<D / 16>& st, const float* s, uint32_t mb, float scale,
+                                           PV&& pv) {
+    constexpr int NJ = 8 * NCH;
+    float x[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) x[j] = (FULL || ((mb >> j) & 1u)) ? s[j] : -INFINITY;
     float mloc = x[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, x[j]);
-    mloc = col_max(mloc);
+    for (int j = 1; j < NJ; ++j) mloc = fmaxf(mloc, x[j]);
+    mloc = col_max(mloc) * scale;
     const float mnew = fmaxf(st.m, mloc);
-    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
-    float p[8];
+    float p[NJ];
     float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(x[j] - muse);
+    for (int j = 0; j < NJ; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], scale, -muse));
         ps += p[j];
     }
-    st.l = st.l * alpha + ps;
+    st.l = fmaf(st.l, alpha, ps);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) st.acc[dt][r] *= alpha;
-    }
     st.m = mnew;
-    Tr<T, D>::pv(Vt, vst, c, lane, p, st.acc);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) pv(ch, p + 8 * ch, st.acc);
 }
 
 __device__ __forceinline__ long long n_visible(long long t, int W, int m, int N) {
@@ -331,8 +347,9 @@ template <int D, int NT> struct Stage<bf16_t, D, NT> {
     static constexpr int VU = (VUN + NT - 1) / NT;
     uint4 k[KP];
     uint4 v[VU][2];
-    // rows [0, nvalid) of the tile start at kb / vb, rs elements apart; rows
-    // past nvalid are zero.  Branch-free: out-of-range lanes load row 0.
+    // rows [0, nvalid) of the tile start at kb / vb, rs elements apart.  Rows
+    // past nvalid repeat row 0 (finite data, never attended: their weights
+    // are exactly 0).  Branch-free.
     __device__ void load(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, int rs, int nvalid,
                          int tid) {
 #pragma unroll
@@ -340,8 +357,7 @@ template <int D, int NT> struct Stage<bf16_t, D, NT> {
             const int u = tid + j * NT;
             const int kk = u / PIECES, pc = u % PIECES;
             const bool ok = kk < nvalid && (KU % NT == 0 || u < KU);
-            const uint4 x = ld16(kb + (ok ? kk : 0) * rs + pc * 8);
-            k[j] = ok ? x : make_uint4(0, 0, 0, 0);
+            k[j] = ld16(kb + (ok ? kk : 0) * rs + pc * 8);
         }
         // V: key pairs fastest across lanes (conflict-free transposed LDS writes)
 #pragma unroll
@@ -350,10 +366,8 @@ template <int D, int NT> struct Stage<bf16_t, D, NT> {
             const int kp = u % (KT / 2), oc = u / (KT / 2);
             const bool in = VUN % NT == 0 || u < VUN;
             const bool ok0 = in && 2 * kp < nvalid, ok1 = in && 2 * kp + 1 < nvalid;
-            const uint4 x0 = ld16(vb + (ok0 ? 2 * kp : 0) * rs + (in ? oc : 0) * 8);
-            const uint4 x1 = ld16(vb + (ok1 ? 2 * kp + 1 : 0) * rs + (in ? oc : 0) * 8);
-            v[j][0] = ok0 ? x0 : make_uint4(0, 0, 0, 0);
-            v[j][1] = ok1 ? x1 : make_uint4(0, 0, 0, 0);
+            v[j][0] = ld16(vb + (ok0 ? 2 * kp : 0) * rs + (in ? oc : 0) * 8);
+            v[j][1] = ld16(vb + (ok1 ? 2 * kp + 1 : 0) * rs + (in ? oc : 0) * 8);
         }
     }
     __device__ void store(bf16_t* Ks, bf16_t* Vt, int tid) const {
@@ -415,6 +429,136 @@ template <int D, int NT> struct Stage<float, D, NT> {
     }
 };
 
+// ---------------------------------------------------------------- tile I/O
+// How a KT-key tile of one K/V source gets into LDS and into the MFMA operands.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <typename T, int D, int NW> struct TileIO;
+
+// bf16: K and V tiles are [KT][D] row-major in LDS, their 16-byte pieces
+// XOR-swizzled per row, filled by direct global->LDS loads (each wave load
+// writes 64 lanes x 16 bytes = RPI whole rows) with no register staging.
+//  * K A-operand reads (16 rows per lane group, one piece each) and V^T
+//    reads (4 rows x 32 bytes per lane group) hit distinct banks.
+//  * V^T operands come from transposing LDS reads: within each 16-lane
+//    group, lane i of ds_read_b64_tr_b16 receives element (i mod 4) of the 4
+//    elements read by lane 4k + i/4 in slot k.  Lane s reading 4 elements of
+//    key row (8 g + s/4) at dims 4 (s mod 4) .. +3 makes lane i hold keys
+//    8 g + k, dim i: the A layout of O^T = V^T P^T.
+template <int D, int NW> struct TileIO<bf16_t, D, NW> {
+    static constexpr int PIECES = D / 8;        // 16-byte pieces per row
+    static constexpr int ROWB = D * 2;          // bytes per row
+    static constexpr int RPI = 1024 / ROWB;     // rows per wave load
+    static constexpr int NI = KT / (RPI * NW);  // wave loads per matrix per tile
+    static constexpr int KS = D / 32;
+    static constexpr int DT = D / 16;
+    static constexpr int MAT_BYTES = KT * ROWB;
+    static_assert(NI >= 1 && NI * RPI * NW == KT, "tile split");
+    int goff_k[NI], goff_v[NI];  // element offsets of this lane's global pieces
+    int grow[NI];                // their tile rows
+    int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
+    int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative)
+    int wave;
+
+    __device__ static int swz_k(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); }
+    __device__ static int swz_v(int row) { return (2 * (row & 3)) & (PIECES - 1); }
+
+    __device__ void init(int tid, int rs) {
+        const int lane = tid & 63;
+        wave = tid >> 6;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int row = (j * NW + wave) * RPI + lane / PIECES;
+            const int pc = lane % PIECES;  // LDS slot piece; it holds global piece pc ^ swz(row)
+            grow[j] = row;
+            goff_k[j] = row * rs + (pc ^ swz_k(row)) * 8;
+            goff_v[j] = row * rs + (pc ^ swz_v(row)) * 8;
+        }
+        const int rho = lane & 15, q4 = lane >> 4;
+        const int key0 = 8 * (rho >> 2) + (rho & 3);  // S^T row rho of a chunk's first tile
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kro[ks] = key0 * ROWB + (((4 * ks + q4) ^ swz_k(key0)) * 16);
+        const int g4 = lane >> 4, sl = lane & 15;
+        const int vrow = 8 * g4 + (sl >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1);
+    }
+    // start loading rows [0, nvalid) of a tile (rows past nvalid repeat row 0)
+    __device__ void issue(const bf16_t* kb, const bf16_t* vb, int nvalid, char* buf) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const bool ok = grow[j] < nvalid;
+            char* dst = buf + (j * NW + wave) * 1024;
+            __builtin_amdgcn_global_load_lds(kb + (ok ? goff_k[j] : 0), (lds_void_t*)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + (ok ? goff_v[j] : 0), (lds_void_t*)(dst + MAT_BYTES), 16, 0, 0);
+        }
+    }
+    // the issued loads have landed in LDS (a barrier must follow)
+    __device__ void commit(char*) const { __builtin_amdgcn_s_waitcnt(0); }
+    // S^T for keys [c, c+32) of the tile in buf.  s[j] <-> key 8 q4 + j of the chunk.
+    __device__ void scores(const char* buf, int c, const bf16x8_t* qf, float* s) const {
+        const char* kb = buf + c * ROWB;
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks]);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks] + 4 * ROWB);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = s0[r];
+            s[4 + r] = s1[r];
+        }
+    }
+    // acc += V^T P^T for keys [c, c+32) of the tile in buf
+    __device__ void pv(const char* buf, int c, const float* p, f32x4_t* acc) const {
+        const char* vb = buf + MAT_BYTES + c * ROWB;
+        bf16x8_t bop;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bop[j] = (__bf16)p[j];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const char* a = vb + vro[dt & 3] + (dt >> 2) * 128;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
+            const i16x4_t lohi[2] = {lo, hi};
+            bf16x8_t aop;
+            __builtin_memcpy(&aop, lohi, 16);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[dt], 0, 0, 0);
+        }
+    }
+    static constexpr int buf_bytes() { return 2 * MAT_BYTES; }
+};
+
+// fp32: register staging (global -> registers -> LDS), K row-major, V
+// row-major, MFMA 16x16x4 operands read directly.
+template <int D, int NW> struct TileIO<float, D, NW> {
+    typedef Tr<float, D> TR;
+    Stage<float, D, NW * 64> stg;
+    int tid, lane, rs;
+    __device__ void init(int tid_, int rs_) {
+        tid = tid_;
+        lane = tid_ & 63;
+        rs = rs_;
+    }
+    __device__ void issue(const float* kb, const float* vb, int nvalid, char*) { stg.load(kb, vb, rs, nvalid, tid); }
+    __device__ void commit(char* buf) const {
+        stg.store(reinterpret_cast<float*>(buf), reinterpret_cast<float*>(buf) + KT * TR::KPAD, tid);
+    }
+    __device__ void scores(const char* buf, int c, const float* qf, float* s) const {
+        TR::scores(reinterpret_cast<const float*>(buf), c, lane, qf, s);
+    }
+    __device__ void pv(const char* buf, int c, const float* p, f32x4_t* acc) const {
+        TR::pv(reinterpret_cast<const float*>(buf) + KT * TR::KPAD, TR::VST, c, lane, p, acc);
+    }
+    static constexpr int buf_bytes() { return (KT * TR::KPAD + KT * TR::VST) * 4; }
+};
+
 // bits [a, b] of a 32-bit mask (empty when b < a or the range misses [0, 31])
 __device__ __forceinline__ uint32_t range_mask(int a, int b) {
     a = a < 0 ? 0 : a;
@@ -427,17 +571,17 @@ __device__ __forceinline__ uint32_t range_mask(int a, int b) {
 // ---------------------------------------------------------------- main kernel
 enum { ITEM_WIN = 0, ITEM_HCA = 1, ITEM_CSA = 2 };
 
-template <typename T, int D, int NW>
+// GATHER: CSA entries are gathered per wave (else: attended densely with the
+// selection bitmap, or absent); the two variants are separate kernels so that
+// each carries only its own CSA code.
+template <typename T, int D, int NW, bool GATHER>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     typedef Tr<T, D> TR;
     constexpr int DT = D / 16;
     constexpr int NT = NW * 64;
-    constexpr int TILE_ELEMS = KT * TR::KPAD + (sizeof(T) == 2 ? D * TR::VST : KT * TR::VST);
+    typedef TileIO<T, D, NW> TIO;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T* Kb0 = reinterpret_cast<T*>(smem);
-    T* Vb0 = Kb0 + KT * TR::KPAD;
-    T* Kb1 = Kb0 + TILE_ELEMS;
-    T* Vb1 = Kb1 + KT * TR::KPAD;
+    auto tbuf = [&](int par) { return smem + par * TIO::buf_bytes(); };  // double-buffered K/V tiles
     __shared__ int sflag[4];
     __shared__ int emax_s;
 
@@ -533,7 +677,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     }
 
     // ---- CSA selection bitmap (dense-masked mode)
-    const bool dense_csa = do_csa && p.csa_mode == CSA_DENSE;
+    const bool dense_csa = !GATHER && do_csa && p.csa_mode == CSA_DENSE;
     uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
     if (dense_csa) {
         for (int u = tid; u < p.QW * p.bm_words; u += NT) bm[u] = 0u;
@@ -576,41 +720,74 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * rs + hoff;
     const T* vcsa = reinterpret_cast<const T*>(p.v_csa) + (long long)b * p.N_csa * rs + hoff;
 
+    // ---- wave-uniform key ranges attended by every valid column of the wave:
+    // chunks inside them need no per-key mask
+    auto wave_max = [](int v) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    const bool wave_any = __any(valid);
+    const int wf_lo = wave_any ? wave_max(valid ? wv_lo : INT_MIN) : INT_MAX;
+    const int wf_hi = wave_any ? -wave_max(valid ? -wv_hi : INT_MIN + 1) : INT_MIN;
+    const int hf_hi = wave_any ? -wave_max(valid ? -hv : INT_MIN + 1) : INT_MIN;
+
     // ---- a pipelined stream of KT-key tiles of one source into S: tile i+1 is
-    // loaded into registers while tile i is computed from LDS (double buffer)
-    Stage<T, D, NT> stg;
+    // on its way into the other LDS buffer while tile i is computed
+    TIO tio;
+    tio.init(tid, rs);
     int parity = 0;
     auto stream = [&](const T* kb, const T* vb, int k_begin, int k_end, int type) {
         const int n = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
         if (n == 0) return;
-        stg.load(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, rs, min(KT, k_end - k_begin), tid);
-        stg.store(parity ? Kb1 : Kb0, parity ? Vb1 : Vb0, tid);
+        tio.issue(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, min(KT, k_end - k_begin),
+                  tbuf(parity));
+        tio.commit(tbuf(parity));
         __syncthreads();
         for (int i = 0; i < n; ++i) {
             const int k0 = k_begin + i * KT;
-            const T* Ks = parity ? Kb1 : Kb0;
-            const T* Vs = parity ? Vb1 : Vb0;
+            const char* buf = tbuf(parity);
             if (i + 1 < n) {
                 const int k1 = k0 + KT;
-                stg.load(kb + (long long)k1 * rs, vb + (long long)k1 * rs, rs, min(KT, k_end - k1), tid);
+                tio.issue(kb + (long long)k1 * rs, vb + (long long)k1 * rs, min(KT, k_end - k1), tbuf(parity ^ 1));
             }
-#pragma unroll
-            for (int c = 0; c < KT; c += KC) {
-                const int kc0 = k0 + c;
-                uint32_t m;
-                if (type == ITEM_WIN) m = range_mask(wv_lo - kc0, wv_hi - kc0);
-                else if (type == ITEM_HCA) m = range_mask(0, hv - kc0 - 1);
-                else m = (valid && kc0 < c_hi) ? bm[ql * p.bm_words + (kc0 >> 5)] : 0u;
-                const uint32_t mb = TR::lane_bits(m, q4);
-                if (!__any(mb != 0u)) continue;
-                float sc[8], x[8];
-                TR::scores(Ks, c, lane, qf, sc);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = ((mb >> j) & 1u) ? sc[j] * p.scale_log2 : -INFINITY;
-                softmax_pv<T, D>(S, x, Vs, TR::VST, c, lane);
+            auto pvf = [&](int ch, const float* pp, f32x4_t* acc) { tio.pv(buf, ch * KC, pp, acc); };
+            {
+                // one softmax step over the whole KT = 2 KC key tile
+                bool full;
+                if (type == ITEM_WIN) full = k0 >= wf_lo && k0 + KT - 1 <= wf_hi;
+                else if (type == ITEM_HCA) full = k0 + KT <= hf_hi;
+                else full = false;
+                float sc[16];
+                if (full) {
+                    tio.scores(buf, 0, qf, sc);
+                    tio.scores(buf, KC, qf, sc + 8);
+                    softmax_pv<D, 2, true>(S, sc, 0xFFFFu, p.scale_log2, pvf);
+                } else {
+                    uint32_t m0, m1;
+                    if (type == ITEM_WIN) {
+                        m0 = range_mask(wv_lo - k0, wv_hi - k0);
+                        m1 = range_mask(wv_lo - k0 - KC, wv_hi - k0 - KC);
+                    } else if (type == ITEM_HCA) {
+                        m0 = range_mask(0, hv - k0 - 1);
+                        m1 = range_mask(0, hv - k0 - KC - 1);
+                    } else {
+                        const bool ok = valid && k0 < c_hi;
+                        const uint2 w2 = ok ? *reinterpret_cast<const uint2*>(bm + ql * p.bm_words + (k0 >> 5))
+                                            : make_uint2(0u, 0u);
+                        m0 = w2.x;
+                        m1 = w2.y;
+                    }
+                    const uint32_t mb = TR::lane_bits(m0, q4) | (TR::lane_bits(m1, q4) << 8);
+                    if (__any(mb != 0u)) {
+                        tio.scores(buf, 0, qf, sc);
+                        tio.scores(buf, KC, qf, sc + 8);
+                        softmax_pv<D, 2, false>(S, sc, mb, p.scale_log2, pvf);
+                    }
+                }
             }
             parity ^= 1;
-            if (i + 1 < n) stg.store(parity ? Kb1 : Kb0, parity ? Vb1 : Vb0, tid);
+            if (i + 1 < n) tio.commit(tbuf(parity));
             __syncthreads();
         }
     };
@@ -648,14 +825,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 }
                 TR::stage(gK, gV, TR::GVST, kc, vc, grows, KC, lane, 64);
                 wave_lds_sync();
-                float x[8], sc[8];
+                float sc[8];
                 TR::scores(gK, 0, lane, qf, sc);
+                uint32_t mb = 0u;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const bool vis = valid && ql == qq && grows[TR::key_of(q4, j)] >= 0;
-                    x[j] = vis ? sc[j] * p.scale_log2 : -INFINITY;
+                    mb |= (vis ? 1u : 0u) << j;
                 }
-                softmax_pv<T, D>(S, x, gV, TR::GVST, 0, lane);
+                softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2, [&](int, const float* pp, f32x4_t* acc) {
+                    TR::pv(gV, TR::GVST, 0, lane, pp, acc);
+                });
                 wave_lds_sync();
             }
         }
@@ -667,8 +847,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         if (!p.nsplit) fold(gate[2]);
     }
     if (do_csa) {
-        if (dense_csa) stream(kcsa, vcsa, 0, c_hi, ITEM_CSA);
-        else {
+        if constexpr (!GATHER) {
+            stream(kcsa, vcsa, 0, c_hi, ITEM_CSA);
+        } else {
             __syncthreads();  // the stream buffers become the per-wave gather tiles
             gather();
             __syncthreads();
@@ -712,6 +893,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 }
 
 // Merge the split partial states: one thread per (column, 4 dims).
+// Every variant the launcher can select, instantiated explicitly (the host
+// compiler otherwise dropped the stubs of some variants).
+#define SHATTN_ATTN_INST(T, D)                                               \
+    template __global__ void attn_fwd_kernel<T, D, 4, false>(AttnParams);    \
+    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);     \
+    template __global__ void attn_fwd_kernel<T, D, 8, false>(AttnParams);    \
+    template __global__ void attn_fwd_kernel<T, D, 8, true>(AttnParams);
+SHATTN_ATTN_INST(bf16_t, 64)
+SHATTN_ATTN_INST(bf16_t, 128)
+SHATTN_ATTN_INST(float, 64)
+SHATTN_ATTN_INST(float, 128)
+#undef SHATTN_ATTN_INST
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -894,7 +1088,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     const int esz = bf ? 2 : 4;
     const int kpad = bf ? a->d + 8 : a->d + 4;
     // two staged tiles (double buffer)
-    const size_t tile_b = bf ? (size_t)(KT * kpad + a->d * (KT + 8)) * esz : (size_t)(2 * KT * kpad) * esz;
+    // bf16: K and V [KT][d] unpadded (swizzled); fp32: padded K and V rows
+    const size_t tile_b = bf ? (size_t)(2 * KT * a->d) * esz : (size_t)(2 * KT * kpad) * esz;
     const size_t shared_b = 2 * tile_b;
     const size_t gather_b = bf ? (size_t)(KC * kpad + a->d * (KC + 8)) * esz + KC * 8
                                : (size_t)(2 * KC * kpad) * esz + KC * 8;
@@ -907,7 +1102,7 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
                            span_q * a->k >= a->N_csa / 2;
         if (dense) {
             p.csa_mode = CSA_DENSE;
-            p.bm_words = (a->N_csa + 31) / 32;
+            p.bm_words = (a->N_csa + 63) / 64 * 2;   // even: a 64-key tile reads two words
             p.lds_bm = (int)shared_b;
             lds = shared_b + (size_t)p.QW * p.bm_words * 4;
         } else {
@@ -933,11 +1128,11 @@ extern "C" size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
     return pl.ws_bytes;
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool GATHER>
 static int launch_attn_nw(Plan& pl, hipStream_t s) {
     if (pl.lds > 64 * 1024) {
         // dynamic LDS beyond 64 KiB must be opted into per kernel
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D, NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D, NW, GATHER>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -945,7 +1140,7 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
                         pl.lds, hipGetErrorString(e));
         }
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s, pl.p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, GATHER>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s, pl.p);
     hipError_t le = hipGetLastError();
     if (le != hipSuccess)
         return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
@@ -959,7 +1154,9 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
 
 template <typename T, int D>
 static int launch_attn(Plan& pl, hipStream_t s) {
-    return pl.waves == 8 ? launch_attn_nw<T, D, 8>(pl, s) : launch_attn_nw<T, D, 4>(pl, s);
+    if (pl.p.csa_mode == CSA_GATHER)
+        return pl.waves == 8 ? launch_attn_nw<T, D, 8, true>(pl, s) : launch_attn_nw<T, D, 4, true>(pl, s);
+    return pl.waves == 8 ? launch_attn_nw<T, D, 8, false>(pl, s) : launch_attn_nw<T, D, 4, false>(pl, s);
 }
 
 extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {

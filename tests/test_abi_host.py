@@ -46,6 +46,13 @@ def test_exports_every_declared_symbol(lib):
     assert exported == set(syms)
 
 
+def test_no_unresolved_library_symbols(lib):
+    # every kernel the launchers reference is defined in the library itself
+    out = subprocess.run(["nm", "-C", "--undefined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert not [l for l in out.splitlines() if "shattn" in l]
+
+
 def test_struct_layout_matches_c(lib, tmp_path):
     fields = [f for f, _ in binding.FwdArgs._fields_]
     src = tmp_path / "layout.c"
