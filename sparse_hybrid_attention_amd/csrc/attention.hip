@@ -302,7 +302,15 @@ __device__ __forceinline__ void softmax_pv(State<D / 16>& st, const float* s, ui
     constexpr int NJ = 8 * NCH;
     float x[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) x[j] = (FULL || ((mb >> j) & 1u)) ? s[j] : -INFINITY;
+    for (int j = 0; j < NJ; ++j) {
+        if constexpr (FULL) {
+            x[j] = s[j];
+        } else {
+            // bit j of mb selects s[j], else -inf: sign-extended bit + bitfield insert
+            const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mb, j, 1);
+            x[j] = __uint_as_float((__float_as_uint(s[j]) & sel) | (0xFF800000u & ~sel));
+        }
+    }
     float mloc = x[0];
 #pragma unroll
     for (int j = 1; j < NJ; ++j) mloc = fmaxf(mloc, x[j]);
@@ -676,6 +684,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
     }
 
+    // ---- window geometry; the first window tile starts loading now, under the
+    // bitmap set-up
+    const long long w_lo = t_first - p.W + 1 > 0 ? t_first - p.W + 1 : 0;
+    const int wlen = (int)(t_last + 1 - w_lo);
+    const int rs = p.Hkv * D;  // row stride of every K/V tensor (elements)
+    const long long hoff = (long long)g * D;
+    const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    TIO tio;
+    tio.init(tid, rs);
+    int parity = 0;
+    bool pf = false;  // the first tile of the next stream is already on its way into tbuf(parity)
+    if (do_win && wlen > 0) {
+        tio.issue(kraw, vraw, min(KT, wlen), tbuf(0));
+        pf = true;
+    }
+
     // ---- CSA selection bitmap (dense-masked mode)
     const bool dense_csa = !GATHER && do_csa && p.csa_mode == CSA_DENSE;
     uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
@@ -701,8 +726,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     // ---- geometry: every index inside a stream is a 32-bit offset from the
     // workgroup's window start (window) or from entry 0 (HCA, CSA)
-    const long long w_lo = t_first - p.W + 1 > 0 ? t_first - p.W + 1 : 0;
-    const int wlen = (int)(t_last + 1 - w_lo);
     int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
     if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
     const int h_lo = do_hca ? (int)hca_lo : 0;
@@ -711,10 +734,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int wv_hi = valid ? (int)(t - w_lo) : 0;
     int hv = (valid && do_hca) ? (int)n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
     if (hv > h_hi) hv = h_hi;
-    const int rs = p.Hkv * D;  // row stride of every K/V tensor (elements)
-    const long long hoff = (long long)g * D;
-    const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
-    const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
     const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * rs + hoff;
     const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * rs + hoff;
     const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * rs + hoff;
@@ -733,15 +752,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int hf_hi = wave_any ? -wave_max(valid ? -hv : INT_MIN + 1) : INT_MIN;
 
     // ---- a pipelined stream of KT-key tiles of one source into S: tile i+1 is
-    // on its way into the other LDS buffer while tile i is computed
-    TIO tio;
-    tio.init(tid, rs);
-    int parity = 0;
-    auto stream = [&](const T* kb, const T* vb, int k_begin, int k_end, int type) {
+    // on its way into the other LDS buffer while tile i is computed, and the
+    // last tile of a stream overlaps the first tile of the next stream
+    // (nkb, nvb, [nk_begin, nk_end)), so the pipeline does not drain between
+    // branches
+    auto stream = [&](const T* kb, const T* vb, int k_begin, int k_end, int type, const T* nkb, const T* nvb,
+                      int nk_begin, int nk_end) {
         const int n = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
         if (n == 0) return;
-        tio.issue(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, min(KT, k_end - k_begin),
-                  tbuf(parity));
+        if (!pf)
+            tio.issue(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, min(KT, k_end - k_begin),
+                      tbuf(parity));
+        pf = false;
         tio.commit(tbuf(parity));
         __syncthreads();
         for (int i = 0; i < n; ++i) {
@@ -750,20 +772,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
             if (i + 1 < n) {
                 const int k1 = k0 + KT;
                 tio.issue(kb + (long long)k1 * rs, vb + (long long)k1 * rs, min(KT, k_end - k1), tbuf(parity ^ 1));
+            } else if (nk_end > nk_begin) {
+                tio.issue(nkb + (long long)nk_begin * rs, nvb + (long long)nk_begin * rs,
+                          min(KT, nk_end - nk_begin), tbuf(parity ^ 1));
+                pf = true;
             }
             auto pvf = [&](int ch, const float* pp, f32x4_t* acc) { tio.pv(buf, ch * KC, pp, acc); };
             {
-                // one softmax step over the whole KT = 2 KC key tile
+                // one softmax step over the whole KT = 2 KC key tile.  One code
+                // path for every tile (the softmax state stays in place): a tile
+                // inside the range of every column of the wave takes an all-ones
+                // mask without computing it.
                 bool full;
                 if (type == ITEM_WIN) full = k0 >= wf_lo && k0 + KT - 1 <= wf_hi;
                 else if (type == ITEM_HCA) full = k0 + KT <= hf_hi;
                 else full = false;
-                float sc[16];
-                if (full) {
-                    tio.scores(buf, 0, qf, sc);
-                    tio.scores(buf, KC, qf, sc + 8);
-                    softmax_pv<D, 2, true>(S, sc, 0xFFFFu, p.scale_log2, pvf);
-                } else {
+                uint32_t mb = 0xFFFFu;
+                if (!full) {
                     uint32_t m0, m1;
                     if (type == ITEM_WIN) {
                         m0 = range_mask(wv_lo - k0, wv_hi - k0);
@@ -778,13 +803,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                         m0 = w2.x;
                         m1 = w2.y;
                     }
-                    const uint32_t mb = TR::lane_bits(m0, q4) | (TR::lane_bits(m1, q4) << 8);
-                    if (__any(mb != 0u)) {
-                        tio.scores(buf, 0, qf, sc);
-                        tio.scores(buf, KC, qf, sc + 8);
-                        softmax_pv<D, 2, false>(S, sc, mb, p.scale_log2, pvf);
-                    }
+                    mb = TR::lane_bits(m0, q4) | (TR::lane_bits(m1, q4) << 8);
                 }
+                float sc[16];
+                tio.scores(buf, 0, qf, sc);
+                tio.scores(buf, KC, qf, sc + 8);
+                softmax_pv<D, 2, false>(S, sc, mb, p.scale_log2, pvf);
             }
             parity ^= 1;
             if (i + 1 < n) tio.commit(tbuf(parity));
@@ -842,13 +866,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     };
 
     // ---- the branch schedule
+    // window -> [CSA -> window again] -> HCA; each stream names the one that
+    // follows it (none before a gather: the gather reuses the tile buffers)
+    const bool win2 = do_csa && do_hca && !p.nsplit;
     if (do_win) {
-        stream(kraw, vraw, 0, wlen, ITEM_WIN);
+        if (do_csa && !GATHER) stream(kraw, vraw, 0, wlen, ITEM_WIN, kcsa, vcsa, 0, c_hi);
+        else if (!do_csa && do_hca) stream(kraw, vraw, 0, wlen, ITEM_WIN, khca, vhca, h_lo, h_hi);
+        else stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
         if (!p.nsplit) fold(gate[2]);
     }
     if (do_csa) {
         if constexpr (!GATHER) {
-            stream(kcsa, vcsa, 0, c_hi, ITEM_CSA);
+            stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, kraw, vraw, 0, win2 ? wlen : 0);
         } else {
             __syncthreads();  // the stream buffers become the per-wave gather tiles
             gather();
@@ -856,14 +885,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
         if (!p.nsplit) {
             fold(gate[1]);
-            if (do_hca) {
+            if (win2) {
                 S.init();
-                stream(kraw, vraw, 0, wlen, ITEM_WIN);
+                stream(kraw, vraw, 0, wlen, ITEM_WIN, khca, vhca, h_lo, h_hi);
             }
         }
     }
     if (do_hca) {
-        stream(khca, vhca, h_lo, h_hi, ITEM_HCA);
+        stream(khca, vhca, h_lo, h_hi, ITEM_HCA, nullptr, nullptr, 0, 0);
         if (!p.nsplit) fold(gate[0]);
     }
 
