@@ -8,19 +8,25 @@
 //
 // Design:
 //  * One workgroup = (sequence b, KV head g, a tile of QW query rows) with the
-//    G = H/Hkv query heads of that KV head: 16..64 "columns" (query, head),
-//    16 per wave.  All columns of a workgroup share the window and HCA keys,
-//    so those K/V tiles are staged once in LDS and read by every wave.
-//  * Transposed MFMA formulation: S^T = K Q^T (rows = 32 keys per chunk,
+//    G = H/Hkv query heads of that KV head: 64 "columns" (query, head), 16 per
+//    wave.  All columns of a workgroup share the window and HCA keys, so those
+//    K/V tiles are staged once in LDS and read by every wave.
+//  * Transposed MFMA formulation: S^T = K Q^T (rows = 32 keys per tile,
 //    columns = the wave's 16 (query, head) pairs) and O^T = V^T P^T.  The key
 //    rows of the two 16-row S^T tiles are interleaved so that the C layout of
 //    S^T is already the B-operand layout of P^T: no LDS round trip for P.
-//    V is stored transposed in LDS (written transposed while staging).
-//  * Three online-softmax states per column (window, HCA part, CSA part) in
-//    registers; the window state is shared by all branches and merged with
-//    the HCA / CSA states in the epilogue:
-//       O_SWA = win, O_HCA = merge(win, hca), O_CSA = merge(win, csa),
-//       out   = g0 O_HCA + g1 O_CSA + g2 O_SWA  (float32, rounded once).
+//  * bf16 K/V tiles arrive by direct global->LDS loads into XOR-swizzled rows
+//    (no register staging); V^T operands come from transposing LDS reads.
+//    Tiles are double-buffered and the pipeline runs on across the branches
+//    of a workgroup (the last tile of one key source overlaps the first tile
+//    of the next).  32-key tiles keep LDS at 32 KB and VGPRs at ~160 per
+//    wave, so three workgroups share a CU.
+//  * One running online-softmax state per column (log2 domain, the scale
+//    folded into the exponent's FMA) and one gated output accumulator:
+//    window -> fold g2 O_SWA; continue with the selected CSA entries -> fold
+//    g1 O_CSA; restart, window again + HCA entries -> fold g0 O_HCA.  The
+//    window is recomputed only when both compressed branches are active.
+//    out = g0 O_HCA + g1 O_CSA + g2 O_SWA is rounded once.
 //  * CSA keys: when the selections of a tile's queries cover most visible
 //    entries (small N, G < 8) the CSA entries are attended densely with a
 //    per-(query, entry) selection bitmap in LDS ("dense-masked"); otherwise
@@ -30,6 +36,8 @@
 //  * Long key lists with few workgroups (decode) are split along the key
 //    list; each split writes (m, l, acc) partial states to the workspace and a
 //    combine kernel merges them in split order (deterministic).
+//  * Workgroups are remapped so that each XCD (own L2) runs a contiguous
+//    range of (sequence, head, query tile) work.
 #include <algorithm>
 #include <cmath>
 
@@ -46,7 +54,7 @@ long long n_visible_host(long long t, int W, int m, int N) {
 
 namespace {
 
-constexpr int KT = 64;  // keys per shared LDS tile
+constexpr int KT = 32;  // keys per shared LDS tile (one MFMA chunk; small tiles keep 3 workgroups per CU)
 constexpr int KC = 32;  // keys per MFMA chunk
 
 enum CsaMode { CSA_NONE = 0, CSA_DENSE = 1, CSA_GATHER = 2 };
@@ -346,65 +354,6 @@ __device__ __forceinline__ long long n_visible(long long t, int W, int m, int N)
 // Register staging of one KT-key tile (global -> registers -> LDS), so the next
 // tile's loads are in flight while the current tile is computed.
 template <typename T, int D, int NT> struct Stage;
-
-template <int D, int NT> struct Stage<bf16_t, D, NT> {
-    static constexpr int PIECES = D / 8;                          // 16-byte pieces per row
-    static constexpr int KU = KT * PIECES;                        // K pieces per tile
-    static constexpr int VUN = (KT / 2) * PIECES;                 // V units (2 keys x 8 dims)
-    static constexpr int KP = (KU + NT - 1) / NT;
-    static constexpr int VU = (VUN + NT - 1) / NT;
-    uint4 k[KP];
-    uint4 v[VU][2];
-    // rows [0, nvalid) of the tile start at kb / vb, rs elements apart.  Rows
-    // past nvalid repeat row 0 (finite data, never attended: their weights
-    // are exactly 0).  Branch-free.
-    __device__ void load(const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb, int rs, int nvalid,
-                         int tid) {
-#pragma unroll
-        for (int j = 0; j < KP; ++j) {
-            const int u = tid + j * NT;
-            const int kk = u / PIECES, pc = u % PIECES;
-            const bool ok = kk < nvalid && (KU % NT == 0 || u < KU);
-            k[j] = ld16(kb + (ok ? kk : 0) * rs + pc * 8);
-        }
-        // V: key pairs fastest across lanes (conflict-free transposed LDS writes)
-#pragma unroll
-        for (int j = 0; j < VU; ++j) {
-            const int u = tid + j * NT;
-            const int kp = u % (KT / 2), oc = u / (KT / 2);
-            const bool in = VUN % NT == 0 || u < VUN;
-            const bool ok0 = in && 2 * kp < nvalid, ok1 = in && 2 * kp + 1 < nvalid;
-            v[j][0] = ld16(vb + (ok0 ? 2 * kp : 0) * rs + (in ? oc : 0) * 8);
-            v[j][1] = ld16(vb + (ok1 ? 2 * kp + 1 : 0) * rs + (in ? oc : 0) * 8);
-        }
-    }
-    __device__ void store(bf16_t* Ks, bf16_t* Vt, int tid) const {
-        constexpr int KPAD = D + 8, VST = KT + 8;
-#pragma unroll
-        for (int j = 0; j < KP; ++j) {
-            const int u = tid + j * NT;
-            if (KU % NT == 0 || u < KU) {
-                const int kk = u / PIECES, pc = u % PIECES;
-                *reinterpret_cast<uint4*>(Ks + kk * KPAD + pc * 8) = k[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < VU; ++j) {
-            const int u = tid + j * NT;
-            const int kp = u % (KT / 2), oc = u / (KT / 2);
-            if (VUN % NT == 0 || u < VUN) {
-                const uint32_t a[4] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w};
-                const uint32_t c[4] = {v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
-#pragma unroll
-                for (int dd = 0; dd < 8; ++dd) {
-                    const uint32_t lo = (dd & 1) ? (a[dd >> 1] >> 16) : (a[dd >> 1] & 0xFFFFu);
-                    const uint32_t hi = (dd & 1) ? (c[dd >> 1] & 0xFFFF0000u) : (c[dd >> 1] << 16);
-                    *reinterpret_cast<uint32_t*>(Vt + (oc * 8 + dd) * VST + 2 * kp) = lo | hi;
-                }
-            }
-        }
-    }
-};
 
 template <int D, int NT> struct Stage<float, D, NT> {
     static constexpr int PIECES = D / 4;
@@ -787,28 +736,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 if (type == ITEM_WIN) full = k0 >= wf_lo && k0 + KT - 1 <= wf_hi;
                 else if (type == ITEM_HCA) full = k0 + KT <= hf_hi;
                 else full = false;
-                uint32_t mb = 0xFFFFu;
+                constexpr int NCH = KT / KC;  // 32-key chunks per tile
+                uint32_t mb = NCH == 2 ? 0xFFFFu : 0xFFu;
                 if (!full) {
-                    uint32_t m0, m1;
-                    if (type == ITEM_WIN) {
-                        m0 = range_mask(wv_lo - k0, wv_hi - k0);
-                        m1 = range_mask(wv_lo - k0 - KC, wv_hi - k0 - KC);
-                    } else if (type == ITEM_HCA) {
-                        m0 = range_mask(0, hv - k0 - 1);
-                        m1 = range_mask(0, hv - k0 - KC - 1);
-                    } else {
-                        const bool ok = valid && k0 < c_hi;
-                        const uint2 w2 = ok ? *reinterpret_cast<const uint2*>(bm + ql * p.bm_words + (k0 >> 5))
-                                            : make_uint2(0u, 0u);
-                        m0 = w2.x;
-                        m1 = w2.y;
+                    uint32_t m[NCH];
+#pragma unroll
+                    for (int ch = 0; ch < NCH; ++ch) {
+                        const int kc0 = k0 + ch * KC;
+                        if (type == ITEM_WIN) m[ch] = range_mask(wv_lo - kc0, wv_hi - kc0);
+                        else if (type == ITEM_HCA) m[ch] = range_mask(0, hv - kc0 - 1);
                     }
-                    mb = TR::lane_bits(m0, q4) | (TR::lane_bits(m1, q4) << 8);
+                    if (type == ITEM_CSA) {
+                        const bool ok = valid && k0 < c_hi;
+                        if constexpr (NCH == 2) {
+                            const uint2 w2 = ok ? *reinterpret_cast<const uint2*>(bm + ql * p.bm_words + (k0 >> 5))
+                                                : make_uint2(0u, 0u);
+                            m[0] = w2.x;
+                            m[NCH - 1] = w2.y;
+                        } else {
+                            m[0] = ok ? bm[ql * p.bm_words + (k0 >> 5)] : 0u;
+                        }
+                    }
+                    mb = 0u;
+#pragma unroll
+                    for (int ch = 0; ch < NCH; ++ch) mb |= TR::lane_bits(m[ch], q4) << (8 * ch);
                 }
-                float sc[16];
-                tio.scores(buf, 0, qf, sc);
-                tio.scores(buf, KC, qf, sc + 8);
-                softmax_pv<D, 2, false>(S, sc, mb, p.scale_log2, pvf);
+                float sc[8 * NCH];
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) tio.scores(buf, ch * KC, qf, sc + 8 * ch);
+                softmax_pv<D, NCH, false>(S, sc, mb, p.scale_log2, pvf);
             }
             parity ^= 1;
             if (i + 1 < n) tio.commit(tbuf(parity));
@@ -926,9 +882,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 // compiler otherwise dropped the stubs of some variants).
 #define SHATTN_ATTN_INST(T, D)                                               \
     template __global__ void attn_fwd_kernel<T, D, 4, false>(AttnParams);    \
-    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);     \
-    template __global__ void attn_fwd_kernel<T, D, 8, false>(AttnParams);    \
-    template __global__ void attn_fwd_kernel<T, D, 8, true>(AttnParams);
+    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);
 SHATTN_ATTN_INST(bf16_t, 64)
 SHATTN_ATTN_INST(bf16_t, 128)
 SHATTN_ATTN_INST(float, 64)
@@ -1080,13 +1034,9 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.k = has_csa ? a->k : 0;
     const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
     p.scale_log2 = scale * 1.4426950408889634f;
-    // 8 waves (128 columns) per workgroup for prefill: every staged K/V tile is
-    // shared by twice as many (query, head) columns; 4 waves for short launches.
-    const bool small = (long long)a->B * a->Hkv * ((long long)a->Tq * G) < 128LL * 1024;
-    // the CSA gather path keeps per-wave gather tiles: 4 waves keep LDS in budget
-    const bool gather_likely = has_csa && !(G < 8 && a->N_csa <= 4096);
-    (void)small;
-    (void)gather_likely;
+    // 4 waves (64 (query, head) columns) per workgroup: two workgroups share a
+    // CU, so one computes while the other waits at a barrier or on its loads
+    // (8-wave workgroups measured slower)
     pl.waves = 4;
     p.ncol = pl.waves * 16;
     p.QW = G >= p.ncol ? 1 : p.ncol / G;
@@ -1183,9 +1133,8 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
 
 template <typename T, int D>
 static int launch_attn(Plan& pl, hipStream_t s) {
-    if (pl.p.csa_mode == CSA_GATHER)
-        return pl.waves == 8 ? launch_attn_nw<T, D, 8, true>(pl, s) : launch_attn_nw<T, D, 4, true>(pl, s);
-    return pl.waves == 8 ? launch_attn_nw<T, D, 8, false>(pl, s) : launch_attn_nw<T, D, 4, false>(pl, s);
+    if (pl.p.csa_mode == CSA_GATHER) return launch_attn_nw<T, D, 4, true>(pl, s);
+    return launch_attn_nw<T, D, 4, false>(pl, s);
 }
 
 extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
