@@ -302,25 +302,59 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
     float mx[VW];
 #pragma unroll
     for (int v = 0; v < VW; ++v) mx[v] = -INFINITY;
+    // logits of this thread's PPT positions, VW channels: 16-byte loads
+    auto load_logits = [&](const float* z, int i, float* out) {
+        const float4* src = reinterpret_cast<const float4*>(z + (size_t)i * C + (size_t)j * VW);
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-        const int i = s * PPT + q;
-#pragma unroll
-        for (int v = 0; v < VW; ++v) {
-            pb[q][v] = active ? zb[(size_t)i * C + (size_t)j * VW + v] : -INFINITY;
-            mx[v] = fmaxf(mx[v], pb[q][v]);
+        for (int u = 0; u < VW / 4; ++u) {
+            const float4 f = src[u];
+            out[4 * u + 0] = f.x;
+            out[4 * u + 1] = f.y;
+            out[4 * u + 2] = f.z;
+            out[4 * u + 3] = f.w;
         }
-    }
-#pragma unroll
-    for (int v = 0; v < VW; ++v) red[0][tid * VW + v] = mx[v];
-    __syncthreads();
+    };
     if (active) {
 #pragma unroll
-        for (int v = 0; v < VW; ++v) {
-            float a = -INFINITY;
-            for (int r = 0; r < R; ++r) a = fmaxf(a, red[0][(r * NGt + jl) * VW + v]);
-            mx[v] = a;
+        for (int q = 0; q < PPT; ++q) load_logits(zb, s * PPT + q, pb[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PPT; ++q)
+#pragma unroll
+            for (int v = 0; v < VW; ++v) pb[q][v] = -INFINITY;
+    }
+#pragma unroll
+    for (int q = 0; q < PPT; ++q)
+#pragma unroll
+        for (int v = 0; v < VW; ++v) mx[v] = fmaxf(mx[v], pb[q][v]);
+    // per-thread partials -> LDS; the R partials of a channel group combine in a
+    // fixed order (16-byte LDS reads)
+    auto reduce_rows = [&](float* buf, const float* mine, float* out, bool is_max) {
+#pragma unroll
+        for (int u = 0; u < VW / 4; ++u)
+            reinterpret_cast<float4*>(buf + tid * VW)[u] =
+                make_float4(mine[4 * u], mine[4 * u + 1], mine[4 * u + 2], mine[4 * u + 3]);
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int v = 0; v < VW; ++v) out[v] = is_max ? -INFINITY : 0.f;
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int u = 0; u < VW / 4; ++u) {
+                    const float4 f = reinterpret_cast<const float4*>(buf + (r * NGt + jl) * VW)[u];
+                    const float g[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        out[4 * u + e] = is_max ? fmaxf(out[4 * u + e], g[e]) : out[4 * u + e] + g[e];
+                }
+            }
         }
+    };
+    {
+        float part[VW];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) part[v] = mx[v];
+        reduce_rows(red[0], part, mx, true);
     }
     float sum[VW];
 #pragma unroll
@@ -333,17 +367,16 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
             pb[q][v] = e;
             sum[v] += e;
         }
+    {
+        float tot[VW];
+        reduce_rows(red[1], sum, tot, false);
+        if (active) {
 #pragma unroll
-    for (int v = 0; v < VW; ++v) red[1][tid * VW + v] = sum[v];
-    __syncthreads();
-    if (active) {
+            for (int v = 0; v < VW; ++v) {
+                const float inv = 1.0f / tot[v];
 #pragma unroll
-        for (int v = 0; v < VW; ++v) {
-            float a = 0.f;
-            for (int r = 0; r < R; ++r) a += red[1][(r * NGt + jl) * VW + v];
-            const float inv = 1.0f / a;
-#pragma unroll
-            for (int q = 0; q < PPT; ++q) pb[q][v] *= inv;
+                for (int q = 0; q < PPT; ++q) pb[q][v] *= inv;
+            }
         }
     }
     // ---- m1 weights (the thread sees whole m1-blocks)
@@ -352,13 +385,19 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
         float am[VW], as[VW];
 #pragma unroll
         for (int v = 0; v < VW; ++v) { am[v] = -INFINITY; as[v] = 0.f; }
+        if (active) {
+#pragma unroll
+            for (int q = 0; q < M1; ++q) load_logits(za, q, pa[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < M1; ++q)
+#pragma unroll
+                for (int v = 0; v < VW; ++v) pa[q][v] = 0.f;
+        }
 #pragma unroll
         for (int q = 0; q < M1; ++q)
 #pragma unroll
-            for (int v = 0; v < VW; ++v) {
-                pa[q][v] = active ? za[(size_t)q * C + (size_t)j * VW + v] : 0.f;
-                am[v] = fmaxf(am[v], pa[q][v]);
-            }
+            for (int v = 0; v < VW; ++v) am[v] = fmaxf(am[v], pa[q][v]);
 #pragma unroll
         for (int q = 0; q < M1; ++q)
 #pragma unroll
@@ -375,8 +414,10 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
     }
     __syncthreads();
 
-    int buf = 0;
-    for (long long bc = bc0; bc < bc1; ++bc) {
+    // One block: compute from `cur` while the next block's rows load into
+    // `nxt`.  The two register buffers alternate by unrolling the block loop
+    // by two, so rows in flight are never copied (a copy would wait for them).
+    auto step = [&](long long bc, const uint4 (&cur)[PPT], uint4 (&nxt)[PPT], int buf) {
         const long long b = bc / N2;
         const long long c = bc - b * N2;
         float acc[VW];
@@ -384,15 +425,12 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
         for (int v = 0; v < VW; ++v) acc[v] = 0.f;
         if (active) {
             const long long row0 = (long long)c * m2 + (long long)s * PPT;  // first row in the sequence
-            uint4 raw[PPT];
-#pragma unroll
-            for (int q = 0; q < PPT; ++q) raw[q] = nxt[q];
             if (bc + 1 < bc1) load_rows(bc + 1, nxt);   // next block's rows in flight
             float o[VW];
 #pragma unroll
             for (int q = 0; q < PPT; ++q) {
                 float f[VW];
-                Elem<T>::unpack(raw[q], f);
+                Elem<T>::unpack(cur[q], f);
                 if (q % M1 == 0) {
 #pragma unroll
                     for (int v = 0; v < VW; ++v) o[v] = 0.f;
@@ -411,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
         float* r = red[buf];
 #pragma unroll
         for (int v = 0; v < VW; ++v) r[tid * VW + v] = acc[v];
-        __syncthreads();
+        __syncthreads();   // (waits for LDS only: the rows in flight stay in flight)
         T* __restrict__ dst = yb + (size_t)bc * C;
         // channel ch of the tile is summed by 4 consecutive threads (R/4 partials
         // each), then combined in a fixed order across those 4 lanes
@@ -436,7 +474,12 @@ __global__ __launch_bounds__(kThreads) void compress_dual_kernel(
                 if (j2 < NG) Elem<T>::store1(dst + (size_t)j2 * VW + v2, tot);
             }
         }
-        buf ^= 1;   // next block writes the other buffer: one barrier per block
+        // the next block writes the other red buffer: one barrier per block
+    };
+    uint4 nxt2[PPT];
+    for (long long bc = bc0; bc < bc1; bc += 2) {
+        step(bc, nxt, nxt2, 0);
+        if (bc + 1 < bc1) step(bc + 1, nxt2, nxt, 1);
     }
 }
 
@@ -485,8 +528,8 @@ extern "C" int hca_compress_kv_dual(const void* k, const void* v, const float* z
     if (B == 0 || N1 == 0) return SHATTN_OK;
     if (!k || !v || !zk1 || !zv1 || !kc1 || !vc1 || !zk2 || !zv2 || (N2 > 0 && (!kc2 || !vc2)))
         return fail(SHATTN_EINVAL, "hca_compress_kv_dual: null pointer");
-    if (!aligned16(k) || !aligned16(v) || !aligned16(kc1) || !aligned16(vc1) ||
-        (N2 > 0 && (!aligned16(kc2) || !aligned16(vc2))))
+    if (!aligned16(k) || !aligned16(v) || !aligned16(kc1) || !aligned16(vc1) || !aligned16(zk1) ||
+        !aligned16(zv1) || !aligned16(zk2) || !aligned16(zv2) || (N2 > 0 && (!aligned16(kc2) || !aligned16(vc2))))
         return fail(SHATTN_EINVAL, "hca_compress_kv_dual: tensors must be 16-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // the rows past the last full m2-block only feed ratio m1: compress them on their own
@@ -502,8 +545,10 @@ extern "C" int hca_compress_kv_dual(const void* k, const void* v, const float* z
         if (NGt > NG) NGt = NG;
         const int tiles = (NG + NGt - 1) / NGt;
         const long long total = (long long)B * N2;
-        // about one resident round of workgroups (4 per CU, K and V slices)
-        long long per = (total * tiles * 2 + 1023) / 1024;
+        // about one resident round of workgroups (3 per CU, K and V slices): the
+        // per-workgroup set-up (softmax weights of both ratios) is amortised
+        // over many blocks
+        long long per = (total * tiles * 2 + 767) / 768;
         if (per < 2) per = 2;
         if (per > 64) per = 64;
         const long long ywgs = (total + per - 1) / per;
