@@ -49,7 +49,24 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     const int ppt = (m < kPPT) ? m : kPPT;
     const int spos = R == 1 ? 0 : s;  // which positions of the block this thread owns
 
-    // ---- softmax weights of this thread's positions and channels
+    const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
+    long long bc1 = bc0 + blocks_per_wg;
+    if (bc1 > total_blocks) bc1 = total_blocks;
+    // rows of block bc owned by this thread (R > 1: positions s*ppt .. +ppt)
+    auto load_rows = [&](long long bc, uint4* raw) {
+        const long long b = bc / N;
+        const long long c = bc - b * N;
+        const T* __restrict__ src = x + ((size_t)b * T_len + (size_t)c * m + (size_t)s * ppt) * C + (size_t)j * VW;
+#pragma unroll
+        for (int q = 0; q < kPPT; ++q)
+            raw[q] = (q < ppt && s * ppt + q < m) ? ld16_stream(src + (size_t)q * C) : make_uint4(0, 0, 0, 0);
+    };
+    uint4 rowsA[kPPT];
+    if (R > 1 && active && bc0 < bc1) load_rows(bc0, rowsA);   // first block in flight during the set-up
+
+    // ---- softmax weights of this thread's positions and channels (16-byte
+    // logit loads; the partials of the R threads of a channel group combine
+    // in LDS in a fixed order)
     float p[kPPT][VW];
     float mx[VW];
 #pragma unroll
@@ -57,27 +74,46 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 #pragma unroll
     for (int q = 0; q < kPPT; ++q) {
         const int i = spos * ppt + q;
-        const bool ok = active && q < ppt && i < m;
+        if (active && q < ppt && i < m) {
+            const float4* zs = reinterpret_cast<const float4*>(z + (size_t)i * C + (size_t)j * VW);
 #pragma unroll
-        for (int v = 0; v < VW; ++v) {
-            p[q][v] = ok ? z[(size_t)i * C + (size_t)j * VW + v] : -INFINITY;
-            mx[v] = fmaxf(mx[v], p[q][v]);
+            for (int u = 0; u < VW / 4; ++u) {
+                const float4 f = zs[u];
+                p[q][4 * u + 0] = f.x;
+                p[q][4 * u + 1] = f.y;
+                p[q][4 * u + 2] = f.z;
+                p[q][4 * u + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < VW; ++v) p[q][v] = -INFINITY;
         }
-    }
-    if (R > 1) {
 #pragma unroll
-        for (int v = 0; v < VW; ++v) red[tid * VW + v] = mx[v];
+        for (int v = 0; v < VW; ++v) mx[v] = fmaxf(mx[v], p[q][v]);
+    }
+    auto combine = [&](float* vals, bool is_max) {
+#pragma unroll
+        for (int u = 0; u < VW / 4; ++u)
+            reinterpret_cast<float4*>(red + tid * VW)[u] =
+                make_float4(vals[4 * u], vals[4 * u + 1], vals[4 * u + 2], vals[4 * u + 3]);
         __syncthreads();
         if (active) {
 #pragma unroll
-            for (int v = 0; v < VW; ++v) {
-                float a = -INFINITY;
-                for (int r = 0; r < R; ++r) a = fmaxf(a, red[(r * NGt + jl) * VW + v]);
-                mx[v] = a;
+            for (int v = 0; v < VW; ++v) vals[v] = is_max ? -INFINITY : 0.f;
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int u = 0; u < VW / 4; ++u) {
+                    const float4 f = reinterpret_cast<const float4*>(red + (r * NGt + jl) * VW)[u];
+                    const float g[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        vals[4 * u + e] = is_max ? fmaxf(vals[4 * u + e], g[e]) : vals[4 * u + e] + g[e];
+                }
             }
         }
         __syncthreads();
-    }
+    };
+    if (R > 1) combine(mx, true);
     float sum[VW];
 #pragma unroll
     for (int v = 0; v < VW; ++v) sum[v] = 0.f;
@@ -90,20 +126,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             sum[v] += e;
         }
     }
-    if (R > 1) {
-#pragma unroll
-        for (int v = 0; v < VW; ++v) red[tid * VW + v] = sum[v];
-        __syncthreads();
-        if (active) {
-#pragma unroll
-            for (int v = 0; v < VW; ++v) {
-                float a = 0.f;
-                for (int r = 0; r < R; ++r) a += red[(r * NGt + jl) * VW + v];
-                sum[v] = a;
-            }
-        }
-        __syncthreads();
-    }
+    if (R > 1) combine(sum, false);
 #pragma unroll
     for (int v = 0; v < VW; ++v) {
         const float inv = 1.0f / sum[v];
@@ -112,9 +135,6 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     }
 
     // ---- stream the blocks assigned to this workgroup
-    const long long bc0 = (long long)blockIdx.y * blocks_per_wg;
-    long long bc1 = bc0 + blocks_per_wg;
-    if (bc1 > total_blocks) bc1 = total_blocks;
     if (R == 1) {
         // whole blocks per thread: thread s of a channel group takes blocks
         // bc0 + s, bc0 + s + nsub, ...; two blocks' loads are in flight at once
@@ -151,27 +171,19 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
         }
         return;
     }
-    for (long long bc = bc0; bc < bc1; ++bc) {
-        const long long b = bc / N;
-        const long long c = bc - b * N;
+    // R > 1: the R threads of a channel group each sum ppt positions; block
+    // bc + 1 loads into the other register buffer while block bc is reduced
+    // (the loop is unrolled by two so rows in flight are never copied)
+    auto step = [&](long long bc, const uint4 (&cur)[kPPT], uint4 (&nxt)[kPPT]) {
         float acc[VW];
 #pragma unroll
         for (int v = 0; v < VW; ++v) acc[v] = 0.f;
         if (active) {
-            const T* __restrict__ src =
-                x + ((size_t)b * T_len + (size_t)c * m + (size_t)s * ppt) * C + (size_t)j * VW;
-            uint4 raw[kPPT];
-#pragma unroll
-            for (int q = 0; q < kPPT; ++q) {
-                if (q < ppt && s * ppt + q < m)
-                    raw[q] = ld16_stream(src + (size_t)q * C);
-                else
-                    raw[q] = make_uint4(0, 0, 0, 0);
-            }
+            if (bc + 1 < bc1) load_rows(bc + 1, nxt);
 #pragma unroll
             for (int q = 0; q < kPPT; ++q) {
                 float f[VW];
-                Elem<T>::unpack(raw[q], f);
+                Elem<T>::unpack(cur[q], f);
 #pragma unroll
                 for (int v = 0; v < VW; ++v) acc[v] = fmaf(p[q][v], f[v], acc[v]);
             }
@@ -192,6 +204,11 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             }
         }
         __syncthreads();
+    };
+    uint4 rowsB[kPPT];
+    for (long long bc = bc0; bc < bc1; bc += 2) {
+        step(bc, rowsA, rowsB);
+        if (bc + 1 < bc1) step(bc + 1, rowsB, rowsA);
     }
 }
 
@@ -216,7 +233,7 @@ extern "C" int hca_compress_kv(const void* k, const void* v, const float* zk, co
     if (B == 0 || N == 0) return SHATTN_OK;
     if (!k || !v || !zk || !zv || !kc || !vc)
         return fail(SHATTN_EINVAL, "hca_compress_kv: null pointer");
-    if (!aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc))
+    if (!aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc) || !aligned16(zk) || !aligned16(zv))
         return fail(SHATTN_EINVAL, "hca_compress_kv: tensors must be 16-byte aligned");
     const int C = Hkv * d;
     const int VW = dtype == SHATTN_DTYPE_BF16 ? 8 : 4;
