@@ -22,11 +22,14 @@
 //    of the next).  32-key tiles keep LDS at 32 KB and VGPRs at ~160 per
 //    wave, so three workgroups share a CU.
 //  * One running online-softmax state per column (log2 domain, the scale
-//    folded into the exponent's FMA) and one gated output accumulator:
-//    window -> fold g2 O_SWA; continue with the selected CSA entries -> fold
-//    g1 O_CSA; restart, window again + HCA entries -> fold g0 O_HCA.  The
-//    window is recomputed only when both compressed branches are active.
-//    out = g0 O_HCA + g1 O_CSA + g2 O_SWA is rounded once.
+//    folded into the exponent's FMA) and one gated output accumulator.  The
+//    HCA entries are attended alone first (their raw state parks in the
+//    output accumulator), then the window once: O_SWA is the window state and
+//    O_HCA the merge of the window and HCA states, which needs only their
+//    maxima and sums.  The CSA entries then continue the window's state
+//    (O_CSA).  Every key is attended once per branch that contains it and the
+//    window is never recomputed.  out = g0 O_HCA + g1 O_CSA + g2 O_SWA is
+//    rounded once.
 //  * CSA keys: when the selections of a tile's queries cover most visible
 //    entries (small N, G < 8) the CSA entries are attended densely with a
 //    per-(query, entry) selection bitmap in LDS ("dense-masked"); otherwise
@@ -597,11 +600,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const long long win_lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;  // this column's window start
 
     // One running online-softmax state S and one output accumulator oacc per
-    // column.  Branches are folded into oacc (normalised and gated) as soon as
-    // they are complete:  S = window -> fold g2 (SWA);  S continues with the
-    // CSA entries -> fold g1;  S restarts, window again + HCA entries -> fold
-    // g0.  The window is recomputed only when both HCA and CSA are active;
-    // this keeps two accumulator arrays live instead of three.
+    // column (two d-wide float32 arrays live); the branch schedule below folds
+    // each branch into oacc, normalised and gated, as soon as it is complete.
     State<DT> S;
     S.init();
     f32x4_t oacc[DT];
@@ -641,11 +641,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const long long hoff = (long long)g * D;
     const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
     const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
+    if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
+    const int h_lo = do_hca ? (int)hca_lo : 0;
+    const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * rs + hoff;
+    const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * rs + hoff;
     TIO tio;
     tio.init(tid, rs);
     int parity = 0;
     bool pf = false;  // the first tile of the next stream is already on its way into tbuf(parity)
-    if (do_win && wlen > 0) {
+    // the first stream is the HCA one when it has entries, else the window
+    if (do_hca && h_hi > h_lo) {
+        tio.issue(khca + (long long)h_lo * rs, vhca + (long long)h_lo * rs, min(KT, h_hi - h_lo), tbuf(0));
+        pf = true;
+    } else if (do_win && wlen > 0) {
         tio.issue(kraw, vraw, min(KT, wlen), tbuf(0));
         pf = true;
     }
@@ -675,16 +684,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     // ---- geometry: every index inside a stream is a 32-bit offset from the
     // workgroup's window start (window) or from entry 0 (HCA, CSA)
-    int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
-    if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
-    const int h_lo = do_hca ? (int)hca_lo : 0;
     const int c_hi = dense_csa ? emax_s + 1 : 0;
     const int wv_lo = valid ? (int)(win_lo - w_lo) : 1;  // column's window [wv_lo, wv_hi]
     const int wv_hi = valid ? (int)(t - w_lo) : 0;
     int hv = (valid && do_hca) ? (int)n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
     if (hv > h_hi) hv = h_hi;
-    const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * rs + hoff;
-    const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * rs + hoff;
     const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * rs + hoff;
     const T* vcsa = reinterpret_cast<const T*>(p.v_csa) + (long long)b * p.N_csa * rs + hoff;
 
@@ -822,34 +826,66 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     };
 
     // ---- the branch schedule
-    // window -> [CSA -> window again] -> HCA; each stream names the one that
-    // follows it (none before a gather: the gather reuses the tile buffers)
-    const bool win2 = do_csa && do_hca && !p.nsplit;
-    if (do_win) {
-        if (do_csa && !GATHER) stream(kraw, vraw, 0, wlen, ITEM_WIN, kcsa, vcsa, 0, c_hi);
-        else if (!do_csa && do_hca) stream(kraw, vraw, 0, wlen, ITEM_WIN, khca, vhca, h_lo, h_hi);
-        else stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
-        if (!p.nsplit) fold(gate[2]);
-    }
-    if (do_csa) {
-        if constexpr (!GATHER) {
-            stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, kraw, vraw, 0, win2 ? wlen : 0);
-        } else {
-            __syncthreads();  // the stream buffers become the per-wave gather tiles
-            gather();
-            __syncthreads();
+    if (!p.nsplit) {
+        // HCA entries alone first; their raw state parks in oacc.  Then the
+        // window once: O_SWA is the window state, and O_HCA merges the window
+        // and HCA states, which needs only their maxima and sums:
+        //   O_HCA = (e_w A_w + e_h A_h) / (e_w l_w + e_h l_h),  e_x = 2^(m_x - M).
+        // Finally the CSA entries continue the window's state (O_CSA).
+        // Each stream names the one that follows it (none before a gather:
+        // the gather reuses the tile buffers).
+        float m_h = -INFINITY, l_h = 0.f;
+        if (do_hca) {
+            stream(khca, vhca, h_lo, h_hi, ITEM_HCA, kraw, vraw, 0, wlen);
+            m_h = S.m;
+            l_h = col_sum(S.l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] = S.acc[dt];
+            S.init();
         }
-        if (!p.nsplit) {
+        if (do_csa && !GATHER) stream(kraw, vraw, 0, wlen, ITEM_WIN, kcsa, vcsa, 0, c_hi);
+        else stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
+        {
+            const float l_w = col_sum(S.l);
+            float c_w = valid ? gate[2] / l_w : 0.f, c_h = 0.f;
+            if (do_hca) {
+                const float M = fmaxf(S.m, m_h);
+                const float e_w = __builtin_amdgcn_exp2f(S.m - M);
+                const float e_h = m_h == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_h - M);
+                const float den = fmaf(l_w, e_w, l_h * e_h);
+                if (valid) {
+                    c_w += gate[0] * e_w / den;
+                    c_h = gate[0] * e_h / den;
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[dt][r] = fmaf(c_w, S.acc[dt][r], c_h * oacc[dt][r]);
+        }
+        if (do_csa) {
+            if constexpr (!GATHER) {
+                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
+            } else {
+                __syncthreads();  // the stream buffers become the per-wave gather tiles
+                gather();
+                __syncthreads();
+            }
             fold(gate[1]);
-            if (win2) {
-                S.init();
-                stream(kraw, vraw, 0, wlen, ITEM_WIN, khca, vhca, h_lo, h_hi);
+        }
+    } else {
+        // one key range per workgroup; partial states are merged by the combine kernel
+        if (do_win) stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
+        if (do_csa) {
+            if constexpr (!GATHER) {
+                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
+            } else {
+                __syncthreads();
+                gather();
+                __syncthreads();
             }
         }
-    }
-    if (do_hca) {
-        stream(khca, vhca, h_lo, h_hi, ITEM_HCA, nullptr, nullptr, 0, 0);
-        if (!p.nsplit) fold(gate[0]);
+        if (do_hca) stream(khca, vhca, h_lo, h_hi, ITEM_HCA, nullptr, nullptr, 0, 0);
     }
 
     // ------------------------------------------------------------ epilogue
