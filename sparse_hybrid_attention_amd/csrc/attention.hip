@@ -326,9 +326,21 @@ __device__ __forceinline__ void softmax_pv(State<D / 16>& st, const float* s, ui
 #pragma unroll
     for (int j = 1; j < NJ; ++j) mloc = fmaxf(mloc, x[j]);
     mloc = col_max(mloc) * scale;
-    const float mnew = fmaxf(st.m, mloc);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+    // Lazy rescaling: the reference m of a column only moves when a new
+    // maximum exceeds it by more than 8 (log2 units); weights are then at most
+    // 2^8, which float32 sums and bf16 P operands hold without loss of
+    // relative precision, and the reference cancels in acc / l.
+    if (__builtin_expect(__any(mloc > st.m + 8.0f), 0)) {
+        const float mnew = fmaxf(st.m, mloc);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
+        st.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.acc[dt][r] *= alpha;
+        st.m = mnew;
+    }
+    const float muse = st.m == -INFINITY ? 0.f : st.m;
     float p[NJ];
     float ps = 0.f;
 #pragma unroll
@@ -336,12 +348,7 @@ __device__ __forceinline__ void softmax_pv(State<D / 16>& st, const float* s, ui
         p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], scale, -muse));
         ps += p[j];
     }
-    st.l = fmaf(st.l, alpha, ps);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.acc[dt][r] *= alpha;
-    st.m = mnew;
+    st.l += ps;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) pv(ch, p + 8 * ch, st.acc);
 }
