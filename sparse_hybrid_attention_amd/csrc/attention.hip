@@ -670,16 +670,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const bool dense_csa = !GATHER && do_csa && p.csa_mode == CSA_DENSE;
     uint32_t* bm = reinterpret_cast<uint32_t*>(smem + p.lds_bm);
     if (dense_csa) {
-        for (int u = tid; u < p.QW * p.bm_words; u += NT) bm[u] = 0u;
+        // bitmap of the selections of the workgroup's queries; the nq index rows
+        // are one contiguous [nq, k] block, read 4 entries at a time (k % 4 == 0,
+        // checked on the host).  A row is ascending, so entries of one bitmap
+        // word are adjacent: their bits are merged before one atomicOr.
+        for (int u = tid; u < p.QW * p.bm_words / 4; u += NT)
+            reinterpret_cast<uint4*>(bm)[u] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
         int emax = -1;
-        for (int u = tid; u < nq * p.k; u += NT) {
-            const int qq = u / p.k, j = u - qq * p.k;
-            const int e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
-            if (e >= 0 && e < p.N_csa) {
-                atomicOr(&bm[qq * p.bm_words + (e >> 5)], 1u << (e & 31));
-                emax = e > emax ? e : emax;
+        const int4* rows = reinterpret_cast<const int4*>(p.idx + ((long long)b * p.Tq + i0) * p.k);
+        const int n4 = nq * p.k / 4;
+        for (int u = tid; u < n4; u += NT) {
+            const int4 e4 = rows[u];
+            const int qq = (4 * u) / p.k;
+            uint32_t* brow = bm + qq * p.bm_words;
+            const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
+            int cw = -1;
+            uint32_t cbits = 0u;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int e = ev[x];
+                if (e >= 0 && e < p.N_csa) {
+                    emax = e > emax ? e : emax;
+                    if ((e >> 5) != cw) {
+                        if (cw >= 0) atomicOr(&brow[cw], cbits);
+                        cw = e >> 5;
+                        cbits = 0u;
+                    }
+                    cbits |= 1u << (e & 31);
+                }
             }
+            if (cw >= 0) atomicOr(&brow[cw], cbits);
         }
         for (int off = 32; off > 0; off >>= 1) {
             const int o = __shfl_xor(emax, off);
@@ -701,15 +722,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     // ---- wave-uniform key ranges attended by every valid column of the wave:
     // chunks inside them need no per-key mask
-    auto wave_max = [](int v) {
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off));
-        return __builtin_amdgcn_readfirstlane(v);
-    };
-    const bool wave_any = __any(valid);
-    const int wf_lo = wave_any ? wave_max(valid ? wv_lo : INT_MIN) : INT_MAX;
-    const int wf_hi = wave_any ? -wave_max(valid ? -wv_hi : INT_MIN + 1) : INT_MIN;
-    const int hf_hi = wave_any ? -wave_max(valid ? -hv : INT_MIN + 1) : INT_MIN;
+    // (scalar arithmetic: the wave's valid queries are qa..qb, and the window
+    // start, window end and visible HCA count all grow with the position)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int qa = (16 * wave_u) / p.G;
+    const int qb = min((16 * wave_u + 15) / p.G, nq - 1);
+    const bool wave_any = qa < nq;
+    const long long ta = p.q_pos0 + i0 + qa, tb = p.q_pos0 + i0 + qb;
+    int hf = do_hca ? (int)n_visible(ta, p.W, p.m_hca, p.N_hca) : 0;
+    if (hf > h_hi) hf = h_hi;
+    const int wf_lo = wave_any ? (int)((tb - p.W + 1 > 0 ? tb - p.W + 1 : 0) - w_lo) : INT_MAX;
+    const int wf_hi = wave_any ? (int)(ta - w_lo) : INT_MIN;
+    const int hf_hi = wave_any ? hf : INT_MIN;
 
     // ---- a pipelined stream of KT-key tiles of one source into S: tile i+1 is
     // on its way into the other LDS buffer while tile i is computed, and the
@@ -1121,10 +1145,10 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
         // dense-masked when the union of a tile's selections is likely dense
         const long long span_q = (long long)std::min(p.QW, a->Tq);
         const bool dense = p.nsplit == 0 && G < 8 && a->N_csa <= 4096 &&
-                           span_q * a->k >= a->N_csa / 2;
+                           span_q * a->k >= a->N_csa / 2 && a->k % 4 == 0 && aligned16(a->idx);
         if (dense) {
             p.csa_mode = CSA_DENSE;
-            p.bm_words = (a->N_csa + 63) / 64 * 2;   // even: a 64-key tile reads two words
+            p.bm_words = (a->N_csa + 127) / 128 * 4;   // multiple of 4: rows clear as 16-byte units
             p.lds_bm = (int)shared_b;
             lds = shared_b + (size_t)p.QW * p.bm_words * 4;
         } else {
