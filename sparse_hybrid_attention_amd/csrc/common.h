@@ -111,4 +111,59 @@ __device__ __forceinline__ long long xcd_work_id(long long i, long long n) {
     return x * q + (x < r ? x : r) + j;
 }
 
+
+// ---- wave-wide operations in registers (DPP / permlane; no LDS round trip)
+// dpp_ctrl values: quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), [2,3,0,1] = 0x4E
+// (lane ^ 2), row_ror:n = 0x120 + n, row_shr:n = 0x110 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// the two values held by lanes l and l ^ 16 (r[0] from the lower row of the pair)
+__device__ __forceinline__ void xor16_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
+    auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    lo = a[0];
+    hi = a[1];
+}
+__device__ __forceinline__ void xor32_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
+    auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = a[0];
+    hi = a[1];
+}
+// all-lane reduction with an associative, commutative op on 32-bit patterns
+template <typename F> __device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, F op) {
+    v = op(v, dpp_mov<0xB1>(v));
+    v = op(v, dpp_mov<0x4E>(v));
+    v = op(v, dpp_mov<0x124>(v));
+    v = op(v, dpp_mov<0x128>(v));
+    uint32_t lo, hi;
+    xor16_pair(v, lo, hi);
+    v = op(lo, hi);
+    xor32_pair(v, lo, hi);
+    return op(lo, hi);
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+    return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+// sum over the lanes l, l^16, l^32, l^48 in the fixed order (l0 + l16) + (l32 + l48)
+__device__ __forceinline__ float sum_xrows(float v) {
+    uint32_t lo, hi;
+    xor16_pair(__float_as_uint(v), lo, hi);
+    const float s = __uint_as_float(lo) + __uint_as_float(hi);
+    xor32_pair(__float_as_uint(s), lo, hi);
+    return __uint_as_float(lo) + __uint_as_float(hi);
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row 0 -> 1, row 2 -> 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // rows 0..1 -> 2, 3
+    return v;
+}
+
 }  // namespace shattn

@@ -111,11 +111,8 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         andv &= key;
         orv |= key;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        andv &= __shfl_xor(andv, off);
-        orv |= __shfl_xor(orv, off);
-    }
+    andv = wave_allreduce(andv, [](uint32_t a, uint32_t b) { return a & b; });
+    orv = wave_allreduce(orv, [](uint32_t a, uint32_t b) { return a | b; });
     const uint32_t diff = andv ^ orv;
     if (diff == 0u) {
         *n_gt = 0;
@@ -137,12 +134,9 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         const uint32_t c0 = hist[lane * 4 + 0], c1 = hist[lane * 4 + 1];
         const uint32_t c2 = hist[lane * 4 + 2], c3 = hist[lane * 4 + 3];
         const int mine = (int)(c0 + c1 + c2 + c3);
-        int suf = mine;  // sum over lanes >= this lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_down(suf, off);
-            if (lane + off < 64) suf += o;
-        }
+        const int incl = wave_incl_scan(mine);                      // sum over lanes <= this lane
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        const int suf = total - incl + mine;                        // sum over lanes >= this lane
         const int above = suf - mine;  // sum over bins of higher lanes
         int bin = -1, cnt_above = 0;
         if (above < want && want <= suf) {
@@ -160,8 +154,8 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         }
         const unsigned long long who = __ballot(bin >= 0);
         const int src = __ffsll((long long)who) - 1;
-        const int b = __shfl(bin, src);
-        const int ca = __shfl(cnt_above, src);
+        const int b = __builtin_amdgcn_readlane(bin, src);
+        const int ca = __builtin_amdgcn_readlane(cnt_above, src);
         prefix |= ((uint32_t)b) << shift;
         pmask |= 255u << shift;
         want -= ca;
@@ -319,16 +313,21 @@ __device__ __noinline__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k
         wave_lds_sync();
         const int need = k_eff - nD;
         if (nM <= mcap) {
-            exact_scores<T, HI, DI>(qrow, kI_b, wrow, wb.ids, wb.mpos, nM, wb.mex);
-            wave_lds_sync();
+            // a band of exactly `need` entries is kept whole: no re-scoring
+            if (nM > need) {
+                exact_scores<T, HI, DI>(qrow, kI_b, wrow, wb.ids, wb.mpos, nM, wb.mex);
+                wave_lds_sync();
+            }
             // rank within M by (exact desc, index asc); keep the first `need`
             for (int j = lane; j < nM; j += 64) {
-                const double ex = wb.mex[j];
-                const int id = wb.ids[wb.mpos[j]];
                 int rank = 0;
-                for (int y = 0; y < nM; ++y) {
-                    const double ey = wb.mex[y];
-                    rank += (ey > ex) || (ey == ex && wb.ids[wb.mpos[y]] < id);
+                if (nM > need) {
+                    const double ex = wb.mex[j];
+                    const int id = wb.ids[wb.mpos[j]];
+                    for (int y = 0; y < nM; ++y) {
+                        const double ey = wb.mex[y];
+                        rank += (ey > ex) || (ey == ex && wb.ids[wb.mpos[y]] < id);
+                    }
                 }
                 wb.keys[wb.mpos[j]] = rank < need ? 0xFFFFFFFFu : 0u;
             }
@@ -430,8 +429,9 @@ __device__ __forceinline__ int tile_scores(const f32x4_t& c, const float* wr, in
             qs[0] = q4;
             own[0] = true;
         } else if constexpr (HI == 8) {
-            const float other = __shfl_xor(part, 16);
-            s[0] = (q4 & 1) ? other + part : part + other;
+            uint32_t lo, hi;
+            xor16_pair(__float_as_uint(part), lo, hi);
+            s[0] = __uint_as_float(lo) + __uint_as_float(hi);   // (row 2r) + (row 2r+1)
             qs[0] = q4 >> 1;
             own[0] = (q4 & 1) == 0;
         } else {
@@ -493,8 +493,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
         }
         // sum_h |w_h| ||q_h|| per query (row norms combined in fixed head order)
         float n2 = MM::sq(a[rt]);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         if (rt < RT) {
             // lane rho (q4 == 0) holds ||row rho||^2; gather the HI rows of each query
             const int qsl = lane < QPT ? lane : 0;  // lane j < QPT finishes query slot j
@@ -550,8 +549,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     auto process_tile = [&](long long c0, const typename MM::F* bf) {
         const long long c = c0 + rho;
         float n2 = MM::sq(bf);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         kmax2 = fmaxf(kmax2, n2);
 #pragma unroll
         for (int rt = 0; rt < MAX_RT; ++rt) {
@@ -714,8 +712,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
             wr[rt][r] = (rt < RT && qr < qpw && ir < p.Tq) ? p.w[((long long)b * p.Tq + ir) * HI + hr] : 0.f;
         }
         float n2 = MM::sq(a[rt]);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         if (rt < RT) {
             const int qsl = lane < QPT ? lane : 0;
             float acc = 0.f;
@@ -739,8 +736,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
     auto score_tile = [&](int c0, const typename MM::F* bf) {
         const int c = c0 + rho;
         float n2 = MM::sq(bf);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         kmax2 = fmaxf(kmax2, n2);
 #pragma unroll
         for (int rt = 0; rt < MAX_RT; ++rt) {
@@ -782,7 +778,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
         group(g0, bq0, bq1);
         if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
     }
-    for (int off = 32; off > 0; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+    kmax2 = wave_max_f(kmax2);
     wave_lds_sync();
 
     // ---- one exact selection per query
@@ -820,15 +816,20 @@ __global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
             wave_lds_sync();
             const int need = k_eff - nD;
             if (nM <= mcap) {
-                exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, nullptr, mpos, nM, mex);
-                wave_lds_sync();
+                // a band of exactly `need` entries is kept whole: no re-scoring
+                if (nM > need) {
+                    exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, nullptr, mpos, nM, mex);
+                    wave_lds_sync();
+                }
                 for (int j = lane; j < nM; j += 64) {
-                    const double ex = mex[j];
                     const int id = mpos[j];
                     int rank = 0;
-                    for (int y = 0; y < nM; ++y) {
-                        const double ey = mex[y];
-                        rank += (ey > ex) || (ey == ex && mpos[y] < id);
+                    if (nM > need) {
+                        const double ex = mex[j];
+                        for (int y = 0; y < nM; ++y) {
+                            const double ey = mex[y];
+                            rank += (ey > ex) || (ey == ex && mpos[y] < id);
+                        }
                     }
                     keys[id] = rank < need ? 0xFFFFFFFFu : 0u;
                 }
@@ -899,8 +900,7 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
     }
     if (chunk_id == 0) {
         float n2 = MM::sq(a);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         float acc = 0.f;
         for (int h = 0; h < HI; ++h) acc += fabsf(p.w[row * HI + h]) * sqrtf(__shfl(n2, h));
         if (lane == 0) p.row_qn[row] = acc;
@@ -912,8 +912,7 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
         typename MM::F bf[MM::KS];
         MM::load_a(kI_b + (cok ? c : 0) * DI, cok, q4, bf);
         float n2 = MM::sq(bf);
-        n2 += __shfl_xor(n2, 16);
-        n2 += __shfl_xor(n2, 32);
+        n2 = sum_xrows(n2);
         kmax2 = fmaxf(kmax2, n2);
         const f32x4_t acc = MM::mma(a, bf);
         float s[4];
@@ -926,7 +925,7 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
             skeys[c - c_lo] = fkey(s[0]);
         }
     }
-    for (int off = 32; off > 0; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+    kmax2 = wave_max_f(kmax2);
     wave_lds_sync();
     const int n = c_hi > c_lo ? (int)(c_hi - c_lo) : 0;
     float lb = -INFINITY;
