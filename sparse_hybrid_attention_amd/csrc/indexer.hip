@@ -596,9 +596,9 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                 for (int g4 = 0; g4 < 4; ++g4) {
                     if (((fm >> (16 * g4)) & 0xFFFFull) == 0ull) continue;
                     const int src = 16 * g4;
-                    const int qw = rt * QPT + __shfl(qw_l, src);
-                    const int cq = __shfl(cnt[rt][sl], src);
-                    const int nvq = __shfl(nv[rt][sl], src);
+                    const int qw = rt * QPT + __builtin_amdgcn_readlane(qw_l, src);
+                    const int cq = __builtin_amdgcn_readlane(cnt[rt][sl], src);
+                    const int nvq = __builtin_amdgcn_readlane(nv[rt][sl], src);
                     WaveBuf q = wb;
                     q.keys = keys_all + qw * cap;
                     q.ids = ids_all + qw * cap;
@@ -654,8 +654,8 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                 const int i = q0 + qw;
                 if (qw >= qpw || i >= p.Tq) continue;
                 const int src = 16 * g4;
-                const int cq = __shfl(cnt[rt][sl], src);
-                const int nvq = __shfl(nv[rt][sl], src);
+                const int cq = __builtin_amdgcn_readlane(cnt[rt][sl], src);
+                const int nvq = __builtin_amdgcn_readlane(nv[rt][sl], src);
                 WaveBuf q = wb;
                 q.keys = keys_all + qw * cap;
                 q.ids = ids_all + qw * cap;
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
         float n2 = MM::sq(a);
         n2 = sum_xrows(n2);
         float acc = 0.f;
-        for (int h = 0; h < HI; ++h) acc += fabsf(p.w[row * HI + h]) * sqrtf(__shfl(n2, h));
+        for (int h = 0; h < HI; ++h) acc += fabsf(p.w[row * HI + h]) * sqrtf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(n2), h)));
         if (lane == 0) p.row_qn[row] = acc;
     }
     float kmax2 = 0.f;
