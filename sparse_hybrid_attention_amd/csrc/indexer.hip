@@ -906,11 +906,14 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
         if (lane == 0) p.row_qn[row] = acc;
     }
     float kmax2 = 0.f;
-    for (long long c0 = c_lo; c0 < c_hi; c0 += TILE) {
+    auto load_b = [&](long long c0, typename MM::F* bf) {
         const long long c = c0 + rho;
         const bool cok = c < c_hi;
-        typename MM::F bf[MM::KS];
         MM::load_a(kI_b + (cok ? c : 0) * DI, cok, q4, bf);
+    };
+    auto score_tile = [&](long long c0, const typename MM::F* bf) {
+        const long long c = c0 + rho;
+        const bool cok = c < c_hi;
         float n2 = MM::sq(bf);
         n2 = sum_xrows(n2);
         kmax2 = fmaxf(kmax2, n2);
@@ -924,6 +927,29 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
             p.scores[row * p.N + c] = s[0];
             skeys[c - c_lo] = fkey(s[0]);
         }
+    };
+    // the chunk streams through registers PF tiles at a time: the next group's
+    // loads are in flight while a group is scored (two alternating buffers, so
+    // rows in flight are never copied)
+    constexpr int PF = 4;
+    typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
+    auto group = [&](long long g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+        const long long g1 = g0 + PF * TILE;
+        if (g1 < c_hi) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+            if (g0 + t * TILE < c_hi) score_tile(g0 + t * TILE, cur[t]);
+    };
+    if (c_lo < c_hi) {
+#pragma unroll
+        for (int t = 0; t < PF; ++t) load_b(c_lo + t * TILE, bq0[t]);
+    }
+    for (long long g0 = c_lo; g0 < c_hi; g0 += 2 * PF * TILE) {
+        group(g0, bq0, bq1);
+        if (g0 + PF * TILE < c_hi) group(g0 + PF * TILE, bq1, bq0);
     }
     kmax2 = wave_max_f(kmax2);
     wave_lds_sync();
@@ -1101,7 +1127,7 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     const long long rows = (long long)B * Tq;
     pl.split = rows > 0 && rows <= 64 && N >= 8192;
     if (pl.split) {
-        p.chunk = 4096;
+        p.chunk = 2048;   // 2 waves per SIMD at 1M context x 16 rows
         p.nchunks = (N + p.chunk - 1) / p.chunk;
         p.chunk_k = (k + p.nchunks - 1) / p.nchunks;
         p.list_cap = 256;
