@@ -674,7 +674,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
 // (no streaming compactions).  Same scoring tiles and the same exact decision
 // rule as the streaming kernel.
 template <typename T, int HI, int DI>
-__global__ __launch_bounds__(WAVES * 64) void index_dense_kernel(IdxParams p) {
+__global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void index_dense_kernel(IdxParams p) {
     typedef IdxMma<T, DI> MM;
     constexpr int QPT = 16 / HI;
     constexpr int SLOTS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
@@ -1157,8 +1157,11 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     const int qpt = 16 / Hi;
     pl.dense = N > 0 && N <= kDenseMaxN;
     if (pl.dense) {
-        // p.cap = per-query key slots (N rounded up to a tile)
+        // p.cap = per-query key slots (N rounded up to a tile).  The band list is
+        // short (an overflowing band falls back to the float32 order): the
+        // workgroup's LDS stays small enough for four workgroups per CU.
         p.cap = (N + TILE - 1) / TILE * TILE;
+        p.mcap = std::min(p.mcap, 64);
         auto dense_wave = [&](int q) { return (4ull * q * p.cap + 1024 + 12ull * p.mcap + 4ull * q + 15) / 16 * 16; };
         int qpw = 4 * qpt;
         while (qpw > qpt && WAVES * dense_wave(qpw) > (size_t)kMaxLds) qpw -= qpt;
