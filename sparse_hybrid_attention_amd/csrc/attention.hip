@@ -418,11 +418,12 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
     static constexpr int PIECES = D / 8;        // 16-byte pieces per row
     static constexpr int ROWB = D * 2;          // bytes per row
     static constexpr int RPI = 1024 / ROWB;     // rows per wave load
-    static constexpr int NI = KT / (RPI * NW);  // wave loads per matrix per tile
+    static constexpr int NLOADS = KT / RPI;             // wave loads per matrix per tile
+    static constexpr int NI = (NLOADS + NW - 1) / NW;   // of them per wave (at most)
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     static constexpr int MAT_BYTES = KT * ROWB;
-    static_assert(NI >= 1 && NI * RPI * NW == KT, "tile split");
+    static_assert(NLOADS * RPI == KT, "tile split");
     int goff_k[NI], goff_v[NI];  // element offsets of this lane's global pieces
     int grow[NI];                // their tile rows
     int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
@@ -437,6 +438,7 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
         wave = tid >> 6;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
+            // wave load j * NW + wave (when it exists) covers rows RPI * that .. +RPI
             const int row = (j * NW + wave) * RPI + lane / PIECES;
             const int pc = lane % PIECES;  // LDS slot piece; it holds global piece pc ^ swz(row)
             grow[j] = row;
@@ -457,6 +459,7 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
     __device__ void issue(const bf16_t* kb, const bf16_t* vb, int nvalid, char* buf) const {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
+            if (NLOADS % NW != 0 && j * NW + wave >= NLOADS) break;   // uniform per wave
             const bool ok = grow[j] < nvalid;
             char* dst = buf + (j * NW + wave) * 1024;
             __builtin_amdgcn_global_load_lds(kb + (ok ? goff_k[j] : 0), (lds_void_t*)dst, 16, 0, 0);
@@ -1101,9 +1104,11 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.k = has_csa ? a->k : 0;
     const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
     p.scale_log2 = scale * 1.4426950408889634f;
-    // 4 waves (64 (query, head) columns) per workgroup: two workgroups share a
-    // CU, so one computes while the other waits at a barrier or on its loads
-    // (8-wave workgroups measured slower)
+    // 4 waves (64 (query, head) columns) per workgroup, one per SIMD: three
+    // workgroups share a CU, so one computes while the others wait at a
+    // barrier or on their loads.  (Measured: 8 waves leave one workgroup per
+    // CU; 6 waves put two waves of a workgroup on some SIMDs, and every tile
+    // barrier then waits for those.)
     pl.waves = 4;
     p.ncol = pl.waves * 16;
     p.QW = G >= p.ncol ? 1 : p.ncol / G;
