@@ -571,7 +571,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         item = (int)(wg % p.nsplit);
         wg /= p.nsplit;
     }
-    const int qt = (int)(wg % p.nqt);
+    // later query tiles first: they attend the most CSA entries, so the
+    // lightest work runs last and the tail of the launch is short
+    const int qt = p.nqt - 1 - (int)(wg % p.nqt);
     const long long bg = wg / p.nqt;
     const int g = (int)(bg % p.Hkv);
     const int b = (int)(bg / p.Hkv);
@@ -969,7 +971,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const long long cg = gid / DQ;           // global column
     const int col = (int)(cg % p.ncol);
     const long long wg = cg / p.ncol;
-    const int qt = (int)(wg % p.nqt);
+    // the work-id -> query-tile map of the main kernel
+    const int qt = p.nqt - 1 - (int)(wg % p.nqt);
     const long long bg = wg / p.nqt;
     const int g = (int)(bg % p.Hkv);
     const int b = (int)(bg / p.Hkv);
