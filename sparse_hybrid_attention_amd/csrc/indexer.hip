@@ -467,7 +467,8 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     wb.mpos = reinterpret_cast<int32_t*>(base + 8ull * qpw * cap + 1024 + 8ull * mcap);
     float* qn = reinterpret_cast<float*>(base + 8ull * qpw * cap + 1024 + 12ull * mcap);
 
-    const int qt = blockIdx.x % p.nqt;
+    // later queries (more visible entries) first: the light work runs last
+    const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
     const int b = blockIdx.x / p.nqt;
     const int q0 = (qt * WAVES + wave) * qpw;  // first query row of this wave
     const T* qI = reinterpret_cast<const T*>(p.qI);
@@ -689,7 +690,8 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     int32_t* mpos = reinterpret_cast<int32_t*>(base + 4ull * qpw * np + 1024 + 8ull * mcap);
     float* qn = reinterpret_cast<float*>(base + 4ull * qpw * np + 1024 + 12ull * mcap);
 
-    const int qt = blockIdx.x % p.nqt;
+    // later queries (more visible entries) first: the light work runs last
+    const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
     const int b = blockIdx.x / p.nqt;
     const int q0 = (qt * WAVES + wave) * qpw;
     const T* qI = reinterpret_cast<const T*>(p.qI);
