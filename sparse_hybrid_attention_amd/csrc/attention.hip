@@ -88,6 +88,7 @@ struct AttnParams {
     // split mode (0 = off): work item list over [window | HCA | CSA] keys
     int nsplit;
     int split_keys;
+    int split_csa;   // selected CSA entries per split item (gathers are slower per key)
     int n_win_items, n_hca_items;
     int has_hca, has_csa;  // branch present (its gate column is used)
     int ncol;              // columns (query, head) per workgroup = 16 * waves
@@ -640,8 +641,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
             hca_hi = hca_lo + p.split_keys;
         }
         if (do_csa) {
-            csa_lo = (long long)(item - p.n_win_items - p.n_hca_items) * p.split_keys;
-            csa_hi = csa_lo + p.split_keys;
+            csa_lo = (long long)(item - p.n_win_items - p.n_hca_items) * p.split_csa;
+            csa_hi = csa_lo + p.split_csa;
         }
     }
 
@@ -929,6 +930,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         // partial state of this item: [m, l, -, -, acc[D]] per column at
         // ws[((wg * nsplit + item) * ncol + col) * (D + 4)]
         const float ltot = col_sum(S.l);
+        if (!valid) return;   // the combine kernel reads valid columns only
         float* dst = p.ws + (wid * p.ncol + col) * (D + 4);
         if (q4 == 0) {
             dst[0] = S.m;
@@ -961,14 +963,21 @@ SHATTN_ATTN_INST(float, 64)
 SHATTN_ATTN_INST(float, 128)
 #undef SHATTN_ATTN_INST
 
+// Merge of the split partial states.  Eight consecutive threads share one
+// (column, 4 dims): each merges every eighth item of a range, then the eight
+// partial states combine across the lanes in a fixed order (deterministic).
+constexpr int kCombineSub = 8;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     constexpr int DQ = D / 4;
+    const int sub = (int)(gid % kCombineSub);
+    const long long rest = gid / kCombineSub;
     const long long ncols_total = (long long)p.B * p.Hkv * p.nqt * p.ncol;
-    if (gid >= ncols_total * DQ) return;
-    const int dq = (int)(gid % DQ);
-    const long long cg = gid / DQ;           // global column
+    if (rest >= ncols_total * DQ) return;   // whole groups of eight
+    const int dq = (int)(rest % DQ);
+    const long long cg = rest / DQ;          // global column
     const int col = (int)(cg % p.ncol);
     const long long wg = cg / p.ncol;
     // the work-id -> query-tile map of the main kernel
@@ -979,7 +988,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const int i0 = qt * p.QW;
     const int nq = min(p.QW, p.Tq - i0);
     const int ql = col / p.G, hl = col - (col / p.G) * p.G;
-    if (ql >= nq) return;
+    if (ql >= nq) return;                    // uniform over the group of eight
     const int h = g * p.G + hl;
     const int qi = i0 + ql;
     const float g0 = p.gates[h * 3 + 0], g1 = p.gates[h * 3 + 1], g2 = p.gates[h * 3 + 2];
@@ -988,22 +997,45 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     auto part = [&](int item) -> const float* {
         return p.ws + ((wg * p.nsplit + item) * p.ncol + col) * (D + 4);
     };
-    // merge a range of items into (m, l, acc4)
+    // (m, l, a) <- merge of (m, l, a) and (mi, li, ai)
+    auto fold_in = [](float& m, float& l, float* a, float mi, float li, const float* ai) {
+        if (mi == -INFINITY) return;
+        const float mn = fmaxf(m, mi);
+        const float x = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float y = __builtin_amdgcn_exp2f(mi - mn);
+        l = l * x + li * y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = a[r] * x + ai[r] * y;
+        m = mn;
+    };
+    // merge items [it0, it1) into (m, l, a): strided over the group, then across it
     auto merge = [&](int it0, int it1, float& m, float& l, float* a) {
-        for (int it = it0; it < it1; ++it) {
+        float pm = -INFINITY, pl = 0.f, pa[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int it = it0 + sub; it < it1; it += kCombineSub) {
             const float* s = part(it);
-            const float mi = s[0], li = s[1];
-            if (mi == -INFINITY) continue;
             const float4 ai = *reinterpret_cast<const float4*>(s + 4 + 4 * dq);
-            const float mn = fmaxf(m, mi);
-            const float x = __builtin_amdgcn_exp2f(m - mn), y = __builtin_amdgcn_exp2f(mi - mn);
-            l = l * x + li * y;
-            a[0] = a[0] * x + ai.x * y;
-            a[1] = a[1] * x + ai.y * y;
-            a[2] = a[2] * x + ai.z * y;
-            a[3] = a[3] * x + ai.w * y;
-            m = mn;
+            const float av[4] = {ai.x, ai.y, ai.z, ai.w};
+            fold_in(pm, pl, pa, s[0], s[1], av);
         }
+#pragma unroll
+        for (int off = 1; off < kCombineSub; off <<= 1) {
+            const float om = __shfl_xor(pm, off), ol = __shfl_xor(pl, off);
+            float oa[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oa[r] = __shfl_xor(pa[r], off);
+            // lower lane's state first on both lanes
+            if (sub & off) {
+                float tm = om, tl = ol, ta[4] = {oa[0], oa[1], oa[2], oa[3]};
+                fold_in(tm, tl, ta, pm, pl, pa);
+                pm = tm;
+                pl = tl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pa[r] = ta[r];
+            } else {
+                fold_in(pm, pl, pa, om, ol, oa);
+            }
+        }
+        fold_in(m, l, a, pm, pl, pa);
     };
     float mw = -INFINITY, lw = 0.f, aw[4] = {0.f, 0.f, 0.f, 0.f};
     merge(0, p.n_win_items, mw, lw, aw);
@@ -1019,8 +1051,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
         merge(p.n_win_items + p.n_hca_items, p.nsplit, m, l, a);
         for (int r = 0; r < 4; ++r) o[r] += g1 * a[r] / l;
     }
-    T* orow = reinterpret_cast<T*>(p.out) + (((long long)b * p.Tq + qi) * p.H + h) * D;
-    Tr<T, D>::store_out(orow + 4 * dq, o);
+    if (sub == 0) {
+        T* orow = reinterpret_cast<T*>(p.out) + (((long long)b * p.Tq + qi) * p.H + h) * D;
+        Tr<T, D>::store_out(orow + 4 * dq, o);
+    }
 }
 
 struct Plan {
@@ -1127,10 +1161,13 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     if (has_csa) keys += a->k;
     p.nsplit = 0;
     if (nwg < 128 && keys > 1024) {
+        // one split item per 256 streamed HCA keys and per 64 gathered CSA
+        // entries: a gather of 32 rows costs about as much as 4 streamed tiles
         p.split_keys = 256;
+        p.split_csa = 64;
         p.n_win_items = 1;
         p.n_hca_items = (int)((nh_max + p.split_keys - 1) / p.split_keys);
-        const int n_csa_items = has_csa ? (a->k + p.split_keys - 1) / p.split_keys : 0;
+        const int n_csa_items = has_csa ? (a->k + p.split_csa - 1) / p.split_csa : 0;
         p.nsplit = p.n_win_items + p.n_hca_items + n_csa_items;
         pl.ws_bytes = (size_t)nwg * p.nsplit * p.ncol * (a->d + 4) * sizeof(float);
         pl.grid = nwg * p.nsplit;
@@ -1200,7 +1237,7 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
         return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
                     pl.grid, NW * 64, pl.lds, hipGetErrorString(le));
     if (!pl.p.nsplit) return SHATTN_OK;
-    const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * pl.p.ncol * (D / 4);
+    const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * pl.p.ncol * (D / 4) * kCombineSub;
     hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        pl.p);
     return check_launch("hybrid_sparse_attn_fwd (combine)");
