@@ -66,6 +66,7 @@ struct IdxParams {
     int32_t* list_cnt;  // [rows, nchunks] (may exceed list_cap: then the
                         //  chunk is re-read from `scores`)
     int nchunks, chunk, list_cap, chunk_k;
+    int stream_cap;     // split final: candidate buffer of the streaming fallback
 };
 
 // ----------------------------------------------------------- key encoding
@@ -1017,25 +1018,77 @@ __global__ __launch_bounds__(64) void index_split_collect_kernel(IdxParams p) {
     if (lane == 0) p.list_cnt[row * p.nchunks + chunk_id] = out;
 }
 
-// S3: one wave per row: stream the chunk lists in entry order through the
-// candidate buffer, then the exact final selection.
+// S3: one workgroup (kFinalThreads) per row.  When no chunk list overflowed
+// and the lists fit in LDS, all their entries are gathered in parallel, in
+// entry order, and one wave makes the exact final selection over them;
+// otherwise one wave streams the lists (and overflowed chunks' scores)
+// through the candidate buffer as before.
+constexpr int kFinalThreads = 256;
+
 template <typename T, int HI, int DI>
-__global__ __launch_bounds__(64) void index_split_final_kernel(IdxParams p) {
+__global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const long long row = blockIdx.x;
     const long long b = row / p.Tq, i = row % p.Tq;
-    const int cap = p.cap;
+    const int cap = p.cap;   // LDS candidate slots (>= the streaming buffer)
     WaveBuf wb;
     wb.keys = reinterpret_cast<uint32_t*>(smem);
     wb.ids = reinterpret_cast<int32_t*>(smem + 4ull * cap);
     wb.hist = reinterpret_cast<uint32_t*>(smem + 8ull * cap);
     wb.mex = reinterpret_cast<double*>(smem + 8ull * cap + 1024);
     wb.mpos = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 8ull * p.mcap);
+    int32_t* offs = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 12ull * p.mcap);  // [nchunks + 1]
+    __shared__ int s_total, s_over;
     const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
     const int k_eff = (int)std::min<long long>(p.k, nvq);
     float lb, delta;
     row_bound(p, row, &lb, &delta);
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
+
+    // ---- list sizes -> entry offsets (exclusive prefix in chunk order)
+    if (wave == 0) {
+        int base = 0, over = 0;
+        for (int j0 = 0; j0 < p.nchunks; j0 += 64) {
+            const int j = j0 + lane;
+            const int lc = j < p.nchunks ? p.list_cnt[row * p.nchunks + j] : 0;
+            over |= lc > p.list_cap;
+            const int incl = wave_incl_scan(lc);
+            if (j < p.nchunks) offs[j] = base + incl - lc;
+            base += __builtin_amdgcn_readlane(incl, 63);
+        }
+        over = __any(over);
+        if (lane == 0) {
+            offs[p.nchunks] = base;
+            s_total = base;
+            s_over = over;
+        }
+    }
+    __syncthreads();
+    const int total = s_total;
+    if (!s_over && total <= cap) {
+        // ---- parallel gather: entry t belongs to the chunk whose offset range holds it
+        for (int t = tid; t < total; t += kFinalThreads) {
+            int lo = 0, hi = p.nchunks - 1;   // last chunk with offs[j] <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (offs[mid] <= t) lo = mid;
+                else hi = mid - 1;
+            }
+            const long long src = (row * p.nchunks + lo) * (long long)p.list_cap + (t - offs[lo]);
+            wb.keys[t] = p.lists[src];
+            wb.ids[t] = p.list_idx[src];
+        }
+        __syncthreads();
+        if (wave == 0)
+            final_select<T, HI, DI>(wb, total, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b,
+                                    p.w + row * HI, p.idx + row * p.k);
+        return;
+    }
+    if (wave != 0) return;
+    // ---- fallback: stream the chunk lists (or whole chunks) through the buffer
     uint32_t tau = lb == -INFINITY ? 0u : fkey(lb - 2.0f * delta);
     int cnt = 0;
     for (int j = 0; j < p.nchunks; ++j) {
@@ -1068,15 +1121,13 @@ __global__ __launch_bounds__(64) void index_split_final_kernel(IdxParams p) {
                 wb.ids[pos] = id;
             }
             cnt += __popcll(msk);
-            if (cnt > cap - 64) {
+            if (cnt > p.stream_cap - 64) {
                 wave_lds_sync();
-                cnt = compact_stream(wb, cnt, k_eff, delta, cap, 64, &tau);
+                cnt = compact_stream(wb, cnt, k_eff, delta, p.stream_cap, 64, &tau);
             }
         }
     }
     wave_lds_sync();
-    const T* qI = reinterpret_cast<const T*>(p.qI);
-    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
     final_select<T, HI, DI>(wb, cnt, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b, p.w + row * HI,
                             p.idx + row * p.k);
 }
@@ -1152,7 +1203,16 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
         p.list_idx = reinterpret_cast<int32_t*>(o_li);
         p.list_cnt = reinterpret_cast<int32_t*>(o_lc);
         pl.lds_score = 4ull * p.chunk + 1024;
-        pl.lds = 8ull * p.cap + 1024 + 12ull * p.mcap;
+        // final kernel: LDS slots for every listed candidate of a row (parallel
+        // path); the streaming fallback uses the first stream_cap of them
+        p.stream_cap = p.cap;
+        const long long fixed = 1024 + 12ll * p.mcap + 4ll * (p.nchunks + 1) + 16;
+        const long long cap_fit = (kMaxLds - fixed) / 8;
+        if (cap_fit < p.stream_cap)
+            return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: N=%d needs more LDS than available", N);
+        p.cap = (int)std::min<long long>(12288, cap_fit);
+        if (p.cap < p.stream_cap) p.cap = p.stream_cap;
+        pl.lds = (8ull * p.cap + (size_t)fixed + 15) / 16 * 16;
         pl.grid = rows;
         return SHATTN_OK;
     }
@@ -1240,7 +1300,8 @@ int launch_idx(IdxPlan& pl, hipStream_t s) {
             return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
         }
     }
-    hipLaunchKernelGGL((index_split_final_kernel<T, HI, DI>), dim3((unsigned)rows), dim3(64), pl.lds, s, pl.p);
+    hipLaunchKernelGGL((index_split_final_kernel<T, HI, DI>), dim3((unsigned)rows), dim3(kFinalThreads), pl.lds, s,
+                       pl.p);
     return check_launch("csa_index_topk (final)");
 }
 

@@ -174,6 +174,21 @@ def test_decode_ragged_chunks():
     assert_rows_equal([got[b, 0] for b, _ in rows], want, rows, "decode ragged")
 
 
+def test_decode_identical_keys_list_overflow():
+    # every score of a row ties: every chunk's candidate list overflows, the
+    # final pass streams whole chunks and the lowest indices win
+    lib()
+    inp = synth.make_inputs("decode_1m", seed=19, B=2, N_csa=10000, N_hca=64, k=100)
+    inp["kI"] = np.ascontiguousarray(np.broadcast_to(inp["kI"][:, :1], inp["kI"].shape))
+    cfg = inp["cfg"]
+    got = gpu_topk(inp["qI"], inp["kI"], inp["w"], inp["q_pos0"], cfg["m_csa"], cfg["W"], cfg["k"])
+    rows = [(b, 0) for b in range(2)]
+    want = oracle_rows(inp["qI"], inp["kI"], inp["w"], inp["q_pos0"], cfg["m_csa"], cfg["W"], cfg["k"],
+                       cfg["dtype"], rows)
+    assert_rows_equal([got[b, 0] for b, _ in rows], want, rows, "decode identical keys")
+    assert got[0, 0].tolist() == list(range(100))
+
+
 def test_indexer_deterministic():
     lib()
     inp = synth.make_inputs("tinyr2_bf16", seed=18, B=2, T=1024)
