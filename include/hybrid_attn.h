@@ -117,8 +117,16 @@ SHATTN_API int hca_compress_kv_dual(const void* k, const void* v, const float* z
  *
  *   qI  : [B, Tq, Hi, d_idx] dtype      kI : [B, N, d_idx] dtype
  *   w   : [B, Tq, Hi]        float32    idx: [B, Tq, k] int32, written
- *   ws  : device workspace of at least csa_index_topk_workspace_size() bytes
- *         (may be NULL when that size is 0); its contents are scratch.
+ *   ws  : device workspace of at least csa_index_topk_workspace_size() bytes,
+ *         256-byte aligned (may be NULL when that size is 0); its contents are
+ *         scratch.  Sizes: 0 for N <= 2048; for longer prefill about
+ *         8 * B * Tq * L bytes, L = per-query candidate list length (a few
+ *         times k); for decode shapes (B * Tq <= 64, N >= 8192) about
+ *         4 * B * Tq * N bytes.
+ * Long prefill (N > 2048) is decided per query from a list of the entries
+ * whose float32 score reaches a threshold estimated from every S-th entry;
+ * queries whose list cannot decide are recomputed by streaming all entries,
+ * so the result never depends on the estimate.
  * Supported: Hi in {1, 2, 4, 8, 16}; d_idx in {64, 128}; 1 <= k <= 2048;
  *            m >= 1; W >= 1; N >= 0.
  */

@@ -33,6 +33,7 @@
 //    query runs the same buffer / exact-final logic over those lists.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 
@@ -67,6 +68,17 @@ struct IdxParams {
                         //  chunk is re-read from `scores`)
     int nchunks, chunk, list_cap, chunk_k;
     int stream_cap;     // split final: candidate buffer of the streaming fallback
+    // long prefill pipeline workspace (rows = B * Tq); lists/list_idx/list_cnt
+    // then hold one list of list_cap entries per row
+    float* kmax_part;   // [B, kblk] max ||k||^2 over blocks of kKmaxBlock entries
+    uint32_t* row_thr;  // [rows] entries whose key is >= row_thr enter the row's list
+    uint32_t* row_tau;  // [rows] key of the sampled threshold (0: every visible entry is listed)
+    float* row_delta;   // [rows] bound of |float32 score - exact score| for the row
+    int32_t* row_fail;  // [rows] 1: the list cannot decide the row (the streaming kernel does)
+    uint2* row_lists;   // [rows, list_cap] (key, entry) pairs in entry order
+    int kblk;           // entry blocks per sequence for kmax_part
+    int sample_stride;  // sampled entries are 0, S, 2S, ... (S = sample_stride)
+    int sample_j;       // the threshold is the sample_j-th largest sampled score
 };
 
 // ----------------------------------------------------------- key encoding
@@ -96,21 +108,54 @@ __device__ __forceinline__ long long n_visible(long long t, int W, int m, int N)
 // ----------------------------------------------------------- wave selection
 struct WaveBuf {
     uint32_t* keys;  // [cap]
-    int32_t* ids;    // [cap]
+    int32_t* ids;    // [cap] (unused when the entries come from an accessor)
     uint32_t* hist;  // [256]
-    int32_t* mpos;   // [mcap]
-    double* mex;     // [mcap]
+    int32_t* mpos;   // [mcap] buffer positions of the band candidates
+    double* mex;     // [mcap] their exact scores
+    int32_t* mid;    // [mcap] their entries
 };
+
+// Entry of buffer position e: from an LDS array, from a (key, entry) list in
+// global memory, or the position itself.
+struct LdsIds {
+    const int32_t* ids;
+    __device__ int operator()(int e) const { return ids[e]; }
+};
+struct ListIds {
+    const uint2* lst;
+    __device__ int operator()(int e) const { return (int)lst[e].y; }
+};
+struct PosIds {
+    __device__ int operator()(int e) const { return e; }
+};
+
+// Buffers read by the selection passes below are 16-byte aligned and their
+// capacity is a multiple of 4 keys: lane l of a pass over 256 keys takes the
+// 4 consecutive keys 4l..4l+3 with one 16-byte LDS read (keys past `cnt` are
+// read but ignored).
+__device__ __forceinline__ uint4 keys4(const uint32_t* keys, int e0) {
+    return *reinterpret_cast<const uint4*>(keys + e0);
+}
+__device__ __forceinline__ uint32_t key_at(const uint4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
 
 // k-th largest key among keys[0..cnt), 1 <= kk <= cnt.  *n_gt = #keys > result.
 __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
     const int lane = __lane_id();
     // bytes shared by every key need no histogram pass
     uint32_t andv = 0xFFFFFFFFu, orv = 0u;
-    for (int e = lane; e < cnt; e += 64) {
-        const uint32_t key = keys[e];
-        andv &= key;
-        orv |= key;
+    for (int base = 0; base < cnt; base += 256) {
+        const int e0 = base + 4 * lane;
+        if (e0 < cnt) {
+            const uint4 v = keys4(keys, e0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (e0 + j < cnt) {
+                    andv &= key_at(v, j);
+                    orv |= key_at(v, j);
+                }
+        }
     }
     andv = wave_allreduce(andv, [](uint32_t a, uint32_t b) { return a & b; });
     orv = wave_allreduce(orv, [](uint32_t a, uint32_t b) { return a | b; });
@@ -127,9 +172,16 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
 #pragma unroll
         for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
         wave_lds_sync();
-        for (int e = lane; e < cnt; e += 64) {
-            const uint32_t key = keys[e];
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        for (int base = 0; base < cnt; base += 256) {
+            const int e0 = base + 4 * lane;
+            if (e0 < cnt) {
+                const uint4 v = keys4(keys, e0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t key = key_at(v, j);
+                    if (e0 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                }
+            }
         }
         wave_lds_sync();
         const uint32_t c0 = hist[lane * 4 + 0], c1 = hist[lane * 4 + 1];
@@ -244,14 +296,14 @@ __device__ __noinline__ int compact_stream(WaveBuf& wb, int cnt, int kk, float d
 }
 
 // Exact (float64) scores of the band candidates, 4 per pass (candidate j is
-// entry ids[mpos[j]], or mpos[j] itself when ids is null): 16 lanes per
-// candidate, each holding DI/16 dims of the query's HI heads and of the
-// candidate's key; products of the inputs are exact in float64 and the 16
-// partial dot products are combined in a fixed order.
-template <typename T, int HI, int DI>
+// entry ids(mpos[j])): 16 lanes per candidate, each holding DI/16 dims of the
+// query's HI heads and of the candidate's key; products of the inputs are
+// exact in float64 and the 16 partial dot products are combined in a fixed
+// order.  mex[j] = exact score, mid[j] = entry (when mid is not null).
+template <typename T, int HI, int DI, class Ids>
 __device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T* __restrict__ kI_b,
-                             const float* __restrict__ wrow, const int32_t* ids, const int32_t* mpos, int nM,
-                             double* mex) {
+                             const float* __restrict__ wrow, Ids ids, const int32_t* mpos, int nM, double* mex,
+                             int32_t* mid) {
     constexpr int PER = DI / 16;  // dims per lane (4 or 8)
     const int lane = __lane_id();
     const int slot = lane >> 4, dl = lane & 15;
@@ -263,7 +315,7 @@ __device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T*
     for (int j0 = 0; j0 < nM; j0 += 4) {
         const int j = j0 + slot;
         const bool ok = j < nM;
-        const int c = ok ? (ids ? ids[mpos[j]] : mpos[j]) : 0;
+        const int c = ok ? ids(mpos[j]) : 0;
         float kv[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u) kv[u] = Elem<T>::load1(kI_b + (long long)c * DI + dl * PER + u);
@@ -280,43 +332,64 @@ __device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T*
             }
             s += (double)wrow[h] * (d > 0.0 ? d : 0.0);
         }
-        if (ok && dl == 0) mex[j] = s;
+        if (ok && dl == 0) {
+            mex[j] = s;
+            if (mid) mid[j] = c;
+        }
     }
 }
 
-// Final exact selection of one query and output of its idx row.
-template <typename T, int HI, int DI>
-__device__ __noinline__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k, float delta, int mcap,
+// Final exact selection of one query over its candidate buffer (in ascending
+// entry order) and output of its idx row: the kept entries are written in
+// buffer order, then -1 up to k.
+template <typename T, int HI, int DI, class Ids>
+__device__ __noinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_eff, int k, float delta, int mcap,
                              const T* __restrict__ qrow, const T* __restrict__ kI_b,
                              const float* __restrict__ wrow, int32_t* __restrict__ out_row) {
     const int lane = __lane_id();
+    // kept: key >= keep_ge; in the float32 fallback, key > kth plus the first
+    // eq_need entries with key == kth
+    uint32_t keep_ge = 0u, kth = 0u;
+    int eq_need = -1;
     if (cnt > k_eff) {
         int n_gt;
-        const uint32_t kth = radix_kth(wb.keys, cnt, k_eff, wb.hist, &n_gt);
+        kth = radix_kth(wb.keys, cnt, k_eff, wb.hist, &n_gt);
         const float Tf = key_f(kth);
         const uint32_t hi = fkey(Tf + 2.0f * delta);
         const uint32_t lo = fkey(Tf - 2.0f * delta);
-        // D = key > hi (certain), M = lo <= key <= hi (band)
+        // D = key > hi (certain), M = lo <= key <= hi (band); the order of
+        // the band list does not matter
         int nD = 0, nM = 0;
-        for (int base = 0; base < cnt; base += 64) {
-            const int e = base + lane;
-            const uint32_t key = e < cnt ? wb.keys[e] : 0u;
-            const bool inD = e < cnt && key > hi;
-            const bool inM = e < cnt && key >= lo && key <= hi;
-            const unsigned long long mm = __ballot(inM);
-            if (inM) {
-                const int pos = nM + __popcll(mm & lanemask_lt());
-                if (pos < mcap) wb.mpos[pos] = e;
+        for (int base = 0; base < cnt; base += 256) {
+            const int e0 = base + 4 * lane;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (e0 < cnt) v = keys4(wb.keys, e0);
+            int cm = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_at(v, j);
+                nD += e0 + j < cnt && key > hi;
+                cm += e0 + j < cnt && key >= lo && key <= hi;
             }
-            nD += __popcll(__ballot(inD));
-            nM += __popcll(mm);
+            const int incl = wave_incl_scan(cm);
+            int pos = nM + incl - cm;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_at(v, j);
+                if (e0 + j < cnt && key >= lo && key <= hi) {
+                    if (pos < mcap) wb.mpos[pos] = e0 + j;
+                    ++pos;
+                }
+            }
+            nM += __builtin_amdgcn_readlane(incl, 63);
         }
+        nD = (int)wave_allreduce((uint32_t)nD, [](uint32_t x, uint32_t y) { return x + y; });
         wave_lds_sync();
         const int need = k_eff - nD;
         if (nM <= mcap) {
             // a band of exactly `need` entries is kept whole: no re-scoring
             if (nM > need) {
-                exact_scores<T, HI, DI>(qrow, kI_b, wrow, wb.ids, wb.mpos, nM, wb.mex);
+                exact_scores<T, HI, DI>(qrow, kI_b, wrow, ids, wb.mpos, nM, wb.mex, wb.mid);
                 wave_lds_sync();
             }
             // rank within M by (exact desc, index asc); keep the first `need`
@@ -324,24 +397,58 @@ __device__ __noinline__ void final_select(WaveBuf& wb, int cnt, int k_eff, int k
                 int rank = 0;
                 if (nM > need) {
                     const double ex = wb.mex[j];
-                    const int id = wb.ids[wb.mpos[j]];
+                    const int id = wb.mid[j];
                     for (int y = 0; y < nM; ++y) {
                         const double ey = wb.mex[y];
-                        rank += (ey > ex) || (ey == ex && wb.ids[wb.mpos[y]] < id);
+                        rank += (ey > ex) || (ey == ex && wb.mid[y] < id);
                     }
                 }
                 wb.keys[wb.mpos[j]] = rank < need ? 0xFFFFFFFFu : 0u;
             }
             wave_lds_sync();
-            cnt = compact_ge(wb.keys, wb.ids, cnt, hi == 0xFFFFFFFFu ? hi : hi + 1u);
+            keep_ge = hi == 0xFFFFFFFFu ? hi : hi + 1u;
         } else {
             // more entries in the error band than the band list holds: decide
             // on float32 scores (index tie-break)
-            cnt = compact_topk(wb.keys, wb.ids, cnt, kth, k_eff - n_gt);
+            eq_need = k_eff - n_gt;
         }
     }
-    // buffer is in ascending entry order: write it, pad with -1
-    for (int j = lane; j < k; j += 64) out_row[j] = j < cnt ? wb.ids[j] : -1;
+    // kept entries in buffer order: lane l holds 4 consecutive positions, so
+    // a prefix sum over lanes orders them
+    int out = 0, eq_seen = 0;
+    for (int base = 0; base < cnt; base += 256) {
+        const int e0 = base + 4 * lane;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (e0 < cnt) v = keys4(wb.keys, e0);
+        int keepm = 0;
+        if (eq_need < 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) keepm |= (e0 + j < cnt && key_at(v, j) >= keep_ge) << j;
+        } else {
+            int ce = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ce += e0 + j < cnt && key_at(v, j) == kth;
+            const int ie = wave_incl_scan(ce);
+            int eq_rank = eq_seen + ie - ce;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_at(v, j);
+                const bool valid = e0 + j < cnt;
+                bool kp = valid && key > kth;
+                if (valid && key == kth) kp = eq_rank++ < eq_need;
+                keepm |= kp << j;
+            }
+            eq_seen += __builtin_amdgcn_readlane(ie, 63);
+        }
+        const int ck = __popc(keepm);
+        const int incl = wave_incl_scan(ck);
+        int pos = out + incl - ck;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (keepm & (1 << j)) out_row[pos++] = ids(e0 + j);
+        out += __builtin_amdgcn_readlane(incl, 63);
+    }
+    for (int j = out + lane; j < k; j += 64) out_row[j] = -1;
     wave_lds_sync();
 }
 
@@ -400,6 +507,10 @@ template <int DI> struct IdxMma<float, DI> {
     }
 };
 
+// max(x, 0) as one integer max: every negative float32 (-0.0 included) is a
+// negative int32, every other one keeps its bits.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores of the lane's query slots from one 16-row accumulator tile.
 // Returns the number of slots; s[j], qs[j] = query index within the tile, own[j].
 template <int HI>
@@ -408,7 +519,7 @@ __device__ __forceinline__ int tile_scores(const f32x4_t& c, const float* wr, in
     if constexpr (HI == 1) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            s[r] = wr[r] * fmaxf(c[r], 0.f);
+            s[r] = wr[r] * relu(c[r]);
             qs[r] = 4 * q4 + r;
             own[r] = true;
         }
@@ -416,7 +527,7 @@ __device__ __forceinline__ int tile_scores(const f32x4_t& c, const float* wr, in
     } else if constexpr (HI == 2) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            s[j] = wr[2 * j] * fmaxf(c[2 * j], 0.f) + wr[2 * j + 1] * fmaxf(c[2 * j + 1], 0.f);
+            s[j] = wr[2 * j] * relu(c[2 * j]) + wr[2 * j + 1] * relu(c[2 * j + 1]);
             qs[j] = 2 * q4 + j;
             own[j] = true;
         }
@@ -424,7 +535,7 @@ __device__ __forceinline__ int tile_scores(const f32x4_t& c, const float* wr, in
     } else {
         float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += wr[r] * fmaxf(c[r], 0.f);
+        for (int r = 0; r < 4; ++r) part += wr[r] * relu(c[r]);
         if constexpr (HI == 4) {
             s[0] = part;
             qs[0] = q4;
@@ -458,7 +569,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     const int qpw = p.qpw, cap = p.cap, mcap = p.mcap;
     const int RT = qpw / QPT;
 
-    // per-wave LDS: keys[qpw][cap] ids[qpw][cap] hist[256] mpos[mcap] mex[mcap] qn[qpw]
+    // per-wave LDS: keys[qpw][cap] ids[qpw][cap] hist[256] mex[mcap] mpos[mcap] mid[mcap] qn[qpw]
     char* base = smem + (size_t)wave * p.wave_stride;
     uint32_t* keys_all = reinterpret_cast<uint32_t*>(base);
     int32_t* ids_all = reinterpret_cast<int32_t*>(base + 4ull * qpw * cap);
@@ -466,7 +577,8 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     wb.hist = reinterpret_cast<uint32_t*>(base + 8ull * qpw * cap);
     wb.mex = reinterpret_cast<double*>(base + 8ull * qpw * cap + 1024);
     wb.mpos = reinterpret_cast<int32_t*>(base + 8ull * qpw * cap + 1024 + 8ull * mcap);
-    float* qn = reinterpret_cast<float*>(base + 8ull * qpw * cap + 1024 + 12ull * mcap);
+    wb.mid = reinterpret_cast<int32_t*>(base + 8ull * qpw * cap + 1024 + 12ull * mcap);
+    float* qn = reinterpret_cast<float*>(base + 8ull * qpw * cap + 1024 + 16ull * mcap);
 
     // later queries (more visible entries) first: the light work runs last
     const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
@@ -474,6 +586,16 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
     const int q0 = (qt * WAVES + wave) * qpw;  // first query row of this wave
     const T* qI = reinterpret_cast<const T*>(p.qI);
     const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
+    if (p.row_fail) {
+        // fallback of the long prefill pipeline: only rows its lists could not
+        // decide are (re)computed; a wave without such a row has nothing to do
+        bool any = false;
+        for (int qw = lane; qw < qpw; qw += 64) {
+            const int i = q0 + qw;
+            any |= i < p.Tq && p.row_fail[(long long)b * p.Tq + i] != 0;
+        }
+        if (!__any(any)) return;
+    }
 
     // ---- A fragments (rows = (query, head)), weights, norms
     typename MM::F a[MAX_RT][MM::KS];
@@ -663,7 +785,8 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
                 q.ids = ids_all + qw * cap;
                 const int k_eff = min(p.k, nvq);
                 const long long row = (long long)b * p.Tq + i;
-                final_select<T, HI, DI>(q, cq, k_eff, p.k, delta0 * qn[qw], mcap, qI + row * HI * DI, kI_b,
+                if (p.row_fail && p.row_fail[row] == 0) continue;
+                final_select<T, HI, DI>(q, LdsIds{q.ids}, cq, k_eff, p.k, delta0 * qn[qw], mcap, qI + row * HI * DI, kI_b,
                                         p.w + row * HI, p.idx + row * p.k);
             }
         }
@@ -675,7 +798,11 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
 // to LDS once as an order-preserving key, then one exact selection per query
 // (no streaming compactions).  Same scoring tiles and the same exact decision
 // rule as the streaming kernel.
-template <typename T, int HI, int DI>
+//
+// SAMPLE mode (first pass of the long prefill pipeline): the same scoring over
+// the sampled entries 0, S, 2S, ... only; per query the sample_j-th largest
+// sampled score becomes the row's threshold estimate (no selection output).
+template <typename T, int HI, int DI, bool SAMPLE>
 __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void index_dense_kernel(IdxParams p) {
     typedef IdxMma<T, DI> MM;
     constexpr int QPT = 16 / HI;
@@ -728,12 +855,14 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             if (lane < QPT && rt * QPT + lane < qpw) qn[rt * QPT + lane] = acc;
         }
     }
-    // visible entries of the wave's queries
+    // visible entries of the wave's queries (SAMPLE: sampled entries)
+    const int S = SAMPLE ? p.sample_stride : 1;
     int nv_max = 0;
     for (int qw = 0; qw < qpw; ++qw) {
         const int i = q0 + qw;
         if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N));
     }
+    if (SAMPLE) nv_max = (nv_max + S - 1) / S;
     float kmax2 = 0.f;
     // ---- all scores -> LDS keys
     auto score_tile = [&](int c0, const typename MM::F* bf) {
@@ -758,8 +887,8 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         }
     };
     auto load_b = [&](int c0, typename MM::F* bf) {
-        const int c = c0 + rho;
-        MM::load_a(kI_b + (long long)(c < p.N ? c : 0) * DI, c < p.N, q4, bf);
+        const long long e = (long long)(c0 + rho) * S;
+        MM::load_a(kI_b + (e < p.N ? e : 0) * DI, e < p.N, q4, bf);
     };
     constexpr int PF = 2;
     typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
@@ -783,6 +912,33 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     }
     kmax2 = wave_max_f(kmax2);
     wave_lds_sync();
+
+    if constexpr (SAMPLE) {
+        // largest ||k||^2 of the sequence (every entry, not only the sampled ones)
+        float km2 = 0.f;
+        for (int j = lane; j < p.kblk; j += 64) km2 = fmaxf(km2, p.kmax_part[(long long)b * p.kblk + j]);
+        const float kmax_all = sqrtf(wave_max_f(km2));
+        for (int qw = 0; qw < qpw; ++qw) {
+            const int i = q0 + qw;
+            if (i >= p.Tq) break;
+            const long long row = (long long)b * p.Tq + i;
+            const int n = (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+            const int ns = (n + S - 1) / S;
+            const float delta = p.err_c * qn[qw] * kmax_all;
+            uint32_t thr = 0u, tau = 0u;   // 0: list every visible entry
+            if (n > p.list_cap && ns >= p.sample_j) {
+                int n_gt;
+                tau = radix_kth(keys_all + qw * np, ns, p.sample_j, hist, &n_gt);
+                thr = fkey(key_f(tau) - 2.0f * delta);
+            }
+            if (lane == 0) {
+                p.row_thr[row] = thr;
+                p.row_tau[row] = tau;
+                p.row_delta[row] = delta;
+            }
+        }
+        return;
+    }
 
     // ---- one exact selection per query
     const float kmax = sqrtf(kmax2);
@@ -821,7 +977,7 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             if (nM <= mcap) {
                 // a band of exactly `need` entries is kept whole: no re-scoring
                 if (nM > need) {
-                    exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, nullptr, mpos, nM, mex);
+                    exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, PosIds{}, mpos, nM, mex, nullptr);
                     wave_lds_sync();
                 }
                 for (int j = lane; j < nM; j += 64) {
@@ -868,6 +1024,237 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         for (int j = out + lane; j < p.k; j += 64) out_row[j] = -1;
         wave_lds_sync();
     }
+}
+
+// ----------------------------------------------------------- long prefill
+// Long candidate sets (N > 2048) in prefill, four passes:
+//  L0 (index_kmax_kernel): max ||k||^2 per block of entries (for delta);
+//  L1 (index_dense_kernel, SAMPLE): per query, a threshold tau from every S-th
+//     entry: the sample_j-th largest sampled float32 score;
+//  L2 (index_filter_kernel): all float32 scores, entries with
+//     score >= tau - 2 delta appended in entry order to the row's list;
+//  L3 (index_list_final_kernel): when the list did not overflow and holds at
+//     least k_eff entries with score >= tau, the row's float32 k-th score T is
+//     >= tau, so the list holds every entry with score >= T - 2 delta: the same
+//     exact selection as the other kernels runs over the list.  Any other row
+//     is flagged and recomputed by the streaming kernel.
+constexpr int kKmaxBlock = 1024;
+
+template <typename T, int DI>
+__global__ __launch_bounds__(256) void index_kmax_kernel(IdxParams p) {
+    __shared__ float part[4];
+    const int tid = threadIdx.x;
+    const long long b = blockIdx.x / p.kblk, blk = blockIdx.x % p.kblk;
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
+    constexpr int V = Elem<T>::kVec;
+    float m = 0.f;
+    for (int e = tid; e < kKmaxBlock; e += 256) {
+        const long long c = blk * kKmaxBlock + e;
+        if (c >= p.N) break;
+        float s = 0.f;
+#pragma unroll
+        for (int d0 = 0; d0 < DI; d0 += V) {
+            float f[V];
+            Elem<T>::unpack(ld16(kI_b + c * DI + d0), f);
+#pragma unroll
+            for (int j = 0; j < V; ++j) s = fmaf(f[j], f[j], s);
+        }
+        m = fmaxf(m, s);
+    }
+    m = wave_max_f(m);
+    if ((tid & 63) == 0) part[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) p.kmax_part[blockIdx.x] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+// Row tiles per wave of the filter pass (host and device agree on it): more
+// queries per wave read each key tile fewer times; register budget bounds it.
+__host__ __device__ constexpr int filter_row_tiles(bool f32, int hi, int di) {
+    return f32 ? 1 : 4;
+}
+
+// L2: no LDS; each wave scores FRT row tiles of queries against all their
+// visible entries (MFMA tiles as above) and appends the entries that pass the
+// row's threshold to the row's list in global memory.
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(WAVES * 64) void index_filter_kernel(IdxParams p) {
+    typedef IdxMma<T, DI> MM;
+    constexpr int QPT = 16 / HI;
+    constexpr int SLOTS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
+    constexpr int FRT = filter_row_tiles(std::is_same<T, float>::value, HI, DI);
+    constexpr int QPW = FRT * QPT;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, rho = lane & 15;
+    const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
+    const int b = blockIdx.x / p.nqt;
+    const int q0 = (qt * WAVES + wave) * QPW;
+    if (q0 >= p.Tq) return;
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
+    const int lcap = p.list_cap;
+
+    typename MM::F a[FRT][MM::KS];
+    float wr[FRT][4];
+#pragma unroll
+    for (int rt = 0; rt < FRT; ++rt) {
+        const int qw = rt * QPT + rho / HI, hh = rho % HI;
+        const int i = q0 + qw;
+        const bool ok = i < p.Tq;
+        MM::load_a(qI + (((long long)b * p.Tq + (ok ? i : 0)) * HI + hh) * DI, ok, q4, a[rt]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * q4 + r;
+            const int ir = q0 + rt * QPT + row / HI;
+            wr[rt][r] = ir < p.Tq ? p.w[((long long)b * p.Tq + ir) * HI + row % HI] : 0.f;
+        }
+    }
+    // per (row tile, slot): the lane group's list, visible entries, threshold
+    // (as a float: score >= thr_f <=> key >= row_thr), count
+    uint2* lst[FRT][SLOTS];
+    int nv[FRT][SLOTS], cnt[FRT][SLOTS];
+    float thr_f[FRT][SLOTS];
+    int nv_max = 0;
+#pragma unroll
+    for (int rt = 0; rt < FRT; ++rt)
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            int qw;
+            if (HI == 1) qw = 4 * q4 + sl;
+            else if (HI == 2) qw = 2 * q4 + sl;
+            else if (HI == 4) qw = q4;
+            else if (HI == 8) qw = q4 >> 1;
+            else qw = 0;
+            const int i = q0 + rt * QPT + qw;
+            const bool ok = i < p.Tq;
+            const long long row = (long long)b * p.Tq + (ok ? i : 0);
+            lst[rt][sl] = p.row_lists + row * lcap;
+            nv[rt][sl] = ok ? (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
+            const uint32_t tk = ok ? p.row_thr[row] : 0u;
+            thr_f[rt][sl] = tk == 0u ? -INFINITY : key_f(tk);
+            cnt[rt][sl] = 0;
+            nv_max = max(nv_max, nv[rt][sl]);
+        }
+    nv_max = (int)wave_allreduce((uint32_t)nv_max, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    const uint32_t below = (1u << rho) - 1u;   // lanes of this 16-lane group below this one
+
+    auto load_b = [&](int c0, typename MM::F* bf) {
+        const int c = c0 + rho;
+        MM::load_a(kI_b + (long long)(c < p.N ? c : 0) * DI, c < p.N, q4, bf);
+    };
+    auto filter_tile = [&](int c0, const typename MM::F* bf) {
+        const int c = c0 + rho;
+        f32x4_t acc[FRT];
+#pragma unroll
+        for (int rt = 0; rt < FRT; ++rt) acc[rt] = MM::mma(a[rt], bf);
+#pragma unroll
+        for (int rt = 0; rt < FRT; ++rt) {
+            float sc[4];
+            int qs[4];
+            bool own[4];
+            const int ns = tile_scores<HI>(acc[rt], wr[rt], q4, sc, qs, own);
+#pragma unroll
+            for (int sl = 0; sl < SLOTS; ++sl) {
+                if (sl >= ns) break;
+                const bool ins = own[sl] && c < nv[rt][sl] && sc[sl] >= thr_f[rt][sl];
+                const unsigned long long msk = __ballot(ins);
+                if (msk == 0ull) continue;
+                const uint32_t gb = (uint32_t)(msk >> (16 * q4)) & 0xFFFFu;
+                if (ins) {
+                    const int pos = cnt[rt][sl] + __popc(gb & below);
+                    if (pos < lcap) lst[rt][sl][pos] = make_uint2(fkey(sc[sl]), (uint32_t)c);
+                }
+                cnt[rt][sl] += __popc(gb);
+            }
+        }
+    };
+    constexpr int PF = 2;
+    typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
+    auto group = [&](int g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+        const int g1 = g0 + PF * TILE;
+        if (g1 < nv_max) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+            if (g0 + t * TILE < nv_max) filter_tile(g0 + t * TILE, cur[t]);
+    };
+    if (nv_max > 0) {
+#pragma unroll
+        for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
+    }
+    for (int g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
+        group(g0, bq0, bq1);
+        if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
+    }
+    // counts (a count above list_cap marks an overflowed list)
+    const bool owner = (HI <= 4) || (HI == 8 ? (q4 & 1) == 0 : q4 == 0);
+#pragma unroll
+    for (int rt = 0; rt < FRT; ++rt)
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            int qw;
+            if (HI == 1) qw = 4 * q4 + sl;
+            else if (HI == 2) qw = 2 * q4 + sl;
+            else if (HI == 4) qw = q4;
+            else if (HI == 8) qw = q4 >> 1;
+            else qw = 0;
+            const int i = q0 + rt * QPT + qw;
+            if (owner && rho == 0 && i < p.Tq) p.list_cnt[(long long)b * p.Tq + i] = cnt[rt][sl];
+        }
+}
+
+// L3: one wave per row: exact selection over the row's list, or a failure flag.
+template <typename T, int HI, int DI>
+__global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x;
+    const long long row = blockIdx.x;
+    const long long b = row / p.Tq, i = row % p.Tq;
+    const int lcap = p.list_cap;
+    // LDS: keys[lcap] hist[256] mex[mcap] mpos[mcap] mid[mcap]; entries stay in the list
+    WaveBuf wb;
+    wb.keys = reinterpret_cast<uint32_t*>(smem);
+    wb.ids = nullptr;
+    wb.hist = reinterpret_cast<uint32_t*>(smem + 4ull * lcap);
+    wb.mex = reinterpret_cast<double*>(smem + 4ull * lcap + 1024);
+    wb.mpos = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 8ull * p.mcap);
+    wb.mid = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 12ull * p.mcap);
+    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const int k_eff = (int)std::min<long long>(p.k, nvq);
+    const int cnt = p.list_cnt[row];
+    bool ok = cnt <= lcap;
+    if (ok) {
+        // two (key, entry) pairs per lane and 16-byte load, four loads in flight
+        const uint32_t tau = p.row_tau[row];
+        const uint2* lst = p.row_lists + row * lcap;
+        int n_ge = 0;
+        for (int base = 0; base < cnt; base += 512) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = base + 128 * u + 2 * lane;
+                if (e < cnt) v[u] = ld16(lst + e);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = base + 128 * u + 2 * lane;
+                if (e < cnt) {
+                    *reinterpret_cast<uint2*>(wb.keys + e) = make_uint2(v[u].x, v[u].z);
+                    n_ge += (v[u].x >= tau) + (e + 1 < cnt && v[u].z >= tau);
+                }
+            }
+        }
+        n_ge = (int)wave_allreduce((uint32_t)n_ge, [](uint32_t x, uint32_t y) { return x + y; });
+        ok = n_ge >= k_eff;
+    }
+    if (lane == 0) p.row_fail[row] = ok ? 0 : 1;
+    if (!ok) return;
+    wave_lds_sync();
+    const T* qI = reinterpret_cast<const T*>(p.qI);
+    const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
+    final_select<T, HI, DI>(wb, ListIds{p.row_lists + row * lcap}, cnt, k_eff, p.k, p.row_delta[row], p.mcap,
+                            qI + row * HI * DI, kI_b,
+                            p.w + row * HI, p.idx + row * p.k);
 }
 
 // ----------------------------------------------------------- split pipeline
@@ -1039,7 +1426,8 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
     wb.hist = reinterpret_cast<uint32_t*>(smem + 8ull * cap);
     wb.mex = reinterpret_cast<double*>(smem + 8ull * cap + 1024);
     wb.mpos = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 8ull * p.mcap);
-    int32_t* offs = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 12ull * p.mcap);  // [nchunks + 1]
+    wb.mid = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 12ull * p.mcap);
+    int32_t* offs = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 16ull * p.mcap);  // [nchunks + 1]
     __shared__ int s_total, s_over;
     const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
     const int k_eff = (int)std::min<long long>(p.k, nvq);
@@ -1083,7 +1471,7 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
         }
         __syncthreads();
         if (wave == 0)
-            final_select<T, HI, DI>(wb, total, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b,
+            final_select<T, HI, DI>(wb, LdsIds{wb.ids}, total, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b,
                                     p.w + row * HI, p.idx + row * p.k);
         return;
     }
@@ -1128,23 +1516,35 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
         }
     }
     wave_lds_sync();
-    final_select<T, HI, DI>(wb, cnt, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b, p.w + row * HI,
+    final_select<T, HI, DI>(wb, LdsIds{wb.ids}, cnt, k_eff, p.k, delta, p.mcap, qI + row * HI * DI, kI_b,
+                            p.w + row * HI,
                             p.idx + row * p.k);
 }
 
 // ----------------------------------------------------------- host planning
+// launch shape of a kernel that tiles queries over waves (dense / prefill kernels)
+struct IdxLaunch {
+    int qpw, nqt, wave_stride, cap;
+    long long grid;
+    size_t lds;
+};
+
 struct IdxPlan {
     IdxParams p;
     bool split;
     bool dense;  // small N: all scores of a query in LDS, one exact select
-    size_t lds;  // prefill: per workgroup; split: final kernel
+    bool longp;  // long prefill pipeline (sample, filter, list final, fallback)
+    size_t lds;  // dense: per workgroup; split: final kernel; long: list final kernel
     size_t lds_score;
     long long grid;
     size_t ws_bytes;
+    IdxLaunch ls, lf;  // long: sampling pass (dense kernel) and streaming fallback
+    long long grid_kmax, grid_filter;
 };
 
 constexpr int kMaxLds = 160 * 1024;
 constexpr int kDenseMaxN = 2048;
+constexpr int kSampleMax = 1024;  // long prefill: sampled entries per query at most
 
 int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k,
                   int dtype, IdxPlan& pl) {
@@ -1177,6 +1577,10 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     pl.ws_bytes = 0;
     pl.grid = 0;
     pl.dense = false;
+    pl.longp = false;
+    pl.ls = IdxLaunch{};
+    pl.lf = IdxLaunch{};
+    pl.grid_kmax = pl.grid_filter = 0;
     const long long rows = (long long)B * Tq;
     pl.split = rows > 0 && rows <= 64 && N >= 8192;
     if (pl.split) {
@@ -1206,11 +1610,11 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
         // final kernel: LDS slots for every listed candidate of a row (parallel
         // path); the streaming fallback uses the first stream_cap of them
         p.stream_cap = p.cap;
-        const long long fixed = 1024 + 12ll * p.mcap + 4ll * (p.nchunks + 1) + 16;
+        const long long fixed = 1024 + 16ll * p.mcap + 4ll * (p.nchunks + 1) + 16;
         const long long cap_fit = (kMaxLds - fixed) / 8;
         if (cap_fit < p.stream_cap)
             return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: N=%d needs more LDS than available", N);
-        p.cap = (int)std::min<long long>(12288, cap_fit);
+        p.cap = (int)std::min<long long>(12288, cap_fit / 64 * 64);
         if (p.cap < p.stream_cap) p.cap = p.stream_cap;
         pl.lds = (8ull * p.cap + (size_t)fixed + 15) / 16 * 16;
         pl.grid = rows;
@@ -1239,67 +1643,152 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
         }
         p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
     }
-    // prefill: choose queries per wave so that 4 waves fit the LDS budget
-    int qpw = std::max(16, qpt);
-    if (qpw > 4 * qpt) qpw = 4 * qpt;
-    auto per_wave = [&](int q) { return (8ull * q * p.cap + 1024 + 12ull * p.mcap + 4ull * q + 31) / 16 * 16; };
-    while (qpw > qpt && WAVES * per_wave(qpw) > (size_t)kMaxLds) qpw -= qpt;
-    if (WAVES * per_wave(qpw) > (size_t)kMaxLds)
-        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: k=%d needs more LDS than available", k);
-    // fewer queries per wave when the batch is small (more waves in flight)
-    while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 512) qpw -= qpt;
-    p.qpw = qpw;
-    p.wave_stride = (int)per_wave(qpw);
-    p.nqt = (Tq + WAVES * qpw - 1) / (WAVES * qpw);
-    pl.lds = WAVES * per_wave(qpw);
-    pl.grid = (long long)B * p.nqt;
+    if (N == 0) {
+        // no candidates: the dense kernel writes the -1 rows
+        pl.dense = true;
+        p.cap = 0;
+        p.qpw = qpt;
+        p.wave_stride = (int)((1024 + 12ull * p.mcap + 4ull * qpt + 15) / 16 * 16);
+        p.nqt = (Tq + WAVES * qpt - 1) / (WAVES * qpt);
+        pl.lds = (size_t)WAVES * p.wave_stride;
+        pl.grid = (long long)B * p.nqt;
+        return SHATTN_OK;
+    }
+    // ---- long prefill pipeline
+    pl.longp = true;
+    // streaming fallback: queries per wave so that 4 waves fit the LDS budget
+    {
+        int qpw = std::max(16, qpt);
+        if (qpw > 4 * qpt) qpw = 4 * qpt;
+        auto per_wave = [&](int q) { return (8ull * q * p.cap + 1024 + 16ull * p.mcap + 4ull * q + 31) / 16 * 16; };
+        while (qpw > qpt && WAVES * per_wave(qpw) > (size_t)kMaxLds) qpw -= qpt;
+        if (WAVES * per_wave(qpw) > (size_t)kMaxLds)
+            return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: k=%d needs more LDS than available", k);
+        while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 512) qpw -= qpt;
+        pl.lf.qpw = qpw;
+        pl.lf.cap = p.cap;
+        pl.lf.wave_stride = (int)per_wave(qpw);
+        pl.lf.nqt = (Tq + WAVES * qpw - 1) / (WAVES * qpw);
+        pl.lf.lds = WAVES * per_wave(qpw);
+        pl.lf.grid = (long long)B * pl.lf.nqt;
+    }
+    // sampling pass: stride S (a power of two) with at most kSampleMax sampled
+    // entries per query whose keys fit the dense kernel's LDS
+    auto sample_wave = [&](int q, int np) { return (4ull * q * np + 1024 + 12ull * p.mcap + 4ull * q + 15) / 16 * 16; };
+    int S = 1, np = 0;
+    for (;; S *= 2) {
+        np = ((N + S - 1) / S + TILE - 1) / TILE * TILE;
+        if (np <= kSampleMax && WAVES * sample_wave(qpt, np) <= (size_t)kMaxLds) break;
+    }
+    {
+        int qpw = 4 * qpt;
+        while (qpw > qpt && WAVES * sample_wave(qpw, np) > (size_t)kMaxLds) qpw -= qpt;
+        while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 1024) qpw -= qpt;
+        pl.ls.qpw = qpw;
+        pl.ls.cap = np;
+        pl.ls.wave_stride = (int)sample_wave(qpw, np);
+        pl.ls.nqt = (Tq + WAVES * qpw - 1) / (WAVES * qpw);
+        pl.ls.lds = WAVES * sample_wave(qpw, np);
+        pl.ls.grid = (long long)B * pl.ls.nqt;
+    }
+    // threshold rank j among the samples and list capacity: with r = k / S the
+    // expected number of entries above the j-th sampled score is about j * S
+    // (standard deviation about sqrt(j) * S); j = r + 5 sqrt(r) + 2 keeps it
+    // above k, the capacity j * S + 7 sqrt(j) * S keeps the list from
+    // overflowing, except on inputs with structure at the sampling period (those
+    // rows fail over to the streaming kernel).
+    const double r = (double)k / S;
+    const int j = (int)std::ceil(r) + (int)std::ceil(5.0 * std::sqrt(r)) + 2;
+    long long lcap = (long long)std::ceil(j * (double)S + 7.0 * std::sqrt((double)j) * S) + 64;
+    const long long lcap_fit = (kMaxLds - 1024 - 16ll * p.mcap - 16) / 4 / 64 * 64;
+    lcap = std::min((lcap + 63) / 64 * 64, lcap_fit);
+    p.sample_stride = S;
+    p.sample_j = j;
+    p.list_cap = (int)lcap;
+    p.kblk = (N + kKmaxBlock - 1) / kKmaxBlock;
+    const int frt = filter_row_tiles(dtype == SHATTN_DTYPE_F32, Hi, d_idx);
+    const int qpw_f = frt * qpt;
+    p.nqt = (Tq + WAVES * qpw_f - 1) / (WAVES * qpw_f);
+    pl.grid_filter = (long long)B * p.nqt;
+    pl.grid_kmax = (long long)B * p.kblk;
+    pl.grid = rows;
+    pl.lds = (4ull * lcap + 1024 + 16ull * p.mcap + 15) / 16 * 16;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
+    const size_t o_km = take((size_t)B * p.kblk * 4);
+    const size_t o_thr = take((size_t)rows * 4);
+    const size_t o_tau = take((size_t)rows * 4);
+    const size_t o_del = take((size_t)rows * 4);
+    const size_t o_fail = take((size_t)rows * 4);
+    const size_t o_cnt = take((size_t)rows * 4);
+    const size_t o_lst = take((size_t)rows * lcap * 8);
+    pl.ws_bytes = off;
+    p.kmax_part = reinterpret_cast<float*>(o_km);
+    p.row_thr = reinterpret_cast<uint32_t*>(o_thr);
+    p.row_tau = reinterpret_cast<uint32_t*>(o_tau);
+    p.row_delta = reinterpret_cast<float*>(o_del);
+    p.row_fail = reinterpret_cast<int32_t*>(o_fail);
+    p.list_cnt = reinterpret_cast<int32_t*>(o_cnt);
+    p.row_lists = reinterpret_cast<uint2*>(o_lst);
     return SHATTN_OK;
+}
+
+int allow_lds(const void* kernel, size_t lds) {
+    if (lds <= 64 * 1024) return SHATTN_OK;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", lds);
+    }
+    return SHATTN_OK;
+}
+
+IdxParams with_launch(const IdxParams& p, const IdxLaunch& l) {
+    IdxParams q = p;
+    q.qpw = l.qpw;
+    q.nqt = l.nqt;
+    q.wave_stride = l.wave_stride;
+    q.cap = l.cap;
+    return q;
 }
 
 template <typename T, int HI, int DI>
 int launch_idx(IdxPlan& pl, hipStream_t s) {
+    int rc;
     if (pl.dense) {
-        if (pl.lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
-            if (e != hipSuccess) {
-                (void)hipGetLastError();
-                return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
-            }
-        }
-        hipLaunchKernelGGL((index_dense_kernel<T, HI, DI>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds, s,
-                           pl.p);
-        return check_launch("csa_index_topk");
-    }
-    if (!pl.split) {
-        if (pl.lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_prefill_kernel<T, HI, DI>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
-            if (e != hipSuccess) {
-                (void)hipGetLastError();
-                return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
-            }
-        }
-        hipLaunchKernelGGL((index_prefill_kernel<T, HI, DI>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds,
+        if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, false>), pl.lds))) return rc;
+        hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, false>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds,
                            s, pl.p);
         return check_launch("csa_index_topk");
+    }
+    if (pl.longp) {
+        hipLaunchKernelGGL((index_kmax_kernel<T, DI>), dim3((unsigned)pl.grid_kmax), dim3(256), 0, s, pl.p);
+        if ((rc = check_launch("csa_index_topk (kmax)"))) return rc;
+        if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, true>), pl.ls.lds)))
+            return rc;
+        hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, true>), dim3((unsigned)pl.ls.grid), dim3(WAVES * 64),
+                           pl.ls.lds, s, with_launch(pl.p, pl.ls));
+        if ((rc = check_launch("csa_index_topk (sample)"))) return rc;
+        hipLaunchKernelGGL((index_filter_kernel<T, HI, DI>), dim3((unsigned)pl.grid_filter), dim3(WAVES * 64), 0, s,
+                           pl.p);
+        if ((rc = check_launch("csa_index_topk (filter)"))) return rc;
+        if ((rc = allow_lds(reinterpret_cast<const void*>(&index_list_final_kernel<T, HI, DI>), pl.lds))) return rc;
+        hipLaunchKernelGGL((index_list_final_kernel<T, HI, DI>), dim3((unsigned)pl.grid), dim3(64), pl.lds, s, pl.p);
+        if ((rc = check_launch("csa_index_topk (list final)"))) return rc;
+        if ((rc = allow_lds(reinterpret_cast<const void*>(&index_prefill_kernel<T, HI, DI>), pl.lf.lds))) return rc;
+        hipLaunchKernelGGL((index_prefill_kernel<T, HI, DI>), dim3((unsigned)pl.lf.grid), dim3(WAVES * 64),
+                           pl.lf.lds, s, with_launch(pl.p, pl.lf));
+        return check_launch("csa_index_topk (fallback)");
     }
     const long long rows = pl.grid;
     hipLaunchKernelGGL((index_split_score_kernel<T, HI, DI>), dim3((unsigned)(rows * pl.p.nchunks)), dim3(64),
                        pl.lds_score, s, pl.p);
-    int rc = check_launch("csa_index_topk (score)");
+    rc = check_launch("csa_index_topk (score)");
     if (rc) return rc;
     hipLaunchKernelGGL(index_split_collect_kernel, dim3((unsigned)(rows * pl.p.nchunks)), dim3(64), 0, s, pl.p);
     rc = check_launch("csa_index_topk (collect)");
     if (rc) return rc;
-    if (pl.lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&index_split_final_kernel<T, HI, DI>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: %zu bytes of LDS unavailable", pl.lds);
-        }
-    }
+    if ((rc = allow_lds(reinterpret_cast<const void*>(&index_split_final_kernel<T, HI, DI>), pl.lds))) return rc;
     hipLaunchKernelGGL((index_split_final_kernel<T, HI, DI>), dim3((unsigned)rows), dim3(kFinalThreads), pl.lds, s,
                        pl.p);
     return check_launch("csa_index_topk (final)");
@@ -1351,19 +1840,33 @@ extern "C" int csa_index_topk(const void* qI, const void* kI, const float* w, in
             return fail(SHATTN_EINVAL, "csa_index_topk: workspace must be 256-byte aligned");
         char* base = reinterpret_cast<char*>(ws);
         IdxParams& p = pl.p;
-        p.scores = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.scores));
-        p.chunk_lb = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.chunk_lb));
-        p.chunk_kmax = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.chunk_kmax));
-        p.row_qn = reinterpret_cast<float*>(base + reinterpret_cast<size_t>(p.row_qn));
-        p.lists = reinterpret_cast<uint32_t*>(base + reinterpret_cast<size_t>(p.lists));
-        p.list_idx = reinterpret_cast<int32_t*>(base + reinterpret_cast<size_t>(p.list_idx));
-        p.list_cnt = reinterpret_cast<int32_t*>(base + reinterpret_cast<size_t>(p.list_cnt));
+        auto at = [&](auto* off) { return reinterpret_cast<decltype(off)>(base + reinterpret_cast<size_t>(off)); };
+        if (pl.split) {
+            p.scores = at(p.scores);
+            p.chunk_lb = at(p.chunk_lb);
+            p.chunk_kmax = at(p.chunk_kmax);
+            p.row_qn = at(p.row_qn);
+        } else {
+            p.kmax_part = at(p.kmax_part);
+            p.row_thr = at(p.row_thr);
+            p.row_tau = at(p.row_tau);
+            p.row_delta = at(p.row_delta);
+            p.row_fail = at(p.row_fail);
+            p.row_lists = at(p.row_lists);
+        }
+        if (pl.split) {
+            p.lists = at(p.lists);
+            p.list_idx = at(p.list_idx);
+        }
+        p.list_cnt = at(p.list_cnt);
     }
     pl.p.qI = qI;
     pl.p.kI = kI;
     pl.p.w = w;
     pl.p.idx = idx;
-    if (pl.grid > 2147483647LL / 64) return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: problem too large");
+    if (pl.grid > 2147483647LL / 64 || pl.ls.grid > 2147483647LL / 64 || pl.lf.grid > 2147483647LL / 64 ||
+        pl.grid_kmax > 2147483647LL)
+        return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: problem too large");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return dtype == SHATTN_DTYPE_BF16 ? launch_idx_hi<bf16_t>(pl, Hi, d_idx, s)
                                       : launch_idx_hi<float>(pl, Hi, d_idx, s);
