@@ -425,8 +425,8 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
     static constexpr int DT = D / 16;
     static constexpr int MAT_BYTES = KT * ROWB;
     static_assert(NLOADS * RPI == KT, "tile split");
-    int goff_k[NI], goff_v[NI];  // element offsets of this lane's global pieces
-    int grow[NI];                // their tile rows
+    uint32_t boff_k[NI], boff_v[NI];  // byte offsets of this lane's global pieces
+    int grow[NI];                     // their tile rows
     int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
     int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative)
     int wave;
@@ -436,15 +436,15 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
 
     __device__ void init(int tid, int rs) {
         const int lane = tid & 63;
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             // wave load j * NW + wave (when it exists) covers rows RPI * that .. +RPI
             const int row = (j * NW + wave) * RPI + lane / PIECES;
             const int pc = lane % PIECES;  // LDS slot piece; it holds global piece pc ^ swz(row)
             grow[j] = row;
-            goff_k[j] = row * rs + (pc ^ swz_k(row)) * 8;
-            goff_v[j] = row * rs + (pc ^ swz_v(row)) * 8;
+            boff_k[j] = (uint32_t)(row * rs + (pc ^ swz_k(row)) * 8) * 2u;
+            boff_v[j] = (uint32_t)(row * rs + (pc ^ swz_v(row)) * 8) * 2u;
         }
         const int rho = lane & 15, q4 = lane >> 4;
         const int key0 = 8 * (rho >> 2) + (rho & 3);  // S^T row rho of a chunk's first tile
@@ -456,15 +456,29 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
         for (int dt = 0; dt < 4; ++dt)
             vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1);
     }
-    // start loading rows [0, nvalid) of a tile (rows past nvalid repeat row 0)
+    // start loading rows [0, nvalid) of a tile (rows past nvalid repeat row 0).
+    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
     __device__ void issue(const bf16_t* kb, const bf16_t* vb, int nvalid, char* buf) const {
+        const char* kbb = reinterpret_cast<const char*>(kb);
+        const char* vbb = reinterpret_cast<const char*>(vb);
+        if (nvalid >= KT) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            if (NLOADS % NW != 0 && j * NW + wave >= NLOADS) break;   // uniform per wave
-            const bool ok = grow[j] < nvalid;
-            char* dst = buf + (j * NW + wave) * 1024;
-            __builtin_amdgcn_global_load_lds(kb + (ok ? goff_k[j] : 0), (lds_void_t*)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb + (ok ? goff_v[j] : 0), (lds_void_t*)(dst + MAT_BYTES), 16, 0, 0);
+            for (int j = 0; j < NI; ++j) {
+                if (NLOADS % NW != 0 && j * NW + wave >= NLOADS) break;   // uniform per wave
+                char* dst = buf + (j * NW + wave) * 1024;
+                __builtin_amdgcn_global_load_lds(kbb + boff_k[j], (lds_void_t*)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vbb + boff_v[j], (lds_void_t*)(dst + MAT_BYTES), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                if (NLOADS % NW != 0 && j * NW + wave >= NLOADS) break;
+                const bool ok = grow[j] < nvalid;
+                char* dst = buf + (j * NW + wave) * 1024;
+                __builtin_amdgcn_global_load_lds(kbb + (ok ? boff_k[j] : 0u), (lds_void_t*)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vbb + (ok ? boff_v[j] : 0u), (lds_void_t*)(dst + MAT_BYTES), 16, 0,
+                                                 0);
+            }
         }
     }
     // the issued loads have landed in LDS (a barrier must follow)
