@@ -44,6 +44,8 @@
 #include <algorithm>
 #include <cmath>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace shattn {
@@ -415,24 +417,82 @@ template <typename T, int D, int NW> struct TileIO;
 //    elements read by lane 4k + i/4 in slot k.  Lane s reading 4 elements of
 //    key row (8 g + s/4) at dims 4 (s mod 4) .. +3 makes lane i hold keys
 //    8 g + k, dim i: the A layout of O^T = V^T P^T.
-template <int D, int NW> struct TileIO<bf16_t, D, NW> {
+// Reads of a bf16 K/V tile laid out as above ([rows][D], 16-byte pieces of
+// row r at slot piece ^ swz(r)): S^T from K pieces, O^T += V^T P^T with
+// transposing reads of V.
+template <int D> struct TileReadBf16 {
     static constexpr int PIECES = D / 8;        // 16-byte pieces per row
     static constexpr int ROWB = D * 2;          // bytes per row
-    static constexpr int RPI = 1024 / ROWB;     // rows per wave load
-    static constexpr int NLOADS = KT / RPI;             // wave loads per matrix per tile
-    static constexpr int NI = (NLOADS + NW - 1) / NW;   // of them per wave (at most)
+    static constexpr int RPI = 1024 / ROWB;     // rows per wave load (64 lanes x 16 bytes)
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
+    int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
+    int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative)
+
+    __device__ static int swz_k(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); }
+    __device__ static int swz_v(int row) { return (2 * (row & 3)) & (PIECES - 1); }
+
+    __device__ void init_read(int lane) {
+        const int rho = lane & 15, q4 = lane >> 4;
+        const int key0 = 8 * (rho >> 2) + (rho & 3);  // S^T row rho of a chunk's first tile
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kro[ks] = key0 * ROWB + (((4 * ks + q4) ^ swz_k(key0)) * 16);
+        const int g4 = lane >> 4, sl = lane & 15;
+        const int vrow = 8 * g4 + (sl >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1);
+    }
+    // S^T for keys [c, c+32) of the K tile at kbuf.  s[j] <-> key 8 q4 + j of the chunk.
+    __device__ void scores_at(const char* kbuf, int c, const bf16x8_t* qf, float* s) const {
+        const char* kb = kbuf + c * ROWB;
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks]);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks] + 4 * ROWB);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = s0[r];
+            s[4 + r] = s1[r];
+        }
+    }
+    // acc += V^T P^T for keys [c, c+32) of the V tile at vbuf
+    __device__ void pv_at(const char* vbuf, int c, const float* p, f32x4_t* acc) const {
+        const char* vb = vbuf + c * ROWB;
+        bf16x8_t bop;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bop[j] = (__bf16)p[j];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const char* a = vb + vro[dt & 3] + (dt >> 2) * 128;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
+            const i16x4_t lohi[2] = {lo, hi};
+            bf16x8_t aop;
+            __builtin_memcpy(&aop, lohi, 16);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[dt], 0, 0, 0);
+        }
+    }
+};
+
+template <int D, int NW> struct TileIO<bf16_t, D, NW> : TileReadBf16<D> {
+    typedef TileReadBf16<D> R;
+    using R::PIECES;
+    using R::ROWB;
+    using R::RPI;
+    using R::swz_k;
+    using R::swz_v;
+    static constexpr int NLOADS = KT / RPI;             // wave loads per matrix per tile
+    static constexpr int NI = (NLOADS + NW - 1) / NW;   // of them per wave (at most)
     static constexpr int MAT_BYTES = KT * ROWB;
     static_assert(NLOADS * RPI == KT, "tile split");
     uint32_t boff_k[NI], boff_v[NI];  // byte offsets of this lane's global pieces
     int grow[NI];                     // their tile rows
-    int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
-    int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative)
     int wave;
-
-    __device__ static int swz_k(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); }
-    __device__ static int swz_v(int row) { return (2 * (row & 3)) & (PIECES - 1); }
 
     __device__ void init(int tid, int rs) {
         const int lane = tid & 63;
@@ -446,15 +506,7 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
             boff_k[j] = (uint32_t)(row * rs + (pc ^ swz_k(row)) * 8) * 2u;
             boff_v[j] = (uint32_t)(row * rs + (pc ^ swz_v(row)) * 8) * 2u;
         }
-        const int rho = lane & 15, q4 = lane >> 4;
-        const int key0 = 8 * (rho >> 2) + (rho & 3);  // S^T row rho of a chunk's first tile
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kro[ks] = key0 * ROWB + (((4 * ks + q4) ^ swz_k(key0)) * 16);
-        const int g4 = lane >> 4, sl = lane & 15;
-        const int vrow = 8 * g4 + (sl >> 2);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1);
+        this->init_read(lane);
     }
     // start loading rows [0, nvalid) of a tile (rows past nvalid repeat row 0).
     // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
@@ -483,41 +535,50 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> {
     }
     // the issued loads have landed in LDS (a barrier must follow)
     __device__ void commit(char*) const { __builtin_amdgcn_s_waitcnt(0); }
-    // S^T for keys [c, c+32) of the tile in buf.  s[j] <-> key 8 q4 + j of the chunk.
     __device__ void scores(const char* buf, int c, const bf16x8_t* qf, float* s) const {
-        const char* kb = buf + c * ROWB;
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks]);
-            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kb + kro[ks] + 4 * ROWB);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[r] = s0[r];
-            s[4 + r] = s1[r];
-        }
+        this->scores_at(buf, c, qf, s);
     }
-    // acc += V^T P^T for keys [c, c+32) of the tile in buf
     __device__ void pv(const char* buf, int c, const float* p, f32x4_t* acc) const {
-        const char* vb = buf + MAT_BYTES + c * ROWB;
-        bf16x8_t bop;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bop[j] = (__bf16)p[j];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const char* a = vb + vro[dt & 3] + (dt >> 2) * 128;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
-            const i16x4_t lohi[2] = {lo, hi};
-            bf16x8_t aop;
-            __builtin_memcpy(&aop, lohi, 16);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[dt], 0, 0, 0);
-        }
+        this->pv_at(buf + MAT_BYTES, c, p, acc);
     }
     static constexpr int buf_bytes() { return 2 * MAT_BYTES; }
+};
+
+// Per-wave chunk of KC gathered K and V rows (entries listed by lanes 0..KC-1)
+// loaded straight into the wave's own LDS tiles, in the tile layout above.
+template <int D> struct GatherBf16 : TileReadBf16<D> {
+    typedef TileReadBf16<D> R;
+    using R::PIECES;
+    using R::ROWB;
+    using R::RPI;
+    using R::swz_k;
+    using R::swz_v;
+    static constexpr int NL = KC / RPI;       // wave loads per matrix
+    static constexpr int MAT_BYTES = KC * ROWB;
+    static_assert(NL * RPI == KC, "chunk split");
+    int lrow[NL];                   // chunk row of this lane's piece in load j
+    uint32_t poff_k[NL], poff_v[NL];  // byte offset of that piece within its row
+
+    __device__ void init(int lane) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int row = j * RPI + lane / PIECES;
+            const int pc = lane % PIECES;
+            lrow[j] = row;
+            poff_k[j] = (uint32_t)((pc ^ swz_k(row)) * 16);
+            poff_v[j] = (uint32_t)((pc ^ swz_v(row)) * 16);
+        }
+        this->init_read(lane);
+    }
+    // load the rows of entries e (lane r < KC holds row r's entry, >= 0) of one
+    // matrix: row r of entry e starts at base + e * rsb bytes
+    __device__ void issue(const char* base, long long rsb, int e, const uint32_t* poff, char* dst) const {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int er = __shfl(e, lrow[j]);
+            __builtin_amdgcn_global_load_lds(base + er * rsb + poff[j], (lds_void_t*)(dst + j * 1024), 16, 0, 0);
+        }
+    }
 };
 
 // fp32: register staging (global -> registers -> LDS), K row-major, V
@@ -827,6 +888,68 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
     };
 
+    // ---- CSA gather, bf16: per-wave K/V chunk tiles in LDS (aliasing the
+    // stream buffers), loaded by DMA; the next chunk's K rows load during this
+    // chunk's softmax and PV and its V rows after the PV, and the entry list
+    // is read one chunk ahead.
+    auto gather_dma = [&]() {
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        char* gk = smem + p.lds_gather + wave * p.lds_gather_stride;
+        char* gv = gk + GatherBf16<D>::MAT_BYTES;
+        GatherBf16<D> gio;
+        gio.init(lane);
+        const long long rsb = (long long)p.Hkv * D * 2;   // bytes between entries
+        const char* kc = reinterpret_cast<const char*>(p.k_csa) + (long long)b * p.N_csa * rsb + hoff * 2;
+        const char* vc = reinterpret_cast<const char*>(p.v_csa) + (long long)b * p.N_csa * rsb + hoff * 2;
+        const int ql_a = (wave * 16) / p.G;
+        const int ql_b = min((wave * 16 + 15) / p.G, nq - 1);
+        int j_lo = 0, j_hi = p.k;
+        if (p.nsplit) {
+            j_lo = (int)csa_lo;
+            j_hi = csa_hi < p.k ? (int)csa_hi : p.k;
+        }
+        const int nj = j_hi > j_lo ? (j_hi - j_lo + KC - 1) / KC : 0;
+        const int nchunks = ql_b >= ql_a ? (ql_b - ql_a + 1) * nj : 0;
+        if (nchunks == 0 || p.N_csa == 0) return;   // no entries: nothing to attend (or to load)
+        // lanes < KC: entry of row `lane` of chunk ci (-1: none)
+        auto entry = [&](int ci) -> int {
+            const int qq = ql_a + ci / nj;
+            const int j = j_lo + (ci - (qq - ql_a) * nj) * KC + lane;
+            int e = -1;
+            if (lane < KC && j < j_hi) {
+                e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
+                if (e < 0 || e >= p.N_csa) e = -1;
+            }
+            return e;
+        };
+        int e_cur = entry(0);
+        gio.issue(kc, rsb, max(e_cur, 0), gio.poff_k, gk);
+        gio.issue(vc, rsb, max(e_cur, 0), gio.poff_v, gv);
+        int e_nxt = nchunks > 1 ? entry(1) : -1;
+        for (int ci = 0; ci < nchunks; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0);   // chunk ci in LDS, entries of ci + 1 loaded
+            wave_lds_sync();
+            const int qq = ql_a + ci / nj;
+            const unsigned long long vrows = __ballot(lane < KC && e_cur >= 0);
+            float sc[8];
+            gio.scores_at(gk, 0, qf, sc);
+            const bool more = ci + 1 < nchunks;
+            wave_lds_sync();   // this wave's K reads are complete
+            if (more) gio.issue(kc, rsb, max(e_nxt, 0), gio.poff_k, gk);   // K tile is free again
+            const uint32_t mb = (valid && ql == qq) ? (uint32_t)(vrows >> (8 * q4)) & 0xFFu : 0u;
+            softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2,
+                                    [&](int, const float* pp, f32x4_t* acc) { gio.pv_at(gv, 0, pp, acc); });
+            wave_lds_sync();   // this wave's V reads are complete
+            if (more) {
+                gio.issue(vc, rsb, max(e_nxt, 0), gio.poff_v, gv);        // V tile is free again
+                e_cur = e_nxt;
+                e_nxt = ci + 2 < nchunks ? entry(ci + 2) : -1;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    };
+
     // ---- CSA gather (per wave, private LDS tiles aliasing the stream buffers)
     auto gather = [&]() {
         char* gbase = smem + p.lds_gather + wave * p.lds_gather_stride;
@@ -919,7 +1042,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
             } else {
                 __syncthreads();  // the stream buffers become the per-wave gather tiles
-                gather();
+                if constexpr (std::is_same<T, bf16_t>::value) gather_dma();
+                else gather();
                 __syncthreads();
             }
             fold(gate[1]);
@@ -932,7 +1056,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
             } else {
                 __syncthreads();
-                gather();
+                if constexpr (std::is_same<T, bf16_t>::value) gather_dma();
+                else gather();
                 __syncthreads();
             }
         }
@@ -1196,8 +1321,9 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     // bf16: K and V [KT][d] unpadded (swizzled); fp32: padded K and V rows
     const size_t tile_b = bf ? (size_t)(2 * KT * a->d) * esz : (size_t)(2 * KT * kpad) * esz;
     const size_t shared_b = 2 * tile_b;
-    const size_t gather_b = bf ? (size_t)(KC * kpad + a->d * (KC + 8)) * esz + KC * 8
-                               : (size_t)(2 * KC * kpad) * esz + KC * 8;
+    // per-wave gather tiles: bf16 K and V [KC][d] (DMA-loaded, swizzled); fp32
+    // padded K and V rows plus the row list
+    const size_t gather_b = bf ? (size_t)(2 * KC * a->d) * esz : (size_t)(2 * KC * kpad) * esz + KC * 8;
     p.csa_mode = CSA_NONE;
     size_t lds = shared_b;
     if (has_csa) {
