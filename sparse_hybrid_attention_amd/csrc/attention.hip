@@ -427,10 +427,14 @@ template <int D> struct TileReadBf16 {
     static constexpr int KS = D / 32;
     static constexpr int DT = D / 16;
     int kro[KS];                 // byte offsets of this lane's K pieces (chunk-relative)
-    int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative)
+    int vro[4];                  // byte offsets of this lane's V^T reads (chunk-relative, dims < 64)
+    int vhs;                     // byte step to this lane's V^T reads of dims 64..127
 
     __device__ static int swz_k(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); }
-    __device__ static int swz_v(int row) { return (2 * (row & 3)) & (PIECES - 1); }
+    // V: rows 8g + r (lane group g of a transposing read) use pieces 2 (r ^ t) + {0, 1};
+    // at d = 128 bit 3 of the row also flips the upper half of the pieces, so
+    // lane groups 0 / 1 (and 2 / 3) of one read use different LDS bank halves
+    __device__ static int swz_v(int row) { return ((2 * (row & 3)) | (((row >> 3) & 1) << 3)) & (PIECES - 1); }
 
     __device__ void init_read(int lane) {
         const int rho = lane & 15, q4 = lane >> 4;
@@ -439,9 +443,11 @@ template <int D> struct TileReadBf16 {
         for (int ks = 0; ks < KS; ++ks) kro[ks] = key0 * ROWB + (((4 * ks + q4) ^ swz_k(key0)) * 16);
         const int g4 = lane >> 4, sl = lane & 15;
         const int vrow = 8 * g4 + (sl >> 2);
+        const int hb = PIECES > 8 ? (g4 & 1) : 0;   // the row's upper-half flip (d = 128)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-            vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1);
+            vro[dt] = vrow * ROWB + (2 * (dt ^ (sl >> 2)) + ((sl & 3) >> 1)) * 16 + 8 * (sl & 1) + hb * 128;
+        vhs = hb ? -128 : 128;
     }
     // S^T for keys [c, c+32) of the K tile at kbuf.  s[j] <-> key 8 q4 + j of the chunk.
     __device__ void scores_at(const char* kbuf, int c, const bf16x8_t* qf, float* s) const {
@@ -468,7 +474,7 @@ template <int D> struct TileReadBf16 {
         for (int j = 0; j < 8; ++j) bop[j] = (__bf16)p[j];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const char* a = vb + vro[dt & 3] + (dt >> 2) * 128;
+            const char* a = vb + vro[dt & 3] + (dt >> 2) * vhs;
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
             const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
             const i16x4_t lohi[2] = {lo, hi};
