@@ -108,6 +108,14 @@ def test_index_errors(lib):
     assert lib.csa_index_topk_workspace_size(16, 1, 262144, 4, 64, 1024) > 0
     assert call(B=16, Tq=1, N=262144, k=1024) == binding.SHATTN_EWORKSPACE
     assert "workspace" in err(lib)
+    # prefill with N <= 2048 keeps every score in LDS: no workspace
+    assert lib.csa_index_topk_workspace_size(2, 4096, 2048, 4, 64, 64) == 0
+    # longer prefill keeps per-query candidate lists ((key, entry) pairs, at
+    # least k per query) in the workspace: it grows with the query rows
+    ws1 = lib.csa_index_topk_workspace_size(1, 4096, 8192, 4, 64, 64)
+    ws2 = lib.csa_index_topk_workspace_size(2, 4096, 8192, 4, 64, 64)
+    assert ws1 >= 8 * 4096 * 64 and ws2 >= 2 * ws1 - 4096
+    assert call(B=1, Tq=4096, N=8192, k=64) == binding.SHATTN_EWORKSPACE
     assert f(None, P, P, P, 1, 16, 64, 4, 64, 0, 4, 8, 8, 0, None, 0, None) == binding.SHATTN_EINVAL
 
 
