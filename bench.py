@@ -137,7 +137,69 @@ def algorithmic(inp, pipe):
     pairs = B * H * keys.sum()
     out["attention"] = dict(bytes=float(byt), flops=4.0 * d * pairs, units=B * keys.sum(),
                             unit="attended (query, key) pairs")
+    if use_csa:
+        # K and V rows of every selected entry, as the kernel reads them (once
+        # per query and KV head): served mostly from L2 / MALL, not HBM
+        out["attention"]["gathered_bytes"] = float(B * sel.sum() * Hkv * 2 * d * esz)
     return out
+
+
+def measure_peaks(torch, binding):
+    """Measured device peaks to read the roofline fractions against: a 1 GiB
+    device-to-device copy (bytes read + written per second) and the bf16 MFMA
+    issue rate of a loop of independent MFMAs (shattn_mfma_peak_probe)."""
+    import ctypes
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(4):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    copy_gbs = 2.0 * n / (best * 1e-3) / 1e9
+    del a, b
+    lib = binding.load_library()
+    wgs, iters = 2048, 2048
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for _ in range(4):
+        e0.record()
+        rc = lib.shattn_mfma_peak_probe(wgs, iters, ctypes.c_void_p(sink.data_ptr()), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(lib.shattn_last_error().decode())
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    mfma_tf = wgs * 4 * iters * 8 * 16384 / (best * 1e-3) / 1e12
+    return {"copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+            "method": "best of 4: 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 iterations "
+                      "of 8 independent 16x16x32 bf16 MFMAs per wave"}
+
+
+def cold_steps(torch, pipe, reps=20, flush_bytes=512 << 20):
+    """Median step time with L2 / MALL flushed before every step (a 512 MiB
+    buffer is overwritten between steps; the flush is outside the timed span)."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for r in range(reps):
+        scratch.fill_(r & 255)
+        e0.record(pipe.stream)
+        pipe.run()
+        e1.record(pipe.stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    times.sort()
+    return {"ms_per_step_median": round(times[len(times) // 2], 5), "reps": reps,
+            "flush_MiB": flush_bytes >> 20}
 
 
 def source_hash(fname):
@@ -225,6 +287,8 @@ def main():
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cache-flushed step timing and the measured-peak probes")
     ap.add_argument("--cpu-rows", type=int, default=10000,
                     help="query rows of the CPU-baseline sample (about 10-15 s of oracle work at the default workload)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -303,6 +367,8 @@ def main():
             e[a["unit"] + "/s"] = a["units"] / (ms * 1e-3)
             e["alg_bytes"] = a["bytes"]
             e["alg_flops"] = a["flops"]
+            if "gathered_bytes" in a:
+                e["gathered GB/s"] = round(a["gathered_bytes"] / (ms * 1e-3) / 1e9, 1)
         kernels[n] = e
     dom = max(names, key=lambda n: ktime[n])
     a = alg[dom]
@@ -319,6 +385,14 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
     roof["traffic"] = traffic_for(dom, args.workload)
+
+    # after the timed region: the same step with caches flushed, and the
+    # measured device peaks (extra fields beside the headline)
+    cold = cold_steps(torch, pipe) if not args.no_extras else None
+    peaks = measure_peaks(torch, binding) if not args.no_extras else None
+    if peaks is not None and (roof["unit"] == "GB/s" or dtype == "bf16"):
+        roof["measured_peak"] = peaks["copy_GBps"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_TFLOPs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / roof["measured_peak"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -357,6 +431,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "cold": cold,
+        "measured_peaks": peaks,
     }
     print(json.dumps(line))
 

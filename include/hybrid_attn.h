@@ -187,6 +187,17 @@ SHATTN_API size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
  *            k <= 4096. */
 SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement aid (not part of the attention path): launches `workgroups`
+ * workgroups of 256 threads, each wave issuing `iters` x 8 independent
+ * 16x16x32 bf16 MFMAs (16384 flops each), i.e.
+ * workgroups * 4 * iters * 8 * 16384 flops; time it on `stream` to read the
+ * device's dense bf16 MFMA rate.  sink: device float32 [workgroups * 256],
+ * written (garbage values that keep the work live).
+ * Supported: 1 <= workgroups <= 65536, 1 <= iters <= 2^20.
+ */
+SHATTN_API int shattn_mfma_peak_probe(int workgroups, int iters, float* sink, void* stream);
+
 /* Message describing the calling thread's last failure ("" if none). */
 SHATTN_API const char* shattn_last_error(void);
 

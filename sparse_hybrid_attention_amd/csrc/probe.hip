@@ -1,0 +1,44 @@
+// Measurement aid, not part of the attention path: the bf16 MFMA issue rate
+// of the device, measured by a loop of independent 16x16x32 bf16 MFMAs, so
+// that roofline fractions can be read against a measured as well as the
+// published peak.
+#include "common.h"
+
+namespace shattn {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeChains = 8;   // independent accumulators per wave: no MFMA waits on another
+
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, float* sink) {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)(1e-3f * (float)((threadIdx.x + j) & 7));
+        b[j] = (__bf16)(2e-3f * (float)j);
+    }
+    f32x4_t c[kProbeChains];
+#pragma unroll
+    for (int k = 0; k < kProbeChains; ++k) c[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kProbeChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kProbeChains; ++k) s += (c[k][0] + c[k][1]) + (c[k][2] + c[k][3]);
+    sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = s;   // keeps every MFMA live
+}
+
+}  // namespace
+}  // namespace shattn
+
+using namespace shattn;
+
+extern "C" int shattn_mfma_peak_probe(int workgroups, int iters, float* sink, void* stream) {
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20) || !sink)
+        return fail(SHATTN_EINVAL, "shattn_mfma_peak_probe: workgroups %d, iters %d", workgroups, iters);
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), iters, sink);
+    return check_launch("shattn_mfma_peak_probe");
+}

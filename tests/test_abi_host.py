@@ -119,6 +119,14 @@ def test_index_errors(lib):
     assert f(None, P, P, P, 1, 16, 64, 4, 64, 0, 4, 8, 8, 0, None, 0, None) == binding.SHATTN_EINVAL
 
 
+def test_mfma_probe_rejects_bad_arguments(lib):
+    f = lib.shattn_mfma_peak_probe
+    assert f(0, 16, P, None) == binding.SHATTN_EINVAL
+    assert f(16, 0, P, None) == binding.SHATTN_EINVAL
+    assert f(16, 16, None, None) == binding.SHATTN_EINVAL
+    assert "probe" in lib.shattn_last_error().decode()
+
+
 def fwd(**kw):
     a = binding.FwdArgs()
     a.struct_size = ctypes.sizeof(binding.FwdArgs)
