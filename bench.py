@@ -167,20 +167,23 @@ def measure_peaks(torch, binding):
     wgs, iters = 2048, 2048
     sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    best = None
-    for _ in range(4):
-        e0.record()
-        rc = lib.shattn_mfma_peak_probe(wgs, iters, ctypes.c_void_p(sink.data_ptr()), stream)
-        e1.record()
-        torch.cuda.synchronize()
-        if rc != 0:
-            raise RuntimeError(lib.shattn_last_error().decode())
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    mfma_tf = wgs * 4 * iters * 8 * 16384 / (best * 1e-3) / 1e12
-    return {"copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": round(mfma_tf, 1),
-            "method": "best of 4: 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 iterations "
-                      "of 8 independent 16x16x32 bf16 MFMAs per wave"}
+    rates = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        best = None
+        for _ in range(4):
+            e0.record()
+            rc = lib.shattn_mfma_peak_probe(wgs, iters, shape, ctypes.c_void_p(sink.data_ptr()), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(lib.shattn_last_error().decode())
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        rates[name] = round(wgs * 4 * iters * 131072 / (best * 1e-3) / 1e12, 1)
+    return {"copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": max(rates.values()),
+            "mfma_bf16_TFLOPs_by_shape": rates,
+            "method": "best of 4: 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 rounds of "
+                      "independent bf16 MFMAs per wave (8 x 16x16x32 or 4 x 32x32x16)"}
 
 
 def cold_steps(torch, pipe, reps=20, flush_bytes=512 << 20):

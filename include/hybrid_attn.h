@@ -189,14 +189,15 @@ SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t
 
 /*
  * Measurement aid (not part of the attention path): launches `workgroups`
- * workgroups of 256 threads, each wave issuing `iters` x 8 independent
- * 16x16x32 bf16 MFMAs (16384 flops each), i.e.
- * workgroups * 4 * iters * 8 * 16384 flops; time it on `stream` to read the
- * device's dense bf16 MFMA rate.  sink: device float32 [workgroups * 256],
- * written (garbage values that keep the work live).
- * Supported: 1 <= workgroups <= 65536, 1 <= iters <= 2^20.
+ * workgroups of 256 threads; every wave issues `iters` rounds of independent
+ * bf16 MFMAs: shape 0 = 8 x v_mfma_f32_16x16x32_bf16 per round, shape 1 =
+ * 4 x v_mfma_f32_32x32x16_bf16 per round (131072 flops per round and wave
+ * either way), i.e. workgroups * 4 * iters * 131072 flops.  Time it on
+ * `stream` to read the device's dense bf16 MFMA rate.  sink: device float32
+ * [workgroups * 256], written (values that keep the work live).
+ * Supported: 1 <= workgroups <= 65536, 1 <= iters <= 2^20, shape 0 or 1.
  */
-SHATTN_API int shattn_mfma_peak_probe(int workgroups, int iters, float* sink, void* stream);
+SHATTN_API int shattn_mfma_peak_probe(int workgroups, int iters, int shape, float* sink, void* stream);
 
 /* Message describing the calling thread's last failure ("" if none). */
 SHATTN_API const char* shattn_last_error(void);

@@ -104,7 +104,7 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_sparse_attn_fwd_workspace_size.restype = sz
         lib.hybrid_sparse_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp, sz, vp]
         lib.hybrid_sparse_attn_fwd.restype = i32
-        lib.shattn_mfma_peak_probe.argtypes = [i32, i32, vp, vp]
+        lib.shattn_mfma_peak_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.shattn_mfma_peak_probe.restype = i32
         lib.shattn_last_error.argtypes = []
         lib.shattn_last_error.restype = ctypes.c_char_p

@@ -10,6 +10,8 @@ namespace {
 constexpr int kProbeThreads = 256;
 constexpr int kProbeChains = 8;   // independent accumulators per wave: no MFMA waits on another
 
+// SHAPE 0: v_mfma_f32_16x16x32_bf16 (16384 flops), 1: v_mfma_f32_32x32x16_bf16 (32768 flops)
+template <int SHAPE>
 __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, float* sink) {
     bf16x8_t a, b;
 #pragma unroll
@@ -17,16 +19,33 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, fl
         a[j] = (__bf16)(1e-3f * (float)((threadIdx.x + j) & 7));
         b[j] = (__bf16)(2e-3f * (float)j);
     }
-    f32x4_t c[kProbeChains];
-#pragma unroll
-    for (int k = 0; k < kProbeChains; ++k) c[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int k = 0; k < kProbeChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
-    }
     float s = 0.f;
+    if constexpr (SHAPE == 0) {
+        f32x4_t c[kProbeChains];
 #pragma unroll
-    for (int k = 0; k < kProbeChains; ++k) s += (c[k][0] + c[k][1]) + (c[k][2] + c[k][3]);
+        for (int k = 0; k < kProbeChains; ++k) c[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int k = 0; k < kProbeChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kProbeChains; ++k) s += (c[k][0] + c[k][1]) + (c[k][2] + c[k][3]);
+    } else {
+        constexpr int CH = kProbeChains / 2;   // 16 accumulator registers each
+        f32x16_t c[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[k][r] = 0.f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += c[k][r];
+    }
     sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = s;   // keeps every MFMA live
 }
 
@@ -35,10 +54,14 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, fl
 
 using namespace shattn;
 
-extern "C" int shattn_mfma_peak_probe(int workgroups, int iters, float* sink, void* stream) {
-    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20) || !sink)
-        return fail(SHATTN_EINVAL, "shattn_mfma_peak_probe: workgroups %d, iters %d", workgroups, iters);
-    hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream), iters, sink);
+extern "C" int shattn_mfma_peak_probe(int workgroups, int iters, int shape, float* sink, void* stream) {
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20) || !sink || shape < 0 || shape > 1)
+        return fail(SHATTN_EINVAL, "shattn_mfma_peak_probe: workgroups %d, iters %d, shape %d", workgroups, iters,
+                    shape);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (shape == 0)
+        hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, s, iters, sink);
+    else
+        hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, s, iters, sink);
     return check_launch("shattn_mfma_peak_probe");
 }

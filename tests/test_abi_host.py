@@ -121,9 +121,10 @@ def test_index_errors(lib):
 
 def test_mfma_probe_rejects_bad_arguments(lib):
     f = lib.shattn_mfma_peak_probe
-    assert f(0, 16, P, None) == binding.SHATTN_EINVAL
-    assert f(16, 0, P, None) == binding.SHATTN_EINVAL
-    assert f(16, 16, None, None) == binding.SHATTN_EINVAL
+    assert f(0, 16, 0, P, None) == binding.SHATTN_EINVAL
+    assert f(16, 0, 0, P, None) == binding.SHATTN_EINVAL
+    assert f(16, 16, 2, P, None) == binding.SHATTN_EINVAL
+    assert f(16, 16, 0, None, None) == binding.SHATTN_EINVAL
     assert "probe" in lib.shattn_last_error().decode()
 
 
