@@ -40,6 +40,9 @@ def hipcc() -> str:
 # masked keys are -inf), so their float max needs no NaN-quieting instructions
 FILE_FLAGS = {
     "attention.hip": ["-fno-honor-nans"],
+    # the MFMA rate probe: accumulators in ordinary VGPRs (the accumulator-
+    # register form of its loop is compiled with register copies per round)
+    "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 
 

@@ -21,13 +21,20 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, fl
     }
     float s = 0.f;
     if constexpr (SHAPE == 0) {
-        f32x4_t c[kProbeChains];
-#pragma unroll
-        for (int k = 0; k < kProbeChains; ++k) c[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // eight named accumulators, each updated in place every round
+        f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+#pragma unroll 2
         for (int it = 0; it < iters; ++it) {
-#pragma unroll
-            for (int k = 0; k < kProbeChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+            c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c4, 0, 0, 0);
+            c5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c5, 0, 0, 0);
+            c6 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c6, 0, 0, 0);
+            c7 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c7, 0, 0, 0);
         }
+        const f32x4_t c[kProbeChains] = {c0, c1, c2, c3, c4, c5, c6, c7};
 #pragma unroll
         for (int k = 0; k < kProbeChains; ++k) s += (c[k][0] + c[k][1]) + (c[k][2] + c[k][3]);
     } else {
