@@ -159,6 +159,32 @@ def test_indexer_brute_force():
         assert abs(tot - s[c]) < 1e-12
 
 
+def test_indexer_invariants():
+    """The score is a weighted sum over heads of ReLU'd dot products: it is
+    additive over heads even when dot products have mixed signs (ReLU applied
+    per head, before the weights and the sum), a negative weight multiplies
+    outside the ReLU, and a head whose query equals a key scores w * ||k||^2
+    for that key (computed here with a CPU torch matmul)."""
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((200, 32))
+    q = rng.standard_normal((2, 32))
+    d0, d1 = k @ q[0], k @ q[1]
+    assert (np.sign(d0) != np.sign(d1)).sum() > 50          # mixed signs are exercised
+    both = O.indexer_scores(q, np.ones(2), k)
+    np.testing.assert_allclose(both, O.indexer_scores(q[:1], np.ones(1), k) +
+                               O.indexer_scores(q[1:], np.ones(1), k), rtol=0, atol=1e-12)
+    # ReLU of the summed dots would differ exactly where the signs differ
+    assert np.abs(both - np.maximum(d0 + d1, 0.0)).max() > 1.0
+    neg = O.indexer_scores(q[:1], np.array([-0.5]), k)
+    assert (neg <= 0).all() and (neg[d0 < 0] == 0).all()
+    np.testing.assert_allclose(neg, -0.5 * np.maximum(d0, 0.0), rtol=1e-12, atol=0)
+    qs = np.stack([k[17], q[1]])
+    ref = torch.relu(torch.from_numpy(k) @ torch.from_numpy(qs).T) @ torch.tensor([0.75, 0.0], dtype=torch.float64)
+    got = O.indexer_scores(qs, np.array([0.75, 0.0]), k)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert abs(got[17] - 0.75 * float(k[17] @ k[17])) < 1e-9
+
+
 def test_indexer_single_head_ranking_is_library_sort():
     rng = np.random.default_rng(8)
     q = rng.standard_normal((1, 16))
