@@ -767,8 +767,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         int emax = -1;
         const int4* rows = reinterpret_cast<const int4*>(p.idx + ((long long)b * p.Tq + i0) * p.k);
         const int n4 = nq * p.k / 4;
-        for (int u = tid; u < n4; u += NT) {
-            const int4 e4 = rows[u];
+        // up to 4 of this thread's 16-byte index groups load together
+        constexpr int NPF = 4;
+        for (int u0 = tid; u0 < n4; u0 += NPF * NT) {
+          int4 pre[NPF];
+#pragma unroll
+          for (int xp = 0; xp < NPF; ++xp)
+            if (u0 + xp * NT < n4) pre[xp] = rows[u0 + xp * NT];
+#pragma unroll
+          for (int xp = 0; xp < NPF; ++xp) {
+            const int u = u0 + xp * NT;
+            if (u >= n4) break;
+            const int4 e4 = pre[xp];
             const int qq = (4 * u) / p.k;
             uint32_t* brow = bm + qq * p.bm_words;
             const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
@@ -788,6 +798,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 }
             }
             if (cw >= 0) atomicOr(&brow[cw], cbits);
+          }
         }
         for (int off = 32; off > 0; off >>= 1) {
             const int o = __shfl_xor(emax, off);
