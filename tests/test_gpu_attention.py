@@ -119,6 +119,24 @@ def test_csa_gather_many_heads_per_group():
     check(inp, hca, csa, got, rows=sample_rows(1, 1024, 128, n=48), what="G=16 gather")
 
 
+def test_csa_gather_d64():
+    # the direct-to-LDS gather tiles at d = 64 (8 rows per wave load)
+    lib()
+    inp, hca, csa = prefill_case("csa_prefill_128k", seed=11, T=2048, d=64, k=64)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(1, 2048, 128, n=64), what="csa gather d=64")
+
+
+def test_gather_with_no_cache_entries():
+    # T < m: the CSA branch is present (G = 8: gather mode) but its cache holds
+    # no entry; the branch is its window-only attention
+    lib()
+    inp, hca, csa = prefill_case("csa_prefill_128k", seed=13, T=3, W=2, k=8)
+    assert csa[0].shape[1] == 0
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, what="empty CSA cache")
+
+
 def decode_case(seed=0, **over):
     inp = synth.make_inputs("decode_1m", seed=seed, **over)
     cfg = inp["cfg"]
@@ -137,6 +155,15 @@ def test_decode_split_reduced():
                    k_raw="k_win", v_raw="v_win")
     check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
           v_raw="v_win", what="decode split")
+
+
+def test_decode_split_d64():
+    lib()
+    inp, hca, csa = decode_case(seed=12, B=2, N_csa=2048, N_hca=512, k=128, d=64)
+    got = gpu_attn(inp, hca, csa, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
+                   k_raw="k_win", v_raw="v_win")
+    check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+          v_raw="v_win", what="decode split d=64")
 
 
 def test_decode_full_size():
