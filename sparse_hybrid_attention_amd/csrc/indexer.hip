@@ -116,18 +116,28 @@ struct WaveBuf {
 };
 
 // Entry of buffer position e: from an LDS array, from a (key, entry) list in
-// global memory, or the position itself.
+// global memory, or the position itself.  ids4(e0) gives the entries of the
+// 4 positions e0 .. e0 + 3 (e0 a multiple of 4 inside the buffer's capacity).
 struct LdsIds {
     const int32_t* ids;
     __device__ int operator()(int e) const { return ids[e]; }
+    __device__ int4 ids4(int e0) const { return *reinterpret_cast<const int4*>(ids + e0); }
 };
 struct ListIds {
     const uint2* lst;
     __device__ int operator()(int e) const { return (int)lst[e].y; }
+    __device__ int4 ids4(int e0) const {
+        const uint4 a = ld16(lst + e0), b = ld16(lst + e0 + 2);
+        return make_int4((int)a.y, (int)a.w, (int)b.y, (int)b.w);
+    }
 };
 struct PosIds {
     __device__ int operator()(int e) const { return e; }
+    __device__ int4 ids4(int e0) const { return make_int4(e0, e0 + 1, e0 + 2, e0 + 3); }
 };
+__device__ __forceinline__ int int4_at(const int4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
 
 // Buffers read by the selection passes below are 16-byte aligned and their
 // capacity is a multiple of 4 keys: lane l of a pass over 256 keys takes the
@@ -414,10 +424,15 @@ __device__ __noinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_e
         }
     }
     // kept entries in buffer order: lane l holds 4 consecutive positions, so
-    // a prefix sum over lanes orders them
+    // a prefix sum over lanes orders them; the entries of the next 256
+    // positions are fetched while these are placed
     int out = 0, eq_seen = 0;
+    int4 idn = make_int4(0, 0, 0, 0);
+    if (4 * lane < cnt) idn = ids.ids4(4 * lane);
     for (int base = 0; base < cnt; base += 256) {
         const int e0 = base + 4 * lane;
+        const int4 idc = idn;
+        if (e0 + 256 < cnt) idn = ids.ids4(e0 + 256);
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (e0 < cnt) v = keys4(wb.keys, e0);
         int keepm = 0;
@@ -445,7 +460,7 @@ __device__ __noinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_e
         int pos = out + incl - ck;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (keepm & (1 << j)) out_row[pos++] = ids(e0 + j);
+            if (keepm & (1 << j)) out_row[pos++] = int4_at(idc, j);
         out += __builtin_amdgcn_readlane(incl, 63);
     }
     for (int j = out + lane; j < k; j += 64) out_row[j] = -1;
