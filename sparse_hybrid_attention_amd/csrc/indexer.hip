@@ -182,15 +182,20 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
 #pragma unroll
         for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
         wave_lds_sync();
-        for (int base = 0; base < cnt; base += 256) {
-            const int e0 = base + 4 * lane;
-            if (e0 < cnt) {
-                const uint4 v = keys4(keys, e0);
+        for (int base = 0; base < cnt; base += 512) {
+            const int e0 = base + 4 * lane, e1 = e0 + 256;
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (e0 < cnt) v0 = keys4(keys, e0);
+            if (e1 < cnt) v1 = keys4(keys, e1);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t key = key_at(v, j);
-                    if (e0 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_at(v0, j);
+                if (e0 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_at(v1, j);
+                if (e1 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
             }
         }
         wave_lds_sync();
@@ -1239,19 +1244,19 @@ __global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
     const int cnt = p.list_cnt[row];
     bool ok = cnt <= lcap;
     if (ok) {
-        // two (key, entry) pairs per lane and 16-byte load, four loads in flight
+        // two (key, entry) pairs per lane and 16-byte load, eight loads in flight
         const uint32_t tau = p.row_tau[row];
         const uint2* lst = p.row_lists + row * lcap;
         int n_ge = 0;
-        for (int base = 0; base < cnt; base += 512) {
-            uint4 v[4];
+        for (int base = 0; base < cnt; base += 1024) {
+            uint4 v[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int e = base + 128 * u + 2 * lane;
                 if (e < cnt) v[u] = ld16(lst + e);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int e = base + 128 * u + 2 * lane;
                 if (e < cnt) {
                     *reinterpret_cast<uint2*>(wb.keys + e) = make_uint2(v[u].x, v[u].z);
