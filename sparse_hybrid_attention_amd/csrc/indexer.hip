@@ -151,9 +151,14 @@ __device__ __forceinline__ uint32_t key_at(const uint4& v, int j) {
 }
 
 // k-th largest key among keys[0..cnt), 1 <= kk <= cnt.  *n_gt = #keys > result.
+// MSD radix select with digits of up to 8 bits taken from the highest bit in
+// which the keys differ (the bits above it are common to all keys).  Invariant:
+// kk - want keys lie above the current bucket (keys sharing `prefix` on
+// `pmask`), and the result is the want-th largest key inside it.  When that is
+// the bucket's largest (want == 1) or smallest (want == bucket size) key, one
+// min/max scan ends the search.
 __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
     const int lane = __lane_id();
-    // bytes shared by every key need no histogram pass
     uint32_t andv = 0xFFFFFFFFu, orv = 0u;
     for (int base = 0; base < cnt; base += 256) {
         const int e0 = base + 4 * lane;
@@ -174,11 +179,14 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         *n_gt = 0;
         return andv;
     }
-    const int top_byte = (31 - __clz(diff)) >> 3;
-    uint32_t pmask = top_byte == 3 ? 0u : (0xFFFFFFFFu << (8 * (top_byte + 1)));
+    int shift = 32 - __clz(diff);   // bits [shift, 32) are common to all keys
+    uint32_t pmask = shift >= 32 ? 0u : (0xFFFFFFFFu << shift);
     uint32_t prefix = andv & pmask;
     int want = kk;
-    for (int shift = 8 * top_byte; shift >= 0; shift -= 8) {
+    while (shift > 0) {
+        const int width = min(8, shift);
+        shift -= width;
+        const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
         wave_lds_sync();
@@ -190,12 +198,12 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t key = key_at(v0, j);
-                if (e0 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                if (e0 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t key = key_at(v1, j);
-                if (e1 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                if (e1 + j < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
             }
         }
         wave_lds_sync();
@@ -206,17 +214,17 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         const int total = __builtin_amdgcn_readlane(incl, 63);
         const int suf = total - incl + mine;                        // sum over lanes >= this lane
         const int above = suf - mine;  // sum over bins of higher lanes
-        int bin = -1, cnt_above = 0;
+        int bin = -1, cnt_above = 0, cnt_bin = 0;
         if (above < want && want <= suf) {
             int acc = above;
-            if (acc + (int)c3 >= want) { bin = lane * 4 + 3; cnt_above = acc; }
+            if (acc + (int)c3 >= want) { bin = lane * 4 + 3; cnt_above = acc; cnt_bin = (int)c3; }
             else {
                 acc += c3;
-                if (acc + (int)c2 >= want) { bin = lane * 4 + 2; cnt_above = acc; }
+                if (acc + (int)c2 >= want) { bin = lane * 4 + 2; cnt_above = acc; cnt_bin = (int)c2; }
                 else {
                     acc += c2;
-                    if (acc + (int)c1 >= want) { bin = lane * 4 + 1; cnt_above = acc; }
-                    else { acc += c1; bin = lane * 4 + 0; cnt_above = acc; }
+                    if (acc + (int)c1 >= want) { bin = lane * 4 + 1; cnt_above = acc; cnt_bin = (int)c1; }
+                    else { acc += c1; bin = lane * 4 + 0; cnt_above = acc; cnt_bin = (int)c0; }
                 }
             }
         }
@@ -224,10 +232,43 @@ __device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk
         const int src = __ffsll((long long)who) - 1;
         const int b = __builtin_amdgcn_readlane(bin, src);
         const int ca = __builtin_amdgcn_readlane(cnt_above, src);
+        const int cb = __builtin_amdgcn_readlane(cnt_bin, src);
         prefix |= ((uint32_t)b) << shift;
-        pmask |= 255u << shift;
+        pmask |= dmask << shift;
         want -= ca;
         wave_lds_sync();
+        if (shift > 0 && (want == 1 || want == cb)) {
+            const bool top = want == 1;
+            uint32_t m = top ? 0u : 0xFFFFFFFFu;
+            for (int base = 0; base < cnt; base += 256) {
+                const int e0 = base + 4 * lane;
+                if (e0 < cnt) {
+                    const uint4 v = keys4(keys, e0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t key = key_at(v, j);
+                        if (e0 + j < cnt && (key & pmask) == prefix) m = top ? max(m, key) : min(m, key);
+                    }
+                }
+            }
+            m = top ? wave_allreduce(m, [](uint32_t x, uint32_t y) { return max(x, y); })
+                    : wave_allreduce(m, [](uint32_t x, uint32_t y) { return min(x, y); });
+            if (top) {
+                *n_gt = kk - 1;
+                return m;
+            }
+            int eq = 0;
+            for (int base = 0; base < cnt; base += 256) {
+                const int e0 = base + 4 * lane;
+                if (e0 < cnt) {
+                    const uint4 v = keys4(keys, e0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) eq += (e0 + j < cnt && key_at(v, j) == m) ? 1 : 0;
+                }
+            }
+            *n_gt = kk - (int)wave_allreduce((uint32_t)eq, [](uint32_t x, uint32_t y) { return x + y; });
+            return m;
+        }
     }
     *n_gt = kk - want;
     return prefix;
@@ -845,43 +886,59 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     const T* qI = reinterpret_cast<const T*>(p.qI);
     const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
 
+    // Cooperative scoring (one row tile per wave): the waves score the queries
+    // of the whole workgroup together, wave w taking every WAVES-th entry tile,
+    // so that each loaded key tile feeds WAVES row tiles (a quarter of the tile
+    // loads on the longest wave's path).  Row tile rt is then wave rt's block
+    // of queries and its keys go to that wave's LDS region.
+    const bool coop = RT == 1 && WAVES <= MAX_RT;
+    const int NRT = coop ? WAVES : RT;   // row tiles this wave scores
+    auto rt_q0 = [&](int rt) { return coop ? (qt * WAVES + rt) * qpw : q0 + rt * QPT; };
+    auto rt_has = [&](int rt, int ql) { return rt < NRT && (coop ? ql < qpw : rt * QPT + ql < qpw); };
+    auto rt_keys = [&](int rt) {
+        return coop ? reinterpret_cast<uint32_t*>(smem + (size_t)rt * p.wave_stride) : keys_all + rt * QPT * np;
+    };
+
     typename MM::F a[MAX_RT][MM::KS];
     float wr[MAX_RT][4];
     const int rho = lane & 15;
 #pragma unroll
     for (int rt = 0; rt < MAX_RT; ++rt) {
-        const int qw = rt * QPT + rho / HI, hh = rho % HI;
-        const int i = q0 + qw;
-        const bool ok = rt < RT && qw < qpw && i < p.Tq;
+        const int ql = rho / HI, hh = rho % HI;
+        const int i = rt_q0(rt) + ql;
+        const bool ok = rt_has(rt, ql) && i < p.Tq;
         MM::load_a(qI + (((long long)b * p.Tq + (ok ? i : 0)) * HI + hh) * DI, ok, q4, a[rt]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * q4 + r;
-            const int qr = rt * QPT + row / HI, hr = row % HI;
-            const int ir = q0 + qr;
-            wr[rt][r] = (rt < RT && qr < qpw && ir < p.Tq) ? p.w[((long long)b * p.Tq + ir) * HI + hr] : 0.f;
+            const int qr = row / HI, hr = row % HI;
+            const int ir = rt_q0(rt) + qr;
+            wr[rt][r] = (rt_has(rt, qr) && ir < p.Tq) ? p.w[((long long)b * p.Tq + ir) * HI + hr] : 0.f;
         }
         float n2 = MM::sq(a[rt]);
         n2 = sum_xrows(n2);
-        if (rt < RT) {
+        if (coop ? rt == wave : rt < RT) {
+            // sum_h |w_h| ||q_h|| of the wave's own queries
             const int qsl = lane < QPT ? lane : 0;
             float acc = 0.f;
             for (int h = 0; h < HI; ++h) {
                 const float nr = __shfl(n2, qsl * HI + h);
-                const int ir = q0 + rt * QPT + qsl;
-                const float wv = (ir < p.Tq && rt * QPT + qsl < qpw) ? p.w[((long long)b * p.Tq + ir) * HI + h] : 0.f;
+                const int ir = rt_q0(rt) + qsl;
+                const float wv = (ir < p.Tq && rt_has(rt, qsl)) ? p.w[((long long)b * p.Tq + ir) * HI + h] : 0.f;
                 acc += fabsf(wv) * sqrtf(nr);
             }
-            if (lane < QPT && rt * QPT + lane < qpw) qn[rt * QPT + lane] = acc;
+            const int qs = coop ? lane : rt * QPT + lane;
+            if (lane < QPT && qs < qpw) qn[qs] = acc;
         }
     }
-    // visible entries of the wave's queries (SAMPLE: sampled entries)
+    // visible entries of the scored queries (SAMPLE: sampled entries)
     const int S = SAMPLE ? p.sample_stride : 1;
     int nv_max = 0;
-    for (int qw = 0; qw < qpw; ++qw) {
-        const int i = q0 + qw;
-        if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N));
-    }
+    for (int rt = 0; rt < (coop ? NRT : 1); ++rt)
+        for (int qw = 0; qw < qpw; ++qw) {
+            const int i = (coop ? rt_q0(rt) : q0) + qw;
+            if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N));
+        }
     if (SAMPLE) nv_max = (nv_max + S - 1) / S;
     float kmax2 = 0.f;
     // ---- all scores -> LDS keys
@@ -892,17 +949,17 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         kmax2 = fmaxf(kmax2, n2);
 #pragma unroll
         for (int rt = 0; rt < MAX_RT; ++rt) {
-            if (rt >= RT) break;
+            if (rt >= NRT) break;
             const f32x4_t acc = MM::mma(a[rt], bf);
             float sc[4];
             int qs[4];
             bool own[4];
             const int ns = tile_scores<HI>(acc, wr[rt], q4, sc, qs, own);
+            uint32_t* kd = rt_keys(rt);
 #pragma unroll
             for (int sl = 0; sl < SLOTS; ++sl) {
                 if (sl >= ns) break;
-                const int qw = rt * QPT + qs[sl];
-                if (own[sl] && qw < qpw && c < np) keys_all[qw * np + c] = fkey(sc[sl]);
+                if (own[sl] && rt_has(rt, qs[sl]) && c < np) kd[qs[sl] * np + c] = fkey(sc[sl]);
             }
         }
     };
@@ -910,28 +967,44 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         const long long e = (long long)(c0 + rho) * S;
         MM::load_a(kI_b + (e < p.N ? e : 0) * DI, e < p.N, q4, bf);
     };
+    // the wave's entry tiles j = 0 .. ntl-1 (cooperative: every WAVES-th tile)
+    const int ntot = (nv_max + TILE - 1) / TILE;
+    const int ntl = coop ? (ntot > wave ? (ntot - wave + WAVES - 1) / WAVES : 0) : ntot;
+    auto tile_c0 = [&](int j) { return (coop ? wave + WAVES * j : j) * TILE; };
     constexpr int PF = 2;
     typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
-    auto group = [&](int g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
-        const int g1 = g0 + PF * TILE;
-        if (g1 < nv_max) {
-#pragma unroll
-            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
-        }
+    auto group = [&](int l0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+        const int l1 = l0 + PF;
 #pragma unroll
         for (int t = 0; t < PF; ++t)
-            if (g0 + t * TILE < nv_max) score_tile(g0 + t * TILE, cur[t]);
-    };
-    if (nv_max > 0) {
+            if (l1 + t < ntl) load_b(tile_c0(l1 + t), nxt[t]);
 #pragma unroll
-        for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
-    }
-    for (int g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
-        group(g0, bq0, bq1);
-        if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
+        for (int t = 0; t < PF; ++t)
+            if (l0 + t < ntl) score_tile(tile_c0(l0 + t), cur[t]);
+    };
+#pragma unroll
+    for (int t = 0; t < PF; ++t)
+        if (t < ntl) load_b(tile_c0(t), bq0[t]);
+    for (int l0 = 0; l0 < ntl; l0 += 2 * PF) {
+        group(l0, bq0, bq1);
+        if (l0 + PF < ntl) group(l0 + PF, bq1, bq0);
     }
     kmax2 = wave_max_f(kmax2);
-    wave_lds_sync();
+    if (coop) {
+        // every wave's keys complete; largest ||k||^2 over the workgroup's tiles
+        // (each wave's hist slot 0 carries it across; read before any wave
+        // reuses its hist)
+        if (lane == 0) hist[0] = __float_as_uint(kmax2);
+        __syncthreads();
+        float km = 0.f;
+        for (int w = 0; w < WAVES; ++w)
+            km = fmaxf(km, __uint_as_float(*reinterpret_cast<const uint32_t*>(smem + (size_t)w * p.wave_stride +
+                                                                             4ull * qpw * np)));
+        kmax2 = km;
+        __syncthreads();
+    } else {
+        wave_lds_sync();
+    }
 
     if constexpr (SAMPLE) {
         // largest ||k||^2 of the sequence (every entry, not only the sampled ones)

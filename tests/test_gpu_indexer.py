@@ -64,6 +64,17 @@ def test_head_counts(Hi, d_idx):
     run_case(inp, what=f"Hi={Hi} d_idx={d_idx}")
 
 
+def test_dense_two_row_tiles_per_wave():
+    # 32768 query rows: the dense plan gives each wave 8 queries (two row
+    # tiles of 4 queries x 4 heads), the per-wave scoring path; smaller row
+    # counts give one row tile per wave and the workgroup-cooperative path
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=21, B=16)
+    B, T = inp["qI"].shape[:2]
+    rows = [(b, i) for b in range(B) for i in range(b % 7, T, 37)] + [(b, T - 1) for b in range(B)]
+    run_case(inp, rows=rows, what="two row tiles per wave")
+
+
 def test_fp32_small_ragged():
     lib()
     inp = synth.make_inputs("tiny_fp32", seed=11, T=203, k=5, W=9, m_hca=8)
