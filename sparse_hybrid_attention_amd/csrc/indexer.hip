@@ -157,7 +157,7 @@ __device__ __forceinline__ uint32_t key_at(const uint4& v, int j) {
 // `pmask`), and the result is the want-th largest key inside it.  When that is
 // the bucket's largest (want == 1) or smallest (want == bucket size) key, one
 // min/max scan ends the search.
-__device__ __noinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int kk, uint32_t* hist, int* n_gt) {
     const int lane = __lane_id();
     uint32_t andv = 0xFFFFFFFFu, orv = 0u;
     for (int base = 0; base < cnt; base += 256) {
@@ -399,7 +399,7 @@ __device__ void exact_scores(const T* __restrict__ qrow /* [HI][DI] */, const T*
 // entry order) and output of its idx row: the kept entries are written in
 // buffer order, then -1 up to k.
 template <typename T, int HI, int DI, class Ids>
-__device__ __noinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_eff, int k, float delta, int mcap,
+__device__ __forceinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_eff, int k, float delta, int mcap,
                              const T* __restrict__ qrow, const T* __restrict__ kI_b,
                              const float* __restrict__ wrow, int32_t* __restrict__ out_row) {
     const int lane = __lane_id();
@@ -449,14 +449,16 @@ __device__ __noinline__ void final_select(WaveBuf& wb, Ids ids, int cnt, int k_e
                 wave_lds_sync();
             }
             // rank within M by (exact desc, index asc); keep the first `need`
+            // (with positions as entries, the band list itself holds them)
+            const int32_t* rid = std::is_same<Ids, PosIds>::value ? wb.mpos : wb.mid;
             for (int j = lane; j < nM; j += 64) {
                 int rank = 0;
                 if (nM > need) {
                     const double ex = wb.mex[j];
-                    const int id = wb.mid[j];
+                    const int id = rid[j];
                     for (int y = 0; y < nM; ++y) {
                         const double ey = wb.mex[y];
-                        rank += (ey > ex) || (ey == ex && wb.mid[y] < id);
+                        rank += (ey > ex) || (ey == ex && rid[y] < id);
                     }
                 }
                 wb.keys[wb.mpos[j]] = rank < need ? 0xFFFFFFFFu : 0u;
@@ -1039,83 +1041,10 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         const int i = q0 + qw;
         if (i >= p.Tq) break;
         const long long row = (long long)b * p.Tq + i;
-        int32_t* out_row = p.idx + row * p.k;
         const int n = (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N);
-        const int k_eff = min(p.k, n);
-        uint32_t* keys = keys_all + qw * np;
-        uint32_t hi = 0u;  // entries with key > hi are kept
-        if (n > k_eff) {
-            const float delta = p.err_c * qn[qw] * kmax;
-            int n_gt;
-            const uint32_t kth = radix_kth(keys, n, k_eff, hist, &n_gt);
-            const float Tf = key_f(kth);
-            hi = fkey(Tf + 2.0f * delta);
-            const uint32_t lo = fkey(Tf - 2.0f * delta);
-            int nD = 0, nM = 0;
-            for (int base0 = 0; base0 < n; base0 += 64) {
-                const int e = base0 + lane;
-                const uint32_t key = e < n ? keys[e] : 0u;
-                const bool inD = e < n && key > hi;
-                const bool inM = e < n && key >= lo && key <= hi;
-                const unsigned long long mm = __ballot(inM);
-                if (inM) {
-                    const int pos = nM + __popcll(mm & lanemask_lt());
-                    if (pos < mcap) mpos[pos] = e;
-                }
-                nD += __popcll(__ballot(inD));
-                nM += __popcll(mm);
-            }
-            wave_lds_sync();
-            const int need = k_eff - nD;
-            if (nM <= mcap) {
-                // a band of exactly `need` entries is kept whole: no re-scoring
-                if (nM > need) {
-                    exact_scores<T, HI, DI>(qI + row * HI * DI, kI_b, p.w + row * HI, PosIds{}, mpos, nM, mex, nullptr);
-                    wave_lds_sync();
-                }
-                for (int j = lane; j < nM; j += 64) {
-                    const int id = mpos[j];
-                    int rank = 0;
-                    if (nM > need) {
-                        const double ex = mex[j];
-                        for (int y = 0; y < nM; ++y) {
-                            const double ey = mex[y];
-                            rank += (ey > ex) || (ey == ex && mpos[y] < id);
-                        }
-                    }
-                    keys[id] = rank < need ? 0xFFFFFFFFu : 0u;
-                }
-            } else {
-                // band larger than the band list: decide on float32 keys (index tie-break)
-                int eq_seen = 0;
-                for (int base0 = 0; base0 < n; base0 += 64) {
-                    const int e = base0 + lane;
-                    const uint32_t key = e < n ? keys[e] : 0u;
-                    const bool inM = e < n && key >= lo && key <= hi;
-                    const unsigned long long meq = __ballot(inM && key == kth);
-                    const bool keq = inM && key == kth && eq_seen + __popcll(meq & lanemask_lt()) < k_eff - n_gt;
-                    if (inM) keys[e] = (key > kth || keq) ? 0xFFFFFFFFu : 0u;
-                    eq_seen += __popcll(meq);
-                }
-            }
-            wave_lds_sync();
-            if (hi == 0xFFFFFFFFu) hi = 0xFFFFFFFEu;
-        } else {
-            hi = 0u;   // keep every visible entry (keys are never 0 for finite scores)
-            for (int e = lane; e < n; e += 64) keys[e] = 0xFFFFFFFFu;
-            wave_lds_sync();
-        }
-        // ascending entry order: stable pass over the visible entries
-        int out = 0;
-        for (int base0 = 0; base0 < n; base0 += 64) {
-            const int e = base0 + lane;
-            const bool keep = e < n && keys[e] > hi;
-            const unsigned long long msk = __ballot(keep);
-            if (keep) out_row[out + __popcll(msk & lanemask_lt())] = e;
-            out += __popcll(msk);
-        }
-        for (int j = out + lane; j < p.k; j += 64) out_row[j] = -1;
-        wave_lds_sync();
+        WaveBuf q{keys_all + qw * np, nullptr, hist, mpos, mex, nullptr};
+        final_select<T, HI, DI>(q, PosIds{}, n, min(p.k, n), p.k, p.err_c * qn[qw] * kmax, mcap, qI + row * HI * DI,
+                                kI_b, p.w + row * HI, p.idx + row * p.k);
     }
 }
 
