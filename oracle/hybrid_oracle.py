@@ -42,6 +42,13 @@ Readings taken where the pages are silent (each repeated at its function):
   R6  out = g[h,0]*O_HCA + g[h,1]*O_CSA + g[h,2]*O_SWA with the per-head gates
       as given (no renormalisation); an absent branch contributes nothing.
   R7  KV head of query head h is h // (H // Hkv).
+  R8  Decode cache maintenance: the raw window is a ring of W rows per
+      sequence, the token at position t in slot t % W.  When that token
+      completes a block of ratio m ((t + 1) % m == 0), entry c = (t+1)/m - 1
+      is the block compression of positions [c*m, (c+1)*m) (needs m <= W, so
+      the ring still holds the whole block).  Indexer keys of CSA entries are
+      the same compression of per-token indexer keys with their own logits.
+      An entry at or beyond a cache's capacity is not stored.
 """
 from __future__ import annotations
 
@@ -60,6 +67,7 @@ __all__ = [
     "indexer_scores", "select_topk", "index_topk", "index_topk_row",
     "attend", "attn_row", "hybrid_attn_fwd",
     "score_key_order",
+    "cache_append",
 ]
 
 
@@ -342,3 +350,49 @@ def hybrid_attn_fwd(q, k_raw, v_raw, gates, *, W, dtype, q_pos0=0, raw_pos0=0,
     if branches:
         return stored, per_branch
     return stored
+
+
+# --------------------------------------------------------------------------
+# Decode cache maintenance ([V4-blog] "1. hybrid attn", the paragraph on the
+# separate caches: the raw window K/V ages out as decode advances, the
+# compressed entries live as long as the sequence).  Reading R8.
+# --------------------------------------------------------------------------
+def cache_append(pos, k_new, v_new, k_ring, v_ring, *, W: int, dtype: int, branches=(),
+                 kI_new=None, kI_ring=None, kI_branch=None) -> int:
+    """Append one token per sequence; update rings and caches in place.
+
+    pos[b]: position of sequence b's new token.  k_new, v_new: [B, Hkv, d]
+    and k_ring, v_ring: [B, W, Hkv, d] in the storage dtype.  branches: tuples
+    (m, zk, zv, kc, vc) with logits [m, Hkv, d] and caches [B, cap, Hkv, d].
+    kI_new [B, d_idx], kI_ring [B, W, d_idx] and kI_branch = (m, zI, kIc) with
+    zI [m, d_idx], kIc [B, cap, d_idx] maintain the indexer keys the same way.
+    Returns the number of (sequence, cache) entries not stored (capacity).
+    """
+    dropped = 0
+    B = len(pos)
+    for b in range(B):
+        t = int(pos[b])
+        s = t % W
+        k_ring[b, s] = k_new[b]
+        v_ring[b, s] = v_new[b]
+        if kI_ring is not None:
+            kI_ring[b, s] = kI_new[b]
+        jobs = [(m, ((zk, k_ring, kc), (zv, v_ring, vc))) for (m, zk, zv, kc, vc) in branches]
+        if kI_branch is not None:
+            m, zI, kIc = kI_branch
+            jobs.append((m, ((np.asarray(zI)[:, None, :], kI_ring[:, :, None, :], kIc[:, :, None, :]),)))
+        for m, parts in jobs:
+            if m > W:
+                raise ValueError("block ratio larger than the ring")
+            if (t + 1) % m != 0:
+                continue
+            c = (t + 1) // m - 1
+            if c >= parts[0][2].shape[1]:
+                dropped += 1
+                continue
+            slots = [p % W for p in range(c * m, c * m + m)]
+            for z, ring, cache in parts:
+                x = to_f64(ring[b, slots], dtype)[None]           # [1, m, Hkv, ch]
+                cache[b, c] = to_storage(compress(x, z, m)[0, 0], dtype)
+    return dropped
+

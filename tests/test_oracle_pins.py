@@ -364,3 +364,111 @@ def test_decode_query_sees_all_cache_entries():
     assert O.visible_count(t, cfg["W"], cfg["m_hca"], cfg["N_hca"]) == 8192
     lo, hi = O.window_bounds(t, cfg["W"])
     assert lo == cfg["N_csa"] * cfg["m_csa"] and hi - lo == cfg["W"]
+
+
+# ------------------------------------------------- decode cache maintenance
+def _append_run(streams, starts, *, W, m_pairs, dtype, cap=None, seed=0):
+    """Append the token streams (each [T_b, Hkv, d] plus indexer keys) in
+    lockstep, sequence b starting at position starts[b] from a state that
+    already holds its first starts[b] tokens.  Returns rings, caches, drops."""
+    rng = np.random.default_rng(seed)
+    B = len(streams)
+    ks, vs, kis = zip(*streams)
+    Hkv, d = ks[0].shape[1:]
+    d_idx = kis[0].shape[1]
+    T = max(len(x) for x in ks)
+    st = lambda a: O.to_storage(a, dtype)
+    k_ring = np.zeros((B, W, Hkv, d), dtype=st(np.zeros(1)).dtype)
+    v_ring = np.zeros_like(k_ring)
+    kI_ring = np.zeros((B, W, d_idx), dtype=k_ring.dtype)
+    branches, zs = [], []
+    for m in m_pairs:
+        n = cap if cap is not None else T // m
+        zk, zv = rng.standard_normal((m, Hkv, d)), rng.standard_normal((m, Hkv, d))
+        branches.append((m, zk, zv, np.zeros((B, n, Hkv, d), k_ring.dtype), np.zeros((B, n, Hkv, d), k_ring.dtype)))
+    m0 = m_pairs[0]
+    zI = rng.standard_normal((m0, d_idx))
+    kIc = np.zeros((B, branches[0][3].shape[1], d_idx), k_ring.dtype)
+    # state before the first append: ring rows and complete entries of the prefix
+    for b in range(B):
+        p0 = starts[b]
+        for t in range(max(0, p0 - W), p0):
+            k_ring[b, t % W], v_ring[b, t % W], kI_ring[b, t % W] = st(ks[b][t]), st(vs[b][t]), st(kis[b][t])
+        for (m, zk, zv, kc, vc) in branches:
+            n_pre = min(p0 // m, kc.shape[1])
+            kc[b, :n_pre] = O.to_storage(O.compress(ks[b][None, :p0], zk, m)[0], dtype)[:n_pre]
+            vc[b, :n_pre] = O.to_storage(O.compress(vs[b][None, :p0], zv, m)[0], dtype)[:n_pre]
+        n_pre = min(p0 // m0, kIc.shape[1])
+        kIc[b, :n_pre] = O.to_storage(O.compress(kis[b][None, :p0, None, :], zI[:, None, :], m0)[0, :, 0], dtype)[:n_pre]
+    dropped = 0
+    steps = min(len(ks[b]) - starts[b] for b in range(B))
+    for s in range(steps):
+        pos = [starts[b] + s for b in range(B)]
+        kn = np.stack([st(ks[b][pos[b]]) for b in range(B)])
+        vn = np.stack([st(vs[b][pos[b]]) for b in range(B)])
+        kin = np.stack([st(kis[b][pos[b]]) for b in range(B)])
+        dropped += O.cache_append(pos, kn, vn, k_ring, v_ring, W=W, dtype=dtype, branches=branches,
+                                  kI_new=kin, kI_ring=kI_ring, kI_branch=(m0, zI, kIc))
+    return k_ring, v_ring, kI_ring, branches, (m0, zI, kIc), dropped, steps
+
+
+def _tokens(rng, T, Hkv, d, d_idx, dtype):
+    # values exactly representable in the storage dtype
+    rt = lambda a: O.to_f64(O.to_storage(a, dtype), dtype)
+    return (rt(rng.standard_normal((T, Hkv, d))), rt(rng.standard_normal((T, Hkv, d))),
+            rt(rng.standard_normal((T, d_idx))))
+
+
+def test_cache_append_m1_stores_each_token_and_ring_keeps_last_w():
+    # ratio 1: every token completes its own block, entry c is token c itself
+    rng = np.random.default_rng(3)
+    dt, W, T = O.DTYPE_BF16, 5, 23
+    s0 = _tokens(rng, T, 2, 4, 3, dt)
+    k_ring, v_ring, kI_ring, br, kib, dropped, steps = _append_run([s0], [0], W=W, m_pairs=[1], dtype=dt)
+    assert dropped == 0 and steps == T
+    _, _, _, kc, vc = br[0]
+    assert np.array_equal(kc[0], O.to_storage(s0[0], dt))
+    assert np.array_equal(vc[0], O.to_storage(s0[1], dt))
+    assert np.array_equal(kib[2][0], O.to_storage(s0[2], dt))
+    for t in range(T - W, T):            # brute force: slot of each of the last W tokens
+        assert np.array_equal(k_ring[0, t % W], O.to_storage(s0[0][t], dt))
+        assert np.array_equal(kI_ring[0, t % W], O.to_storage(s0[2][t], dt))
+
+
+@pytest.mark.parametrize("dtype", [O.DTYPE_BF16, O.DTYPE_F32])
+def test_cache_append_reproduces_full_sequence_compression(dtype):
+    # two sequences at different positions (the second resumes at 37 from the
+    # state its first 37 tokens leave); token-by-token appends must end with
+    # the caches that compressing each whole sequence at once gives
+    rng = np.random.default_rng(4)
+    W, m_csa, m_hca = 16, 4, 16
+    sa = _tokens(rng, 70, 2, 4, 3, dtype)
+    sb = _tokens(rng, 107, 2, 4, 3, dtype)
+    k_ring, v_ring, kI_ring, br, kib, dropped, steps = _append_run(
+        [sa, sb], [0, 37], W=W, m_pairs=[m_csa, m_hca], dtype=dtype)
+    assert dropped == 0 and steps == 70
+    for b, (s, end) in enumerate([(sa, 70), (sb, 107)]):
+        for (m, zk, zv, kc, vc) in br:
+            n = end // m
+            assert np.array_equal(kc[b, :n], O.to_storage(O.compress(s[0][None, :end], zk, m)[0], dtype))
+            assert np.array_equal(vc[b, :n], O.to_storage(O.compress(s[1][None, :end], zv, m)[0], dtype))
+            assert not np.any(kc[b, n:])          # entries of incomplete blocks stay unwritten
+        m0, zI, kIc = kib
+        n = end // m0
+        want = O.compress(s[2][None, :end, None, :], zI[:, None, :], m0)[0, :, 0]
+        assert np.array_equal(kIc[b, :n], O.to_storage(want, dtype))
+        for t in range(end - W, end):
+            assert np.array_equal(v_ring[b, t % W], O.to_storage(s[1][t], dtype))
+
+
+def test_cache_append_capacity_drops_late_entries():
+    rng = np.random.default_rng(5)
+    dt = O.DTYPE_F32
+    s0 = _tokens(rng, 41, 1, 4, 2, dt)
+    _, _, _, br, kib, dropped, _ = _append_run([s0], [0], W=8, m_pairs=[4, 8], dtype=dt, cap=3)
+    # 10 ratio-4 blocks and 5 ratio-8 blocks complete; 3 of each fit.  The
+    # ratio-4 K/V cache, the ratio-8 K/V cache and the indexer-key cache each
+    # count their own entries that do not fit
+    assert dropped == (10 - 3) + (5 - 3) + (10 - 3)
+    (m, zk, _, kc, _) = br[0]
+    assert np.array_equal(kc[0], O.to_storage(O.compress(s0[0][None, :12], zk, 4)[0], dt))
