@@ -188,6 +188,71 @@ SHATTN_API size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
 SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Decode cache maintenance, one new token per sequence ([V4-blog] "1. hybrid
+ * attn": the raw window K/V and the compressed caches are kept apart; the raw
+ * rows age out as decode advances, the compressed entries stay; the block
+ * merge of [V4-code] section 1 as in hca_compress_kv).
+ *
+ * For each sequence b whose new token has absolute position t = pos[b] >= 0:
+ *   - ring row t % W of k_ring / v_ring (and kI_ring) takes k_new[b] /
+ *     v_new[b] (and kI_new[b]);
+ *   - for each present ratio m (m_csa, m_hca) with (t + 1) % m == 0, entry
+ *     c = (t + 1) / m - 1 of that ratio's K and V caches becomes the block
+ *     compression of positions [c*m, (c+1)*m) with that ratio's logits: the
+ *     first m - 1 rows from the ring (written by earlier calls), the last from
+ *     k_new / v_new.  With d_idx > 0 the CSA entry's indexer key is the same
+ *     compression of the per-token indexer keys with logits zI.
+ *   - An entry with c >= its cache's capacity is not written; for each such
+ *     (sequence, cache) -- the K/V pair of a ratio counts once, the
+ *     indexer-key cache once -- *dropped grows by 1 (when dropped != NULL).
+ * A sequence with pos[b] < 0 is left untouched (inactive batch slot).  The
+ * caller advances pos between calls; calls for one sequence must be issued
+ * in position order on one stream (each reads ring rows the earlier ones
+ * wrote).  Rows of the ring older than t - W + 1 are overwritten.
+ *
+ *   pos            : [B] int64, DEVICE memory, 8-byte aligned
+ *   k_new, v_new   : [B, Hkv, d]           dtype
+ *   k_ring, v_ring : [B, W, Hkv, d]        dtype, row t % W written
+ *   zk_*, zv_*     : [m, Hkv, d]           float32 logits of each ratio
+ *   k_csa, v_csa   : [B, cap_csa, Hkv, d]  dtype;  k_hca, v_hca: [B, cap_hca, Hkv, d]
+ *   kI_new         : [B, d_idx]; kI_ring: [B, W, d_idx]; kI_csa: [B, cap_csa, d_idx]
+ *   zI             : [m_csa, d_idx]        float32
+ *   dropped        : int32 counter in DEVICE memory (incremented atomically), or NULL
+ * Supported: d in {64, 128}; d_idx in {0, 64, 128} (d_idx > 0 needs m_csa > 0);
+ *            0 <= m_csa, m_hca <= min(W, 1024) (0 = no cache of that ratio);
+ *            B <= 65535.
+ */
+typedef struct shattn_append_args {
+    int32_t struct_size;   /* must equal sizeof(shattn_append_args) */
+    int32_t dtype;
+    int32_t B, Hkv, d, W;
+    int32_t m_csa, m_hca, d_idx;
+    int32_t reserved0;     /* must be 0 */
+    const int64_t* pos;
+    const void* k_new;
+    const void* v_new;
+    void* k_ring;
+    void* v_ring;
+    const float* zk_csa;
+    const float* zv_csa;
+    void* k_csa;
+    void* v_csa;
+    int64_t cap_csa;
+    const float* zk_hca;
+    const float* zv_hca;
+    void* k_hca;
+    void* v_hca;
+    int64_t cap_hca;
+    const void* kI_new;
+    void* kI_ring;
+    const float* zI;
+    void* kI_csa;
+    int32_t* dropped;
+} shattn_append_args;
+
+SHATTN_API int hybrid_cache_append(const shattn_append_args* a, void* stream);
+
+/*
  * Measurement aid (not part of the attention path): launches `workgroups`
  * workgroups of 256 threads; every wave issues `iters` rounds of independent
  * bf16 MFMAs: shape 0 = 8 x v_mfma_f32_16x16x32_bf16 per round, shape 1 =

@@ -367,11 +367,14 @@ def cache_append(pos, k_new, v_new, k_ring, v_ring, *, W: int, dtype: int, branc
     kI_new [B, d_idx], kI_ring [B, W, d_idx] and kI_branch = (m, zI, kIc) with
     zI [m, d_idx], kIc [B, cap, d_idx] maintain the indexer keys the same way.
     Returns the number of (sequence, cache) entries not stored (capacity).
+    A sequence with pos[b] < 0 (an inactive batch slot) is left untouched.
     """
     dropped = 0
     B = len(pos)
     for b in range(B):
         t = int(pos[b])
+        if t < 0:
+            continue
         s = t % W
         k_ring[b, s] = k_new[b]
         v_ring[b, s] = v_new[b]

@@ -33,6 +33,7 @@ EXPORTED = (
     "csa_index_topk",
     "hybrid_sparse_attn_fwd_workspace_size",
     "hybrid_sparse_attn_fwd",
+    "hybrid_cache_append",
     "shattn_mfma_peak_probe",
     "shattn_last_error",
 )
@@ -74,6 +75,29 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    """Mirror of shattn_append_args (same field order; C alignment rules)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("m_csa", ctypes.c_int32), ("m_hca", ctypes.c_int32), ("d_idx", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("pos", ctypes.c_void_p),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p),
+        ("zk_csa", ctypes.c_void_p), ("zv_csa", ctypes.c_void_p),
+        ("k_csa", ctypes.c_void_p), ("v_csa", ctypes.c_void_p),
+        ("cap_csa", ctypes.c_int64),
+        ("zk_hca", ctypes.c_void_p), ("zv_hca", ctypes.c_void_p),
+        ("k_hca", ctypes.c_void_p), ("v_hca", ctypes.c_void_p),
+        ("cap_hca", ctypes.c_int64),
+        ("kI_new", ctypes.c_void_p), ("kI_ring", ctypes.c_void_p),
+        ("zI", ctypes.c_void_p), ("kI_csa", ctypes.c_void_p),
+        ("dropped", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -104,6 +128,8 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_sparse_attn_fwd_workspace_size.restype = sz
         lib.hybrid_sparse_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp, sz, vp]
         lib.hybrid_sparse_attn_fwd.restype = i32
+        lib.hybrid_cache_append.argtypes = [ctypes.POINTER(AppendArgs), vp]
+        lib.hybrid_cache_append.restype = i32
         lib.shattn_mfma_peak_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.shattn_mfma_peak_probe.restype = i32
         lib.shattn_last_error.argtypes = []
@@ -271,6 +297,73 @@ def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, h
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.hybrid_sparse_attn_fwd(ctypes.byref(a), _ptr(ws), ws_bytes, _stream(q)))
     return out
+
+
+def make_append_args(pos, k_new, v_new, k_ring, v_ring, *, csa=None, hca=None, indexer=None, dropped=None):
+    """Argument struct of hybrid_cache_append (tensors are checked here, the
+    library checks the rest).  csa / hca: (m, zk, zv, k_cache, v_cache);
+    indexer: (kI_new, kI_ring, zI, kI_cache) with the CSA ratio."""
+    _need(k_new, "k_new")
+    dev = k_new.device
+    _need(pos, "pos", torch.int64, dev)
+    for t, n in ((v_new, "v_new"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _need(t, n, k_new.dtype, dev)
+    B, Hkv, d = k_new.shape
+    W = k_ring.shape[1]
+    if tuple(pos.shape) != (B,) or v_new.shape != k_new.shape or tuple(k_ring.shape) != (B, W, Hkv, d) \
+            or k_ring.shape != v_ring.shape:
+        raise ValueError("cache_append: pos / new rows / ring shapes disagree")
+    a = AppendArgs()
+    a.struct_size = ctypes.sizeof(AppendArgs)
+    a.dtype = _dtype_code(k_new)
+    a.B, a.Hkv, a.d, a.W = B, Hkv, d, W
+    a.pos = pos.data_ptr()
+    a.k_new, a.v_new, a.k_ring, a.v_ring = k_new.data_ptr(), v_new.data_ptr(), k_ring.data_ptr(), v_ring.data_ptr()
+    keep = [pos, k_new, v_new, k_ring, v_ring]
+    for name, br in (("csa", csa), ("hca", hca)):
+        if br is None:
+            continue
+        m, zk, zv, kc, vc = br
+        _need(zk, f"zk_{name}", torch.float32, dev)
+        _need(zv, f"zv_{name}", torch.float32, dev)
+        _need(kc, f"k_{name}", k_new.dtype, dev)
+        _need(vc, f"v_{name}", k_new.dtype, dev)
+        if tuple(zk.shape) != (m, Hkv, d) or zk.shape != zv.shape or kc.shape != vc.shape \
+                or kc.shape[0] != B or tuple(kc.shape[2:]) != (Hkv, d):
+            raise ValueError(f"cache_append: {name} logits / cache shapes disagree")
+        setattr(a, f"m_{name}", m)
+        setattr(a, f"zk_{name}", zk.data_ptr())
+        setattr(a, f"zv_{name}", zv.data_ptr())
+        setattr(a, f"k_{name}", kc.data_ptr())
+        setattr(a, f"v_{name}", vc.data_ptr())
+        setattr(a, f"cap_{name}", kc.shape[1])
+        keep += [zk, zv, kc, vc]
+    if indexer is not None:
+        kin, kir, zI, kic = indexer
+        _need(kin, "kI_new", k_new.dtype, dev)
+        _need(kir, "kI_ring", k_new.dtype, dev)
+        _need(zI, "zI", torch.float32, dev)
+        _need(kic, "kI_csa", k_new.dtype, dev)
+        d_idx = kin.shape[1]
+        if csa is None or tuple(kin.shape) != (B, d_idx) or tuple(kir.shape) != (B, W, d_idx) \
+                or tuple(zI.shape) != (csa[0], d_idx) or tuple(kic.shape) != (B, csa[3].shape[1], d_idx):
+            raise ValueError("cache_append: indexer-key shapes disagree (or no CSA ratio)")
+        a.d_idx = d_idx
+        a.kI_new, a.kI_ring, a.zI, a.kI_csa = kin.data_ptr(), kir.data_ptr(), zI.data_ptr(), kic.data_ptr()
+        keep += [kin, kir, zI, kic]
+    if dropped is not None:
+        _need(dropped, "dropped", torch.int32, dev)
+        a.dropped = dropped.data_ptr()
+        keep.append(dropped)
+    return a, keep
+
+
+def cache_append(pos, k_new, v_new, k_ring, v_ring, *, csa=None, hca=None, indexer=None, dropped=None):
+    """One decode step of cache maintenance (rings and caches updated in place)."""
+    lib = load_library()
+    a, _keep = make_append_args(pos, k_new, v_new, k_ring, v_ring, csa=csa, hca=hca, indexer=indexer,
+                                dropped=dropped)
+    _check(lib.hybrid_cache_append(ctypes.byref(a), _stream(k_new)))
 
 
 def default_scale(d: int) -> float:

@@ -144,6 +144,35 @@ def make_decode(cfg: dict, seed: int = 0) -> dict:
     return out
 
 
+def make_append(*, B, Hkv, d, W, m_csa, m_hca, d_idx, cap_csa, cap_hca, steps, dtype=DTYPE_BF16,
+                zero_state=False, seed: int = 0) -> dict:
+    """Decode cache-maintenance inputs.  Draw order: ring K, ring V, ring kI,
+    Zk_csa, Zv_csa, Zk_hca, Zv_hca, Z_I, cache K/V (CSA, HCA), cache kI, new K,
+    new V, new kI.  The state is random (so a stray write shows) unless
+    zero_state; new rows are [steps, B, ...]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(B=B, Hkv=Hkv, d=d, W=W, m_csa=m_csa, m_hca=m_hca, d_idx=d_idx, dtype=dtype)
+    st = (lambda shape: np.zeros(shape, np.uint16 if dtype == DTYPE_BF16 else np.float32)) if zero_state \
+        else (lambda shape: _normal(rng, shape, dtype))
+    out["k_ring"] = st((B, W, Hkv, d))
+    out["v_ring"] = st((B, W, Hkv, d))
+    out["kI_ring"] = st((B, W, d_idx))
+    out["zk_csa"] = rng.standard_normal(size=(m_csa, Hkv, d), dtype=np.float32)
+    out["zv_csa"] = rng.standard_normal(size=(m_csa, Hkv, d), dtype=np.float32)
+    out["zk_hca"] = rng.standard_normal(size=(m_hca, Hkv, d), dtype=np.float32)
+    out["zv_hca"] = rng.standard_normal(size=(m_hca, Hkv, d), dtype=np.float32)
+    out["zI"] = rng.standard_normal(size=(m_csa, d_idx), dtype=np.float32)
+    out["k_csa"] = st((B, cap_csa, Hkv, d))
+    out["v_csa"] = st((B, cap_csa, Hkv, d))
+    out["k_hca"] = st((B, cap_hca, Hkv, d))
+    out["v_hca"] = st((B, cap_hca, Hkv, d))
+    out["kI_csa"] = st((B, cap_csa, d_idx))
+    out["k_new"] = _normal(rng, (steps, B, Hkv, d), dtype)
+    out["v_new"] = _normal(rng, (steps, B, Hkv, d), dtype)
+    out["kI_new"] = _normal(rng, (steps, B, d_idx), dtype)
+    return out
+
+
 def make_inputs(name: str, seed: int = 0, **overrides) -> dict:
     cfg = config(name, **overrides)
     if cfg["kind"] == "decode":

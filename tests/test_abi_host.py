@@ -53,22 +53,24 @@ def test_no_unresolved_library_symbols(lib):
     assert not [l for l in out.splitlines() if "shattn" in l]
 
 
-def test_struct_layout_matches_c(lib, tmp_path):
-    fields = [f for f, _ in binding.FwdArgs._fields_]
+@pytest.mark.parametrize("cls,cname", [(binding.FwdArgs, "shattn_fwd_args"),
+                                       (binding.AppendArgs, "shattn_append_args")])
+def test_struct_layout_matches_c(lib, tmp_path, cls, cname):
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "\n".join(f'printf("{f} %zu\\n", offsetof(shattn_fwd_args, {f}));' for f in fields)
+    body = "\n".join(f'printf("{f} %zu\\n", offsetof({cname}, {f}));' for f in fields)
     src.write_text(f"""#include <stdio.h>
 #include <stddef.h>
 #include "hybrid_attn.h"
-int main(void) {{ printf("size %zu\\n", sizeof(shattn_fwd_args)); {body} return 0; }}
+int main(void) {{ printf("size %zu\\n", sizeof({cname})); {body} return 0; }}
 """)
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
                    check=True)
     out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
-    assert int(out["size"]) == ctypes.sizeof(binding.FwdArgs)
+    assert int(out["size"]) == ctypes.sizeof(cls)
     for f in fields:
-        assert int(out[f]) == getattr(binding.FwdArgs, f).offset, f
+        assert int(out[f]) == getattr(cls, f).offset, f
 
 
 def err(lib):
@@ -166,6 +168,47 @@ def test_attention_errors(lib):
     assert lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)) > 0
     assert f(ctypes.byref(a), None, 0, None) == binding.SHATTN_EWORKSPACE
     # empty problem is a no-op
+    assert call(B=0) == binding.SHATTN_OK
+
+
+def append(**kw):
+    a = binding.AppendArgs()
+    a.struct_size = ctypes.sizeof(binding.AppendArgs)
+    a.dtype = binding.DTYPE_BF16
+    a.B, a.Hkv, a.d, a.W = 16, 1, 128, 128
+    a.m_csa, a.m_hca, a.d_idx = 4, 128, 64
+    for f in ("pos", "k_new", "v_new", "k_ring", "v_ring", "zk_csa", "zv_csa", "k_csa", "v_csa", "zk_hca",
+              "zv_hca", "k_hca", "v_hca", "kI_new", "kI_ring", "zI", "kI_csa"):
+        setattr(a, f, P.value)
+    a.cap_csa, a.cap_hca = 1024, 64
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_cache_append_errors(lib):
+    f = lib.hybrid_cache_append
+
+    def call(**kw):
+        return f(ctypes.byref(append(**kw)), None)
+    assert f(None, None) == binding.SHATTN_EINVAL
+    assert call(struct_size=8) == binding.SHATTN_EINVAL
+    assert call(reserved0=1) == binding.SHATTN_EINVAL
+    assert call(dtype=5) == binding.SHATTN_EINVAL
+    assert call(d=96) == binding.SHATTN_EUNSUPPORTED
+    assert call(d_idx=32) == binding.SHATTN_EUNSUPPORTED
+    assert call(m_hca=256) == binding.SHATTN_EUNSUPPORTED      # block longer than the ring
+    assert "W=128" in err(lib)
+    assert call(m_csa=0) == binding.SHATTN_EINVAL              # indexer keys without the CSA ratio
+    assert call(cap_csa=-1) == binding.SHATTN_EINVAL
+    assert call(pos=None) == binding.SHATTN_EINVAL
+    assert call(pos=0x7F0000000004) == binding.SHATTN_EINVAL   # int64 array must be 8-byte aligned
+    assert call(k_ring=0x7F0000000008) == binding.SHATTN_EINVAL
+    assert call(zk_hca=None) == binding.SHATTN_EINVAL
+    assert call(kI_csa=None) == binding.SHATTN_EINVAL
+    assert call(dropped=0x7F0000000002) == binding.SHATTN_EINVAL
+    assert call(B=-1) == binding.SHATTN_EINVAL
+    # an empty batch is a no-op
     assert call(B=0) == binding.SHATTN_OK
 
 
