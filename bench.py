@@ -13,6 +13,7 @@ branches mixed with U(0,1) gates).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -280,13 +281,131 @@ def cpu_baseline(inp, budget_rows):
 
 
 # ------------------------------------------------------------------ main
+APPEND = dict(B=16, Hkv=1, d=128, W=128, m_csa=4, m_hca=128, d_idx=64, pos0=1048576)
+
+
+def append_alg_bytes(c, steps):
+    """Algorithmic HBM bytes of `steps` consecutive appends (positions pos0 ..):
+    per token and sequence the new K, V, kI rows read and written to the ring;
+    per completed block its m - 1 earlier ring rows read and the entry written;
+    each launch reads the logits of the ratios it compresses once."""
+    esz = 2
+    row = (2 * c["Hkv"] * c["d"] + c["d_idx"]) * esz          # K + V + kI of one token
+    kv = 2 * c["Hkv"] * c["d"] * esz
+    total = 0
+    for s in range(steps):
+        t = c["pos0"] + s
+        b = 2 * row                                             # new rows in, ring row out
+        lg = 0
+        if (t + 1) % c["m_csa"] == 0:
+            b += (c["m_csa"] - 1) * row + row                   # earlier rows + entry (K, V, kI)
+            lg += c["m_csa"] * (2 * c["Hkv"] * c["d"] + c["d_idx"]) * 4
+        if (t + 1) % c["m_hca"] == 0:
+            b += (c["m_hca"] - 1) * kv + kv
+            lg += c["m_hca"] * 2 * c["Hkv"] * c["d"] * 4
+        total += c["B"] * b + lg
+    return total
+
+
+def bench_append(args, torch, binding):
+    """Decode cache maintenance at the 1M-context decode shape: one token per
+    sequence per step, positions advancing from pos0 (a steady-state mix of
+    plain appends, CSA completions every 4 tokens, HCA every 128)."""
+    from sparse_hybrid_attention_amd import synth
+    c = APPEND
+    B, Hkv, d, W, d_idx = c["B"], c["Hkv"], c["d"], c["W"], c["d_idx"]
+    steps, warm = max(args.steps, 256), args.warmup
+    nsteps = warm + steps
+    cap_csa = (c["pos0"] + nsteps) // c["m_csa"] + 1
+    cap_hca = (c["pos0"] + nsteps) // c["m_hca"] + 1
+    small = synth.make_append(B=B, Hkv=Hkv, d=d, W=W, m_csa=c["m_csa"], m_hca=c["m_hca"], d_idx=d_idx,
+                              cap_csa=1, cap_hca=1, steps=nsteps, seed=0)
+    dev = "cuda:0"
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    k_ring, v_ring, kI_ring = bf(small["k_ring"]), bf(small["v_ring"]), bf(small["kI_ring"])
+    z = {k: torch.from_numpy(small[k]).to(dev) for k in ("zk_csa", "zv_csa", "zk_hca", "zv_hca", "zI")}
+    k_csa = torch.zeros((B, cap_csa, Hkv, d), dtype=torch.bfloat16, device=dev)
+    v_csa = torch.zeros_like(k_csa)
+    k_hca = torch.zeros((B, cap_hca, Hkv, d), dtype=torch.bfloat16, device=dev)
+    v_hca = torch.zeros_like(k_hca)
+    kI_csa = torch.zeros((B, cap_csa, d_idx), dtype=torch.bfloat16, device=dev)
+    k_new, v_new, kI_new = bf(small["k_new"]), bf(small["v_new"]), bf(small["kI_new"])
+    pos = (torch.arange(nsteps, dtype=torch.int64, device=dev)[:, None] + c["pos0"]).expand(nsteps, B).contiguous()
+    dropped = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib = binding.load_library()
+    argv = []
+    for s in range(nsteps):
+        a, keep = binding.make_append_args(pos[s], k_new[s], v_new[s], k_ring, v_ring,
+                                           csa=(c["m_csa"], z["zk_csa"], z["zv_csa"], k_csa, v_csa),
+                                           hca=(c["m_hca"], z["zk_hca"], z["zv_hca"], k_hca, v_hca),
+                                           indexer=(kI_new[s], kI_ring, z["zI"], kI_csa), dropped=dropped)
+        argv.append((a, keep))
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for s in range(warm):
+        binding._check(lib.hybrid_cache_append(ctypes.byref(argv[s][0]), sp))
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        binding._check(lib.hybrid_cache_append(ctypes.byref(argv[warm + i][0]), sp))
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(dropped.item()) != 0:
+        raise RuntimeError("cache append benchmark dropped entries (capacity too small)")
+    kms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    alg = append_alg_bytes(dict(c, pos0=c["pos0"] + warm), steps) / steps
+    ach = alg / (kms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_limits
+        n_cpu = 512
+        st = synth.make_append(B=B, Hkv=Hkv, d=d, W=W, m_csa=c["m_csa"], m_hca=c["m_hca"], d_idx=d_idx,
+                               cap_csa=n_cpu // c["m_csa"] + 1, cap_hca=n_cpu // c["m_hca"] + 1, steps=n_cpu,
+                               seed=1)
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            for s_ in range(n_cpu):
+                O.cache_append([s_] * B, st["k_new"][s_], st["v_new"][s_], st["k_ring"], st["v_ring"], W=W,
+                               dtype=0, branches=((c["m_csa"], st["zk_csa"], st["zv_csa"], st["k_csa"], st["v_csa"]),
+                                                  (c["m_hca"], st["zk_hca"], st["zv_hca"], st["k_hca"], st["v_hca"])),
+                               kI_new=st["kI_new"][s_], kI_ring=st["kI_ring"], kI_branch=(c["m_csa"], st["zI"], st["kI_csa"]))
+            dt_cpu = time.perf_counter() - t1
+        cpu = {"value": round(B * n_cpu / dt_cpu, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_cpu} consecutive appends of the {B} sequences from position 0 (same mix of block "
+                         f"completions; the oracle's cost does not depend on the position); float64 NumPy, one "
+                         f"thread; {dt_cpu:.1f} s"}
+    line = {
+        "metric": "decode cache append tokens/s (ring write + block compression)",
+        "value": round(B * steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall * 1e3 / steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws, resident in HBM)",
+        "config": {"workload": f"decode cache append, B{B} sequences x 1 token per step at positions from "
+                               f"{c['pos0']}, Hkv{Hkv} d{d} bf16, W{W}, CSA m{c['m_csa']} (+ indexer keys "
+                               f"d_idx {d_idx}), HCA m{c['m_hca']}", "name": "decode_append",
+                   "gpu_ms_per_launch_events": round(kms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 6), "kernel": "cache_append", "traffic": None,
+                     "alg_bytes_per_launch": round(alg, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyr2_bf16",
-                    help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m")
+                    help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m, "
+                         "decode_append (cache maintenance)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -324,6 +443,9 @@ def main():
 
     from sparse_hybrid_attention_amd import binding
     binding.load_library()
+    if args.workload == "decode_append":
+        bench_append(args, torch, binding)
+        return
     log(f"[bench] building inputs for {args.workload}")
     inp = build_inputs(args.workload, gates=args.gates)
     cfg = inp["cfg"]
