@@ -49,6 +49,10 @@ Readings taken where the pages are silent (each repeated at its function):
       the ring still holds the whole block).  Indexer keys of CSA entries are
       the same compression of per-token indexer keys with their own logits.
       An entry at or beyond a cache's capacity is not stored.
+  R9  Per-token gates ([Tiny-R2] 3.2 diagram: branch_gate = Linear + Softmax
+      before the weighted sum): gates may be given per (token, head) as
+      weights, or as logits whose softmax over the three branches (in the
+      order [HCA, CSA, SWA], all three, present or not) gives the weights.
 """
 from __future__ import annotations
 
@@ -67,6 +71,7 @@ __all__ = [
     "indexer_scores", "select_topk", "index_topk", "index_topk_row",
     "attend", "attn_row", "hybrid_attn_fwd",
     "score_key_order",
+    "gate_weights",
     "cache_append",
 ]
 
@@ -294,13 +299,32 @@ def attn_row(q_row, t, *, W, raw_pos0, k_raw_b, v_raw_b, scale,
     return res
 
 
+def gate_weights(gates, gate_mode: int, b: int, i: int) -> np.ndarray:
+    """[H, 3] float64 gate weights of query row (b, i) (readings R6, R9).
+
+    gate_mode 0: gates [H, 3], the same for every row; 1: gates [B, Tq, H, 3]
+    per row; 2: per-row logits [B, Tq, H, 3], weights = softmax over the 3
+    branches of each head."""
+    g = np.asarray(gates, dtype=np.float32).astype(np.float64)
+    if gate_mode == 0:
+        return g
+    if gate_mode == 1:
+        return g[b, i]
+    if gate_mode == 2:
+        x = g[b, i]
+        e = np.exp(x - x.max(axis=-1, keepdims=True))
+        return e / e.sum(axis=-1, keepdims=True)
+    raise ValueError(f"unknown gate_mode {gate_mode}")
+
+
 def hybrid_attn_fwd(q, k_raw, v_raw, gates, *, W, dtype, q_pos0=0, raw_pos0=0,
-                    hca=None, csa=None, scale=None, rows=None, branches=False):
+                    hca=None, csa=None, scale=None, rows=None, branches=False, gate_mode=0):
     """Gated hybrid attention output (reading R6, [Tiny-R2] 3.1.2 mode table
     and 3.2 diagram: a per-branch gate and a weighted sum of the three
     attentions, order [HCA, CSA, SWA]).
 
-    q: [B, Tq, H, d]; k_raw/v_raw: [B, Tr, Hkv, d]; gates: [H, 3] float32.
+    q: [B, Tq, H, d]; k_raw/v_raw: [B, Tr, Hkv, d]; gates: float32 [H, 3]
+    (gate_mode 0) or [B, Tq, H, 3] per-row weights (1) or logits (2).
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None
     (idx int32 [B, Tq, k]).  A branch passed as None contributes nothing.
     Returns the output in the storage dtype ([B, Tq, H, d], or [len(rows), H, d]
@@ -310,7 +334,6 @@ def hybrid_attn_fwd(q, k_raw, v_raw, gates, *, W, dtype, q_pos0=0, raw_pos0=0,
     qf = to_f64(q, dtype)
     kr = to_f64(k_raw, dtype)
     vr = to_f64(v_raw, dtype)
-    g = np.asarray(gates, dtype=np.float32).astype(np.float64)
     B, Tq, H, d = qf.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -338,6 +361,7 @@ def hybrid_attn_fwd(q, k_raw, v_raw, gates, *, W, dtype, q_pos0=0, raw_pos0=0,
             idx_row=None if csa_f is None else csa_f[2][b, i],
             want=want)
         acc = np.zeros((H, d))
+        g = gate_weights(gates, gate_mode, b, i)
         for col, br in ((0, "hca"), (1, "csa"), (2, "swa")):
             if br in res:
                 acc = acc + g[:, col][:, None] * res[br][0]

@@ -338,6 +338,53 @@ def test_gqa_equals_mha_with_repeated_kv_and_gate_linearity():
     np.testing.assert_allclose(out, lin, rtol=1e-6, atol=1e-6)
 
 
+def _small_problem():
+    B, T, H, Hkv, d, W = 2, 30, 4, 2, 8, 6
+    inp = synth.make_inputs("tiny_fp32", B=B, T=T, H=H, Hkv=Hkv, d=d, W=W, m_csa=2, k=4,
+                            Hi=2, d_idx=8, m_hca=4)
+    k, v = inp["k"], inp["v"]
+    kh, vh = O.compress_kv(k, v, inp["zk_hca"], inp["zv_hca"], 4, O.DTYPE_F32)
+    kc, vc = O.compress_kv(k, v, inp["zk_csa"], inp["zv_csa"], 2, O.DTYPE_F32)
+    idx = O.index_topk(inp["qI"], inp["kI"], inp["w"], 0, 2, W, 4, O.DTYPE_F32)
+    run = lambda g, mode: O.hybrid_attn_fwd(inp["q"], k, v, g, W=W, dtype=O.DTYPE_F32, hca=(kh, vh, 4),
+                                            csa=(kc, vc, idx), gate_mode=mode)
+    return (B, T, H), run
+
+
+def test_per_token_gates_reduce_to_per_head_and_switch_modes_per_token():
+    (B, T, H), run = _small_problem()
+    g = np.random.default_rng(41).random((H, 3)).astype(np.float32)
+    # the same weights on every row are the per-head gates
+    np.testing.assert_array_equal(run(np.broadcast_to(g, (B, T, H, 3)).copy(), 1), run(g, 0))
+    # one-hot weights chosen per (row, head) pick that row's output of the
+    # matching one-hot mode
+    modes = [run(np.eye(3, dtype=np.float32)[c][None].repeat(H, 0), 0) for c in range(3)]
+    pick = np.random.default_rng(42).integers(0, 3, size=(B, T, H))
+    out = run(np.eye(3, dtype=np.float32)[pick], 1)
+    for c in range(3):
+        sel = pick == c
+        np.testing.assert_array_equal(out[sel], modes[c][sel])
+
+
+def test_gate_logits_softmax_over_branches():
+    (B, T, H), run = _small_problem()
+    rng = np.random.default_rng(43)
+    # equal logits within each (row, head), different across heads and rows:
+    # a softmax over the three branches gives 1/3 each (over any other axis it
+    # would not)
+    c = rng.standard_normal((B, T, H, 1)).astype(np.float32) * 3
+    third = run(np.full((H, 3), 1.0 / 3.0, dtype=np.float32), 0)
+    np.testing.assert_allclose(run(np.repeat(c, 3, axis=3), 2), third, rtol=1e-6, atol=1e-6)
+    # softmax is shift-invariant per (row, head)
+    x = rng.standard_normal((B, T, H, 3)).astype(np.float32)
+    np.testing.assert_allclose(run(x + c, 2), run(x, 2), rtol=1e-6, atol=1e-6)
+    # a dominant logit selects its branch
+    big = np.zeros((B, T, H, 3), dtype=np.float32)
+    big[..., 1] = 60.0
+    np.testing.assert_allclose(run(big, 2), run(np.eye(3, dtype=np.float32)[1][None].repeat(H, 0), 0),
+                               rtol=1e-6, atol=1e-6)
+
+
 def test_constant_values_give_gate_sum():
     T, H, d, W = 30, 3, 8, 5
     q = _rand((1, T, H, d), 36).astype(np.float32)
