@@ -146,7 +146,11 @@ SHATTN_API int csa_index_topk(const void* qI, const void* kI, const float* w, in
  *   O_HCA = attention over the window rows + every visible HCA entry
  *   O_CSA = attention over the window rows + the entries idx[b,i,:] (those
  *           with 0 <= idx < N_csa; -1 marks padding)
- *   out   = gates[h,0]*O_HCA + gates[h,1]*O_CSA + gates[h,2]*O_SWA
+ *   out   = g[0]*O_HCA + g[1]*O_CSA + g[2]*O_SWA, with the gate weights g of
+ *           (row, head) by gate_mode: 0 = gates[h, :] ([H, 3], per head);
+ *           1 = gates[b, i, h, :] ([B, Tq, H, 3], per token); 2 = softmax over
+ *           the three branches of the logits gates[b, i, h, :] ([B, Tq, H, 3];
+ *           the branch gate's Linear + Softmax of [Tiny-R2] 3.2, softmax fused)
  * The HCA branch is present iff m_hca > 0 and the CSA branch iff k > 0; an
  * absent branch contributes nothing (its gate column is ignored).  A present
  * branch with no entries (N = 0, pointers may then be NULL) still contributes
@@ -159,7 +163,7 @@ typedef struct shattn_fwd_args {
     int32_t dtype;
     int32_t B, Tq, H, Hkv, d, W;
     float sm_scale;      /* 0 -> 1/sqrt(d) */
-    int32_t reserved0;   /* must be 0 */
+    int32_t gate_mode;   /* 0, 1 or 2: how gates is read (see above) */
     int64_t q_pos0;
     const void* q;       /* [B, Tq, H, d] */
     void* out;           /* [B, Tq, H, d], written */
@@ -177,7 +181,7 @@ typedef struct shattn_fwd_args {
     const void* k_csa;   /* [B, N_csa, Hkv, d] */
     const void* v_csa;
     const int32_t* idx;  /* [B, Tq, k] */
-    const float* gates;  /* [H, 3] float32 */
+    const float* gates;  /* float32: [H, 3] (gate_mode 0) or [B, Tq, H, 3] (1, 2) */
 } shattn_fwd_args;
 
 /* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the

@@ -53,7 +53,7 @@ class FwdArgs(ctypes.Structure):
         ("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("H", ctypes.c_int32),
         ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("W", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
-        ("reserved0", ctypes.c_int32),
+        ("gate_mode", ctypes.c_int32),
         ("q_pos0", ctypes.c_int64),
         ("q", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
@@ -237,10 +237,12 @@ def csa_index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, out=None, ws=
 
 
 def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
-                  sm_scale=0.0, out=None):
+                  sm_scale=0.0, out=None, gate_logits=False):
     """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
 
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
+    gates: [H, 3] per-head weights, or [B, Tq, H, 3] per-token weights (or,
+    with gate_logits, per-token logits the kernel softmaxes over the branches).
     Returns (FwdArgs, out, keepalive tuple)."""
     _need(q, "q")
     dev = q.device
@@ -249,9 +251,16 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
     _need(gates, "gates", torch.float32, dev)
     B, Tq, H, d = q.shape
     Tr, Hkv = k_raw.shape[1], k_raw.shape[2]
+    if tuple(gates.shape) == (H, 3) and not gate_logits:
+        gate_mode = 0
+    elif tuple(gates.shape) == (B, Tq, H, 3):
+        gate_mode = 2 if gate_logits else 1
+    else:
+        raise ValueError(f"gates must be [H, 3] or [B, Tq, H, 3] (logits: per token only), got {tuple(gates.shape)}")
     if out is None:
         out = torch.empty_like(q)
     a = FwdArgs()
+    a.gate_mode = gate_mode
     a.struct_size = ctypes.sizeof(FwdArgs)
     a.dtype = _dtype_code(q)
     a.B, a.Tq, a.H, a.Hkv, a.d, a.W = B, Tq, H, Hkv, d, W
@@ -286,11 +295,11 @@ def hybrid_sparse_attn_fwd_workspace_size(args: FwdArgs) -> int:
 
 
 def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None,
-                           csa=None, sm_scale=0.0, out=None, ws=None):
+                           csa=None, sm_scale=0.0, out=None, ws=None, gate_logits=False):
     """Gated hybrid attention forward; returns out [B, Tq, H, d]."""
     lib = load_library()
     a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
-                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out)
+                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits)
     nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
     if ws is None and nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -75,6 +75,7 @@ struct AttnParams {
     const void* v_csa;
     const int32_t* idx;
     const float* gates;
+    int gate_mode;     // 0: [H, 3]; 1: [B, Tq, H, 3] weights; 2: [B, Tq, H, 3] logits
     float* ws;  // split partial states (split mode only)
     long long q_pos0, raw_pos0;
     int B, Tq, H, Hkv, G, W, Tr;
@@ -620,6 +621,23 @@ __device__ __forceinline__ uint32_t range_mask(int a, int b) {
     return hi & ~((1u << a) - 1u);
 }
 
+// Gate weights of (query row qi of batch b, head h): per head, per row, or
+// the softmax over the three branches of per-row logits.
+__device__ __forceinline__ void load_gates(const AttnParams& p, int b, int qi, int h, float* g) {
+    const float* src = p.gate_mode == 0 ? p.gates + h * 3 : p.gates + (((long long)b * p.Tq + qi) * p.H + h) * 3;
+    g[0] = src[0];
+    g[1] = src[1];
+    g[2] = src[2];
+    if (p.gate_mode == 2) {
+        const float m = fmaxf(g[0], fmaxf(g[1], g[2]));
+        const float e0 = expf(g[0] - m), e1 = expf(g[1] - m), e2 = expf(g[2] - m);
+        const float inv = 1.0f / (e0 + e1 + e2);
+        g[0] = e0 * inv;
+        g[1] = e1 * inv;
+        g[2] = e2 * inv;
+    }
+}
+
 // ---------------------------------------------------------------- main kernel
 enum { ITEM_WIN = 0, ITEM_HCA = 1, ITEM_CSA = 2 };
 
@@ -675,11 +693,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     TR::load_q(qrow, q4, valid, qf);
 
     float gate[3] = {0.f, 0.f, 0.f};
-    if (valid) {
-        gate[0] = p.gates[h * 3 + 0];
-        gate[1] = p.gates[h * 3 + 1];
-        gate[2] = p.gates[h * 3 + 2];
-    }
+    if (valid) load_gates(p, b, qi, h, gate);
     if (tid < 4) sflag[tid] = 0;
     if (tid == 0) emax_s = -1;
     __syncthreads();
@@ -1147,7 +1161,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     if (ql >= nq) return;                    // uniform over the group of eight
     const int h = g * p.G + hl;
     const int qi = i0 + ql;
-    const float g0 = p.gates[h * 3 + 0], g1 = p.gates[h * 3 + 1], g2 = p.gates[h * 3 + 2];
+    float gw[3];
+    load_gates(p, b, qi, h, gw);
+    const float g0 = gw[0], g1 = gw[1], g2 = gw[2];
     const bool use_hca = p.has_hca && p.n_hca_items > 0;
     const bool use_csa = p.has_csa && p.nsplit > p.n_win_items + p.n_hca_items;
     auto part = [&](int item) -> const float* {
@@ -1226,7 +1242,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     if (a->struct_size != (int)sizeof(shattn_fwd_args))
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: struct_size %d != %d", a->struct_size,
                     (int)sizeof(shattn_fwd_args));
-    if (a->reserved0 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved0 must be 0");
+    if (a->gate_mode < 0 || a->gate_mode > 2)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: gate_mode %d (0, 1 or 2)", a->gate_mode);
     if (a->dtype != SHATTN_DTYPE_BF16 && a->dtype != SHATTN_DTYPE_F32)
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: unknown dtype %d", a->dtype);
     if (a->B < 0 || a->Tq < 0 || a->H < 1 || a->Hkv < 1 || a->W < 1 || a->Tr < 0)
@@ -1287,6 +1304,7 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.v_csa = has_csa ? a->v_csa : nullptr;
     p.idx = has_csa ? a->idx : nullptr;
     p.gates = a->gates;
+    p.gate_mode = a->gate_mode;
     p.q_pos0 = a->q_pos0;
     p.raw_pos0 = a->raw_pos0;
     p.has_hca = has_hca;

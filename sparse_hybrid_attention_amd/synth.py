@@ -144,6 +144,23 @@ def make_decode(cfg: dict, seed: int = 0) -> dict:
     return out
 
 
+def token_gates(B, T, H, kind, seed: int = 0) -> np.ndarray:
+    """Per-token gates [B, T, H, 3] float32: kind "weights" draws U(0,1) with
+    exact zeros planted (head 0 never uses HCA, head 1 skips CSA on the first
+    half of the tokens) so that branch skipping is exercised; kind "logits"
+    draws N(0, 2^2) logits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if kind == "weights":
+        g = rng.random(size=(B, T, H, 3), dtype=np.float32)
+        g[:, :, 0, 0] = 0.0
+        if H > 1:
+            g[:, : T // 2, 1, 1] = 0.0
+        return g
+    if kind == "logits":
+        return (rng.standard_normal(size=(B, T, H, 3), dtype=np.float32) * np.float32(2.0))
+    raise ValueError(f"unknown gate kind {kind}")
+
+
 def make_append(*, B, Hkv, d, W, m_csa, m_hca, d_idx, cap_csa, cap_hca, steps, dtype=DTYPE_BF16,
                 zero_state=False, seed: int = 0) -> dict:
     """Decode cache-maintenance inputs.  Draw order: ring K, ring V, ring kI,

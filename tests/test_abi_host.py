@@ -153,7 +153,8 @@ def test_attention_errors(lib):
     assert call(H=130, Hkv=1) == binding.SHATTN_EUNSUPPORTED
     assert call(dtype=9) == binding.SHATTN_EINVAL
     assert call(W=0) == binding.SHATTN_EINVAL
-    assert call(reserved0=1) == binding.SHATTN_EINVAL
+    assert call(gate_mode=3) == binding.SHATTN_EINVAL
+    assert call(gate_mode=-1) == binding.SHATTN_EINVAL
     assert call(Tr=10) == binding.SHATTN_EINVAL          # window rows missing
     assert "window rows" in err(lib)
     assert call(raw_pos0=4) == binding.SHATTN_EINVAL     # first rows missing

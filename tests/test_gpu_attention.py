@@ -29,13 +29,14 @@ def prefill_case(name, seed=0, gates=None, branches=("hca", "csa"), **over):
     return inp, hca, csa
 
 
-def gpu_attn(inp, hca, csa, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v"):
+def gpu_attn(inp, hca, csa, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v", gate_mode=0):
     cfg = inp["cfg"]
     hca_d = None if hca is None else (dev(hca[0]), dev(hca[1]), hca[2])
     csa_d = None if csa is None else (dev(csa[0]), dev(csa[1]), dev(csa[2]))
     out = binding.hybrid_sparse_attn_fwd(dev(inp["q"]), dev(inp[k_raw]), dev(inp[v_raw]),
                                          dev(inp["gates"]), cfg["W"], q_pos0=q_pos0,
-                                         raw_pos0=raw_pos0, hca=hca_d, csa=csa_d)
+                                         raw_pos0=raw_pos0, hca=hca_d, csa=csa_d,
+                                         gate_logits=gate_mode == 2)
     return host(out)
 
 
@@ -52,11 +53,12 @@ def sample_rows(B, T, W, n=96, seed=0):
     return sorted(rows)
 
 
-def check(inp, hca, csa, got, rows=None, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v", what=""):
+def check(inp, hca, csa, got, rows=None, q_pos0=0, raw_pos0=0, k_raw="k", v_raw="v", what="",
+          gate_mode=0):
     cfg = inp["cfg"]
     want = O.hybrid_attn_fwd(inp["q"], inp[k_raw], inp[v_raw], inp["gates"], W=cfg["W"],
                              dtype=cfg["dtype"], q_pos0=q_pos0, raw_pos0=raw_pos0, hca=hca,
-                             csa=csa, rows=rows)
+                             csa=csa, rows=rows, gate_mode=gate_mode)
     if rows is not None:
         got = np.stack([got[b, i] for b, i in rows])
     return assert_close(got, want, what)
@@ -76,6 +78,26 @@ def test_tinyr2_reduced(gates):
     inp, hca, csa = prefill_case("tinyr2_bf16", gates=gates, seed=1, B=2, T=640)
     got = gpu_attn(inp, hca, csa)
     check(inp, hca, csa, got, rows=sample_rows(2, 640, 128), what=f"tinyr2 gates={gates}")
+
+
+@pytest.mark.parametrize("mode,kind", [(1, "weights"), (2, "logits")])
+def test_per_token_gates_tiny_fp32_all_rows(mode, kind):
+    lib()
+    inp, hca, csa = prefill_case("tiny_fp32", seed=3)
+    cfg = inp["cfg"]
+    inp["gates"] = synth.token_gates(cfg["B"], cfg["T"], cfg["H"], kind, seed=50 + mode)
+    got = gpu_attn(inp, hca, csa, gate_mode=mode)
+    check(inp, hca, csa, got, what=f"tiny per-token gates mode {mode}", gate_mode=mode)
+
+
+@pytest.mark.parametrize("mode,kind", [(1, "weights"), (2, "logits")])
+def test_per_token_gates_tinyr2_reduced(mode, kind):
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=4, B=2, T=640)
+    inp["gates"] = synth.token_gates(2, 640, inp["cfg"]["H"], kind, seed=60 + mode)
+    got = gpu_attn(inp, hca, csa, gate_mode=mode)
+    check(inp, hca, csa, got, rows=sample_rows(2, 640, 128, seed=5), what=f"tinyr2 per-token gates mode {mode}",
+          gate_mode=mode)
 
 
 def test_gqa_hca_prefill_reduced():
@@ -164,6 +186,17 @@ def test_decode_split_d64():
                    k_raw="k_win", v_raw="v_win")
     check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
           v_raw="v_win", what="decode split d=64")
+
+
+def test_decode_split_per_token_gate_logits():
+    lib()
+    inp, hca, csa = decode_case(seed=13, B=3, N_csa=4096, N_hca=2048, k=300)
+    cfg = inp["cfg"]
+    inp["gates"] = synth.token_gates(cfg["B"], 1, cfg["H"], "logits", seed=70)
+    got = gpu_attn(inp, hca, csa, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+                   v_raw="v_win", gate_mode=2)
+    check(inp, hca, csa, got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+          v_raw="v_win", what="decode split, per-token gate logits", gate_mode=2)
 
 
 def test_decode_full_size():
