@@ -419,8 +419,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; the path's multi-GPU sharding is a "
-              "design note (see the sharding paragraph of the design document). Run with --gpus 1.",
+        print("bench.py measures one GPU: the path has no multi-GPU implementation (prefill would "
+              "shard by query tile or KV head, decode by sequence-sharded caches with an all-gather of "
+              "top-k candidates). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
