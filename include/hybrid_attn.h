@@ -1,7 +1,8 @@
 /*
  * hybrid_attn.h -- C interface of the MI355X (gfx950) hybrid sparse attention
  * forward pass: HCA (heavily compressed), CSA (compressed + sparse-selected) and
- * SWA (sliding window) branches mixed by per-head gates.
+ * SWA (sliding window) branches mixed by gates (per head or per token), and
+ * the decode-time maintenance of the raw window ring and the compressed caches.
  *
  * Pages this interface follows (cited by title and section):
  *   [V4-blog] "deepseek-v4" (astro-blog post), section "1. hybrid attn":
