@@ -1126,7 +1126,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 // compiler otherwise dropped the stubs of some variants).
 #define SHATTN_ATTN_INST(T, D)                                               \
     template __global__ void attn_fwd_kernel<T, D, 4, false>(AttnParams);    \
-    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);
+    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);     \
+    template __global__ void attn_fwd_kernel<T, D, 2, false>(AttnParams);    \
+    template __global__ void attn_fwd_kernel<T, D, 2, true>(AttnParams);
 SHATTN_ATTN_INST(bf16_t, 64)
 SHATTN_ATTN_INST(bf16_t, 128)
 SHATTN_ATTN_INST(float, 64)
@@ -1320,7 +1322,9 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     // barrier or on their loads.  (Measured: 8 waves leave one workgroup per
     // CU; 6 waves put two waves of a workgroup on some SIMDs, and every tile
     // barrier then waits for those.)
-    pl.waves = 4;
+    // Few columns per (batch, KV head) -- decode: one query times G heads --
+    // take two waves, so that no wave attends only padding columns.
+    pl.waves = (G <= 32 && (long long)a->Tq * G <= 32) ? 2 : 4;
     p.ncol = pl.waves * 16;
     p.QW = G >= p.ncol ? 1 : p.ncol / G;
     if (G > p.ncol) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: H/Hkv=%d too large", G);
@@ -1420,8 +1424,9 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
 
 template <typename T, int D>
 static int launch_attn(Plan& pl, hipStream_t s) {
-    if (pl.p.csa_mode == CSA_GATHER) return launch_attn_nw<T, D, 4, true>(pl, s);
-    return launch_attn_nw<T, D, 4, false>(pl, s);
+    const bool gather = pl.p.csa_mode == CSA_GATHER;
+    if (pl.waves == 2) return gather ? launch_attn_nw<T, D, 2, true>(pl, s) : launch_attn_nw<T, D, 2, false>(pl, s);
+    return gather ? launch_attn_nw<T, D, 4, true>(pl, s) : launch_attn_nw<T, D, 4, false>(pl, s);
 }
 
 extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
