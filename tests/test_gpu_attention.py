@@ -100,6 +100,17 @@ def test_per_token_gates_tinyr2_reduced(mode, kind):
           gate_mode=mode)
 
 
+def test_per_token_gate_logits_gqa_ragged():
+    # several query heads per KV head: the gate of column (query, head) uses
+    # the query head, not the KV head
+    lib()
+    inp, hca, csa = prefill_case("tinyr2_bf16", seed=6, B=2, T=333, H=16, Hkv=2)
+    inp["gates"] = synth.token_gates(2, 333, 16, "logits", seed=80)
+    got = gpu_attn(inp, hca, csa, gate_mode=2)
+    check(inp, hca, csa, got, rows=sample_rows(2, 333, 128, seed=7), what="GQA per-token gate logits",
+          gate_mode=2)
+
+
 def test_gqa_hca_prefill_reduced():
     lib()
     inp, hca, csa = prefill_case("hca_prefill_32k", seed=2, T=2048)

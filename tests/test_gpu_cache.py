@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 STATE = ("k_ring", "v_ring", "kI_ring", "k_csa", "v_csa", "k_hca", "v_hca", "kI_csa")
 
 
-def gpu_run(inp, positions):
+def gpu_run(inp, positions, hca=True, indexer=True):
     """positions: [steps][B] ints.  Returns the final state (host) and drops."""
     s = {k: dev(inp[k]) for k in STATE}
     z = {k: dev(inp[k]) for k in ("zk_csa", "zv_csa", "zk_hca", "zv_hca", "zI")}
@@ -25,29 +25,33 @@ def gpu_run(inp, positions):
         p = torch.tensor(pos, dtype=torch.int64, device=DEV)
         binding.cache_append(p, dev(inp["k_new"][step]), dev(inp["v_new"][step]), s["k_ring"], s["v_ring"],
                              csa=(inp["m_csa"], z["zk_csa"], z["zv_csa"], s["k_csa"], s["v_csa"]),
-                             hca=(inp["m_hca"], z["zk_hca"], z["zv_hca"], s["k_hca"], s["v_hca"]),
-                             indexer=(dev(inp["kI_new"][step]), s["kI_ring"], z["zI"], s["kI_csa"]),
+                             hca=(inp["m_hca"], z["zk_hca"], z["zv_hca"], s["k_hca"], s["v_hca"]) if hca else None,
+                             indexer=(dev(inp["kI_new"][step]), s["kI_ring"], z["zI"], s["kI_csa"])
+                             if indexer else None,
                              dropped=dropped)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in s.items()}, int(dropped.item())
 
 
-def oracle_run(inp, positions):
+def oracle_run(inp, positions, hca=True, indexer=True):
     s = {k: inp[k].copy() for k in STATE}
     dropped = 0
     for step, pos in enumerate(positions):
+        branches = [(inp["m_csa"], inp["zk_csa"], inp["zv_csa"], s["k_csa"], s["v_csa"])]
+        if hca:
+            branches.append((inp["m_hca"], inp["zk_hca"], inp["zv_hca"], s["k_hca"], s["v_hca"]))
         dropped += O.cache_append(
             pos, inp["k_new"][step], inp["v_new"][step], s["k_ring"], s["v_ring"], W=inp["W"], dtype=inp["dtype"],
-            branches=((inp["m_csa"], inp["zk_csa"], inp["zv_csa"], s["k_csa"], s["v_csa"]),
-                      (inp["m_hca"], inp["zk_hca"], inp["zv_hca"], s["k_hca"], s["v_hca"])),
-            kI_new=inp["kI_new"][step], kI_ring=s["kI_ring"], kI_branch=(inp["m_csa"], inp["zI"], s["kI_csa"]))
+            branches=branches,
+            kI_new=inp["kI_new"][step] if indexer else None, kI_ring=s["kI_ring"] if indexer else None,
+            kI_branch=(inp["m_csa"], inp["zI"], s["kI_csa"]) if indexer else None)
     return s, dropped
 
 
-def check(inp, positions, what):
+def check(inp, positions, what, hca=True, indexer=True):
     lib()
-    got, gd = gpu_run(inp, positions)
-    want, wd = oracle_run(inp, positions)
+    got, gd = gpu_run(inp, positions, hca=hca, indexer=indexer)
+    want, wd = oracle_run(inp, positions, hca=hca, indexer=indexer)
     assert gd == wd, f"{what}: dropped {gd} != {wd}"
     for k in ("k_ring", "v_ring", "kI_ring"):
         assert np.array_equal(got[k], want[k]), f"{what}: {k}"
@@ -94,3 +98,26 @@ def test_append_stream_matches_whole_sequence_compression(dtype):
         kIseq = inp["kI_new"][start:, b][None, :, None, :]
         want_I = O.to_storage(O.compress(O.to_f64(kIseq, dtype), inp["zI"][:, None, :], m_csa)[:, :, 0], dtype)
         assert_close(got["kI_csa"][b:b + 1, :n // m_csa], want_I, f"kI seq {b} vs whole-sequence oracle")
+
+
+def test_append_fp32_d64_csa_only_without_indexer_keys():
+    # one ratio, no HCA caches, no indexer keys (their ring and cache must stay
+    # untouched), a ring exactly one block long (W = m)
+    inp = synth.make_append(B=4, Hkv=3, d=64, W=4, m_csa=4, m_hca=4, d_idx=64, cap_csa=12, cap_hca=1,
+                            steps=40, dtype=binding.DTYPE_F32, seed=32)
+    got, _ = check(inp, [[s, s + 3, s + 5, s - 7] for s in range(40)], "fp32 d64 CSA only", hca=False,
+                   indexer=False)
+    assert np.array_equal(got["kI_ring"], inp["kI_ring"]) and np.array_equal(got["kI_csa"], inp["kI_csa"])
+    assert np.array_equal(got["k_hca"], inp["k_hca"])
+
+
+def test_append_zero_capacity_drops_every_hca_entry():
+    inp = synth.make_append(B=2, Hkv=1, d=128, W=8, m_csa=2, m_hca=8, d_idx=128, cap_csa=6, cap_hca=0,
+                            steps=20, seed=33)
+    lib()
+    _, gd = gpu_run(inp, [[s, s] for s in range(20)])
+    # HCA: 2 completed blocks per sequence, none stored; CSA K/V and indexer
+    # keys: 10 blocks per sequence, 6 stored
+    assert gd == 2 * 2 + 2 * (10 - 6) * 2
+    check(inp, [[s, s] for s in range(20)], "zero-capacity HCA")
+
