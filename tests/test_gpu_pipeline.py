@@ -106,6 +106,25 @@ def test_csa_prefill_pipeline_reduced():
     assert_close(np.stack([got[b, i] for b, i in rows]), want, "csa prefill")
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,T", [("hca_prefill_32k", 32768), ("csa_prefill_128k", 131072)])
+def test_long_prefill_full_size_sampled(name, T):
+    # the long-prefill shapes at full size, in the launch configuration the
+    # benchmark times: fixed edge rows plus random ones against the oracle
+    # (the input generation alone takes about a minute at 128K tokens)
+    lib()
+    inp = synth.make_inputs(name, seed=1)
+    pipe = pipeline(inp)
+    got = host(pipe.run())
+    rows = rows_for(1, T, 40, 5)
+    want, sel = oracle_pipeline(inp, rows)
+    if sel is not None:
+        idx = host(pipe.idx)
+        for r, (b, i) in enumerate(rows):
+            assert np.array_equal(idx[b, i], sel[r]), f"{name}: idx row {(b, i)}"
+    assert_close(np.stack([got[b, i] for b, i in rows]), want, f"{name} full size")
+
+
 def test_pipeline_repeat_is_bitwise_stable():
     lib()
     inp = synth.make_inputs("tinyr2_bf16", seed=4, B=2, T=1024)
