@@ -53,6 +53,17 @@ Readings taken where the pages are silent (each repeated at its function):
       before the weighted sum): gates may be given per (token, head) as
       weights, or as logits whose softmax over the three branches (in the
       order [HCA, CSA, SWA], all three, present or not) gives the weights.
+  R10 Rotary position embedding ([Tiny-R2] architecture diagram: RoPE on the
+      prepared query, the window keys, the selected CSA keys and the HCA keys;
+      parameter block: a rope part of the head dim next to a non-rope part;
+      [CS336] "位置编码" paragraph: position as a rotation angle, so that a
+      query-key product depends on the position difference).  Channels
+      [off, off + R) of every head are rotated in adjacent pairs
+      (off + 2i, off + 2i + 1) by the angle pos * base^(-2i/R), as
+      (a, b) -> (a cos - b sin, a sin + b cos); base 10000 unless given (the
+      pages give none); every other channel is unchanged.  The position of
+      each row is the caller's (for a compressed entry: whichever position the
+      model assigns it); a row with a negative position is left unchanged.
 """
 from __future__ import annotations
 
@@ -73,6 +84,7 @@ __all__ = [
     "score_key_order",
     "gate_weights",
     "cache_append",
+    "rope",
 ]
 
 
@@ -423,3 +435,29 @@ def cache_append(pos, k_new, v_new, k_ring, v_ring, *, W: int, dtype: int, branc
                 cache[b, c] = to_storage(compress(x, z, m)[0, 0], dtype)
     return dropped
 
+
+# --------------------------------------------------------------------------
+# Rotary position embedding (reading R10: [Tiny-R2] architecture diagram and
+# parameter block; [CS336] "位置编码" paragraph).
+# --------------------------------------------------------------------------
+def rope(x, pos, *, rope_off: int, rope_dim: int, dtype: int, base: float = 10000.0):
+    """x: [rows, heads, d] in storage form; pos: [rows] int64 (negative: row
+    unchanged).  Returns the rotated tensor in storage form (R10)."""
+    xf = to_f64(np.asarray(x), dtype).copy()
+    pos = np.asarray(pos, dtype=np.int64)
+    assert xf.ndim == 3 and pos.shape == (xf.shape[0],)
+    assert rope_dim > 0 and rope_dim % 2 == 0 and 0 <= rope_off and rope_off + rope_dim <= xf.shape[2]
+    freq = np.array([float(base) ** (-2.0 * i / rope_dim) for i in range(rope_dim // 2)])
+    for r in range(xf.shape[0]):
+        p = int(pos[r])
+        if p < 0:
+            continue
+        for i in range(rope_dim // 2):
+            ang = p * freq[i]
+            c, s_ = math.cos(ang), math.sin(ang)
+            ca, cb = rope_off + 2 * i, rope_off + 2 * i + 1
+            a = xf[r, :, ca].copy()
+            b = xf[r, :, cb].copy()
+            xf[r, :, ca] = a * c - b * s_
+            xf[r, :, cb] = a * s_ + b * c
+    return to_storage(xf, dtype)

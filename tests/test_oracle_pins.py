@@ -519,3 +519,57 @@ def test_cache_append_capacity_drops_late_entries():
     assert dropped == (10 - 3) + (5 - 3) + (10 - 3)
     (m, zk, _, kc, _) = br[0]
     assert np.array_equal(kc[0], O.to_storage(O.compress(s0[0][None, :12], zk, 4)[0], dt))
+
+
+# ----------------------------------------------------------------- RoPE (R10)
+COS1, SIN1 = 0.5403023058681398, 0.8414709848078965   # cos(1), sin(1) to double precision
+
+
+def _rope(x, pos, off, rd, base=10000.0):
+    return O.rope(np.asarray(x, np.float32), np.asarray(pos, np.int64), rope_off=off, rope_dim=rd,
+                  dtype=O.DTYPE_F32, base=base).astype(np.float64)
+
+
+def test_rope_rotation_direction_and_frequencies():
+    # pair 0 turns by pos radians, counter-clockwise: (1, 0) -> (cos 1, sin 1), (0, 1) -> (-sin 1, cos 1)
+    e = np.zeros((2, 1, 2))
+    e[0, 0, 0] = 1.0
+    e[1, 0, 1] = 1.0
+    got = _rope(e, [1, 1], 0, 2)
+    assert np.allclose(got[0, 0], [COS1, SIN1], atol=1e-7)
+    assert np.allclose(got[1, 0], [-SIN1, COS1], atol=1e-7)
+    # pair i turns by pos * base^(-2i/R): R = 4, base 1e4 -> pair 1 at 1e-2 rad per position;
+    # R = 8, base 100 -> pair 2 at 0.1 rad per position; both reach 1 rad
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 2] = 1.0
+    assert np.allclose(_rope(x, [100], 0, 4)[0, 0], [0, 0, COS1, SIN1], atol=1e-7)
+    x = np.zeros((1, 1, 8))
+    x[0, 0, 4] = 1.0
+    assert np.allclose(_rope(x, [10], 0, 8, base=100.0)[0, 0], [0, 0, 0, 0, COS1, SIN1, 0, 0], atol=1e-7)
+
+
+def test_rope_identity_cases_and_untouched_channels():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((3, 2, 16)).astype(np.float32)
+    assert np.array_equal(_rope(x, [0, 0, 0], 4, 8), x.astype(np.float64))       # position 0
+    assert np.array_equal(_rope(x, [-1, -5, -1], 4, 8), x.astype(np.float64))    # inactive rows
+    y = _rope(x, [7, 1000, 123456], 4, 8)
+    keep = [c for c in range(16) if not 4 <= c < 12]
+    assert np.array_equal(y[:, :, keep], x[:, :, keep].astype(np.float64))
+    # each rotated pair keeps its length
+    a = x.astype(np.float64)[:, :, 4:12].reshape(3, 2, 4, 2)
+    b = y[:, :, 4:12].reshape(3, 2, 4, 2)
+    assert np.allclose(np.hypot(a[..., 0], a[..., 1]), np.hypot(b[..., 0], b[..., 1]), rtol=1e-6)
+
+
+def test_rope_composes_and_depends_on_position_difference():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    # rotations add: rope(rope(x, a), b) == rope(x, a + b)
+    two = _rope(_rope(q, [300], 0, 64).astype(np.float32), [45], 0, 64)
+    assert np.allclose(two, _rope(q, [345], 0, 64), atol=1e-5)
+    # q . k after rotation depends on the position difference only
+    dots = [float(np.sum(_rope(q, [m], 0, 64) * _rope(k, [m - 17], 0, 64))) for m in (17, 500, 70000)]
+    assert np.allclose(dots, dots[0], atol=1e-4)
+    assert not np.isclose(dots[0], float(np.sum(_rope(q, [40], 0, 64) * _rope(k, [0], 0, 64))), atol=1e-3)
