@@ -258,6 +258,35 @@ typedef struct shattn_append_args {
 SHATTN_API int hybrid_cache_append(const shattn_append_args* a, void* stream);
 
 /*
+ * Rotary position embedding, in place, on a range of channels of every head
+ * (the prologue step before the attention: applied to Q, to the raw window
+ * K rows and to the compressed K entries).
+ *
+ * Pages: [Tiny-R2] architecture diagram (RoPE on the prepared query, the
+ * window keys, the selected CSA keys and the HCA keys) and parameter block
+ * (a rope part of the head dim beside a non-rope part); [CS336] "位置编码"
+ * paragraph (position as a rotation angle, so that a query-key product
+ * depends on the position difference).  The pages fix neither the pairing
+ * nor the base; the reading taken: channels rope_off + 2i and
+ * rope_off + 2i + 1 (0 <= i < rope_dim / 2) of each head turn by the angle
+ * pos * base^(-2i / rope_dim), (a, b) -> (a cos - b sin, a sin + b cos);
+ * the other channels are unchanged.  Arithmetic: the angle is formed and
+ * reduced modulo 2 pi in float64, its sine and cosine and the rotation are
+ * float32, the result is rounded once to the storage dtype.
+ *
+ *   x    : [rows, heads, d]  dtype, DEVICE memory, rotated in place
+ *   pos  : [rows] int64, DEVICE memory, 8-byte aligned: the position of each
+ *          row (for a compressed entry, the position the model assigns it);
+ *          a row with pos < 0 is left unchanged
+ *   base : finite, > 0 (10000 is the usual choice)
+ * Errors (SHATTN_EINVAL): unknown dtype, rows < 0, heads < 1, d < 2, an odd
+ * or empty rope_dim, a channel range outside [0, d), a bad base, null or
+ * misaligned pointers with rows > 0.  rows == 0 is a no-op.
+ */
+SHATTN_API int rope_apply(void* x, const int64_t* pos, int64_t rows, int32_t heads, int32_t d,
+                          int32_t rope_off, int32_t rope_dim, double base, int32_t dtype, void* stream);
+
+/*
  * Measurement aid (not part of the attention path): launches `workgroups`
  * workgroups of 256 threads; every wave issues `iters` rounds of independent
  * bf16 MFMAs: shape 0 = 8 x v_mfma_f32_16x16x32_bf16 per round, shape 1 =

@@ -34,6 +34,7 @@ EXPORTED = (
     "hybrid_sparse_attn_fwd_workspace_size",
     "hybrid_sparse_attn_fwd",
     "hybrid_cache_append",
+    "rope_apply",
     "shattn_mfma_peak_probe",
     "shattn_last_error",
 )
@@ -130,6 +131,8 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_sparse_attn_fwd.restype = i32
         lib.hybrid_cache_append.argtypes = [ctypes.POINTER(AppendArgs), vp]
         lib.hybrid_cache_append.restype = i32
+        lib.rope_apply.argtypes = [vp, vp, i64, i32, i32, i32, i32, ctypes.c_double, i32, vp]
+        lib.rope_apply.restype = i32
         lib.shattn_mfma_peak_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.shattn_mfma_peak_probe.restype = i32
         lib.shattn_last_error.argtypes = []
@@ -373,6 +376,26 @@ def cache_append(pos, k_new, v_new, k_ring, v_ring, *, csa=None, hca=None, index
     a, _keep = make_append_args(pos, k_new, v_new, k_ring, v_ring, csa=csa, hca=hca, indexer=indexer,
                                 dropped=dropped)
     _check(lib.hybrid_cache_append(ctypes.byref(a), _stream(k_new)))
+
+
+def rope_apply(x, pos, *, rope_off: int = 0, rope_dim: int = None, base: float = 10000.0):
+    """Rotary position embedding in place on channels [rope_off, rope_off +
+    rope_dim) of every head.  x: [..., heads, d] contiguous; pos: int64 with
+    one position per row (x.numel() / (heads * d) rows; negative: unchanged)."""
+    _need(x, "x")
+    _need(pos, "pos", torch.int64, x.device)
+    if x.dim() < 2:
+        raise ValueError("rope_apply: x must be [..., heads, d]")
+    heads, d = x.shape[-2], x.shape[-1]
+    rows = x.numel() // (heads * d) if heads * d else 0
+    if pos.numel() != rows:
+        raise ValueError(f"rope_apply: {pos.numel()} positions for {rows} rows")
+    if rope_dim is None:
+        rope_dim = d - rope_off
+    lib = load_library()
+    _check(lib.rope_apply(_ptr(x), _ptr(pos), rows, heads, d, rope_off, rope_dim, float(base), _dtype_code(x),
+                          _stream(x)))
+    return x
 
 
 def default_scale(d: int) -> float:

@@ -195,3 +195,15 @@ def make_inputs(name: str, seed: int = 0, **overrides) -> dict:
     if cfg["kind"] == "decode":
         return make_decode(cfg, seed)
     return make_prefill(cfg, seed)
+
+
+def make_rope(*, rows, heads, d, dtype=DTYPE_BF16, max_pos=1 << 20, seed: int = 0) -> dict:
+    """RoPE inputs.  Draw order: x [rows, heads, d] ~ N(0, 1), then positions
+    U{0, .., max_pos - 1}; row 0 sits at position 0, row 1 is inactive (-1)
+    and the last row at max_pos - 1 when there are rows enough."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal(rng, (rows, heads, d), dtype)
+    pos = rng.integers(0, max_pos, size=(rows,), dtype=np.int64)
+    if rows > 2:
+        pos[0], pos[1], pos[-1] = 0, -1, max_pos - 1
+    return dict(x=x, pos=pos)

@@ -213,6 +213,29 @@ def test_cache_append_errors(lib):
     assert call(B=0) == binding.SHATTN_OK
 
 
+def test_rope_errors(lib):
+    f = lib.rope_apply
+    X, P = 0x7F0000000000, 0x7F0000001000   # never dereferenced: every call below fails validation
+
+    def call(x=X, pos=P, rows=4, heads=2, d=128, off=64, rd=64, base=10000.0, dtype=binding.DTYPE_BF16):
+        return f(x, pos, rows, heads, d, off, rd, base, dtype, None)
+    assert call(dtype=7) == binding.SHATTN_EINVAL
+    assert call(rows=-1) == binding.SHATTN_EINVAL
+    assert call(heads=0) == binding.SHATTN_EINVAL
+    assert call(rd=63) == binding.SHATTN_EINVAL               # odd channel count
+    assert call(rd=0) == binding.SHATTN_EINVAL
+    assert call(off=66) == binding.SHATTN_EINVAL              # range past d
+    assert "inside d=128" in err(lib)
+    assert call(off=-2) == binding.SHATTN_EINVAL
+    assert call(base=0.0) == binding.SHATTN_EINVAL
+    assert call(base=float("inf")) == binding.SHATTN_EINVAL
+    assert call(x=None) == binding.SHATTN_EINVAL
+    assert call(pos=P + 4) == binding.SHATTN_EINVAL           # int64 array must be 8-byte aligned
+    assert call(x=X + 1) == binding.SHATTN_EINVAL             # bf16 elements must be aligned
+    # no rows: a no-op
+    assert call(rows=0, x=None, pos=None) == binding.SHATTN_OK
+
+
 def test_library_refuses_to_fall_back(tmp_path, monkeypatch):
     # a missing library is an error, never a silent CPU path
     monkeypatch.setattr(binding, "_lib", None)
