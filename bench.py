@@ -398,6 +398,71 @@ def bench_append(args, torch, binding):
     print(json.dumps(line))
 
 
+ROPE = dict(B=8, T=2048, H=12, d=128, rope_off=64, rope_dim=64, base=10000.0)
+
+
+def bench_rope(args, torch, binding):
+    """RoPE in place on the Tiny-R2 query tensor (B8 T2048 H12 d128, the last
+    64 channels of each head rotated), one launch per step."""
+    from sparse_hybrid_attention_amd import synth
+    c = ROPE
+    B, T, H, d, off, rd = c["B"], c["T"], c["H"], c["d"], c["rope_off"], c["rope_dim"]
+    rows = B * T
+    inp = synth.make_rope(rows=rows, heads=H, d=d, max_pos=T, seed=0)
+    dev = "cuda:0"
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    pos = torch.arange(T, dtype=torch.int64, device=dev).repeat(B)   # each sequence from position 0
+    lib = binding.load_library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    call = lambda: binding._check(lib.rope_apply(x.data_ptr(), pos.data_ptr(), rows, H, d, off, rd, c["base"],
+                                                 binding.DTYPE_BF16, sp))
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    alg = rows * H * rd * 2 * 2 + rows * 8     # rotated channels read and written once, one position per row
+    ach = alg / (kms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_limits
+        n_cpu = 4096
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            O.rope(inp["x"][:n_cpu], inp["pos"][:n_cpu], rope_off=off, rope_dim=rd, dtype=binding.DTYPE_BF16,
+                   base=c["base"])
+            dt_cpu = time.perf_counter() - t1
+        cpu = {"value": round(n_cpu / dt_cpu, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the first {n_cpu} of the {rows} query rows (all {H} heads); float64 NumPy, one thread; "
+                         f"{dt_cpu:.1f} s"}
+    line = {
+        "metric": "RoPE tokens/s (query tensor, in place)",
+        "value": round(rows * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws, resident in HBM)",
+        "config": {"workload": f"RoPE on the Tiny-R2 query tensor, B{B} T{T} H{H} d{d} bf16, channels "
+                               f"[{off}, {off + rd}) rotated, base {c['base']:g}", "name": "rope_q",
+                   "gpu_ms_per_launch_events": round(kms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 6), "kernel": "rope", "traffic": None,
+                     "alg_bytes_per_launch": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,7 +470,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyr2_bf16",
                     help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m, "
-                         "decode_append (cache maintenance)")
+                         "decode_append (cache maintenance), rope_q (RoPE on the query tensor)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -446,6 +511,9 @@ def main():
     binding.load_library()
     if args.workload == "decode_append":
         bench_append(args, torch, binding)
+        return
+    if args.workload == "rope_q":
+        bench_rope(args, torch, binding)
         return
     log(f"[bench] building inputs for {args.workload}")
     inp = build_inputs(args.workload, gates=args.gates)

@@ -9,12 +9,15 @@
 // difference).  Pairing, angle and base are the reading stated with the
 // declaration in hybrid_attn.h.
 //
-// One thread per (row, head, channel pair), pairs innermost, so a wave reads
-// and writes contiguous bytes; the work is a read and a write of the rotated
-// channels (HBM-bound).  The angle pos * f_i is formed and reduced modulo
-// 2 pi in double precision and only then handed to the float sine / cosine:
-// positions reach a million and more, where a float product would lose the
-// angle's fractional part.
+// One thread per (row, channel pair), pairs innermost, so a wave reads and
+// writes contiguous bytes of each head; the thread turns its pair in every
+// head of the row with one sine / cosine (the angle depends on the row and
+// the pair only), loading eight heads' pairs before the first store so that
+// they are in flight together.  The work is a read and a write of the
+// rotated channels (HBM-bound).  The angle pos * f_i is formed and reduced
+// modulo 2 pi in double precision and only then handed to the float sine /
+// cosine: positions reach a million and more, where a float product would
+// lose the angle's fractional part.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,25 +31,43 @@ namespace {
 constexpr int kRopeThreads = 256;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
+constexpr int kRopeHeadsInFlight = 8;
+
 template <typename T>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(T* __restrict__ x, const int64_t* __restrict__ pos,
                                                             long long total, int heads, int d, int off, int npairs,
                                                             double step) {
     const long long stride = (long long)gridDim.x * kRopeThreads;
     for (long long u = (long long)blockIdx.x * kRopeThreads + threadIdx.x; u < total; u += stride) {
-        const long long rh = u / npairs;          // row * heads + head
-        const int i = (int)(u - rh * npairs);     // channel pair
-        const long long p = pos[rh / heads];
+        const long long row = u / npairs;
+        const int i = (int)(u - row * npairs);    // channel pair
+        const long long p = pos[row];
         if (p < 0) continue;                      // inactive row: unchanged
         // f_i = base^(-2i/R) = 2^(-i * step), step = 2 log2(base) / R
         double a = (double)p * exp2(-(double)i * step);
         a -= kTwoPi * rint(a / kTwoPi);
         float s, c;
         sincosf((float)a, &s, &c);
-        T* e = x + rh * d + off + 2 * i;
-        const float x0 = Elem<T>::load1(e), x1 = Elem<T>::load1(e + 1);
-        Elem<T>::store1(e, x0 * c - x1 * s);
-        Elem<T>::store1(e + 1, x0 * s + x1 * c);
+        T* e0 = x + row * heads * (long long)d + off + 2 * i;
+        for (int h0 = 0; h0 < heads; h0 += kRopeHeadsInFlight) {
+            float x0[kRopeHeadsInFlight], x1[kRopeHeadsInFlight];
+#pragma unroll
+            for (int j = 0; j < kRopeHeadsInFlight; ++j) {
+                if (h0 + j < heads) {
+                    const T* e = e0 + (long long)(h0 + j) * d;
+                    x0[j] = Elem<T>::load1(e);
+                    x1[j] = Elem<T>::load1(e + 1);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kRopeHeadsInFlight; ++j) {
+                if (h0 + j < heads) {
+                    T* e = e0 + (long long)(h0 + j) * d;
+                    Elem<T>::store1(e, x0[j] * c - x1[j] * s);
+                    Elem<T>::store1(e + 1, x0[j] * s + x1[j] * c);
+                }
+            }
+        }
     }
 }
 
@@ -72,7 +93,7 @@ extern "C" int rope_apply(void* x, const int64_t* pos, int64_t rows, int32_t hea
     const int npairs = rope_dim / 2;
     if (rows > (1LL << 62) / ((long long)heads * d))
         return fail(SHATTN_EINVAL, "rope_apply: rows * heads * d overflows");
-    const long long total = rows * heads * (long long)npairs;
+    const long long total = rows * (long long)npairs;   // (row, pair) units
     const double step = 2.0 * std::log2(base) / rope_dim;
     long long blocks = (total + kRopeThreads - 1) / kRopeThreads;
     if (blocks > (1LL << 20)) blocks = 1LL << 20;   // grid-stride beyond
