@@ -1,8 +1,9 @@
 /*
  * hybrid_attn.h -- C interface of the MI355X (gfx950) hybrid sparse attention
  * forward pass: HCA (heavily compressed), CSA (compressed + sparse-selected) and
- * SWA (sliding window) branches mixed by gates (per head or per token), and
- * the decode-time maintenance of the raw window ring and the compressed caches.
+ * SWA (sliding window) branches mixed by gates (per head or per token), the
+ * decode-time maintenance of the raw window ring and the compressed caches,
+ * and the rotary position embedding applied to Q and K before the path.
  *
  * Pages this interface follows (cited by title and section):
  *   [V4-blog] "deepseek-v4" (astro-blog post), section "1. hybrid attn":
@@ -17,7 +18,8 @@
  *   [Tiny-R2] Tiny-R2 README, sections 3.1.2 (modes HCA [1,0,0], CSA [0,1,0],
  *             SWA [0,0,1]) and 3.2 (branch gate + weighted sum, config fields
  *             block_size / window_size / num_tokens_to_keep).
- *   [CS336]   CS336 notes, "Attention Heads 变体" (MQA / GQA head sharing).
+ *   [CS336]   CS336 notes, "Attention Heads 变体" (MQA / GQA head sharing),
+ *             "位置编码" paragraph (RoPE: position as a rotation angle).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
