@@ -64,6 +64,15 @@ Readings taken where the pages are silent (each repeated at its function):
       pages give none); every other channel is unchanged.  The position of
       each row is the caller's (for a compressed entry: whichever position the
       model assigns it); a row with a negative position is left unchanged.
+  R11 4-bit cache storage ([V4-code] section "1. HCA": the merged cache is
+      quantised with one minimum and one maximum over the whole tensor, step
+      (max - min) / 15, codes rounded and clamped to 0..15, decoded as
+      code * step + min; the page keeps one code per byte and names packing
+      two per byte as the real layout).  Reading: the decision is taken in
+      float32 (x - min) / step with round-half-even, as the page's tensor
+      arithmetic does; two codes per byte, element 2j in the low nibble of
+      byte j; a constant tensor (step 0) gets code 0 everywhere and decodes to
+      its value.
 """
 from __future__ import annotations
 
@@ -85,6 +94,7 @@ __all__ = [
     "gate_weights",
     "cache_append",
     "rope",
+    "quant4", "dequant4",
 ]
 
 
@@ -461,3 +471,37 @@ def rope(x, pos, *, rope_off: int, rope_dim: int, dtype: int, base: float = 1000
             xf[r, :, ca] = a * c - b * s_
             xf[r, :, cb] = a * s_ + b * c
     return to_storage(xf, dtype)
+
+
+# --------------------------------------------------------------------------
+# 4-bit cache storage (reading R11: [V4-code] section "1. HCA", the storage
+# of the merged cache).  The code decision is float32 arithmetic on purpose.
+# --------------------------------------------------------------------------
+def quant4(x, dtype: int):
+    """x: any shape, storage form.  Returns (packed codes uint8 [ceil(n/2)],
+    min float32, step float32)."""
+    xf = to_f64(np.asarray(x), dtype).astype(np.float32).reshape(-1)
+    n = xf.size
+    if n == 0:
+        return np.zeros(0, np.uint8), np.float32(0), np.float32(0)
+    mn, mx = np.float32(xf.min()), np.float32(xf.max())
+    step = np.float32((mx - mn) / np.float32(15))
+    if step == 0:
+        codes = np.zeros(n, np.uint8)
+    else:
+        t = (xf - mn) / step                       # float32, correctly rounded
+        codes = np.clip(np.rint(t), 0, 15).astype(np.uint8)
+    if n % 2:
+        codes = np.concatenate([codes, np.zeros(1, np.uint8)])
+    packed = (codes[0::2] | (codes[1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, mn, step
+
+
+def dequant4(packed, mn, step, n: int, dtype: int):
+    """Inverse of quant4: code * step + min, rounded once to the storage dtype."""
+    packed = np.asarray(packed, np.uint8)
+    codes = np.empty(2 * packed.size, np.uint8)
+    codes[0::2] = packed & np.uint8(15)
+    codes[1::2] = packed >> np.uint8(4)
+    vals = codes[:n].astype(np.float64) * float(step) + float(mn)
+    return to_storage(vals, dtype)

@@ -573,3 +573,41 @@ def test_rope_composes_and_depends_on_position_difference():
     dots = [float(np.sum(_rope(q, [m], 0, 64) * _rope(k, [m - 17], 0, 64))) for m in (17, 500, 70000)]
     assert np.allclose(dots, dots[0], atol=1e-4)
     assert not np.isclose(dots[0], float(np.sum(_rope(q, [40], 0, 64) * _rope(k, [0], 0, 64))), atol=1e-3)
+
+
+# ----------------------------------------------------------------- 4-bit storage (R11)
+def _codes(packed, n):
+    c = np.empty(2 * packed.size, np.uint8)
+    c[0::2], c[1::2] = packed & 15, packed >> 4
+    return c[:n]
+
+
+def test_quant4_hand_examples():
+    # 0..15: step 1, every value its own code; packing puts element 2j in the low nibble
+    x = np.arange(16, dtype=np.float32)
+    p, mn, st = O.quant4(x, O.DTYPE_F32)
+    assert (mn, st) == (0.0, 1.0)
+    assert p.tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    # ties round to even: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2 (step 1 from the range [0, 15])
+    x = np.array([0.0, 0.5, 1.5, 2.5, 15.0], np.float32)
+    p, mn, st = O.quant4(x, O.DTYPE_F32)
+    assert _codes(p, 5).tolist() == [0, 0, 2, 2, 15]
+    assert p.size == 3 and p[2] == 15                     # odd count: high nibble of the last byte is 0
+    # min and max map to 0 and 15 on any range; a constant tensor gets code 0 and decodes to itself
+    x = np.array([-3.0, 1.25, 9.0], np.float32)
+    p, mn, st = O.quant4(x, O.DTYPE_F32)
+    assert (mn, st) == (np.float32(-3.0), np.float32(12.0 / 15.0)) and _codes(p, 3)[[0, 2]].tolist() == [0, 15]
+    c = np.full(7, 2.5, np.float32)
+    p, mn, st = O.quant4(c, O.DTYPE_F32)
+    assert st == 0 and not _codes(p, 7).any()
+    assert np.array_equal(O.dequant4(p, mn, st, 7, O.DTYPE_F32), c)
+
+
+def test_quant4_round_trip_error_bound():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(1001).astype(np.float32)
+    p, mn, st = O.quant4(x, O.DTYPE_F32)
+    y = O.dequant4(p, mn, st, x.size, O.DTYPE_F32).astype(np.float64)
+    err = np.abs(y - x)
+    assert err.max() <= float(st) / 2 * (1 + 1e-5)        # nearest code: at most half a step away
+    assert err.max() > float(st) / 4                       # and the bound is not vacuous
