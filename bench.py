@@ -463,6 +463,73 @@ def bench_rope(args, torch, binding):
     print(json.dumps(line))
 
 
+QUANT4 = dict(B=16, N=8192, Hkv=1, d=128)   # the HCA K cache of the 1M-context decode shape
+
+
+def bench_quant4(args, torch, binding):
+    """4-bit storage of the decode HCA K cache (16 x 8192 x 1 x 128 bf16): one
+    encode (min/max pass + code pass) and one decode per step."""
+    from sparse_hybrid_attention_amd import synth
+    c = QUANT4
+    n = c["B"] * c["N"] * c["Hkv"] * c["d"]
+    xh = synth.make_quant(n=n, seed=0)
+    dev = "cuda:0"
+    x = torch.from_numpy(xh.view(np.int16)).to(dev).view(torch.bfloat16)
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
+    params = torch.empty(2, dtype=torch.float32, device=dev)
+    out = torch.empty_like(x)
+    lib = binding.load_library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        binding._check(lib.cache_quant4(x.data_ptr(), n, binding.DTYPE_BF16, codes.data_ptr(), params.data_ptr(), sp))
+        binding._check(lib.cache_dequant4(codes.data_ptr(), params.data_ptr(), n, binding.DTYPE_BF16,
+                                          out.data_ptr(), sp))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    alg = 2 * n * 2 + (n + 1) // 2 + (n + 1) // 2 + n * 2   # encode reads x twice, writes codes; decode reads codes, writes x
+    ach = alg / (kms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            pk, mn, st = O.quant4(xh, binding.DTYPE_BF16)
+            O.dequant4(pk, mn, st, n, binding.DTYPE_BF16)
+            dt_cpu = time.perf_counter() - t1
+        cpu = {"value": round(n / dt_cpu, 1), "unit": "elements/s", "cores": 1, "kind": "oracle",
+               "sample": f"one encode and decode of the whole {n}-element tensor; NumPy, one thread; {dt_cpu:.1f} s"}
+    line = {
+        "metric": "4-bit cache storage elements/s (encode + decode)",
+        "value": round(n * args.steps / wall, 1),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws, resident in HBM)",
+        "config": {"workload": f"4-bit storage of the decode HCA K cache, B{c['B']} x {c['N']} entries x "
+                               f"Hkv{c['Hkv']} x d{c['d']} bf16", "name": "quant4_hca",
+                   "gpu_ms_per_step_events": round(kms, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 6), "kernel": "quant4 (all launches of a step)",
+                     "traffic": None, "alg_bytes_per_step": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,7 +537,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyr2_bf16",
                     help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m, "
-                         "decode_append (cache maintenance), rope_q (RoPE on the query tensor)")
+                         "decode_append (cache maintenance), rope_q (RoPE on the query tensor), "
+                         "quant4_hca (4-bit cache storage)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -514,6 +582,9 @@ def main():
         return
     if args.workload == "rope_q":
         bench_rope(args, torch, binding)
+        return
+    if args.workload == "quant4_hca":
+        bench_quant4(args, torch, binding)
         return
     log(f"[bench] building inputs for {args.workload}")
     inp = build_inputs(args.workload, gates=args.gates)

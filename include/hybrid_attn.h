@@ -289,6 +289,35 @@ SHATTN_API int rope_apply(void* x, const int64_t* pos, int64_t rows, int32_t hea
                           int32_t rope_off, int32_t rope_dim, double base, int32_t dtype, void* stream);
 
 /*
+ * 4-bit storage of a compressed cache (K or V of CSA / HCA, any shape): one
+ * minimum and one step over the whole tensor, two codes per byte.
+ *
+ * Page: [V4-code] section "1. HCA" (the merged cache is stored in 4 bits:
+ * minimum and maximum over the tensor, step = (max - min) / 15, codes rounded
+ * and clamped to 0..15, decoded as code * step + min; packing two codes per
+ * byte is named there as the real layout).  Reading: the code of element i is
+ * rint((x[i] - min) / step) clamped to [0, 15], computed in float32 with
+ * round-half-even; step == 0 (a constant tensor) gives code 0 everywhere.
+ *
+ * cache_quant4:
+ *   x      : [n] dtype, DEVICE memory (finite values)
+ *   codes  : [ceil(n / 2)] uint8, DEVICE memory, written: element 2j in the low
+ *            nibble of byte j, element 2j + 1 in the high nibble (0 past n)
+ *   params : [2] float32, DEVICE memory, 4-byte aligned, written: (min, step);
+ *            it doubles as the scratch of the min / max reduction, so a second
+ *            call must not use the same params while one is in flight
+ * cache_dequant4:
+ *   out[i] = code_i * step + min in float32 (one fused multiply-add), rounded
+ *   once to dtype; codes / params as written by cache_quant4.
+ * Errors (SHATTN_EINVAL): unknown dtype, n < 0, null or misaligned pointers
+ * with n > 0.  n == 0 is a no-op (params untouched).
+ */
+SHATTN_API int cache_quant4(const void* x, int64_t n, int32_t dtype, uint8_t* codes, float* params,
+                            void* stream);
+SHATTN_API int cache_dequant4(const uint8_t* codes, const float* params, int64_t n, int32_t dtype, void* out,
+                              void* stream);
+
+/*
  * Measurement aid (not part of the attention path): launches `workgroups`
  * workgroups of 256 threads; every wave issues `iters` rounds of independent
  * bf16 MFMAs: shape 0 = 8 x v_mfma_f32_16x16x32_bf16 per round, shape 1 =

@@ -35,6 +35,8 @@ EXPORTED = (
     "hybrid_sparse_attn_fwd",
     "hybrid_cache_append",
     "rope_apply",
+    "cache_quant4",
+    "cache_dequant4",
     "shattn_mfma_peak_probe",
     "shattn_last_error",
 )
@@ -133,6 +135,10 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_cache_append.restype = i32
         lib.rope_apply.argtypes = [vp, vp, i64, i32, i32, i32, i32, ctypes.c_double, i32, vp]
         lib.rope_apply.restype = i32
+        lib.cache_quant4.argtypes = [vp, i64, i32, vp, vp, vp]
+        lib.cache_quant4.restype = i32
+        lib.cache_dequant4.argtypes = [vp, vp, i64, i32, vp, vp]
+        lib.cache_dequant4.restype = i32
         lib.shattn_mfma_peak_probe.argtypes = [i32, i32, i32, vp, vp]
         lib.shattn_mfma_peak_probe.restype = i32
         lib.shattn_last_error.argtypes = []
@@ -396,6 +402,37 @@ def rope_apply(x, pos, *, rope_off: int = 0, rope_dim: int = None, base: float =
     _check(lib.rope_apply(_ptr(x), _ptr(pos), rows, heads, d, rope_off, rope_dim, float(base), _dtype_code(x),
                           _stream(x)))
     return x
+
+
+def cache_quant4(x, codes=None, params=None):
+    """4-bit storage of a cache tensor: returns (codes uint8 [ceil(n/2)],
+    params float32 [2] = (min, step)), both on x's device."""
+    _need(x, "x")
+    n = x.numel()
+    if codes is None:
+        codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=x.device)
+    if params is None:
+        params = torch.empty(2, dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, x.device)
+    _need(params, "params", torch.float32, x.device)
+    if codes.numel() != (n + 1) // 2 or params.numel() != 2:
+        raise ValueError("cache_quant4: codes needs ceil(n/2) bytes and params 2 floats")
+    lib = load_library()
+    _check(lib.cache_quant4(_ptr(x), n, _dtype_code(x), _ptr(codes), _ptr(params), _stream(x)))
+    return codes, params
+
+
+def cache_dequant4(codes, params, out):
+    """Decode cache_quant4's codes into out (its dtype and element count)."""
+    _need(out, "out")
+    _need(codes, "codes", torch.uint8, out.device)
+    _need(params, "params", torch.float32, out.device)
+    n = out.numel()
+    if codes.numel() != (n + 1) // 2 or params.numel() != 2:
+        raise ValueError("cache_dequant4: codes needs ceil(n/2) bytes and params 2 floats")
+    lib = load_library()
+    _check(lib.cache_dequant4(_ptr(codes), _ptr(params), n, _dtype_code(out), _ptr(out), _stream(out)))
+    return out
 
 
 def default_scale(d: int) -> float:

@@ -207,3 +207,13 @@ def make_rope(*, rows, heads, d, dtype=DTYPE_BF16, max_pos=1 << 20, seed: int = 
     if rows > 2:
         pos[0], pos[1], pos[-1] = 0, -1, max_pos - 1
     return dict(x=x, pos=pos)
+
+
+def make_quant(*, n, dtype=DTYPE_BF16, constant=None, seed: int = 0) -> np.ndarray:
+    """A flat cache-like tensor of n N(0, 1) draws in storage form (or n
+    copies of `constant`)."""
+    if constant is not None:
+        x = np.full(n, constant, np.float32)
+        return f32_to_bf16_bits(x) if dtype == DTYPE_BF16 else x
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _normal(rng, (n,), dtype)

@@ -236,6 +236,23 @@ def test_rope_errors(lib):
     assert call(rows=0, x=None, pos=None) == binding.SHATTN_OK
 
 
+def test_quant4_errors(lib):
+    q, dq = lib.cache_quant4, lib.cache_dequant4
+    X, C, P = 0x7F0000000000, 0x7F0000002000, 0x7F0000004000   # never dereferenced
+    assert q(X, 10, 7, C, P, None) == binding.SHATTN_EINVAL        # dtype
+    assert q(X, -1, binding.DTYPE_BF16, C, P, None) == binding.SHATTN_EINVAL
+    assert q(None, 10, binding.DTYPE_BF16, C, P, None) == binding.SHATTN_EINVAL
+    assert q(X, 10, binding.DTYPE_BF16, None, P, None) == binding.SHATTN_EINVAL
+    assert q(X + 1, 10, binding.DTYPE_BF16, C, P, None) == binding.SHATTN_EINVAL   # misaligned elements
+    assert q(X, 10, binding.DTYPE_F32, C, P + 2, None) == binding.SHATTN_EINVAL    # params 4-byte aligned
+    assert q(None, 0, binding.DTYPE_BF16, None, None, None) == binding.SHATTN_OK   # empty: no-op
+    assert dq(C, P, 10, 9, X, None) == binding.SHATTN_EINVAL
+    assert dq(None, P, 10, binding.DTYPE_BF16, X, None) == binding.SHATTN_EINVAL
+    assert dq(C, P, 10, binding.DTYPE_F32, X + 2, None) == binding.SHATTN_EINVAL
+    assert "aligned" in err(lib)
+    assert dq(None, None, 0, binding.DTYPE_BF16, None, None) == binding.SHATTN_OK
+
+
 def test_library_refuses_to_fall_back(tmp_path, monkeypatch):
     # a missing library is an error, never a silent CPU path
     monkeypatch.setattr(binding, "_lib", None)
