@@ -3,7 +3,8 @@
  * forward pass: HCA (heavily compressed), CSA (compressed + sparse-selected) and
  * SWA (sliding window) branches mixed by gates (per head or per token), the
  * decode-time maintenance of the raw window ring and the compressed caches,
- * and the rotary position embedding applied to Q and K before the path.
+ * the rotary position embedding applied to Q and K before the path, and the
+ * 4-bit storage of a compressed cache.
  *
  * Pages this interface follows (cited by title and section):
  *   [V4-blog] "deepseek-v4" (astro-blog post), section "1. hybrid attn":
