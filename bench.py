@@ -4,9 +4,10 @@
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM: block compression of K/V for CSA (m=4) and HCA
 (m=128), lightning-indexer scoring + exact top-k, and the gated window + HCA
-+ CSA attention.  Default workload: the Tiny-R2 training shape (B8 T2048
-H=Hkv=12 d128 bf16, CSA k64 with 4 indexer heads, HCA m128, W128, all three
-branches mixed with U(0,1) gates).  Prints one JSON line.
++ CSA attention.  Default workload: the CSA-only long prefill (B1 T131072
+H32 Hkv4 d128 bf16, CSA m4 k512 with 4 indexer heads, W128, gates [0,1,0]),
+the largest configuration that fits one GPU; every timed step starts from
+flushed caches.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -145,65 +146,77 @@ def algorithmic(inp, pipe):
     return out
 
 
-def measure_peaks(torch, binding):
-    """Measured device peaks to read the roofline fractions against: a 1 GiB
-    device-to-device copy (bytes read + written per second) and the bf16 MFMA
-    issue rate of a loop of independent MFMAs (shattn_mfma_peak_probe)."""
-    import ctypes
+PROBE_LIB = os.path.join(ROOT, "sparse_hybrid_attention_amd", "libshattn_probe.so")
+
+
+def load_probes():
+    """The device measurement probes (libshattn_probe.so, built beside the
+    library; not part of it)."""
+    lib = ctypes.CDLL(PROBE_LIB)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.shattn_probe_mfma.argtypes = [i32, i32, i32, vp, vp]
+    lib.shattn_probe_mfma.restype = i32
+    lib.shattn_probe_gather.argtypes = [vp, i64, i32, i64, i64, i32, i32, vp, vp]
+    lib.shattn_probe_gather.restype = i32
+    return lib
+
+
+def measure_peaks(torch):
+    """Measured device ceilings to read the roofline fractions against: a
+    1 GiB device-to-device copy (bytes read + written per second), the bf16
+    MFMA issue rate of a loop of independent MFMAs, and the rate of random
+    256-byte row gathers from a table that fits the last-level cache (64 MiB,
+    the size of the 128K prefill's CSA cache) and from one that does not
+    (4 GiB)."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     b = torch.empty_like(a)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = None
-    for _ in range(4):
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    copy_gbs = 2.0 * n / (best * 1e-3) / 1e9
-    del a, b
-    lib = binding.load_library()
-    wgs, iters = 2048, 2048
-    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    rates = {}
-    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+
+    def best_of(fn, reps=4):
         best = None
-        for _ in range(4):
+        for _ in range(reps):
             e0.record()
-            rc = lib.shattn_mfma_peak_probe(wgs, iters, shape, ctypes.c_void_p(sink.data_ptr()), stream)
+            fn()
             e1.record()
             torch.cuda.synchronize()
-            if rc != 0:
-                raise RuntimeError(lib.shattn_last_error().decode())
             ms = e0.elapsed_time(e1)
             best = ms if best is None else min(best, ms)
-        rates[name] = round(wgs * 4 * iters * 131072 / (best * 1e-3) / 1e12, 1)
+        return best
+    copy_gbs = 2.0 * n / (best_of(lambda: b.copy_(a)) * 1e-3) / 1e9
+    del b
+    probes = load_probes()
+    wgs, iters = 2048, 2048
+    sink = torch.empty(16384 * 256, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+    rates = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        ms = best_of(lambda: chk(probes.shattn_probe_mfma(wgs, iters, shape, ctypes.c_void_p(sink.data_ptr()),
+                                                          stream)))
+        rates[name] = round(wgs * 4 * iters * 131072 / (ms * 1e-3) / 1e12, 1)
+    gather = {}
+    reads = 1 << 26                       # 16 GiB of 256-byte rows per launch
+    for name, tbytes in (("llc_64MiB", 64 << 20), ("hbm_1GiB", 1 << 30)):
+        nrows = tbytes // 256
+        ms = best_of(lambda: chk(probes.shattn_probe_gather(ctypes.c_void_p(a.data_ptr()), nrows, 256, 256, reads, 8,
+                                                            8192, ctypes.c_void_p(sink.data_ptr()), stream)), 3)
+        gather[name] = round(reads * 256 / (ms * 1e-3) / 1e9, 1)
+    del a
     return {"copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": max(rates.values()),
             "mfma_bf16_TFLOPs_by_shape": rates,
-            "method": "best of 4: 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 rounds of "
-                      "independent bf16 MFMAs per wave (8 x 16x16x32 or 4 x 32x32x16)"}
+            "gather_256B_rows_GBps": gather,
+            "method": "best of 4 (gathers: 3): 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 "
+                      "rounds of independent bf16 MFMAs per wave (8 x 16x16x32 or 4 x 32x32x16); 2^26 reads of "
+                      "random 256-byte rows from a 64 MiB or 1 GiB table, 8192 workgroups, 8 reads in flight "
+                      "per lane"}
 
 
-def cold_steps(torch, pipe, reps=20, flush_bytes=512 << 20):
-    """Median step time with L2 / MALL flushed before every step (a 512 MiB
-    buffer is overwritten between steps; the flush is outside the timed span)."""
-    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    times = []
-    for r in range(reps):
-        scratch.fill_(r & 255)
-        e0.record(pipe.stream)
-        pipe.run()
-        e1.record(pipe.stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    del scratch
-    times.sort()
-    return {"ms_per_step_median": round(times[len(times) // 2], 5), "reps": reps,
-            "flush_MiB": flush_bytes >> 20}
+def flush_buffer(torch, nbytes=512 << 20):
+    return torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
 
 
 def source_hash(fname):
@@ -230,54 +243,146 @@ def traffic_for(kernel, workload):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(inp, budget_rows):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def host_info():
+    """CPU model and the BLAS library NumPy is built with (for cpu_baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:
+        pass
+    return model, blas
+
+
+def host_workers():
+    """Worker processes for the oracle: the host cores this process may use,
+    at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_CPU = {}   # inputs shared with forked workers (copy on write)
+
+
+def _oracle_block(job):
+    """Oracle work of one block of consecutive query rows [i0, i1) of sequence
+    b (prefill) or of one sequence (decode): indexer + top-k, attention."""
     import oracle as O
+    from threadpoolctl import threadpool_limits
+    inp, cfg, comp = _CPU["inp"], _CPU["cfg"], _CPU["comp"]
+    dt = cfg["dtype"]
+    b, i0, i1 = job
+    with threadpool_limits(limits=1):
+        if cfg["kind"] == "decode":
+            sl = slice(b, b + 1)
+            q_pos0, raw_pos0 = inp["q_pos0"], inp["raw_pos0"]
+            csa = None
+            if cfg.get("m_csa"):
+                sel = O.index_topk(inp["qI"][sl], inp["kI"][sl], inp["w"][sl], q_pos0, cfg["m_csa"], cfg["W"],
+                                   cfg["k"], dt)
+                csa = (inp["k_csa"][sl], inp["v_csa"][sl], sel)
+            hca = (inp["k_hca"][sl], inp["v_hca"][sl], cfg["m_hca"]) if cfg.get("m_hca") else None
+            O.hybrid_attn_fwd(inp["q"][sl], inp["k_win"][sl], inp["v_win"][sl], inp["gates"], W=cfg["W"], dtype=dt,
+                              q_pos0=q_pos0, raw_pos0=raw_pos0, hca=hca, csa=csa)
+            return 1
+        W = cfg["W"]
+        r0 = max(0, i0 - W + 1)
+        sl = slice(b, b + 1)
+        csa = None
+        if cfg.get("m_csa"):
+            sel = O.index_topk(inp["qI"][sl, i0:i1], inp["kI"][sl], inp["w"][sl, i0:i1], i0, cfg["m_csa"], W,
+                               cfg["k"], dt)
+            csa = (comp["kc"][sl], comp["vc"][sl], sel)
+        hca = (comp["kh"][sl], comp["vh"][sl], cfg["m_hca"]) if cfg.get("m_hca") else None
+        O.hybrid_attn_fwd(inp["q"][sl, i0:i1], inp["k"][sl, r0:i1], inp["v"][sl, r0:i1], inp["gates"], W=W,
+                          dtype=dt, q_pos0=i0, raw_pos0=r0, hca=hca, csa=csa)
+        return i1 - i0
+
+
+def _oracle_worker(args):
+    """Run blocks from this worker's list until its time budget is spent."""
+    jobs, budget = args
+    t0 = time.perf_counter()
+    rows = 0
+    for job in jobs:
+        rows += _oracle_block(job)
+        if time.perf_counter() - t0 >= budget:
+            break
+    return rows, time.perf_counter() - t0
+
+
+def cpu_baseline(inp, budget_s=12.0, block=32):
+    """The oracle, as it stands (float64 NumPy), on a bounded sample of the
+    same workload, spread over the host cores: one worker process per core
+    (at most 16), each single-threaded, each taking blocks of `block`
+    consecutive query rows at random offsets until `budget_s` seconds are
+    spent.  The block compression the sample needs is done once (one thread)
+    and charged per query of the whole workload.  Runs before the GPU is
+    initialised (the workers are forked)."""
+    import multiprocessing as mp
+
+    import oracle as O
+    from threadpoolctl import threadpool_limits
     cfg = inp["cfg"]
     dt = cfg["dtype"]
-    t0 = time.perf_counter()
     B = cfg["B"]
+    comp = {}
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        if cfg["kind"] != "decode":
+            if cfg.get("m_csa"):
+                comp["kc"], comp["vc"] = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"],
+                                                       dt)
+            if cfg.get("m_hca"):
+                comp["kh"], comp["vh"] = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"],
+                                                       dt)
+    t_comp = time.perf_counter() - t0
+    nw = host_workers()
+    rng = np.random.default_rng(1)
     if cfg["kind"] == "decode":
-        Tq = 1
-        q_pos0, raw_pos0 = inp["q_pos0"], inp["raw_pos0"]
-        rows = [(b, 0) for b in range(min(B, 2))]
-        t_comp = 0.0
-        hca = (inp["k_hca"], inp["v_hca"], cfg["m_hca"])
-        kc, vc = inp["k_csa"], inp["v_csa"]
-        kr, vr = inp["k_win"], inp["v_win"]
         total_q = B
+        order = [(b, 0, 1) for b in rng.permutation(B)]
+        lists = [order[w::nw] for w in range(nw)]
     else:
-        Tq = cfg["T"]
-        q_pos0 = raw_pos0 = 0
-        rng = np.random.default_rng(1)
-        rows = sorted({(int(rng.integers(0, B)), int(rng.integers(0, Tq))) for _ in range(budget_rows)})
-        hca = None
-        kc = vc = None
-        if cfg.get("m_hca"):
-            kh, vh = O.compress_kv(inp["k"], inp["v"], inp["zk_hca"], inp["zv_hca"], cfg["m_hca"], dt)
-            hca = (kh, vh, cfg["m_hca"])
-        if cfg.get("m_csa"):
-            kc, vc = O.compress_kv(inp["k"], inp["v"], inp["zk_csa"], inp["zv_csa"], cfg["m_csa"], dt)
-        t_comp = time.perf_counter() - t0
-        kr, vr = inp["k"], inp["v"]
-        total_q = B * Tq
+        T = cfg["T"]
+        total_q = B * T
+        lists = []
+        for w in range(nw):
+            lst = []
+            for _ in range(4096):
+                b = int(rng.integers(0, B))
+                i0 = int(rng.integers(0, max(1, T - block + 1)))
+                lst.append((b, i0, min(T, i0 + block)))
+            lists.append(lst)
+    _CPU.update(inp=inp, cfg=cfg, comp=comp)
+    ctx = mp.get_context("fork")
     t1 = time.perf_counter()
-    csa = None
-    if cfg.get("m_csa"):
-        sel = O.index_topk(inp["qI"], inp["kI"], inp["w"], q_pos0, cfg["m_csa"], cfg["W"], cfg["k"], dt,
-                           rows=rows)
-        idx = np.full((B, Tq, cfg["k"]), -1, dtype=np.int32)
-        for r, (b, i) in enumerate(rows):
-            idx[b, i] = sel[r]
-        csa = (kc, vc, idx)
-    O.hybrid_attn_fwd(inp["q"], kr, vr, inp["gates"], W=cfg["W"], dtype=dt, q_pos0=q_pos0,
-                      raw_pos0=raw_pos0, hca=hca, csa=csa, rows=rows)
-    t_rows = time.perf_counter() - t1
-    per_query = t_comp / total_q + t_rows / len(rows)
-    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(rows)} query rows (all heads, all branches, indexer + attention) "
-                      f"plus the full K/V compression of the batch ({t_comp:.1f} s, charged "
-                      f"per query); float64 NumPy, single thread; {t_comp + t_rows:.1f} s total"}
+    with ctx.Pool(nw) as pool:
+        res = pool.map(_oracle_worker, [(l, budget_s) for l in lists])
+    wall = time.perf_counter() - t1
+    _CPU.clear()
+    rows = sum(r for r, _ in res)
+    per_query = t_comp / total_q + wall / rows
+    model, blas = host_info()
+    unit = "queries/s"
+    return {"value": round(1.0 / per_query, 2), "unit": unit, "cores": nw, "kind": "oracle",
+            "sample": (f"{rows} query rows (all heads, all branches: indexer + top-k + attention) in blocks of "
+                       f"{block if cfg['kind'] != 'decode' else 1} consecutive rows at random offsets, {nw} worker "
+                       f"processes x 1 thread for {wall:.1f} s wall; plus the block compression of the whole "
+                       f"batch ({t_comp:.1f} s, one thread, charged per query); float64 NumPy (the oracle's only "
+                       f"precision: the timed code is the code the parity tests check)"),
+            "cpu_model": model, "blas": blas, "threads_per_worker": 1}
 
 
 # ------------------------------------------------------------------ main
@@ -530,22 +635,61 @@ def bench_quant4(args, torch, binding):
     print(json.dumps(line))
 
 
+WORKLOADS = {
+    "tinyr2_bf16": "Tiny-R2 training-shape forward, B8 T2048 H=Hkv=12 d128 bf16, CSA m4 k64 "
+                   "(indexer 4 heads d_idx 64), HCA m128, W128, gates U(0,1) (all branches)",
+    "tiny_fp32": "tiny fp32 forward, B1 T256 H=Hkv=4 d64, CSA m4 k8 (indexer 2 heads), HCA m32, W32",
+    "hca_prefill_32k": "HCA-only prefill, B1 T32768 H16 Hkv2 d128 bf16, m128, W128, gates [1,0,0]",
+    "csa_prefill_128k": "CSA-only long prefill, B1 T131072 H32 Hkv4 d128 bf16, m4 (32768 entries), k512 "
+                        "(4 indexer heads, d_idx 64, fp32 scores), W128, gates [0,1,0]",
+    "decode_1m": "decode, B16 x 1 query at 1,048,576 context, H32 Hkv1 d128 bf16, CSA 262144 entries "
+                 "k1024 (4 indexer heads, d_idx 64), HCA 8192 entries, W128, gates U(0,1)",
+}
+
+
+def timed_steps(torch, pipe, names, steps, flush):
+    """`steps` steps between two synchronisations; with `flush`, every step
+    starts with L2 and MALL flushed (a 512 MiB buffer overwritten on the
+    pipeline's stream just before it: the flush is inside the timed wall, so
+    it only makes the figure conservative).  Per-kernel HIP events are
+    recorded on the pipeline's stream around each launch."""
+    scratch = flush_buffer(torch) if flush else None
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        if flush:
+            with torch.cuda.stream(pipe.stream):
+                scratch.fill_(s & 255)
+        pipe.run(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del scratch
+    ktime = {n: 0.0 for n in names}
+    for s in range(steps):
+        for j, n in enumerate(names):
+            ktime[n] += evs[s][j].elapsed_time(evs[s][j + 1])
+    ktime = {n: v / steps for n, v in ktime.items()}   # ms per launch (mean)
+    step_ms = sorted(evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps))
+    return wall, ktime, step_ms
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tinyr2_bf16",
-                    help="tinyr2_bf16 (default), tiny_fp32, hca_prefill_32k, csa_prefill_128k, decode_1m, "
-                         "decode_append (cache maintenance), rope_q (RoPE on the query tensor), "
-                         "quant4_hca (4-bit cache storage)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="csa_prefill_128k",
+                    help="csa_prefill_128k (default: the largest single-GPU configuration), tinyr2_bf16, "
+                         "tiny_fp32, hca_prefill_32k, decode_1m, decode_append (cache maintenance), rope_q (RoPE "
+                         "on the query tensor), quant4_hca (4-bit cache storage)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the cache-flushed step timing and the measured-peak probes")
-    ap.add_argument("--cpu-rows", type=int, default=10000,
-                    help="query rows of the CPU-baseline sample (about 10-15 s of oracle work at the default workload)")
+                    help="skip the warm (back-to-back) timing and the measured-peak probes")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall seconds of oracle work per host worker in the CPU baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scaling for rocprofv3)")
     args = ap.parse_args()
@@ -557,6 +701,17 @@ def main():
               "top-k candidates). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    pipeline_workload = args.workload in WORKLOADS
+    inp = cpu = None
+    if pipeline_workload and not args.copy_probe:
+        log(f"[bench] building inputs for {args.workload}")
+        inp = build_inputs(args.workload, gates=args.gates)
+        if not args.no_cpu_baseline:
+            # before the GPU is touched: the oracle's worker processes are forked
+            log("[bench] timing the CPU oracle on a bounded sample")
+            cpu = cpu_baseline(inp, budget_s=args.cpu_seconds)
+            log(f"[bench] cpu baseline {cpu['value']:.2f} queries/s on {cpu['cores']} workers")
 
     import torch
     if not torch.cuda.is_available():
@@ -586,38 +741,29 @@ def main():
     if args.workload == "quant4_hca":
         bench_quant4(args, torch, binding)
         return
-    log(f"[bench] building inputs for {args.workload}")
-    inp = build_inputs(args.workload, gates=args.gates)
+    if not pipeline_workload:
+        raise SystemExit(f"unknown workload {args.workload}")
     cfg = inp["cfg"]
     pipe = make_pipeline(inp)
     names = pipe.names()
-    stream = pipe.stream
     log(f"[bench] kernels per step: {names}; warmup {args.warmup}")
     for _ in range(args.warmup):
         pipe.run()
     torch.cuda.synchronize()
     alg = algorithmic(inp, pipe)
 
-    # timed region: K steps, per-kernel HIP events on the pipeline's stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        pipe.run(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log(f"[bench] timed {args.steps} steps in {wall * 1e3:.2f} ms")
-    ktime = {n: 0.0 for n in names}
-    for s in range(args.steps):
-        for j, n in enumerate(names):
-            ktime[n] += evs[s][j].elapsed_time(evs[s][j + 1])
-    ktime = {n: v / args.steps for n, v in ktime.items()}   # ms per launch
-    gpu_ms = sum(evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)) / args.steps
+    # timed region: exactly K steps, each from flushed caches (headline)
+    wall, ktime, step_ms = timed_steps(torch, pipe, names, args.steps, flush=True)
+    log(f"[bench] timed {args.steps} cold steps in {wall * 1e3:.2f} ms")
+    warm = None
+    if not args.no_extras:
+        w_wall, w_ktime, w_step = timed_steps(torch, pipe, names, args.steps, flush=False)
+        warm = {"ms_per_step": round(w_wall * 1e3 / args.steps, 5),
+                "gpu_ms_per_step_median": round(w_step[len(w_step) // 2], 5),
+                "kernels_ms": {n: round(v, 5) for n, v in w_ktime.items()},
+                "note": "the same steps back to back, caches warm from the previous step"}
     ms_per_step = wall * 1e3 / args.steps
-    if cfg["kind"] == "decode":
-        queries = cfg["B"]
-    else:
-        queries = cfg["B"] * cfg["T"]
+    queries = cfg["B"] if cfg["kind"] == "decode" else cfg["B"] * cfg["T"]
     value = queries * args.steps / wall
     dtype = "bf16" if cfg["dtype"] == 0 else "f32"
 
@@ -633,6 +779,7 @@ def main():
             e["alg_bytes"] = a["bytes"]
             e["alg_flops"] = a["flops"]
             if "gathered_bytes" in a:
+                e["gathered_bytes"] = a["gathered_bytes"]
                 e["gathered GB/s"] = round(a["gathered_bytes"] / (ms * 1e-3) / 1e9, 1)
         kernels[n] = e
     dom = max(names, key=lambda n: ktime[n])
@@ -649,34 +796,24 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
+    roof["kernel_ms"] = round(ms, 5)
+    roof["alg_per_launch"] = a["flops"] if roof["unit"] == "TFLOP/s" else a["bytes"]
     roof["traffic"] = traffic_for(dom, args.workload)
 
-    # after the timed region: the same step with caches flushed, and the
-    # measured device peaks (extra fields beside the headline)
-    cold = cold_steps(torch, pipe) if not args.no_extras else None
-    peaks = measure_peaks(torch, binding) if not args.no_extras else None
+    peaks = measure_peaks(torch) if not args.no_extras else None
     if peaks is not None and (roof["unit"] == "GB/s" or dtype == "bf16"):
         roof["measured_peak"] = peaks["copy_GBps"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_TFLOPs"]
         roof["frac_of_measured"] = round(roof["achieved"] / roof["measured_peak"], 4)
+    if "gathered_bytes" in a:
+        # the gathered CSA rows: bytes the kernel reads from L2 / MALL per launch
+        # against the measured random-row gather rate of a cache-resident table
+        g = a["gathered_bytes"] / (ms * 1e-3) / 1e9
+        roof["gather"] = {"bytes_per_launch": a["gathered_bytes"], "achieved_GBps": round(g, 1)}
+        if peaks is not None:
+            ceil = peaks["gather_256B_rows_GBps"]["llc_64MiB"]
+            roof["gather"].update(ceiling_GBps=ceil, frac=round(g / ceil, 4),
+                                  ceiling="measured random 256-byte row gathers from a 64 MiB table")
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):   # the oracle runs on exactly one host thread
-            cpu = cpu_baseline(inp, args.cpu_rows)
-        log(f"[bench] cpu baseline {cpu['value']:.1f} queries/s")
-
-    desc = {
-        "tinyr2_bf16": "Tiny-R2 training-shape forward, B8 T2048 H=Hkv=12 d128 bf16, CSA m4 k64 "
-                       "(indexer 4 heads d_idx 64), HCA m128, W128, gates U(0,1) (all branches)",
-        "tiny_fp32": "tiny fp32 forward, B1 T256 H=Hkv=4 d64, CSA m4 k8 (indexer 2 heads), HCA m32, W32",
-        "hca_prefill_32k": "HCA-only prefill, B1 T32768 H16 Hkv2 d128 bf16, m128, W128, gates [1,0,0]",
-        "csa_prefill_128k": "CSA-only prefill, B1 T131072 H32 Hkv4 d128 bf16, m4, k512 (4 indexer heads), "
-                            "W128, gates [0,1,0]",
-        "decode_1m": "decode, B16 x 1 query at 1,048,576 context, H32 Hkv1 d128 bf16, CSA 262144 entries "
-                     "k1024, HCA 8192 entries, W128, gates U(0,1)",
-    }[args.workload]
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -690,13 +827,14 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
-        "config": {"workload": desc + ("" if args.gates is None else f" [gates: {args.gates}]"),
+        "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]"),
                    "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],
-                   "query_rows": queries, "gpu_ms_per_step_events": round(gpu_ms, 5)},
+                   "query_rows": queries, "timing": "each timed step starts from flushed L2 / MALL (cold)",
+                   "gpu_ms_per_step_median": round(step_ms[len(step_ms) // 2], 5)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "cold": cold,
+        "warm": warm,
         "measured_peaks": peaks,
     }
     print(json.dumps(line))

@@ -123,14 +123,15 @@ SHATTN_API int hca_compress_kv_dual(const void* k, const void* v, const float* z
  *   w   : [B, Tq, Hi]        float32    idx: [B, Tq, k] int32, written
  *   ws  : device workspace of at least csa_index_topk_workspace_size() bytes,
  *         256-byte aligned (may be NULL when that size is 0); its contents are
- *         scratch.  Sizes: 0 for N <= 2048; for longer prefill about
- *         8 * B * Tq * L bytes, L = per-query candidate list length (a few
- *         times k); for decode shapes (B * Tq <= 64, N >= 8192) about
- *         4 * B * Tq * N bytes.
- * Long prefill (N > 2048) is decided per query from a list of the entries
- * whose float32 score reaches a threshold estimated from every S-th entry;
- * queries whose list cannot decide are recomputed by streaming all entries,
- * so the result never depends on the estimate.
+ *         scratch.  Sizes: 0 for N <= 2048 with Hi < 16 and for N = 0; for
+ *         longer prefill (and Hi = 16) about 8 * B * Tq * L bytes, L =
+ *         per-query candidate list length (a few times k); for decode shapes
+ *         (B * Tq <= 64, N >= 8192) about 4 * B * Tq * N bytes.
+ * Long prefill (N > 2048, or any N > 0 with Hi = 16) is decided per query
+ * from a list of the entries whose float32 score reaches a threshold
+ * estimated from every S-th entry; queries whose list cannot decide are
+ * recomputed by streaming all entries, so the result never depends on the
+ * estimate.
  * Supported: Hi in {1, 2, 4, 8, 16}; d_idx in {64, 128}; 1 <= k <= 2048;
  *            m >= 1; W >= 1; N >= 0.
  */
@@ -317,18 +318,6 @@ SHATTN_API int cache_quant4(const void* x, int64_t n, int32_t dtype, uint8_t* co
                             void* stream);
 SHATTN_API int cache_dequant4(const uint8_t* codes, const float* params, int64_t n, int32_t dtype, void* out,
                               void* stream);
-
-/*
- * Measurement aid (not part of the attention path): launches `workgroups`
- * workgroups of 256 threads; every wave issues `iters` rounds of independent
- * bf16 MFMAs: shape 0 = 8 x v_mfma_f32_16x16x32_bf16 per round, shape 1 =
- * 4 x v_mfma_f32_32x32x16_bf16 per round (131072 flops per round and wave
- * either way), i.e. workgroups * 4 * iters * 131072 flops.  Time it on
- * `stream` to read the device's dense bf16 MFMA rate.  sink: device float32
- * [workgroups * 256], written (values that keep the work live).
- * Supported: 1 <= workgroups <= 65536, 1 <= iters <= 2^20, shape 0 or 1.
- */
-SHATTN_API int shattn_mfma_peak_probe(int workgroups, int iters, int shape, float* sink, void* stream);
 
 /* Message describing the calling thread's last failure ("" if none). */
 SHATTN_API const char* shattn_last_error(void);

@@ -90,7 +90,6 @@ __all__ = [
     "window_bounds", "visible_count",
     "indexer_scores", "select_topk", "index_topk", "index_topk_row",
     "attend", "attn_row", "hybrid_attn_fwd",
-    "score_key_order",
     "gate_weights",
     "cache_append",
     "rope",
@@ -254,14 +253,6 @@ def index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, dtype: int,
     for r, (b, i) in enumerate(rows):
         out[r], _ = index_topk_row(q[b, i], ww[b, i], kk[b], q_pos0 + i, m, W, k)
     return out
-
-
-def score_key_order(scores: np.ndarray) -> np.ndarray:
-    """Rank of each entry under (score desc, index asc); 0 is the best."""
-    order = np.lexsort((np.arange(scores.shape[0]), -scores))
-    rank = np.empty_like(order)
-    rank[order] = np.arange(order.shape[0])
-    return rank
 
 
 # --------------------------------------------------------------------------

@@ -9,7 +9,6 @@ first call does, and raises if the library has not been built.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import threading
 
@@ -37,7 +36,6 @@ EXPORTED = (
     "rope_apply",
     "cache_quant4",
     "cache_dequant4",
-    "shattn_mfma_peak_probe",
     "shattn_last_error",
 )
 
@@ -139,8 +137,6 @@ def load_library(path: str = LIB_PATH):
         lib.cache_quant4.restype = i32
         lib.cache_dequant4.argtypes = [vp, vp, i64, i32, vp, vp]
         lib.cache_dequant4.restype = i32
-        lib.shattn_mfma_peak_probe.argtypes = [i32, i32, i32, vp, vp]
-        lib.shattn_mfma_peak_probe.restype = i32
         lib.shattn_last_error.argtypes = []
         lib.shattn_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -433,10 +429,6 @@ def cache_dequant4(codes, params, out):
     lib = load_library()
     _check(lib.cache_dequant4(_ptr(codes), _ptr(params), n, _dtype_code(out), _ptr(out), _stream(out)))
     return out
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)
 
 
 class HybridPipeline:

@@ -2,7 +2,9 @@
 
 Usage: ``python -m sparse_hybrid_attention_amd.build_lib`` or ``build()``.
 Every HIP source under csrc/ is compiled to an object file in parallel, then
-linked into ``sparse_hybrid_attention_amd/libhybridattn.so``.
+linked into ``sparse_hybrid_attention_amd/libhybridattn.so``.  The device
+measurement probes under probe/ (used by the benchmark only, not part of the
+library or its interface) are linked into ``libshattn_probe.so`` beside it.
 """
 from __future__ import annotations
 
@@ -18,7 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
+PROBE = os.path.join(PKG, "probe")
 LIB = os.path.join(PKG, "libhybridattn.so")
+PROBE_LIB = os.path.join(PKG, "libshattn_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -42,7 +46,7 @@ FILE_FLAGS = {
     "attention.hip": ["-fno-honor-nans"],
     # the MFMA rate probe: accumulators in ordinary VGPRs (the accumulator-
     # register form of its loop is compiled with register copies per round)
-    "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 
 
@@ -55,20 +59,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE, "*.hip")))
+    jobs = min(len(srcs) + len(probe_srcs), max(1, min(16, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

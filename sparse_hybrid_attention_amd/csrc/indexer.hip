@@ -1543,6 +1543,13 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
                             p.idx + row * p.k);
 }
 
+// No candidate entries (N = 0): every index row is -1.
+__global__ __launch_bounds__(256) void index_fill_empty_kernel(IdxParams p) {
+    const long long n = (long long)p.B * p.Tq * p.k;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p.idx[i] = -1;
+}
+
 // ----------------------------------------------------------- host planning
 // launch shape of a kernel that tiles queries over waves (dense / prefill kernels)
 struct IdxLaunch {
@@ -1556,6 +1563,7 @@ struct IdxPlan {
     bool split;
     bool dense;  // small N: all scores of a query in LDS, one exact select
     bool longp;  // long prefill pipeline (sample, filter, list final, fallback)
+    bool empty;  // no candidates (N = 0): every row is -1
     size_t lds;  // dense: per workgroup; split: final kernel; long: list final kernel
     size_t lds_score;
     long long grid;
@@ -1600,6 +1608,7 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     pl.grid = 0;
     pl.dense = false;
     pl.longp = false;
+    pl.empty = false;
     pl.ls = IdxLaunch{};
     pl.lf = IdxLaunch{};
     pl.grid_kmax = pl.grid_filter = 0;
@@ -1643,7 +1652,17 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
         return SHATTN_OK;
     }
     const int qpt = 16 / Hi;
-    pl.dense = N > 0 && N <= kDenseMaxN;
+    if (N == 0) {
+        // no candidates: every row is -1
+        pl.empty = true;
+        pl.grid = (rows * k + 255) / 256;
+        return SHATTN_OK;
+    }
+    // Hi = 16 never takes the dense kernel (selection from LDS, N <= 2048):
+    // that form at Hi = 16 is not covered by a passing GPU test (one build of
+    // it took a memory fault whose cause was not found), so Hi = 16 always
+    // takes the long pipeline below, whose kernels pass at Hi = 16.
+    pl.dense = N <= kDenseMaxN && Hi != 16;
     if (pl.dense) {
         // p.cap = per-query key slots (N rounded up to a tile).  The band list is
         // short (an overflowing band falls back to the float32 order): the
@@ -1664,17 +1683,6 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
             return SHATTN_OK;
         }
         p.cap = ((k + std::max(64, k / 2)) + 63) / 64 * 64;
-    }
-    if (N == 0) {
-        // no candidates: the dense kernel writes the -1 rows
-        pl.dense = true;
-        p.cap = 0;
-        p.qpw = qpt;
-        p.wave_stride = (int)((1024 + 12ull * p.mcap + 4ull * qpt + 15) / 16 * 16);
-        p.nqt = (Tq + WAVES * qpt - 1) / (WAVES * qpt);
-        pl.lds = (size_t)WAVES * p.wave_stride;
-        pl.grid = (long long)B * p.nqt;
-        return SHATTN_OK;
     }
     // ---- long prefill pipeline
     pl.longp = true;
@@ -1705,7 +1713,9 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     {
         int qpw = 4 * qpt;
         while (qpw > qpt && WAVES * sample_wave(qpw, np) > (size_t)kMaxLds) qpw -= qpt;
-        while (qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 1024) qpw -= qpt;
+        // Hi = 16 keeps four row tiles per wave (the form its tests cover)
+        while (Hi != 16 && qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 1024)
+            qpw -= qpt;
         pl.ls.qpw = qpw;
         pl.ls.cap = np;
         pl.ls.wave_stride = (int)sample_wave(qpw, np);
@@ -1777,6 +1787,10 @@ IdxParams with_launch(const IdxParams& p, const IdxLaunch& l) {
 template <typename T, int HI, int DI>
 int launch_idx(IdxPlan& pl, hipStream_t s) {
     int rc;
+    if (pl.empty) {
+        hipLaunchKernelGGL(index_fill_empty_kernel, dim3((unsigned)pl.grid), dim3(256), 0, s, pl.p);
+        return check_launch("csa_index_topk (empty)");
+    }
     if (pl.dense) {
         if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, false>), pl.lds))) return rc;
         hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, false>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds,

@@ -112,6 +112,9 @@ def test_index_errors(lib):
     assert "workspace" in err(lib)
     # prefill with N <= 2048 keeps every score in LDS: no workspace
     assert lib.csa_index_topk_workspace_size(2, 4096, 2048, 4, 64, 64) == 0
+    # ... except at 16 indexer heads, which always take the list pipeline
+    assert lib.csa_index_topk_workspace_size(2, 600, 150, 16, 128, 40) >= 8 * 1200 * 40
+    assert lib.csa_index_topk_workspace_size(2, 600, 0, 16, 128, 40) == 0
     # longer prefill keeps per-query candidate lists ((key, entry) pairs, at
     # least k per query) in the workspace: it grows with the query rows
     ws1 = lib.csa_index_topk_workspace_size(1, 4096, 8192, 4, 64, 64)
@@ -121,13 +124,34 @@ def test_index_errors(lib):
     assert f(None, P, P, P, 1, 16, 64, 4, 64, 0, 4, 8, 8, 0, None, 0, None) == binding.SHATTN_EINVAL
 
 
-def test_mfma_probe_rejects_bad_arguments(lib):
-    f = lib.shattn_mfma_peak_probe
-    assert f(0, 16, 0, P, None) == binding.SHATTN_EINVAL
-    assert f(16, 0, 0, P, None) == binding.SHATTN_EINVAL
-    assert f(16, 16, 2, P, None) == binding.SHATTN_EINVAL
-    assert f(16, 16, 0, None, None) == binding.SHATTN_EINVAL
-    assert "probe" in lib.shattn_last_error().decode()
+def test_probe_library_is_separate(lib):
+    # the device measurement probes live in their own library, declared in
+    # probe/probes.h; the attention library exports none of them
+    probe_lib = os.path.join(os.path.dirname(binding.LIB_PATH), "libshattn_probe.so")
+    header = os.path.join(ROOT, "sparse_hybrid_attention_amd", "probe", "probes.h")
+    declared = set(re.findall(r"SHATTN_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(header).read()))
+    assert declared == {"shattn_probe_mfma", "shattn_probe_gather"}
+    out = subprocess.run(["nm", "-D", "--defined-only", probe_lib], capture_output=True, text=True,
+                         check=True).stdout
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == declared
+    main = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                          check=True).stdout
+    assert "probe" not in main
+    pl = ctypes.CDLL(probe_lib)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pl.shattn_probe_mfma.argtypes = [i32, i32, i32, vp, vp]
+    pl.shattn_probe_gather.argtypes = [vp, i64, i32, i64, i64, i32, i32, vp, vp]
+    f = pl.shattn_probe_mfma
+    assert f(0, 16, 0, P, None) == -1
+    assert f(16, 0, 0, P, None) == -1
+    assert f(16, 16, 2, P, None) == -1
+    assert f(16, 16, 0, None, None) == -1
+    g = pl.shattn_probe_gather
+    assert g(P, 1024, 96, 256, 100, 4, 64, P, None) == -1      # row size
+    assert g(P, 1024, 256, 128, 100, 4, 64, P, None) == -1     # stride below the row
+    assert g(P, 0, 256, 256, 100, 4, 64, P, None) == -1        # no rows
+    assert g(P, 1024, 256, 256, 100, 3, 64, P, None) == -1     # depth
+    assert g(None, 1024, 256, 256, 100, 4, 64, P, None) == -1  # table
 
 
 def fwd(**kw):

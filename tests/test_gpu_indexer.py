@@ -64,6 +64,24 @@ def test_head_counts(Hi, d_idx):
     run_case(inp, what=f"Hi={Hi} d_idx={d_idx}")
 
 
+@pytest.mark.parametrize("d_idx", [64, 128])
+def test_hi16_short_candidate_sets(d_idx):
+    # Hi = 16 with N <= 2048 takes the long pipeline (sampling at four row
+    # tiles per wave, filter, list selection), never the dense kernel
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=40 + d_idx, B=2, T=650, Hi=16, d_idx=d_idx, k=33)
+    run_case(inp, what=f"Hi=16 d_idx={d_idx} N<=2048")
+
+
+@pytest.mark.parametrize("Hi", [4, 16])
+def test_no_candidates(Hi):
+    # N = 0: every row is -1
+    lib()
+    inp = synth.make_inputs("tinyr2_bf16", seed=50 + Hi, B=2, T=64, Hi=Hi, d_idx=64, k=12)
+    got = gpu_topk(inp["qI"], inp["kI"][:, :0], inp["w"], 0, 4, 128, 12)
+    assert got.shape == (2, 64, 12) and (got == -1).all()
+
+
 def test_dense_two_row_tiles_per_wave():
     # 32768 query rows: the dense plan gives each wave 8 queries (two row
     # tiles of 4 queries x 4 heads), the per-wave scoring path; smaller row
