@@ -141,6 +141,20 @@ SHATTN_API int csa_index_topk(const void* qI, const void* kI, const float* w, in
                    int dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_index_topk with one position per sequence (decode of sequences at
+ * different positions, [V4-blog] "1. hybrid attn": the compressed caches live
+ * with each sequence): query row i of sequence b has position q_pos[b] + i.
+ * q_pos is a DEVICE int64 array [B], 8-byte aligned; a negative q_pos[b]
+ * marks an inactive sequence (its rows are written all -1).  N may be the
+ * capacity of the kI cache: an entry is read only when it is visible at the
+ * row's position, so entries not yet written are never read.  Everything
+ * else (shapes, workspace, errors, the exact selection) as csa_index_topk.
+ */
+SHATTN_API int csa_index_topk_varlen(const void* qI, const void* kI, const float* w, int32_t* idx, int B,
+                                     int Tq, int N, int Hi, int d_idx, const int64_t* q_pos, int m, int W,
+                                     int k, int dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Gated hybrid attention forward ([V4-blog] "SWA": the raw window and the
  * compressed history enter one attention; [Tiny-R2] 3.1.2 / 3.2: three
  * branches mixed by a per-head gate, order [HCA, CSA, SWA]).
@@ -161,7 +175,13 @@ SHATTN_API int csa_index_topk(const void* qI, const void* kI, const float* w, in
  * branch with no entries (N = 0, pointers may then be NULL) still contributes
  * its window-only attention.  idx rows list distinct entries.
  * Raw K/V row r holds absolute position raw_pos0 + r; every window row the
- * queries need must lie in [raw_pos0, raw_pos0 + Tr).
+ * queries need must lie in [raw_pos0, raw_pos0 + Tr).  Decode with sequences
+ * at different positions ([V4-blog] "1. hybrid attn": the raw window and the
+ * compressed caches are kept apart, the raw rows age out): q_pos gives each
+ * sequence's position and raw_ring = 1 reads the window from the rings
+ * hybrid_cache_append maintains; the compressed caches hold the entries
+ * visible at each sequence's own position (N_hca / N_csa may be their
+ * capacity: entries a position cannot see are never read).
  */
 typedef struct shattn_fwd_args {
     int32_t struct_size; /* must equal sizeof(shattn_fwd_args) */
@@ -187,6 +207,15 @@ typedef struct shattn_fwd_args {
     const void* v_csa;
     const int32_t* idx;  /* [B, Tq, k] */
     const float* gates;  /* float32: [H, 3] (gate_mode 0) or [B, Tq, H, 3] (1, 2) */
+    const int64_t* q_pos; /* NULL, or DEVICE int64 [B]: position of query row 0 of
+                             each sequence (q_pos0 is then unused); a negative
+                             entry marks an inactive sequence whose output rows
+                             are left untouched.  Needs raw_ring = 1. */
+    int32_t raw_ring;    /* 0: raw row r holds position raw_pos0 + r.
+                            1: k_raw / v_raw are rings of Tr rows per sequence
+                            (as hybrid_cache_append keeps them): position t is
+                            in row t % Tr; raw_pos0 is unused and Tr >= W + Tq - 1. */
+    int32_t reserved0;   /* must be 0 */
 } shattn_fwd_args;
 
 /* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the
@@ -309,8 +338,9 @@ SHATTN_API int rope_apply(void* x, const int64_t* pos, int64_t rows, int32_t hea
  *            it doubles as the scratch of the min / max reduction, so a second
  *            call must not use the same params while one is in flight
  * cache_dequant4:
- *   out[i] = code_i * step + min in float32 (one fused multiply-add), rounded
- *   once to dtype; codes / params as written by cache_quant4.
+ *   out[i] = code_i * step + min, the product exact and the sum rounded to
+ *   float64, then rounded once (nearest even) to dtype; codes / params as
+ *   written by cache_quant4 (or any (min, step) pair the caller stores).
  * Errors (SHATTN_EINVAL): unknown dtype, n < 0, null or misaligned pointers
  * with n > 0.  n == 0 is a no-op (params untouched).
  */

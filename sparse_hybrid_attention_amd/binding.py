@@ -30,6 +30,7 @@ EXPORTED = (
     "hca_compress_kv_dual",
     "csa_index_topk_workspace_size",
     "csa_index_topk",
+    "csa_index_topk_varlen",
     "hybrid_sparse_attn_fwd_workspace_size",
     "hybrid_sparse_attn_fwd",
     "hybrid_cache_append",
@@ -73,6 +74,9 @@ class FwdArgs(ctypes.Structure):
         ("v_csa", ctypes.c_void_p),
         ("idx", ctypes.c_void_p),
         ("gates", ctypes.c_void_p),
+        ("q_pos", ctypes.c_void_p),
+        ("raw_ring", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -125,6 +129,9 @@ def load_library(path: str = LIB_PATH):
         lib.csa_index_topk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32,
                                        i32, i32, vp, sz, vp]
         lib.csa_index_topk.restype = i32
+        lib.csa_index_topk_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32,
+                                              i32, i32, vp, sz, vp]
+        lib.csa_index_topk_varlen.restype = i32
         lib.hybrid_sparse_attn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
         lib.hybrid_sparse_attn_fwd_workspace_size.restype = sz
         lib.hybrid_sparse_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp, sz, vp]
@@ -220,8 +227,11 @@ def csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k) -> int:
     return int(load_library().csa_index_topk_workspace_size(B, Tq, N, Hi, d_idx, k))
 
 
-def csa_index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, out=None, ws=None):
-    """Per-query top-k CSA entries; returns int32 [B, Tq, k] (ascending, -1 padded)."""
+def csa_index_topk(qI, kI, w, q_pos0, m: int, W: int, k: int, out=None, ws=None):
+    """Per-query top-k CSA entries; returns int32 [B, Tq, k] (ascending, -1 padded).
+
+    q_pos0: an int (every sequence's row 0 at that position), or a device
+    int64 tensor [B] of per-sequence positions (csa_index_topk_varlen)."""
     lib = load_library()
     _need(qI, "qI")
     _need(kI, "kI", qI.dtype, qI.device)
@@ -235,6 +245,14 @@ def csa_index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, out=None, ws=
     if ws is None and nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=qI.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if isinstance(q_pos0, torch.Tensor):
+        _need(q_pos0, "q_pos", torch.int64, qI.device)
+        if tuple(q_pos0.shape) != (B,):
+            raise ValueError("q_pos must be [B]")
+        _check(lib.csa_index_topk_varlen(_ptr(qI), _ptr(kI), _ptr(w), _ptr(idx), B, Tq, N, Hi, d_idx,
+                                         _ptr(q_pos0), m, W, k, _dtype_code(qI), _ptr(ws), ws_bytes,
+                                         _stream(qI)))
+        return idx
     _check(lib.csa_index_topk(_ptr(qI), _ptr(kI), _ptr(w), _ptr(idx), B, Tq, N, Hi, d_idx,
                               int(q_pos0), m, W, k, _dtype_code(qI), _ptr(ws), ws_bytes,
                               _stream(qI)))
@@ -242,12 +260,14 @@ def csa_index_topk(qI, kI, w, q_pos0: int, m: int, W: int, k: int, out=None, ws=
 
 
 def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
-                  sm_scale=0.0, out=None, gate_logits=False):
+                  sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False):
     """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
 
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
     gates: [H, 3] per-head weights, or [B, Tq, H, 3] per-token weights (or,
     with gate_logits, per-token logits the kernel softmaxes over the branches).
+    q_pos: device int64 [B] per-sequence positions (needs raw_ring); raw_ring:
+    k_raw / v_raw are rings, position t in row t % Tr.
     Returns (FwdArgs, out, keepalive tuple)."""
     _need(q, "q")
     dev = q.device
@@ -292,6 +312,13 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
         a.N_csa, a.k = kc.shape[1], idx.shape[-1]
         keep += [kc, vc, idx]
     a.gates = gates.data_ptr()
+    a.raw_ring = 1 if raw_ring else 0
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int64, dev)
+        if tuple(q_pos.shape) != (B,):
+            raise ValueError("q_pos must be [B]")
+        a.q_pos = q_pos.data_ptr()
+        keep.append(q_pos)
     return a, out, tuple(keep)
 
 
@@ -300,11 +327,13 @@ def hybrid_sparse_attn_fwd_workspace_size(args: FwdArgs) -> int:
 
 
 def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None,
-                           csa=None, sm_scale=0.0, out=None, ws=None, gate_logits=False):
+                           csa=None, sm_scale=0.0, out=None, ws=None, gate_logits=False, q_pos=None,
+                           raw_ring=False):
     """Gated hybrid attention forward; returns out [B, Tq, H, d]."""
     lib = load_library()
     a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
-                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits)
+                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits,
+                                  q_pos=q_pos, raw_ring=raw_ring)
     nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
     if ws is None and nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -78,6 +78,8 @@ struct AttnParams {
     int gate_mode;     // 0: [H, 3]; 1: [B, Tq, H, 3] weights; 2: [B, Tq, H, 3] logits
     float* ws;  // split partial states (split mode only)
     long long q_pos0, raw_pos0;
+    const int64_t* q_pos;  // per-sequence position of query row 0 (device [B]) or null: q_pos0 for all
+    int ring;              // raw K/V: 0 = row r holds position raw_pos0 + r; 1 = ring, position t in row t % Tr
     int B, Tq, H, Hkv, G, W, Tr;
     int m_hca, N_hca, N_csa, k;
     float scale_log2;
@@ -679,6 +681,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int b = (int)(bg / p.Hkv);
     const int i0 = qt * p.QW;
     const int nq = min(p.QW, p.Tq - i0);
+    // position of the sequence's query row 0; a negative per-sequence
+    // position marks an inactive batch slot (its output rows are not written)
+    const long long pos0 = p.q_pos ? (long long)p.q_pos[b] : p.q_pos0;
+    if (pos0 < 0) return;
 
     const int col = wave * 16 + n;
     const int ql = col / p.G;
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const bool valid = (ql < nq);
     const int h = g * p.G + hl;
     const int qi = i0 + (valid ? ql : 0);
-    const long long t = p.q_pos0 + qi;
+    const long long t = pos0 + qi;
 
     const T* qrow = reinterpret_cast<const T*>(p.q) + (((long long)b * p.Tq + qi) * p.H + (valid ? h : 0)) * D;
     typename TR::QF qf[TR::KS];
@@ -703,8 +709,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const bool use_hca = p.has_hca && sflag[0] != 0;
     const bool use_csa = p.has_csa && sflag[1] != 0;
 
-    const long long t_first = p.q_pos0 + i0;
-    const long long t_last = p.q_pos0 + i0 + nq - 1;
+    const long long t_first = pos0 + i0;
+    const long long t_last = pos0 + i0 + nq - 1;
     const long long win_lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;  // this column's window start
 
     // One running online-softmax state S and one output accumulator oacc per
@@ -747,8 +753,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int wlen = (int)(t_last + 1 - w_lo);
     const int rs = p.Hkv * D;  // row stride of every K/V tensor (elements)
     const long long hoff = (long long)g * D;
-    const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
-    const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + (w_lo - p.raw_pos0)) * rs + hoff;
+    // window rows [w_lo, t_last]: one contiguous run of raw rows, or with a
+    // ring two runs, [0, wlen1) from ring row w_lo % Tr to the ring's end and
+    // [wlen1, wlen) from ring row 0 (its base pointer is offset so that
+    // window index k reads ring row k - wlen1)
+    const long long r_lo = p.ring ? w_lo % p.Tr : w_lo - p.raw_pos0;
+    const int wlen1 = p.ring ? (int)min((long long)wlen, p.Tr - r_lo) : wlen;
+    const T* kraw = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr + r_lo) * rs + hoff;
+    const T* vraw = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr + r_lo) * rs + hoff;
+    const T* kraw2 = reinterpret_cast<const T*>(p.k_raw) + ((long long)b * p.Tr - wlen1) * rs + hoff;
+    const T* vraw2 = reinterpret_cast<const T*>(p.v_raw) + ((long long)b * p.Tr - wlen1) * rs + hoff;
     int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
     if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
     const int h_lo = do_hca ? (int)hca_lo : 0;
@@ -763,7 +777,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         tio.issue(khca + (long long)h_lo * rs, vhca + (long long)h_lo * rs, min(KT, h_hi - h_lo), tbuf(0));
         pf = true;
     } else if (do_win && wlen > 0) {
-        tio.issue(kraw, vraw, min(KT, wlen), tbuf(0));
+        tio.issue(kraw, vraw, min(KT, wlen1), tbuf(0));
         pf = true;
     }
 
@@ -840,7 +854,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int qa = (16 * wave_u) / p.G;
     const int qb = min((16 * wave_u + 15) / p.G, nq - 1);
     const bool wave_any = qa < nq;
-    const long long ta = p.q_pos0 + i0 + qa, tb = p.q_pos0 + i0 + qb;
+    const long long ta = pos0 + i0 + qa, tb = pos0 + i0 + qb;
     int hf = do_hca ? (int)n_visible(ta, p.W, p.m_hca, p.N_hca) : 0;
     if (hf > h_hi) hf = h_hi;
     const int wf_lo = wave_any ? (int)((tb - p.W + 1 > 0 ? tb - p.W + 1 : 0) - w_lo) : INT_MAX;
@@ -880,7 +894,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 // inside the range of every column of the wave takes an all-ones
                 // mask without computing it.
                 bool full;
-                if (type == ITEM_WIN) full = k0 >= wf_lo && k0 + KT - 1 <= wf_hi;
+                if (type == ITEM_WIN) full = k0 >= wf_lo && k0 + KT - 1 <= min(wf_hi, k_end - 1);
                 else if (type == ITEM_HCA) full = k0 + KT <= hf_hi;
                 else full = false;
                 constexpr int NCH = KT / KC;  // 32-key chunks per tile
@@ -890,7 +904,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
                     for (int ch = 0; ch < NCH; ++ch) {
                         const int kc0 = k0 + ch * KC;
-                        if (type == ITEM_WIN) m[ch] = range_mask(wv_lo - kc0, wv_hi - kc0);
+                        if (type == ITEM_WIN) m[ch] = range_mask(wv_lo - kc0, min(wv_hi, k_end - 1) - kc0);
                         else if (type == ITEM_HCA) m[ch] = range_mask(0, hv - kc0 - 1);
                     }
                     if (type == ITEM_CSA) {
@@ -916,6 +930,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
             parity ^= 1;
             if (i + 1 < n) tio.commit(tbuf(parity));
             __syncthreads();
+        }
+    };
+
+    // ---- the window, in one run of raw rows or two (ring wrap-around), then
+    // the stream that follows it
+    auto window = [&](const T* nkb, const T* nvb, int nk_begin, int nk_end) {
+        if (wlen1 < wlen) {
+            stream(kraw, vraw, 0, wlen1, ITEM_WIN, kraw2, vraw2, wlen1, wlen);
+            stream(kraw2, vraw2, wlen1, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end);
+        } else {
+            stream(kraw, vraw, 0, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end);
         }
     };
 
@@ -1041,15 +1066,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         // the gather reuses the tile buffers).
         float m_h = -INFINITY, l_h = 0.f;
         if (do_hca) {
-            stream(khca, vhca, h_lo, h_hi, ITEM_HCA, kraw, vraw, 0, wlen);
+            stream(khca, vhca, h_lo, h_hi, ITEM_HCA, kraw, vraw, 0, wlen1);
             m_h = S.m;
             l_h = col_sum(S.l);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] = S.acc[dt];
             S.init();
         }
-        if (do_csa && !GATHER) stream(kraw, vraw, 0, wlen, ITEM_WIN, kcsa, vcsa, 0, c_hi);
-        else stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
+        if (do_csa && !GATHER) window(kcsa, vcsa, 0, c_hi);
+        else window(nullptr, nullptr, 0, 0);
         {
             const float l_w = col_sum(S.l);
             float c_w = valid ? gate[2] / l_w : 0.f, c_h = 0.f;
@@ -1081,7 +1106,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
     } else {
         // one key range per workgroup; partial states are merged by the combine kernel
-        if (do_win) stream(kraw, vraw, 0, wlen, ITEM_WIN, nullptr, nullptr, 0, 0);
+        if (do_win) window(nullptr, nullptr, 0, 0);
         if (do_csa) {
             if constexpr (!GATHER) {
                 stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
@@ -1161,6 +1186,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const int nq = min(p.QW, p.Tq - i0);
     const int ql = col / p.G, hl = col - (col / p.G) * p.G;
     if (ql >= nq) return;                    // uniform over the group of eight
+    if (p.q_pos && p.q_pos[b] < 0) return;   // inactive batch slot
     const int h = g * p.G + hl;
     const int qi = i0 + ql;
     float gw[3];
@@ -1261,6 +1287,13 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: sm_scale must be finite and >= 0");
     if (a->q_pos0 < 0 || a->raw_pos0 < 0)
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: negative position");
+    if (a->reserved0 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved0 must be 0");
+    if (a->raw_ring != 0 && a->raw_ring != 1)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: raw_ring %d (0 or 1)", a->raw_ring);
+    if (a->q_pos && !a->raw_ring)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: per-sequence positions (q_pos) need raw_ring = 1");
+    if (a->q_pos && (reinterpret_cast<uintptr_t>(a->q_pos) & 7))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: q_pos must be 8-byte aligned");
     // a branch is present iff its ratio (HCA) / row width k (CSA) is positive
     const bool has_hca = a->m_hca > 0;
     const bool has_csa = a->k > 0;
@@ -1290,12 +1323,20 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
         (has_csa && (!aligned16(a->k_csa) || !aligned16(a->v_csa) || (reinterpret_cast<uintptr_t>(a->idx) & 3))))
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: tensors must be 16-byte aligned");
     // every window row the queries need must be present
-    const long long lo_need = a->q_pos0 - a->W + 1 > 0 ? a->q_pos0 - a->W + 1 : 0;
-    const long long hi_need = a->q_pos0 + a->Tq;  // exclusive
-    if (lo_need < a->raw_pos0 || hi_need > a->raw_pos0 + a->Tr)
-        return fail(SHATTN_EINVAL,
-                    "hybrid_sparse_attn_fwd: window rows [%lld, %lld) not inside raw rows [%lld, %lld)",
-                    lo_need, hi_need, (long long)a->raw_pos0, (long long)a->raw_pos0 + a->Tr);
+    if (a->raw_ring) {
+        // a ring of Tr rows holds the last Tr positions: the W + Tq - 1
+        // positions the rows' windows span must fit
+        if ((long long)a->Tr < (long long)a->W + a->Tq - 1)
+            return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: ring of %d rows cannot hold the W + Tq - 1 = %lld "
+                        "window positions", a->Tr, (long long)a->W + a->Tq - 1);
+    } else {
+        const long long lo_need = a->q_pos0 - a->W + 1 > 0 ? a->q_pos0 - a->W + 1 : 0;
+        const long long hi_need = a->q_pos0 + a->Tq;  // exclusive
+        if (lo_need < a->raw_pos0 || hi_need > a->raw_pos0 + a->Tr)
+            return fail(SHATTN_EINVAL,
+                        "hybrid_sparse_attn_fwd: window rows [%lld, %lld) not inside raw rows [%lld, %lld)",
+                        lo_need, hi_need, (long long)a->raw_pos0, (long long)a->raw_pos0 + a->Tr);
+    }
     p.q = a->q;
     p.out = a->out;
     p.k_raw = a->k_raw;
@@ -1309,6 +1350,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.gate_mode = a->gate_mode;
     p.q_pos0 = a->q_pos0;
     p.raw_pos0 = a->raw_pos0;
+    p.q_pos = a->q_pos;
+    p.ring = a->raw_ring;
     p.has_hca = has_hca;
     p.has_csa = has_csa;
     p.m_hca = has_hca ? a->m_hca : 1;
@@ -1334,7 +1377,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     // split the key list when there are too few workgroups to fill the chip
     long long keys = (long long)a->W;
     long long nh_max = 0;
-    if (has_hca) nh_max = n_visible_host(a->q_pos0 + a->Tq - 1, a->W, a->m_hca, a->N_hca);
+    // (per-sequence positions live on the device: every entry may be visible)
+    if (has_hca) nh_max = a->q_pos ? a->N_hca : n_visible_host(a->q_pos0 + a->Tq - 1, a->W, a->m_hca, a->N_hca);
     keys += nh_max;
     if (has_csa) keys += a->k;
     p.nsplit = 0;

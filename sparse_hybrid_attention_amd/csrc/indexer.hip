@@ -50,6 +50,7 @@ struct IdxParams {
     const float* w;
     int32_t* idx;
     long long q_pos0;
+    const int64_t* q_pos;  // per-sequence position of query row 0 (device [B]), or null: q_pos0 for all
     int B, Tq, N, k, m, W;
     int cap;   // candidate buffer entries per query
     int mcap;  // band list capacity
@@ -103,6 +104,15 @@ __device__ __forceinline__ long long n_visible(long long t, int W, int m, int N)
     if (s <= 0) return 0;
     const long long n = s / m;
     return n < N ? n : N;
+}
+
+// Position of query row 0 of sequence b.  A negative per-sequence position
+// (an inactive batch slot) gives every row of the sequence no visible entry,
+// so its index rows are all -1.
+__device__ __forceinline__ long long row_pos0(const IdxParams& p, long long b) {
+    if (!p.q_pos) return p.q_pos0;
+    const long long t = p.q_pos[b];
+    return t < 0 ? -(1ll << 40) : t;
 }
 
 // ----------------------------------------------------------- wave selection
@@ -716,7 +726,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_prefill_kernel(IdxParams p) 
             qw += rt * QPT;
             const int i = q0 + qw;
             const bool ok = rt < RT && sl < SLOTS && qw < qpw && i < p.Tq;
-            nv[rt][sl] = ok ? (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
+            nv[rt][sl] = ok ? (int)n_visible(row_pos0(p, b) + i, p.W, p.m, p.N) : 0;
             nv_max = nv[rt][sl] > nv_max ? nv[rt][sl] : nv_max;
         }
     // wave-wide maximum of visible entries
@@ -939,7 +949,7 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     for (int rt = 0; rt < (coop ? NRT : 1); ++rt)
         for (int qw = 0; qw < qpw; ++qw) {
             const int i = (coop ? rt_q0(rt) : q0) + qw;
-            if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N));
+            if (i < p.Tq) nv_max = max(nv_max, (int)n_visible(row_pos0(p, b) + i, p.W, p.m, p.N));
         }
     if (SAMPLE) nv_max = (nv_max + S - 1) / S;
     float kmax2 = 0.f;
@@ -1017,7 +1027,7 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             const int i = q0 + qw;
             if (i >= p.Tq) break;
             const long long row = (long long)b * p.Tq + i;
-            const int n = (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+            const int n = (int)n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
             const int ns = (n + S - 1) / S;
             const float delta = p.err_c * qn[qw] * kmax_all;
             uint32_t thr = 0u, tau = 0u;   // 0: list every visible entry
@@ -1041,7 +1051,7 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         const int i = q0 + qw;
         if (i >= p.Tq) break;
         const long long row = (long long)b * p.Tq + i;
-        const int n = (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+        const int n = (int)n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
         WaveBuf q{keys_all + qw * np, nullptr, hist, mpos, mex, nullptr};
         final_select<T, HI, DI>(q, PosIds{}, n, min(p.k, n), p.k, p.err_c * qn[qw] * kmax, mcap, qI + row * HI * DI,
                                 kI_b, p.w + row * HI, p.idx + row * p.k);
@@ -1149,7 +1159,7 @@ __global__ __launch_bounds__(WAVES * 64) void index_filter_kernel(IdxParams p) {
             const bool ok = i < p.Tq;
             const long long row = (long long)b * p.Tq + (ok ? i : 0);
             lst[rt][sl] = p.row_lists + row * lcap;
-            nv[rt][sl] = ok ? (int)n_visible(p.q_pos0 + i, p.W, p.m, p.N) : 0;
+            nv[rt][sl] = ok ? (int)n_visible(row_pos0(p, b) + i, p.W, p.m, p.N) : 0;
             const uint32_t tk = ok ? p.row_thr[row] : 0u;
             thr_f[rt][sl] = tk == 0u ? -INFINITY : key_f(tk);
             cnt[rt][sl] = 0;
@@ -1241,7 +1251,7 @@ __global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
     wb.mex = reinterpret_cast<double*>(smem + 4ull * lcap + 1024);
     wb.mpos = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 8ull * p.mcap);
     wb.mid = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 12ull * p.mcap);
-    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const long long nvq = n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
     const int k_eff = (int)std::min<long long>(p.k, nvq);
     const int cnt = p.list_cnt[row];
     bool ok = cnt <= lcap;
@@ -1295,7 +1305,7 @@ __global__ __launch_bounds__(64) void index_split_score_kernel(IdxParams p) {
     const int chunk_id = blockIdx.x % p.nchunks;
     const long long row = blockIdx.x / p.nchunks;
     const long long b = row / p.Tq, i = row % p.Tq;
-    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const long long nvq = n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
     const long long c_lo = (long long)chunk_id * p.chunk;
     const long long c_hi = std::min<long long>(c_lo + p.chunk, nvq);
     const T* qI = reinterpret_cast<const T*>(p.qI);
@@ -1398,8 +1408,8 @@ __global__ __launch_bounds__(64) void index_split_collect_kernel(IdxParams p) {
     const int lane = threadIdx.x;
     const int chunk_id = blockIdx.x % p.nchunks;
     const long long row = blockIdx.x / p.nchunks;
-    const long long i = row % p.Tq;
-    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const long long b = row / p.Tq, i = row % p.Tq;
+    const long long nvq = n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
     float lb, delta;
     row_bound(p, row, &lb, &delta);
     const uint32_t lo = lb == -INFINITY ? 0u : fkey(lb - 2.0f * delta);
@@ -1451,7 +1461,7 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
     wb.mid = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 12ull * p.mcap);
     int32_t* offs = reinterpret_cast<int32_t*>(smem + 8ull * cap + 1024 + 16ull * p.mcap);  // [nchunks + 1]
     __shared__ int s_total, s_over;
-    const long long nvq = n_visible(p.q_pos0 + i, p.W, p.m, p.N);
+    const long long nvq = n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
     const int k_eff = (int)std::min<long long>(p.k, nvq);
     float lb, delta;
     row_bound(p, row, &lb, &delta);
@@ -1857,14 +1867,17 @@ extern "C" size_t csa_index_topk_workspace_size(int B, int Tq, int N, int Hi, in
     return pl.ws_bytes;
 }
 
-extern "C" int csa_index_topk(const void* qI, const void* kI, const float* w, int32_t* idx, int B, int Tq,
-                              int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k, int dtype,
-                              void* ws, size_t ws_bytes, void* stream) {
+static int index_topk_impl(const void* qI, const void* kI, const float* w, int32_t* idx, int B, int Tq, int N,
+                           int Hi, int d_idx, int64_t q_pos0, const int64_t* q_pos, int m, int W, int k,
+                           int dtype, void* ws, size_t ws_bytes, void* stream) {
     IdxPlan pl;
     int rc = make_idx_plan(B, Tq, N, Hi, d_idx, q_pos0, m, W, k, dtype, pl);
     if (rc != SHATTN_OK) return rc;
     if (B == 0 || Tq == 0) return SHATTN_OK;
     if (!qI || !w || !idx || (N > 0 && !kI)) return fail(SHATTN_EINVAL, "csa_index_topk: null pointer");
+    if (q_pos && (reinterpret_cast<uintptr_t>(q_pos) & 7))
+        return fail(SHATTN_EINVAL, "csa_index_topk_varlen: q_pos must be 8-byte aligned");
+    pl.p.q_pos = q_pos;
     if (!aligned16(qI) || (N > 0 && !aligned16(kI)) || (reinterpret_cast<uintptr_t>(w) & 3) ||
         (reinterpret_cast<uintptr_t>(idx) & 3))
         return fail(SHATTN_EINVAL, "csa_index_topk: qI/kI must be 16-byte aligned, w/idx 4-byte aligned");
@@ -1906,4 +1919,18 @@ extern "C" int csa_index_topk(const void* qI, const void* kI, const float* w, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     return dtype == SHATTN_DTYPE_BF16 ? launch_idx_hi<bf16_t>(pl, Hi, d_idx, s)
                                       : launch_idx_hi<float>(pl, Hi, d_idx, s);
+}
+
+extern "C" int csa_index_topk(const void* qI, const void* kI, const float* w, int32_t* idx, int B, int Tq,
+                              int N, int Hi, int d_idx, int64_t q_pos0, int m, int W, int k, int dtype,
+                              void* ws, size_t ws_bytes, void* stream) {
+    return index_topk_impl(qI, kI, w, idx, B, Tq, N, Hi, d_idx, q_pos0, nullptr, m, W, k, dtype, ws, ws_bytes,
+                           stream);
+}
+
+extern "C" int csa_index_topk_varlen(const void* qI, const void* kI, const float* w, int32_t* idx, int B, int Tq,
+                                     int N, int Hi, int d_idx, const int64_t* q_pos, int m, int W, int k,
+                                     int dtype, void* ws, size_t ws_bytes, void* stream) {
+    if (!q_pos && B > 0 && Tq > 0) return fail(SHATTN_EINVAL, "csa_index_topk_varlen: null q_pos");
+    return index_topk_impl(qI, kI, w, idx, B, Tq, N, Hi, d_idx, 0, q_pos, m, W, k, dtype, ws, ws_bytes, stream);
 }

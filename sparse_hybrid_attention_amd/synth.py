@@ -190,6 +190,34 @@ def make_append(*, B, Hkv, d, W, m_csa, m_hca, d_idx, cap_csa, cap_hca, steps, d
     return out
 
 
+def make_decode_stream(*, B, H, Hkv, d, d_idx, Hi, lengths, steps, dtype=DTYPE_BF16, seed: int = 0) -> dict:
+    """Token streams for a multi-step decode of B sequences whose histories
+    have different lengths.  Draw order: per sequence b, raw K, V [L_b, Hkv, d]
+    and indexer keys kI [L_b, d_idx] with L_b = lengths[b] + steps (positions
+    0 .. L_b - 1; the last `steps` are the ones decoded); then per step and
+    sequence the query q [steps, B, H, d], indexer query qI [steps, B, Hi,
+    d_idx], indexer weights w [steps, B, Hi] ~ U(0,1); then per-head gates
+    [H, 3] ~ U(0,1) and the compression logits (CSA K, V, indexer keys; HCA
+    K, V) ~ N(0,1)/8, drawn at their largest block size (1024 rows) so that
+    any ratio takes the leading rows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(B=B, H=H, Hkv=Hkv, d=d, d_idx=d_idx, Hi=Hi, lengths=list(lengths), steps=steps, dtype=dtype)
+    out["k_seq"], out["v_seq"], out["kI_seq"] = [], [], []
+    for b in range(B):
+        L = lengths[b] + steps
+        out["k_seq"].append(_normal(rng, (L, Hkv, d), dtype))
+        out["v_seq"].append(_normal(rng, (L, Hkv, d), dtype))
+        out["kI_seq"].append(_normal(rng, (L, d_idx), dtype))
+    out["q"] = _normal(rng, (steps, B, H, d), dtype)
+    out["qI"] = _normal(rng, (steps, B, Hi, d_idx), dtype)
+    out["w"] = rng.random(size=(steps, B, Hi), dtype=np.float32)
+    out["gates"] = rng.random(size=(H, 3), dtype=np.float32)
+    for name, ch in (("zk_csa", d), ("zv_csa", d), ("zI", d_idx), ("zk_hca", d), ("zv_hca", d)):
+        shape = (1024, Hkv, ch) if name != "zI" else (1024, ch)
+        out[name] = (rng.standard_normal(size=shape, dtype=np.float32) / np.float32(8.0)).astype(np.float32)
+    return out
+
+
 def make_inputs(name: str, seed: int = 0, **overrides) -> dict:
     cfg = config(name, **overrides)
     if cfg["kind"] == "decode":

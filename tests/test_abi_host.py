@@ -140,18 +140,20 @@ def test_probe_library_is_separate(lib):
     pl = ctypes.CDLL(probe_lib)
     i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     pl.shattn_probe_mfma.argtypes = [i32, i32, i32, vp, vp]
-    pl.shattn_probe_gather.argtypes = [vp, i64, i32, i64, i64, i32, i32, vp, vp]
+    pl.shattn_probe_gather.argtypes = [vp, i64, i32, i64, i32, i64, i32, i32, vp, vp]
     f = pl.shattn_probe_mfma
     assert f(0, 16, 0, P, None) == -1
     assert f(16, 0, 0, P, None) == -1
     assert f(16, 16, 2, P, None) == -1
     assert f(16, 16, 0, None, None) == -1
     g = pl.shattn_probe_gather
-    assert g(P, 1024, 96, 256, 100, 4, 64, P, None) == -1      # row size
-    assert g(P, 1024, 256, 128, 100, 4, 64, P, None) == -1     # stride below the row
-    assert g(P, 0, 256, 256, 100, 4, 64, P, None) == -1        # no rows
-    assert g(P, 1024, 256, 256, 100, 3, 64, P, None) == -1     # depth
-    assert g(None, 1024, 256, 256, 100, 4, 64, P, None) == -1  # table
+    assert g(P, 1024, 96, 256, 1, 100, 4, 64, P, None) == -1      # row size
+    assert g(P, 1024, 256, 128, 1, 100, 4, 64, P, None) == -1     # stride below the row
+    assert g(P, 0, 256, 256, 1, 100, 4, 64, P, None) == -1        # no rows
+    assert g(P, 1024, 256, 256, 1, 100, 3, 64, P, None) == -1     # depth
+    assert g(None, 1024, 256, 256, 1, 100, 4, 64, P, None) == -1  # table
+    assert g(P, 1026, 256, 256, 4, 100, 4, 64, P, None) == -1     # slices must divide the rows
+    assert g(P, 1024, 256, 256, 9, 100, 4, 64, P, None) == -1     # at most 8 slices
 
 
 def fwd(**kw):
@@ -192,8 +194,27 @@ def test_attention_errors(lib):
             k_hca=P.value, v_hca=P.value)
     assert lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)) > 0
     assert f(ctypes.byref(a), None, 0, None) == binding.SHATTN_EWORKSPACE
+    # per-sequence positions read the window from rings
+    assert call(q_pos=P.value) == binding.SHATTN_EINVAL           # q_pos without a ring
+    assert "raw_ring" in err(lib)
+    assert call(raw_ring=2) == binding.SHATTN_EINVAL
+    assert call(reserved0=1) == binding.SHATTN_EINVAL
+    assert call(raw_ring=1, q_pos=0x7F0000000004) == binding.SHATTN_EINVAL   # misaligned q_pos
+    assert call(raw_ring=1, q_pos=P.value, Tr=22) == binding.SHATTN_EINVAL   # ring shorter than W + Tq - 1
+    assert "ring" in err(lib)
+    ring = fwd(raw_ring=1, q_pos=P.value, Tr=23, B=1, Tq=16)
+    assert lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(ring)) == 0
     # empty problem is a no-op
     assert call(B=0) == binding.SHATTN_OK
+
+
+def test_index_varlen_errors(lib):
+    f = lib.csa_index_topk_varlen
+    args = lambda qp, **kw: (P, P, P, P, kw.get("B", 2), 1, 64, 4, 64, qp, 4, 8, 8, 0, None, 0, None)
+    assert f(*args(None)) == binding.SHATTN_EINVAL
+    assert "q_pos" in err(lib)
+    assert f(*args(ctypes.c_void_p(0x7F0000000004))) == binding.SHATTN_EINVAL
+    assert f(*args(None, B=0)) == binding.SHATTN_OK     # nothing to do
 
 
 def append(**kw):
