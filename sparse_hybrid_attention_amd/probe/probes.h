@@ -35,18 +35,21 @@ SHATTN_PROBE_API int shattn_probe_mfma(int workgroups, int iters, int shape, flo
 
 /*
  * Random-row gather throughput: `n` reads of one `row_bytes`-byte row each,
- * row r of the table starting at table + r * row_stride (r < nrows), the
- * rows chosen by a hash of the read's index (uniform over the table); each
+ * row r of the table starting at table + r * row_stride (r < nrows).  The
+ * table is split into `slices` equal parts of nrows / slices rows; workgroup
+ * i (placed on XCD i % 8 by the dispatcher) reads part (i % 8) % slices, its
+ * rows chosen by a hash of the read's index (uniform over the part).  Each
  * lane keeps `depth` 16-byte reads in flight.  Bytes moved = n * row_bytes.
  * The table must hold (nrows - 1) * row_stride + row_bytes bytes.  A table
  * that fits the last-level cache measures the cache's gather rate.
  * sink: uint32 [workgroups * 256], written.
  * Supported: row_bytes in {64, 128, 256, 512, 1024}; row_stride >= row_bytes,
- * a multiple of 16; nrows >= 1; depth in {1, 2, 4, 8}; 1 <= workgroups <= 65536.
+ * a multiple of 16; 1 <= slices <= 8 dividing nrows, nrows / slices < 2^32;
+ * depth in {1, 2, 4, 8, 16}; 1 <= workgroups <= 65536.
  */
 SHATTN_PROBE_API int shattn_probe_gather(const void* table, int64_t nrows, int32_t row_bytes, int64_t row_stride,
-                                         int64_t n, int32_t depth, int32_t workgroups, uint32_t* sink,
-                                         void* stream);
+                                         int32_t slices, int64_t n, int32_t depth, int32_t workgroups,
+                                         uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -74,11 +74,14 @@ __device__ __forceinline__ uint32_t mix32(uint32_t h) {
 }
 
 // Each wave reads rows in groups: 64 lanes x 16 bytes cover 1024 / row_bytes
-// rows per load; a lane issues DEPTH such loads before it consumes any.
+// rows per load; a lane issues DEPTH such loads before it consumes any.  The
+// table is split into `slices` equal parts and workgroup i (which the
+// dispatcher places on XCD i % 8) reads only part (i % 8) % slices, so that
+// each XCD's L2 sees one part (slices = 1: the whole table).
 template <int DEPTH>
-__global__ __launch_bounds__(kProbeThreads) void gather_probe_kernel(const char* __restrict__ table, long long nrows,
+__global__ __launch_bounds__(kProbeThreads) void gather_probe_kernel(const char* __restrict__ table, uint32_t srows,
                                                                      int row_bytes, long long row_stride,
-                                                                     long long n, uint32_t* sink) {
+                                                                     int slices, long long n, uint32_t* sink) {
     const int lane = threadIdx.x & 63;
     const int pieces = row_bytes >> 4;           // 16-byte pieces per row
     const int rpl = 64 / pieces;                 // rows per wave load
@@ -86,14 +89,17 @@ __global__ __launch_bounds__(kProbeThreads) void gather_probe_kernel(const char*
     const long long wave = ((long long)blockIdx.x * kProbeThreads + threadIdx.x) >> 6;
     const long long nwaves = ((long long)gridDim.x * kProbeThreads) >> 6;
     const long long per_iter = (long long)rpl * DEPTH;
+    const char* base = table + (long long)((blockIdx.x % 8) % slices) * srows * row_stride + pc * 16;
+    const bool pow2 = (srows & (srows - 1)) == 0;
     uint32_t acc = 0u;
-    for (long long base = wave * per_iter; base < n; base += nwaves * per_iter) {
+    for (long long it = wave * per_iter; it < n; it += nwaves * per_iter) {
         uint4 v[DEPTH];
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
-            const long long j = base + (long long)u * rpl + r;
-            const long long row = j < n ? (long long)(mix32((uint32_t)j ^ (uint32_t)(j >> 32)) % (uint64_t)nrows) : 0;
-            v[u] = *reinterpret_cast<const uint4*>(table + row * row_stride + pc * 16);
+            const long long j = it + (long long)u * rpl + r;
+            const uint32_t h = mix32((uint32_t)j);
+            const uint32_t row = j < n ? (pow2 ? (h & (srows - 1)) : h % srows) : 0u;
+            v[u] = *reinterpret_cast<const uint4*>(base + (long long)row * row_stride);
         }
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -117,20 +123,24 @@ extern "C" int shattn_probe_mfma(int workgroups, int iters, int shape, float* si
 }
 
 extern "C" int shattn_probe_gather(const void* table, int64_t nrows, int32_t row_bytes, int64_t row_stride,
-                                   int64_t n, int32_t depth, int32_t workgroups, uint32_t* sink, void* stream) {
+                                   int32_t slices, int64_t n, int32_t depth, int32_t workgroups, uint32_t* sink,
+                                   void* stream) {
     const bool rb_ok = row_bytes == 64 || row_bytes == 128 || row_bytes == 256 || row_bytes == 512 ||
                        row_bytes == 1024;
     if (!table || !sink || !rb_ok || nrows < 1 || row_stride < row_bytes || (row_stride & 15) || n < 0 ||
-        workgroups < 1 || workgroups > 65536 || (reinterpret_cast<uintptr_t>(table) & 15))
+        workgroups < 1 || workgroups > 65536 || (reinterpret_cast<uintptr_t>(table) & 15) || slices < 1 ||
+        slices > 8 || nrows % slices != 0 || nrows / slices > 0xFFFFFFFFll)
         return -1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const char* t = reinterpret_cast<const char*>(table);
+    const uint32_t srows = (uint32_t)(nrows / slices);
     const dim3 g((unsigned)workgroups), b(kProbeThreads);
     switch (depth) {
-        case 1: hipLaunchKernelGGL(gather_probe_kernel<1>, g, b, 0, s, t, nrows, row_bytes, row_stride, n, sink); break;
-        case 2: hipLaunchKernelGGL(gather_probe_kernel<2>, g, b, 0, s, t, nrows, row_bytes, row_stride, n, sink); break;
-        case 4: hipLaunchKernelGGL(gather_probe_kernel<4>, g, b, 0, s, t, nrows, row_bytes, row_stride, n, sink); break;
-        case 8: hipLaunchKernelGGL(gather_probe_kernel<8>, g, b, 0, s, t, nrows, row_bytes, row_stride, n, sink); break;
+        case 1: hipLaunchKernelGGL(gather_probe_kernel<1>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
+        case 2: hipLaunchKernelGGL(gather_probe_kernel<2>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
+        case 4: hipLaunchKernelGGL(gather_probe_kernel<4>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
+        case 8: hipLaunchKernelGGL(gather_probe_kernel<8>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
+        case 16: hipLaunchKernelGGL(gather_probe_kernel<16>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
         default: return -1;
     }
     return launched();

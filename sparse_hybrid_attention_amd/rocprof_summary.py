@@ -7,6 +7,11 @@ Two subcommands:
     wrote under DIR and prints a markdown table of the top kernels (calls,
     total and mean duration).
 
+``pmc DIR --counters C1 C2 .. --command CMD --title T``
+    reads the counter CSV of one ``rocprofv3 --pmc C1 C2 ..`` pass and
+    prints a markdown table of each counter's mean value per dispatch for
+    the top kernels (by dispatch count times value of the first counter).
+
 ``counters --workload W --runs N --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR``
     reads the ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` counter CSVs of the
     benchmark (N = pipeline steps the profiled run executed, warm-up
@@ -80,6 +85,22 @@ def load_counter(d: str, counter: str) -> dict:
     return agg
 
 
+def pmc_table(d: str, names, command: str, title: str, top: int = 8) -> str:
+    per = {c: load_counter(d, c) for c in names}
+    kernels = sorted(per[names[0]], key=lambda k: -sum(per[names[0]][k]))[:top]
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "Mean value per dispatch (counter units as rocprofv3 reports them).", "",
+           "| kernel | dispatches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for k in kernels:
+        n = len(per[names[0]][k])
+        vals = []
+        for c in names:
+            v = per[c].get(k, [])
+            vals.append(f"{sum(v) / len(v):.4g}" if v else "-")
+        out.append(f"| `{k}` | {n} | " + " | ".join(vals) + " |")
+    return "\n".join(out) + "\n"
+
+
 def copy_factor(d: str, counter: str) -> float:
     agg = load_counter(d, counter)
     vals = [v for k, vs in agg.items() if "copy" in k.lower() for v in vs]
@@ -122,6 +143,11 @@ def main():
     s.add_argument("dir")
     s.add_argument("--command", required=True)
     s.add_argument("--title", required=True)
+    q = sub.add_parser("pmc")
+    q.add_argument("dir")
+    q.add_argument("--counters", nargs="+", required=True)
+    q.add_argument("--command", required=True)
+    q.add_argument("--title", required=True)
     c = sub.add_parser("counters")
     c.add_argument("--workload", required=True)
     c.add_argument("--runs", type=int, required=True, help="pipeline steps in the profiled run")
@@ -135,6 +161,9 @@ def main():
     a = ap.parse_args()
     if a.cmd == "stats":
         print(stats_table(a.dir, a.command, a.title), end="")
+        return
+    if a.cmd == "pmc":
+        print(pmc_table(a.dir, a.counters, a.command, a.title), end="")
         return
     text, res = counters(a)
     print(text, end="")
