@@ -64,6 +64,14 @@ Readings taken where the pages are silent (each repeated at its function):
       pages give none); every other channel is unchanged.  The position of
       each row is the caller's (for a compressed entry: whichever position the
       model assigns it); a row with a negative position is left unchanged.
+  R12 Backward pass (the Tiny-R2 training step differentiates the path):
+      the gradient of the float64 forward value of the output (before its
+      storage rounding) with respect to Q, the raw K/V rows, the compressed
+      caches, the compression logits and the gates, given dL/dout.  The
+      top-k selection is a fixed input (a selection is not differentiable);
+      the storage rounding of the compressed caches is taken as the identity
+      (the gradient reaching a cache flows through the block compression to
+      the raw rows and the logits).
   R11 4-bit cache storage ([V4-code] section "1. HCA": the merged cache is
       quantised with one minimum and one maximum over the whole tensor, step
       (max - min) / 15, codes rounded and clamped to 0..15, decoded as
@@ -82,9 +90,10 @@ import numpy as np
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
+DTYPE_F64 = 2   # oracle only: float64 storage (no rounding anywhere), for derivative checks
 
 __all__ = [
-    "DTYPE_BF16", "DTYPE_F32",
+    "DTYPE_BF16", "DTYPE_F32", "DTYPE_F64",
     "bf16_bits_to_f64", "f64_to_bf16_bits", "to_f64", "to_storage",
     "block_weights", "compress", "compress_kv",
     "window_bounds", "visible_count",
@@ -94,6 +103,7 @@ __all__ = [
     "cache_append",
     "rope",
     "quant4", "dequant4",
+    "compress_backward", "attn_row_backward", "hybrid_attn_bwd", "hybrid_path_bwd",
 ]
 
 
@@ -128,6 +138,8 @@ def to_f64(a: np.ndarray, dtype: int) -> np.ndarray:
         return bf16_bits_to_f64(a)
     if dtype == DTYPE_F32:
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == DTYPE_F64:
+        return np.asarray(a, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -136,6 +148,8 @@ def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
         return f64_to_bf16_bits(x)
     if dtype == DTYPE_F32:
         return np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == DTYPE_F64:
+        return np.asarray(x, dtype=np.float64).copy()
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -496,3 +510,176 @@ def dequant4(packed, mn, step, n: int, dtype: int):
     codes[1::2] = packed >> np.uint8(4)
     vals = codes[:n].astype(np.float64) * float(step) + float(mn)
     return to_storage(vals, dtype)
+
+
+# --------------------------------------------------------------------------
+# Backward pass (reading R12): the chain rule through the forward definitions
+# above, one query row and one branch at a time.
+# --------------------------------------------------------------------------
+def compress_backward(x: np.ndarray, z: np.ndarray, m: int, dxc: np.ndarray):
+    """Gradients of xc = compress(x, z, m) given dxc = dL/dxc (float64).
+
+    xc[b, c] = sum_i P[i] x[b, c*m + i] per channel, P = softmax over i of z:
+      dx[b, c*m + i] = P[i] dxc[b, c]  (rows past the last full block: 0),
+      dP[i] = sum over (b, c) of dxc[b, c] x[b, c*m + i],
+      dz[i] = P[i] (dP[i] - sum_l P[l] dP[l]).
+    Returns (dx [B, T, Hkv, d], dz [m, Hkv, d])."""
+    B, T, Hkv, d = x.shape
+    n = T // m
+    p = block_weights(z)
+    blocks = x[:, : n * m].reshape(B, n, m, Hkv, d)
+    dx = np.zeros_like(x, dtype=np.float64)
+    dx[:, : n * m] = (p[None, None] * dxc[:, :, None]).reshape(B, n * m, Hkv, d)
+    dp = (blocks * dxc[:, :, None]).sum(axis=(0, 1))
+    dz = p * (dp - (p * dp).sum(axis=0, keepdims=True))
+    return dx, dz
+
+
+def attn_row_backward(q_row, t, dO, *, W, raw_pos0, k_raw_b, v_raw_b, scale, hca=None, csa=None,
+                      idx_row=None, want=("hca", "csa", "swa")):
+    """Backward of attn_row for one query row (all heads), float64.
+
+    dO[br]: [H, d] gradient reaching branch br's output.  Returns the branch
+    outputs O[br] ([H, d], for the gate gradient) and the gradients as a
+    dict: dq [H, d]; dk_raw / dv_raw [Tr, Hkv, d]; dk_hca / dv_hca and
+    dk_csa / dv_csa [N, Hkv, d] (present branches only).  Per head and branch
+    with keys K, values V (the branch's key set), s = scale K q, P = softmax(s),
+    O = P V:  dV_j = P_j dO;  dP_j = dO . V_j;  dS_j = P_j (dP_j - dO . O);
+    dq = scale sum_j dS_j K_j;  dK_j = scale dS_j q."""
+    H, d = q_row.shape
+    Hkv = k_raw_b.shape[1]
+    G = H // Hkv
+    lo, hi = window_bounds(t, W)
+    r0, r1 = lo - raw_pos0, hi - raw_pos0
+    if r0 < 0 or r1 > k_raw_b.shape[0]:
+        raise ValueError("window rows fall outside the raw K/V rows given")
+    grads = {"dq": np.zeros((H, d)), "dk_raw": np.zeros(k_raw_b.shape), "dv_raw": np.zeros(v_raw_b.shape)}
+    if hca is not None:
+        grads["dk_hca"] = np.zeros(hca[0].shape)
+        grads["dv_hca"] = np.zeros(hca[1].shape)
+    if csa is not None:
+        grads["dk_csa"] = np.zeros(csa[0].shape)
+        grads["dv_csa"] = np.zeros(csa[1].shape)
+    outs = {}
+    for br in want:
+        out = np.zeros((H, d))
+        for h in range(H):
+            g = h // G
+            # (source, row) of every key of the branch's set, window first
+            srcs = [("raw", r) for r in range(r0, r1)]
+            if br == "hca":
+                n_vis = visible_count(t, W, hca[2], hca[0].shape[0])
+                srcs += [("hca", c) for c in range(n_vis)]
+            elif br == "csa":
+                srcs += [("csa", int(c)) for c in idx_row[idx_row >= 0]]
+            tabs = {"raw": (k_raw_b, v_raw_b)}
+            if hca is not None:
+                tabs["hca"] = hca[:2]
+            if csa is not None:
+                tabs["csa"] = csa[:2]
+            K = np.stack([tabs[sname][0][r, g] for sname, r in srcs])
+            V = np.stack([tabs[sname][1][r, g] for sname, r in srcs])
+            s = scale * (K * q_row[h][None, :]).sum(axis=1)
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            o = (p[:, None] * V).sum(axis=0)
+            out[h] = o
+            do = dO[br][h]
+            dp = (V * do[None, :]).sum(axis=1)
+            ds = p * (dp - np.dot(do, o))
+            grads["dq"][h] += scale * (ds[:, None] * K).sum(axis=0)
+            for j, (sname, r) in enumerate(srcs):
+                grads["dk_" + sname][r, g] += scale * ds[j] * q_row[h]
+                grads["dv_" + sname][r, g] += p[j] * do
+        outs[br] = out
+    return outs, grads
+
+
+def hybrid_attn_bwd(q, k_raw, v_raw, gates, dout, *, W, dtype, q_pos0=0, raw_pos0=0, hca=None, csa=None,
+                    scale=None, gate_mode=0):
+    """Gradients of hybrid_attn_fwd's float64 output (reading R12) given
+    dout = dL/dout [B, Tq, H, d] (float64).  Inputs as for hybrid_attn_fwd.
+
+    Returns a dict of float64 arrays: dq; dk_raw, dv_raw; dk_hca, dv_hca
+    (with hca); dk_csa, dv_csa (with csa); dgates of the gates' shape (for
+    gate_mode 2 the gradient reaches the logits through the branch softmax:
+    dlogit = w (dw - sum w dw))."""
+    qf = to_f64(q, dtype)
+    kr = to_f64(k_raw, dtype)
+    vr = to_f64(v_raw, dtype)
+    B, Tq, H, d = qf.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    hca_f = None if hca is None else (to_f64(hca[0], dtype), to_f64(hca[1], dtype), int(hca[2]))
+    csa_f = None if csa is None else (to_f64(csa[0], dtype), to_f64(csa[1], dtype), np.asarray(csa[2]))
+    want = ["swa"] + (["hca"] if hca_f is not None else []) + (["csa"] if csa_f is not None else [])
+    gdt = np.asarray(gates, dtype=np.float32).astype(np.float64)
+    res = {"dq": np.zeros(qf.shape), "dk_raw": np.zeros(kr.shape), "dv_raw": np.zeros(vr.shape),
+           "dgates": np.zeros(gdt.shape)}
+    if hca_f is not None:
+        res["dk_hca"] = np.zeros(hca_f[0].shape)
+        res["dv_hca"] = np.zeros(hca_f[1].shape)
+    if csa_f is not None:
+        res["dk_csa"] = np.zeros(csa_f[0].shape)
+        res["dv_csa"] = np.zeros(csa_f[1].shape)
+    dout = np.asarray(dout, dtype=np.float64)
+    cols = {"hca": 0, "csa": 1, "swa": 2}
+    for b in range(B):
+        for i in range(Tq):
+            t = q_pos0 + i
+            g = gate_weights(gates, gate_mode, b, i)
+            dO = {br: g[:, cols[br]][:, None] * dout[b, i] for br in want}
+            outs, gr = attn_row_backward(
+                qf[b, i], t, dO, W=W, raw_pos0=raw_pos0, k_raw_b=kr[b], v_raw_b=vr[b], scale=scale,
+                hca=None if hca_f is None else (hca_f[0][b], hca_f[1][b], hca_f[2]),
+                csa=None if csa_f is None else (csa_f[0][b], csa_f[1][b]),
+                idx_row=None if csa_f is None else csa_f[2][b, i], want=want)
+            res["dq"][b, i] = gr["dq"]
+            for name in ("dk_raw", "dv_raw", "dk_hca", "dv_hca", "dk_csa", "dv_csa"):
+                if name in gr:
+                    res[name][b] += gr[name]
+            # gate weights: dL/dw[h, col] = dout . O_col (absent branches: 0)
+            dw = np.zeros((H, 3))
+            for br in want:
+                dw[:, cols[br]] = (dout[b, i] * outs[br]).sum(axis=1)
+            if gate_mode == 0:
+                res["dgates"] += dw
+            elif gate_mode == 1:
+                res["dgates"][b, i] = dw
+            else:
+                res["dgates"][b, i] = g * (dw - (g * dw).sum(axis=1, keepdims=True))
+    return res
+
+
+def hybrid_path_bwd(q, k, v, gates, dout, *, W, dtype, idx=None, hca=None, csa=None, scale=None, gate_mode=0):
+    """Backward of the whole prefill path (reading R12): block compression of
+    K and V for each present branch (hca = (zk, zv, m), csa = (zk, zv, m);
+    caches stored in the storage dtype as in the forward), gated attention
+    with the CSA selection idx given, then the compression backward.
+
+    Returns float64 gradients: dq; dk, dv (raw rows: window part plus every
+    branch's compression part); dzk_hca, dzv_hca, dzk_csa, dzv_csa (present
+    branches); dgates; and the cache gradients dk_hca ... dv_csa."""
+    kf, vf = to_f64(k, dtype), to_f64(v, dtype)
+    hca_c = csa_c = None
+    if hca is not None:
+        kh, vh = compress_kv(k, v, hca[0], hca[1], hca[2], dtype)
+        hca_c = (kh, vh, hca[2])
+    if csa is not None:
+        kc, vc = compress_kv(k, v, csa[0], csa[1], csa[2], dtype)
+        csa_c = (kc, vc, idx)
+    res = hybrid_attn_bwd(q, k, v, gates, dout, W=W, dtype=dtype, hca=hca_c, csa=csa_c, scale=scale,
+                          gate_mode=gate_mode)
+    res["dk"] = res["dk_raw"].copy()
+    res["dv"] = res["dv_raw"].copy()
+    for name, br in (("hca", hca), ("csa", csa)):
+        if br is None:
+            continue
+        zk, zv, m = br
+        dxk, dzk = compress_backward(kf, np.asarray(zk, np.float64), m, res["dk_" + name])
+        dxv, dzv = compress_backward(vf, np.asarray(zv, np.float64), m, res["dv_" + name])
+        res["dk"] += dxk
+        res["dv"] += dxv
+        res["dzk_" + name] = dzk
+        res["dzv_" + name] = dzv
+    return res
