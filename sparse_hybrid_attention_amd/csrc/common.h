@@ -38,6 +38,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// float64 -> bfloat16, round to nearest, ties to even, in one rounding step
+// (normal and zero results; no detour through a float32 rounding): the
+// double is rounded to 8 significant bits, which float32 then holds exactly.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
+    u &= ~0x00001FFFFFFFFFFFull;
+    return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }

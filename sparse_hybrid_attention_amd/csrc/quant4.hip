@@ -119,17 +119,26 @@ __global__ __launch_bounds__(kQ4Threads) void q4_encode_kernel(const T* __restri
     }
 }
 
+// The decoded value code * step + min rounded once to the storage dtype: the
+// product of a 4-bit code and a float32 step is exact in float64 and the sum
+// is rounded once to float64 there, then once to the dtype.
+template <typename T> __device__ __forceinline__ void store_decoded(T* p, double v);
+template <> __device__ __forceinline__ void store_decoded<float>(float* p, double v) { *p = (float)v; }
+template <> __device__ __forceinline__ void store_decoded<bf16_t>(bf16_t* p, double v) {
+    *p = (bf16_t)f64_to_bf16_rne(v);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kQ4Threads) void q4_decode_kernel(const uint8_t* __restrict__ codes,
                                                                const float* __restrict__ params, long long n,
                                                                T* __restrict__ out) {
-    const float mn = params[0], st = params[1];
+    const double mn = params[0], st = params[1];
     const long long nbytes = (n + 1) / 2;
     const long long stride = (long long)gridDim.x * kQ4Threads;
     for (long long j = (long long)blockIdx.x * kQ4Threads + threadIdx.x; j < nbytes; j += stride) {
         const uint32_t b = codes[j];
-        Elem<T>::store1(out + 2 * j, fmaf((float)(b & 15u), st, mn));
-        if (2 * j + 1 < n) Elem<T>::store1(out + 2 * j + 1, fmaf((float)(b >> 4), st, mn));
+        store_decoded<T>(out + 2 * j, fma((double)(b & 15u), st, mn));
+        if (2 * j + 1 < n) store_decoded<T>(out + 2 * j + 1, fma((double)(b >> 4), st, mn));
     }
 }
 

@@ -1,5 +1,5 @@
-"""4-bit cache storage on the GPU against the oracle (reading R11): codes and
-(min, step) bit-exact, decoded values within the float tolerance; both
+"""4-bit cache storage on the GPU against the oracle (reading R11): codes,
+(min, step) and decoded values bit-exact; both
 dtypes, an odd element count, a one-element and a constant tensor, a tensor
 of the HCA decode-cache shape."""
 import numpy as np
@@ -33,7 +33,10 @@ def test_quant4_matches_oracle(dtype, n, constant):
     assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[0]}"
     out = torch.empty_like(xd)
     binding.cache_dequant4(codes, params, out)
-    assert_close(host(out), O.dequant4(want_codes, mn, st, n, dtype), f"dequant4 dtype={dtype} n={n}")
+    want = O.dequant4(want_codes, mn, st, n, dtype)
+    got = host(out)
+    bad = np.nonzero(got.view(np.uint8) != want.view(np.uint8))[0]
+    assert bad.size == 0, f"dequant4 dtype={dtype} n={n}: {bad.size} bytes differ"
 
 
 def test_quant4_repeat_reuses_params():
@@ -47,3 +50,21 @@ def test_quant4_repeat_reuses_params():
     want_codes, mn, st = O.quant4(host(b), binding.DTYPE_BF16)
     assert tuple(host(params)) == (mn, st)
     assert np.array_equal(host(codes_b), want_codes)
+
+
+def test_dequant4_rounds_once():
+    # step 2^-8 + 2^-31 from min 1.0: code 1 decodes to 1 + 2^-8 + 2^-31, just
+    # above the bf16 tie 1 + 2^-8 (float32 would round it onto the tie, and
+    # the tie to even would then give 1.0); the exact value rounds up to
+    # 1 + 2^-7.  Every code, both dtypes, against the oracle's float64 decode.
+    lib()
+    mn, st = np.float32(1.0), np.float32(2.0 ** -8 + 2.0 ** -31)
+    codes = np.arange(16, dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    params = dev(np.array([mn, st], np.float32))
+    for dtype, tdt in ((binding.DTYPE_BF16, torch.bfloat16), (binding.DTYPE_F32, torch.float32)):
+        out = torch.empty(16, dtype=tdt, device="cuda:0")
+        binding.cache_dequant4(dev(packed), params, out)
+        want = O.dequant4(packed, mn, st, 16, dtype)
+        assert np.array_equal(host(out).view(np.uint8), want.view(np.uint8)), (dtype, host(out), want)
+    assert O.dequant4(packed, mn, st, 16, binding.DTYPE_BF16)[1] == 0x3F81   # 1 + 2^-7
