@@ -26,7 +26,8 @@
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer allocated and owned by the caller.
  *    The library never allocates or frees device memory and keeps no state
- *    between calls (apart from the thread-local error string).
+ *    between calls (apart from the thread-local error string and the device
+ *    array of hybrid_sparse_attn_fwd_noalloc).
  *  - dtype: SHATTN_DTYPE_BF16 (bfloat16) or SHATTN_DTYPE_F32 applies to every
  *    tensor operand except logits, indexer weights and gates, which are always
  *    float32.  Accumulation is float32; stored results are rounded once to
@@ -224,6 +225,21 @@ SHATTN_API size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
 /* Supported: d in {64, 128}; H % Hkv == 0 with H/Hkv <= 64; W >= 1;
  *            k <= 4096. */
 SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hybrid_sparse_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * device array inside the library (32 MiB per GPU, held by each GPU the
+ * library runs on until the process ends).  This call itself allocates
+ * nothing.  The array is located on the calling thread's current device,
+ * which must be the device the tensors and the stream belong to.  Arguments
+ * whose hybrid_sparse_attn_fwd_workspace_size() exceeds 32 MiB return
+ * SHATTN_EUNSUPPORTED.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (concurrent streams, threads) race and must be
+ * serialised by the caller.
+ */
+SHATTN_API int hybrid_sparse_attn_fwd_noalloc(const shattn_fwd_args* a, void* stream);
 
 /*
  * Decode cache maintenance, one new token per sequence ([V4-blog] "1. hybrid

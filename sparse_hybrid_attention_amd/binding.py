@@ -33,6 +33,7 @@ EXPORTED = (
     "csa_index_topk_varlen",
     "hybrid_sparse_attn_fwd_workspace_size",
     "hybrid_sparse_attn_fwd",
+    "hybrid_sparse_attn_fwd_noalloc",
     "hybrid_cache_append",
     "rope_apply",
     "cache_quant4",
@@ -136,6 +137,8 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_sparse_attn_fwd_workspace_size.restype = sz
         lib.hybrid_sparse_attn_fwd.argtypes = [ctypes.POINTER(FwdArgs), vp, sz, vp]
         lib.hybrid_sparse_attn_fwd.restype = i32
+        lib.hybrid_sparse_attn_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), vp]
+        lib.hybrid_sparse_attn_fwd_noalloc.restype = i32
         lib.hybrid_cache_append.argtypes = [ctypes.POINTER(AppendArgs), vp]
         lib.hybrid_cache_append.restype = i32
         lib.rope_apply.argtypes = [vp, vp, i64, i32, i32, i32, i32, ctypes.c_double, i32, vp]
@@ -339,6 +342,18 @@ def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, h
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.hybrid_sparse_attn_fwd(ctypes.byref(a), _ptr(ws), ws_bytes, _stream(q)))
+    return out
+
+
+def hybrid_sparse_attn_fwd_noalloc(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
+                                   sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False):
+    """hybrid_sparse_attn_fwd without a caller workspace (the library's own
+    per-GPU scratch array); returns out [B, Tq, H, d]."""
+    lib = load_library()
+    a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
+                                  hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits,
+                                  q_pos=q_pos, raw_ring=raw_ring)
+    _check(lib.hybrid_sparse_attn_fwd_noalloc(ctypes.byref(a), _stream(q)))
     return out
 
 

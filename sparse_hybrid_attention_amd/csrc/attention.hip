@@ -43,6 +43,7 @@
 //    range of (sequence, head, query tile) work.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include <type_traits>
 
@@ -1490,4 +1491,55 @@ extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t
     if (a->dtype == SHATTN_DTYPE_BF16)
         return a->d == 128 ? launch_attn<bf16_t, 128>(pl, s) : launch_attn<bf16_t, 64>(pl, s);
     return a->d == 128 ? launch_attn<float, 128>(pl, s) : launch_attn<float, 64>(pl, s);
+}
+
+// ------------------------------------------------------------ no allocation
+// The same launch for callers that cannot allocate a workspace: the split
+// decode launch's partial states go to one file-scope device array per GPU
+// (each GPU the library runs on holds its own copy until the process ends).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // the array's device address on each GPU
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the array's name is not a device address in host code).
+int scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd_noalloc: hipGetSymbolAddress: %s",
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SHATTN_OK;
+}
+}  // namespace
+
+extern "C" int hybrid_sparse_attn_fwd_noalloc(const shattn_fwd_args* a, void* stream) {
+    Plan pl;
+    int rc = make_plan(a, pl);
+    if (rc != SHATTN_OK) return rc;
+    if (pl.grid == 0) return SHATTN_OK;
+    if (pl.ws_bytes > kScratchBytes)
+        return fail(SHATTN_EUNSUPPORTED,
+                    "hybrid_sparse_attn_fwd_noalloc: these arguments need %zu bytes of scratch, the library holds %zu",
+                    pl.ws_bytes, kScratchBytes);
+    void* ws = nullptr;
+    if (pl.ws_bytes > 0 && (rc = scratch_on_current_device(&ws)) != SHATTN_OK) return rc;
+    // the split partial states are all written before the combine reads
+    // them: nothing in the array needs clearing between calls
+    return hybrid_sparse_attn_fwd(a, ws, pl.ws_bytes, stream);
 }
