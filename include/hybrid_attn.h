@@ -242,6 +242,74 @@ SHATTN_API int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t
 SHATTN_API int hybrid_sparse_attn_fwd_noalloc(const shattn_fwd_args* a, void* stream);
 
 /*
+ * Backward pass of a prefill through the whole path: block compression of K
+ * and V for each present branch, gated hybrid attention, as
+ * hybrid_sparse_attn_fwd defines it with q_pos0 = raw_pos0 = 0 and Tq = Tr = T
+ * ([V4-code] section 1 block merge; [V4-blog] "1. hybrid attn"; [Tiny-R2]
+ * 3.1.2 / 3.2 branch gate).  Gradients are those of the forward's value with
+ * the CSA selection idx held fixed (a top-k has none) and the storage
+ * rounding of the compressed caches taken as the identity:
+ *   per branch b with gate weight w_b, P_bj the branch softmax and
+ *   D_b = dout . O_b:  dS_j = sum_b w_b P_bj (dout . v_j - D_b);
+ *   dq = scale sum_j dS_j k_j;  dk_j = scale sum dS_j q;  dv_j = sum w_b P_bj dout;
+ *   window keys belong to every present branch, HCA entries to HCA, selected
+ *   CSA entries to CSA; cache gradients flow to the raw rows (P_i dkc) and to
+ *   the logits (dz_i = P_i (dP_i - sum_l P_l dP_l), dP_i = sum dkc . x_i);
+ *   gates: dw_b = D_b (per head: summed over rows; logits: through the
+ *   branch softmax).
+ * All gradients are float32 and overwrite their buffers.  Arithmetic is
+ * float32 with no floating-point atomics (bitwise-reproducible).
+ */
+typedef struct shattn_bwd_args {
+    int32_t struct_size; /* must equal sizeof(shattn_bwd_args) */
+    int32_t dtype;       /* of q, k_raw, v_raw, dout and the caches */
+    int32_t B, T, H, Hkv, d, W;
+    float sm_scale;      /* 0 -> 1/sqrt(d) */
+    int32_t gate_mode;   /* 0, 1 or 2 as in hybrid_sparse_attn_fwd */
+    int32_t m_hca;       /* HCA ratio; 0 = HCA branch absent */
+    int32_t m_csa;       /* CSA ratio (>= 1 when k > 0) */
+    int32_t k;           /* entries per row in idx; 0 = CSA branch absent */
+    int32_t reserved0;   /* must be 0 */
+    const void* q;       /* [B, T, H, d] */
+    const void* k_raw;   /* [B, T, Hkv, d], positions 0 .. T-1 */
+    const void* v_raw;
+    const void* dout;    /* [B, T, H, d]: dL/dout */
+    const float* gates;  /* as in hybrid_sparse_attn_fwd */
+    const float* zk_hca; /* [m_hca, Hkv, d] compression logits of the HCA caches */
+    const float* zv_hca;
+    const void* k_hca;   /* [B, T / m_hca, Hkv, d]: hca_compress_kv(k_raw, v_raw, zk_hca, zv_hca) */
+    const void* v_hca;
+    const float* zk_csa; /* [m_csa, Hkv, d] */
+    const float* zv_csa;
+    const void* k_csa;   /* [B, T / m_csa, Hkv, d] */
+    const void* v_csa;
+    const int32_t* idx;  /* [B, T, k]: the forward's selection; -1 = padding.
+                            Entries must be distinct; entries not visible to
+                            their row are ignored (csa_index_topk writes none). */
+    float* dq;           /* [B, T, H, d] */
+    float* dk;           /* [B, T, Hkv, d]: window part plus every compression's part */
+    float* dv;
+    float* dzk_hca;      /* [m_hca, Hkv, d] (HCA present) */
+    float* dzv_hca;
+    float* dzk_csa;      /* [m_csa, Hkv, d] (CSA present) */
+    float* dzv_csa;
+    float* dgates;       /* gates' shape: [H, 3] (mode 0) or [B, T, H, 3] */
+    float* dk_hca;       /* optional (NULL = not returned): [B, T / m_hca, Hkv, d] */
+    float* dv_hca;       /*   gradients of the compressed caches */
+    float* dk_csa;       /* optional: [B, T / m_csa, Hkv, d] */
+    float* dv_csa;
+} shattn_bwd_args;
+
+/* Workspace bytes hybrid_sparse_attn_bwd needs (0 for invalid arguments):
+ * 24 B per (row, head) for the softmax statistics, the cache gradients not
+ * returned, and the compression-logit partial sums. */
+SHATTN_API size_t hybrid_sparse_attn_bwd_workspace_size(const shattn_bwd_args* a);
+/* Supported: d in {64, 128}; H % Hkv == 0; W >= 1; ratios <= 1024;
+ * B T H < 2^31.  Workspace 16-byte aligned, at least the size above
+ * (SHATTN_EWORKSPACE otherwise). */
+SHATTN_API int hybrid_sparse_attn_bwd(const shattn_bwd_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Decode cache maintenance, one new token per sequence ([V4-blog] "1. hybrid
  * attn": the raw window K/V and the compressed caches are kept apart; the raw
  * rows age out as decode advances, the compressed entries stay; the block

@@ -34,6 +34,8 @@ EXPORTED = (
     "hybrid_sparse_attn_fwd_workspace_size",
     "hybrid_sparse_attn_fwd",
     "hybrid_sparse_attn_fwd_noalloc",
+    "hybrid_sparse_attn_bwd_workspace_size",
+    "hybrid_sparse_attn_bwd",
     "hybrid_cache_append",
     "rope_apply",
     "cache_quant4",
@@ -104,6 +106,33 @@ class AppendArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of shattn_bwd_args (same field order; C alignment rules)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("gate_mode", ctypes.c_int32),
+        ("m_hca", ctypes.c_int32), ("m_csa", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k_raw", ctypes.c_void_p), ("v_raw", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p), ("gates", ctypes.c_void_p),
+        ("zk_hca", ctypes.c_void_p), ("zv_hca", ctypes.c_void_p),
+        ("k_hca", ctypes.c_void_p), ("v_hca", ctypes.c_void_p),
+        ("zk_csa", ctypes.c_void_p), ("zv_csa", ctypes.c_void_p),
+        ("k_csa", ctypes.c_void_p), ("v_csa", ctypes.c_void_p),
+        ("idx", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dzk_hca", ctypes.c_void_p), ("dzv_hca", ctypes.c_void_p),
+        ("dzk_csa", ctypes.c_void_p), ("dzv_csa", ctypes.c_void_p),
+        ("dgates", ctypes.c_void_p),
+        ("dk_hca", ctypes.c_void_p), ("dv_hca", ctypes.c_void_p),
+        ("dk_csa", ctypes.c_void_p), ("dv_csa", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -139,6 +168,10 @@ def load_library(path: str = LIB_PATH):
         lib.hybrid_sparse_attn_fwd.restype = i32
         lib.hybrid_sparse_attn_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), vp]
         lib.hybrid_sparse_attn_fwd_noalloc.restype = i32
+        lib.hybrid_sparse_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+        lib.hybrid_sparse_attn_bwd_workspace_size.restype = sz
+        lib.hybrid_sparse_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), vp, sz, vp]
+        lib.hybrid_sparse_attn_bwd.restype = i32
         lib.hybrid_cache_append.argtypes = [ctypes.POINTER(AppendArgs), vp]
         lib.hybrid_cache_append.restype = i32
         lib.rope_apply.argtypes = [vp, vp, i64, i32, i32, i32, i32, ctypes.c_double, i32, vp]
@@ -355,6 +388,101 @@ def hybrid_sparse_attn_fwd_noalloc(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_p
                                   q_pos=q_pos, raw_ring=raw_ring)
     _check(lib.hybrid_sparse_attn_fwd_noalloc(ctypes.byref(a), _stream(q)))
     return out
+
+
+def make_bwd_args(q, k_raw, v_raw, gates, dout, W, *, hca=None, csa=None, sm_scale=0.0, gate_logits=False,
+                  cache_grads=False):
+    """Build the argument struct and the gradient tensors for hybrid_sparse_attn_bwd.
+
+    hca = (zk_hca, zv_hca, k_hca, v_hca, m_hca) or None; csa = (zk_csa, zv_csa,
+    k_csa, v_csa, m_csa, idx) or None (caches: the forward's compressed K/V).
+    cache_grads: also return the gradients of the compressed caches.
+    Returns (BwdArgs, dict of float32 gradient tensors, keepalive tuple)."""
+    _need(q, "q")
+    dev = q.device
+    for t, n in ((k_raw, "k_raw"), (v_raw, "v_raw"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    _need(gates, "gates", torch.float32, dev)
+    B, T, H, d = q.shape
+    Hkv = k_raw.shape[2]
+    if tuple(k_raw.shape) != (B, T, Hkv, d) or tuple(v_raw.shape) != (B, T, Hkv, d) or dout.shape != q.shape:
+        raise ValueError("k_raw / v_raw must be [B, T, Hkv, d] and dout the shape of q")
+    if tuple(gates.shape) == (H, 3) and not gate_logits:
+        gate_mode = 0
+    elif tuple(gates.shape) == (B, T, H, 3):
+        gate_mode = 2 if gate_logits else 1
+    else:
+        raise ValueError(f"gates must be [H, 3] or [B, T, H, 3] (logits: per token only), got {tuple(gates.shape)}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, T, H, d), **f32), "dk": torch.empty((B, T, Hkv, d), **f32),
+         "dv": torch.empty((B, T, Hkv, d), **f32), "dgates": torch.empty(tuple(gates.shape), **f32)}
+    a = BwdArgs()
+    a.struct_size = ctypes.sizeof(BwdArgs)
+    a.dtype = _dtype_code(q)
+    a.B, a.T, a.H, a.Hkv, a.d, a.W = B, T, H, Hkv, d, W
+    a.sm_scale = sm_scale
+    a.gate_mode = gate_mode
+    a.q, a.k_raw, a.v_raw, a.dout, a.gates = (t.data_ptr() for t in (q, k_raw, v_raw, dout, gates))
+    keep = [q, k_raw, v_raw, dout, gates]
+    for name, br in (("hca", hca), ("csa", csa)):
+        if br is None:
+            continue
+        zk, zv, kc, vc, m = br[:5]
+        _need(zk, "zk_" + name, torch.float32, dev)
+        _need(zv, "zv_" + name, torch.float32, dev)
+        _need(kc, "k_" + name, q.dtype, dev)
+        _need(vc, "v_" + name, q.dtype, dev)
+        m = int(m)
+        if tuple(zk.shape) != (m, Hkv, d) or tuple(zv.shape) != (m, Hkv, d):
+            raise ValueError(f"zk_{name} / zv_{name} must be [m, Hkv, d]")
+        if tuple(kc.shape) != (B, T // m, Hkv, d) or tuple(vc.shape) != (B, T // m, Hkv, d):
+            raise ValueError(f"k_{name} / v_{name} must be [B, T // m, Hkv, d]")
+        setattr(a, "m_" + name, m)
+        setattr(a, "zk_" + name, zk.data_ptr())
+        setattr(a, "zv_" + name, zv.data_ptr())
+        setattr(a, "k_" + name, kc.data_ptr())
+        setattr(a, "v_" + name, vc.data_ptr())
+        g["dzk_" + name] = torch.empty((m, Hkv, d), **f32)
+        g["dzv_" + name] = torch.empty((m, Hkv, d), **f32)
+        setattr(a, "dzk_" + name, g["dzk_" + name].data_ptr())
+        setattr(a, "dzv_" + name, g["dzv_" + name].data_ptr())
+        if cache_grads:
+            g["dk_" + name] = torch.empty((B, T // m, Hkv, d), **f32)
+            g["dv_" + name] = torch.empty((B, T // m, Hkv, d), **f32)
+            setattr(a, "dk_" + name, g["dk_" + name].data_ptr())
+            setattr(a, "dv_" + name, g["dv_" + name].data_ptr())
+        keep += [zk, zv, kc, vc]
+        if name == "csa":
+            idx = br[5]
+            _need(idx, "idx", torch.int32, dev)
+            if tuple(idx.shape[:2]) != (B, T) or idx.dim() != 3:
+                raise ValueError("idx must be [B, T, k]")
+            a.idx, a.k = idx.data_ptr(), idx.shape[2]
+            keep.append(idx)
+    if csa is not None and a.k == 0:
+        raise ValueError("idx must have k >= 1 entries per row for the CSA branch")
+    a.dq, a.dk, a.dv, a.dgates = (g[n].data_ptr() for n in ("dq", "dk", "dv", "dgates"))
+    return a, g, tuple(keep)
+
+
+def hybrid_sparse_attn_bwd_workspace_size(args: BwdArgs) -> int:
+    return int(load_library().hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(args)))
+
+
+def hybrid_sparse_attn_bwd(q, k_raw, v_raw, gates, dout, W, *, hca=None, csa=None, sm_scale=0.0,
+                           gate_logits=False, cache_grads=False, ws=None):
+    """Backward of a prefill through compression and gated hybrid attention;
+    returns a dict of float32 gradients (dq, dk, dv, dgates, dzk_hca ...; see
+    make_bwd_args)."""
+    lib = load_library()
+    a, g, _keep = make_bwd_args(q, k_raw, v_raw, gates, dout, W, hca=hca, csa=csa, sm_scale=sm_scale,
+                                gate_logits=gate_logits, cache_grads=cache_grads)
+    nbytes = int(lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(a)))
+    if ws is None and nbytes > 0:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.hybrid_sparse_attn_bwd(ctypes.byref(a), _ptr(ws), ws_bytes, _stream(q)))
+    return g
 
 
 def make_append_args(pos, k_new, v_new, k_ring, v_ring, *, csa=None, hca=None, indexer=None, dropped=None):

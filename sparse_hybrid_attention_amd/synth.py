@@ -225,6 +225,24 @@ def make_inputs(name: str, seed: int = 0, **overrides) -> dict:
     return make_prefill(cfg, seed)
 
 
+def make_backward(name: str, seed: int = 0, gate_mode: int = 0, **overrides) -> dict:
+    """Inputs of the prefill backward: make_inputs(name, seed, **overrides),
+    plus, from a second stream PCG64([seed, 1]) in this order, the incoming
+    gradient dout ~ N(0, 1) [B, T, H, d] (storage dtype) and, for gate_mode 1
+    or 2, per-token gates [B, T, H, 3]: U(0, 1) weights (1) or N(0, 1) logits
+    (2), which replace the per-head gates."""
+    out = make_inputs(name, seed, **overrides)
+    cfg = out["cfg"]
+    rng = np.random.Generator(np.random.PCG64([seed, 1]))
+    B, T, H, d = cfg["B"], cfg["T"], cfg["H"], cfg["d"]
+    out["dout"] = _normal(rng, (B, T, H, d), cfg["dtype"])
+    if gate_mode == 1:
+        out["gates"] = rng.random(size=(B, T, H, 3), dtype=np.float32)
+    elif gate_mode == 2:
+        out["gates"] = rng.standard_normal(size=(B, T, H, 3), dtype=np.float32)
+    return out
+
+
 def make_rope(*, rows, heads, d, dtype=DTYPE_BF16, max_pos=1 << 20, seed: int = 0) -> dict:
     """RoPE inputs.  Draw order: x [rows, heads, d] ~ N(0, 1), then positions
     U{0, .., max_pos - 1}; row 0 sits at position 0, row 1 is inactive (-1)

@@ -54,7 +54,8 @@ def test_no_unresolved_library_symbols(lib):
 
 
 @pytest.mark.parametrize("cls,cname", [(binding.FwdArgs, "shattn_fwd_args"),
-                                       (binding.AppendArgs, "shattn_append_args")])
+                                       (binding.AppendArgs, "shattn_append_args"),
+                                       (binding.BwdArgs, "shattn_bwd_args")])
 def test_struct_layout_matches_c(lib, tmp_path, cls, cname):
     fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
@@ -215,6 +216,57 @@ def test_index_varlen_errors(lib):
     assert "q_pos" in err(lib)
     assert f(*args(ctypes.c_void_p(0x7F0000000004))) == binding.SHATTN_EINVAL
     assert f(*args(None, B=0)) == binding.SHATTN_OK     # nothing to do
+
+
+def bwd(**kw):
+    a = binding.BwdArgs()
+    a.struct_size = ctypes.sizeof(binding.BwdArgs)
+    a.dtype, a.B, a.T, a.H, a.Hkv, a.d, a.W = 0, 2, 256, 4, 2, 128, 16
+    a.m_hca, a.m_csa, a.k = 64, 4, 8
+    for f in ("q", "k_raw", "v_raw", "dout", "gates", "zk_hca", "zv_hca", "k_hca", "v_hca", "zk_csa", "zv_csa",
+              "k_csa", "v_csa", "idx", "dq", "dk", "dv", "dzk_hca", "dzv_hca", "dzk_csa", "dzv_csa", "dgates"):
+        setattr(a, f, P.value)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_backward_errors(lib):
+    f = lib.hybrid_sparse_attn_bwd
+
+    def call(**kw):
+        return f(ctypes.byref(bwd(**kw)), None, 0, None)
+    assert f(None, None, 0, None) == binding.SHATTN_EINVAL
+    assert call(struct_size=8) == binding.SHATTN_EINVAL
+    assert call(reserved0=1) == binding.SHATTN_EINVAL
+    assert call(dtype=4) == binding.SHATTN_EINVAL
+    assert call(H=3) == binding.SHATTN_EINVAL
+    assert call(d=96) == binding.SHATTN_EUNSUPPORTED
+    assert call(W=0) == binding.SHATTN_EINVAL
+    assert call(gate_mode=3) == binding.SHATTN_EINVAL
+    assert call(m_csa=0) == binding.SHATTN_EINVAL              # CSA branch without its ratio
+    assert call(m_hca=2048) == binding.SHATTN_EUNSUPPORTED
+    assert call(sm_scale=float("inf")) == binding.SHATTN_EINVAL
+    assert call(idx=None) == binding.SHATTN_EINVAL
+    assert call(zk_hca=None) == binding.SHATTN_EINVAL
+    assert call(dzv_csa=None) == binding.SHATTN_EINVAL
+    assert call(dq=None) == binding.SHATTN_EINVAL
+    assert call(k_raw=0x7F0000000008) == binding.SHATTN_EINVAL    # 16-byte alignment
+    assert call(idx=0x7F0000000002) == binding.SHATTN_EINVAL      # 4-byte alignment
+    # absent branches need none of their pointers
+    a = bwd(m_hca=0, k=0, zk_hca=None, zv_hca=None, k_hca=None, v_hca=None, zk_csa=None, zv_csa=None,
+            k_csa=None, v_csa=None, idx=None, dzk_hca=None, dzv_hca=None, dzk_csa=None, dzv_csa=None)
+    need = lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(a))
+    assert need >= 2 * 256 * 4 * 24                  # softmax statistics: 24 bytes per (row, head)
+    assert f(ctypes.byref(a), None, 0, None) == binding.SHATTN_EWORKSPACE
+    assert f(ctypes.byref(a), P, need - 1, None) == binding.SHATTN_EWORKSPACE
+    assert "workspace" in err(lib)
+    # returning the cache gradients shrinks the workspace
+    full = bwd()
+    given = bwd(dk_hca=P.value, dv_hca=P.value, dk_csa=P.value, dv_csa=P.value)
+    assert (lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(full)) -
+            lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(given))) >= 2 * 2 * (4 + 64) * 2 * 128 * 4
+    assert lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(bwd(d=96))) == 0
 
 
 def append(**kw):
