@@ -56,17 +56,31 @@ def to_dev(a):
     return torch.from_numpy(a).to("cuda:0")
 
 
-def make_pipeline(inp):
+def make_pipeline(inp, q4=False):
+    from sparse_hybrid_attention_amd import binding
     from sparse_hybrid_attention_amd.binding import HybridPipeline
     cfg = inp["cfg"]
     if cfg["kind"] == "decode":
+        caches = {n: to_dev(inp[n]) for n in ("k_csa", "v_csa", "k_hca", "v_hca")}
+        extra = {}
+        if q4:
+            # 4-bit storage of the compressed caches, made once by the library's
+            # own encoder (outside the timed steps); the attention decodes them
+            for br in ("hca", "csa"):
+                pair = []
+                for n in ("k_" + br, "v_" + br):
+                    x = caches[n]
+                    codes, params = binding.cache_quant4(x)
+                    caches[n] = codes.view(*x.shape[:-1], x.shape[-1] // 2)
+                    pair.append(params)
+                extra["q4_" + br] = tuple(pair)
         return HybridPipeline(q=to_dev(inp["q"]), gates=to_dev(inp["gates"]), W=cfg["W"],
                               k_raw=to_dev(inp["k_win"]), v_raw=to_dev(inp["v_win"]),
                               q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
                               qI=to_dev(inp["qI"]), kI=to_dev(inp["kI"]), w=to_dev(inp["w"]),
-                              k=cfg["k"], m_csa=cfg["m_csa"], m_hca=cfg["m_hca"],
-                              k_csa=to_dev(inp["k_csa"]), v_csa=to_dev(inp["v_csa"]),
-                              k_hca=to_dev(inp["k_hca"]), v_hca=to_dev(inp["v_hca"]))
+                              k=cfg["k"], m_csa=cfg["m_csa"], m_hca=cfg["m_hca"], **caches, **extra)
+    if q4:
+        raise SystemExit("--q4 applies to the decode workload (caches given up front)")
     kw = {}
     if cfg.get("m_csa"):
         kw.update(zk_csa=to_dev(inp["zk_csa"]), zv_csa=to_dev(inp["zv_csa"]), m_csa=cfg["m_csa"],
@@ -122,12 +136,15 @@ def algorithmic(inp, pipe):
     # attention: each tensor once; the CSA cache counts the entries selected by anyone
     use_hca = pipe.k_hca is not None and (g[:, 0] != 0).any()
     use_csa = pipe.idx is not None and (g[:, 1] != 0).any()
+    # bytes of one compressed-cache row: dtype values, or d / 2 bytes of 4-bit codes
+    row_h = d // 2 if getattr(pipe, "q4_hca", False) else d * esz
+    row_c = d // 2 if getattr(pipe, "q4_csa", False) else d * esz
     keys = win.copy()
     byt = 2 * B * Tq * H * d * esz + 2 * B * Tr * Hkv * d * esz + H * 3 * 4
     if use_hca:
         vis_h = np.array([n_visible(x, W, cfg["m_hca"], Nh) for x in t], dtype=np.float64)
         keys += vis_h
-        byt += 2 * B * int(vis_h.max()) * Hkv * d * esz
+        byt += 2 * B * int(vis_h.max()) * Hkv * row_h
     if use_csa:
         idx = pipe.idx
         sel = (idx >= 0).sum(dim=-1).to(torch.float64).mean(dim=0).cpu().numpy()
@@ -135,14 +152,14 @@ def algorithmic(inp, pipe):
         used = 0
         for b in range(B):
             used += int(torch.unique(idx[b]).numel()) - int((idx[b] < 0).any().item())
-        byt += 2 * used * Hkv * d * esz + B * Tq * cfg["k"] * 4
+        byt += 2 * used * Hkv * row_c + B * Tq * cfg["k"] * 4
     pairs = B * H * keys.sum()
     out["attention"] = dict(bytes=float(byt), flops=4.0 * d * pairs, units=B * keys.sum(),
                             unit="attended (query, key) pairs")
     if use_csa:
         # K and V rows of every selected entry, as the kernel reads them (once
         # per query and KV head): served mostly from L2 / MALL, not HBM
-        out["attention"]["gathered_bytes"] = float(B * sel.sum() * Hkv * 2 * d * esz)
+        out["attention"]["gathered_bytes"] = float(B * sel.sum() * Hkv * 2 * row_c)
     return out
 
 
@@ -639,6 +656,115 @@ def bench_quant4(args, torch, binding):
     print(json.dumps(line))
 
 
+def bench_backward(args, torch, binding):
+    """Backward of the Tiny-R2 training-shape prefill (B8 T2048 H=Hkv=12 d128
+    bf16; HCA m128, CSA m4 k64, W128, per-head gates U(0,1)): one
+    hybrid_sparse_attn_bwd call per step (all its launches), with the
+    compressed caches and the CSA selection made beforehand by the forward
+    path's own kernels (untimed)."""
+    import oracle as O
+    from sparse_hybrid_attention_amd import synth
+    inp = synth.make_backward("tinyr2_bf16", seed=0)
+    cfg = inp["cfg"]
+    B, T, H, Hkv, d, W, k = cfg["B"], cfg["T"], cfg["H"], cfg["Hkv"], cfg["d"], cfg["W"], cfg["k"]
+    mh, mc = cfg["m_hca"], cfg["m_csa"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's float64 backward on the last rows of one sequence (every
+        # branch present there), one process
+        rows = 96
+        q0 = T - rows
+        t1 = time.perf_counter()
+        kh, vh = O.compress_kv(inp["k"][:1], inp["v"][:1], inp["zk_hca"], inp["zv_hca"], mh, cfg["dtype"])
+        kc, vc = O.compress_kv(inp["k"][:1], inp["v"][:1], inp["zk_csa"], inp["zv_csa"], mc, cfg["dtype"])
+        idx0 = O.index_topk(inp["qI"][:1, q0:], inp["kI"][:1], inp["w"][:1, q0:], q0, mc, W, k, cfg["dtype"])
+        dout = inp["dout"][:1, q0:]
+        O.hybrid_attn_bwd(inp["q"][:1, q0:], inp["k"][:1], inp["v"][:1], inp["gates"],
+                          (dout.astype(np.uint32) << 16).view(np.float32).astype(np.float64), W=W,
+                          dtype=cfg["dtype"], q_pos0=q0, hca=(kh, vh, mh), csa=(kc, vc, idx0))
+        dt_cpu = time.perf_counter() - t1
+        cpu = {"value": round(rows / dt_cpu, 2), "unit": "query rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"the last {rows} query rows of one sequence (all {H} heads, every branch), with that "
+                         f"sequence's compression and selection; float64 NumPy, one process; {dt_cpu:.1f} s"}
+    dev = "cuda:0"
+    D = lambda a: to_dev(a)
+    q, kr, vr, dout = D(inp["q"]), D(inp["k"]), D(inp["v"]), D(inp["dout"])
+    gates = D(inp["gates"])
+    zk_h, zv_h, zk_c, zv_c = D(inp["zk_hca"]), D(inp["zv_hca"]), D(inp["zk_csa"]), D(inp["zv_csa"])
+    (k_c, v_c), (k_h, v_h) = binding.hca_compress_kv_dual(kr, vr, zk_c, zv_c, mc, zk_h, zv_h, mh)
+    qI, kI, w = D(inp["qI"]), D(inp["kI"]), D(inp["w"])
+    idx = binding.csa_index_topk(qI, kI, w, 0, mc, W, k)
+    torch.cuda.synchronize()
+    lib = binding.load_library()
+    a, grads, keep = binding.make_bwd_args(q, kr, vr, gates, dout, W, hca=(zk_h, zv_h, k_h, v_h, mh),
+                                           csa=(zk_c, zv_c, k_c, v_c, mc, idx))
+    nbytes = int(lib.hybrid_sparse_attn_bwd_workspace_size(ctypes.byref(a)))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    call = lambda: binding._check(lib.hybrid_sparse_attn_bwd(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                                             nbytes, sp))
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    scratch = flush_buffer(torch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        scratch.fill_(i & 255)
+        evs[i][0].record(stream)
+        call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    kms = sum(step_ms) / args.steps
+    # algorithmic work: every (query row, head, key of its branch sets) pair
+    # costs 10 d flops (scores, dout.v, dq, dk, dv); compulsory bytes: Q, dout,
+    # K, V, the caches, idx and gates read once, dq, dk, dv and the small
+    # logit / gate gradients written once
+    pairs = 0
+    for t in range(T):
+        nw = min(W, t + 1)
+        pairs += nw + n_visible(t, W, mh, T // mh) + min(k, n_visible(t, W, mc, T // mc))
+    pairs *= B * H
+    flops = 10 * d * pairs
+    el = 2
+    nbytes_alg = (2 * B * T * H * d + 2 * B * T * Hkv * d) * el + 2 * B * (T // mh + T // mc) * Hkv * d * el \
+        + B * T * k * 4 + H * 3 * 4 + (B * T * H * d + 2 * B * T * Hkv * d) * 4 + 2 * (mh + mc) * Hkv * d * 4 * 2
+    t_hbm = nbytes_alg / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS["bf16"] * 1e12)
+    if t_mfma > t_hbm:
+        ach = flops / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS["bf16"], 6)}
+    else:
+        ach = nbytes_alg / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 6)}
+    roof.update(kernel="hybrid_sparse_attn_bwd (all launches of a step)", kernel_ms=round(kms, 5),
+                alg_bytes_per_launch=nbytes_alg, alg_flops_per_launch=flops, traffic=None,
+                TFLOPs_achieved=round(flops / (kms * 1e-3) / 1e12, 3))
+    line = {
+        "metric": "hybrid sparse attn backward query rows/s",
+        "value": round(B * T * args.steps / wall, 1),
+        "unit": "query rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
+        "config": {"workload": f"backward of the Tiny-R2 training-shape prefill, B{B} T{T} H=Hkv={H} d{d} bf16, "
+                               f"HCA m{mh}, CSA m{mc} k{k} (selection by the indexer), W{W}, gates U(0,1); "
+                               f"gradients float32", "name": "tinyr2_bwd",
+                   "timing": "each timed step starts from flushed L2 / MALL (cold)",
+                   "gpu_ms_per_step_median": round(step_ms[len(step_ms) // 2], 5),
+                   "key_pairs_per_step": pairs},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 WORKLOADS = {
     "tinyr2_bf16": "Tiny-R2 training-shape forward, B8 T2048 H=Hkv=12 d128 bf16, CSA m4 k64 "
                    "(indexer 4 heads d_idx 64), HCA m128, W128, gates U(0,1) (all branches)",
@@ -686,9 +812,12 @@ def main():
     ap.add_argument("--workload", default="csa_prefill_128k",
                     help="csa_prefill_128k (default: the largest single-GPU configuration), tinyr2_bf16, "
                          "tiny_fp32, hca_prefill_32k, decode_1m, decode_append (cache maintenance), rope_q (RoPE "
-                         "on the query tensor), quant4_hca (4-bit cache storage)")
+                         "on the query tensor), quant4_hca (4-bit cache storage), tinyr2_bwd (backward of the "
+                         "Tiny-R2 training-shape prefill)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
+    ap.add_argument("--q4", action="store_true",
+                    help="decode workload: the HCA and CSA caches in 4-bit storage, decoded by the attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm (back-to-back) timing and the measured-peak probes")
@@ -745,10 +874,13 @@ def main():
     if args.workload == "quant4_hca":
         bench_quant4(args, torch, binding)
         return
+    if args.workload == "tinyr2_bwd":
+        bench_backward(args, torch, binding)
+        return
     if not pipeline_workload:
         raise SystemExit(f"unknown workload {args.workload}")
     cfg = inp["cfg"]
-    pipe = make_pipeline(inp)
+    pipe = make_pipeline(inp, q4=args.q4)
     names = pipe.names()
     log(f"[bench] kernels per step: {names}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -831,7 +963,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
-        "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]"),
+        "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]")
+                   + (" [HCA and CSA caches in 4-bit storage]" if args.q4 else ""),
                    "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],
                    "query_rows": queries, "timing": "each timed step starts from flushed L2 / MALL (cold)",
                    "gpu_ms_per_step_median": round(step_ms[len(step_ms) // 2], 5)},

@@ -217,6 +217,17 @@ typedef struct shattn_fwd_args {
                             (as hybrid_cache_append keeps them): position t is
                             in row t % Tr; raw_pos0 is unused and Tr >= W + Tq - 1. */
     int32_t reserved0;   /* must be 0 */
+    int32_t cache_q4;    /* bit 0: k_hca / v_hca hold 4-bit codes, bit 1: k_csa /
+                            v_csa do ([V4-code] section 1, 4-bit storage of the
+                            merged cache): codes as cache_quant4 writes them
+                            ([B, N, Hkv, d/2] bytes, element 2j in the low nibble
+                            of byte j of a row), decoded inside the attention's
+                            loads to the values cache_dequant4 gives.  bf16 only. */
+    int32_t reserved1;   /* must be 0 */
+    const float* q4_k_hca; /* DEVICE float32 [2] (min, step) of each coded tensor, */
+    const float* q4_v_hca; /*   as cache_quant4 writes them (bits of cache_q4 set) */
+    const float* q4_k_csa;
+    const float* q4_v_csa;
 } shattn_fwd_args;
 
 /* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the

@@ -80,6 +80,10 @@ class FwdArgs(ctypes.Structure):
         ("q_pos", ctypes.c_void_p),
         ("raw_ring", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
+        ("cache_q4", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
+        ("q4_k_hca", ctypes.c_void_p), ("q4_v_hca", ctypes.c_void_p),
+        ("q4_k_csa", ctypes.c_void_p), ("q4_v_csa", ctypes.c_void_p),
     ]
 
 
@@ -300,6 +304,10 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
     """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
 
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
+    A 4-bit cache adds its (min, step) tensors: hca = (k_codes, v_codes, m_hca,
+    (params_k, params_v)), csa = (k_codes, v_codes, idx, (params_k, params_v)),
+    codes uint8 [B, N, Hkv, d/2] and params float32 [2] as cache_quant4 writes
+    them.
     gates: [H, 3] per-head weights, or [B, Tq, H, 3] per-token weights (or,
     with gate_logits, per-token logits the kernel softmaxes over the branches).
     q_pos: device int64 [B] per-sequence positions (needs raw_ring); raw_ring:
@@ -333,16 +341,40 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
     a.Tr = Tr
     a.k_raw, a.v_raw = k_raw.data_ptr(), v_raw.data_ptr()
     keep = [q, k_raw, v_raw, gates, out]
+    def cache(t, name, params, bit):
+        if params is None:
+            _need(t, name, q.dtype, dev)
+            if tuple(t.shape[2:]) != (Hkv, d):
+                raise ValueError(f"{name} must be [B, N, Hkv, d]")
+            return
+        _need(t, name, torch.uint8, dev)
+        if tuple(t.shape[2:]) != (Hkv, d // 2):
+            raise ValueError(f"{name} (4-bit codes) must be [B, N, Hkv, d/2]")
+        a.cache_q4 |= bit
+
+    def q4params(pair, names):
+        for t, n in zip(pair, names):
+            _need(t, n, torch.float32, dev)
+            if t.numel() != 2:
+                raise ValueError(f"{n} must hold (min, step)")
+            setattr(a, n, t.data_ptr())
+            keep.append(t)
     if hca is not None:
-        kh, vh, mh = hca
-        _need(kh, "k_hca", q.dtype, dev)
-        _need(vh, "v_hca", q.dtype, dev)
+        kh, vh, mh = hca[:3]
+        ph = hca[3] if len(hca) > 3 else None
+        cache(kh, "k_hca", ph, 1)
+        cache(vh, "v_hca", ph, 1)
+        if ph is not None:
+            q4params(ph, ("q4_k_hca", "q4_v_hca"))
         a.k_hca, a.v_hca, a.m_hca, a.N_hca = kh.data_ptr(), vh.data_ptr(), int(mh), kh.shape[1]
         keep += [kh, vh]
     if csa is not None:
-        kc, vc, idx = csa
-        _need(kc, "k_csa", q.dtype, dev)
-        _need(vc, "v_csa", q.dtype, dev)
+        kc, vc, idx = csa[:3]
+        pc = csa[3] if len(csa) > 3 else None
+        cache(kc, "k_csa", pc, 2)
+        cache(vc, "v_csa", pc, 2)
+        if pc is not None:
+            q4params(pc, ("q4_k_csa", "q4_v_csa"))
         _need(idx, "idx", torch.int32, dev)
         a.k_csa, a.v_csa, a.idx = kc.data_ptr(), vc.data_ptr(), idx.data_ptr()
         a.N_csa, a.k = kc.shape[1], idx.shape[-1]
@@ -615,7 +647,9 @@ class HybridPipeline:
     def __init__(self, *, q, gates, W, k_raw, v_raw, q_pos0=0, raw_pos0=0,
                  zk_csa=None, zv_csa=None, m_csa=None, zk_hca=None, zv_hca=None, m_hca=None,
                  qI=None, kI=None, w=None, k=None,
-                 k_csa=None, v_csa=None, k_hca=None, v_hca=None):
+                 k_csa=None, v_csa=None, k_hca=None, v_hca=None, q4_hca=None, q4_csa=None):
+        """Decode with 4-bit caches: k_hca / v_hca (k_csa / v_csa) are the
+        codes [B, N, Hkv, d/2] and q4_hca (q4_csa) their (params_k, params_v)."""
         lib = load_library()
         self.lib = lib
         dev = q.device
@@ -664,8 +698,9 @@ class HybridPipeline:
                                 int(q_pos0), m_csa, W, k, _dtype_code(qI), _ptr(ws) if nbytes else None,
                                 nbytes, s)))
         self.idx = idx
-        hca = None if k_hca is None else (k_hca, v_hca, m_hca)
-        csa = None if idx is None else (k_csa, v_csa, idx)
+        hca = None if k_hca is None else (k_hca, v_hca, m_hca) + (() if q4_hca is None else (q4_hca,))
+        csa = None if idx is None else (k_csa, v_csa, idx) + (() if q4_csa is None else (q4_csa,))
+        self.q4_hca, self.q4_csa = q4_hca is not None, q4_csa is not None
         a, out, keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
                                      hca=hca, csa=csa)
         self.args = a

@@ -41,6 +41,12 @@
 //    combine kernel merges them in split order (deterministic).
 //  * Workgroups are remapped so that each XCD (own L2) runs a contiguous
 //    range of (sequence, head, query tile) work.
+//  * 4-bit compressed caches ([V4-code] section 1, 4-bit storage of the
+//    merged cache): a kernel variant (Q4) loads the codes of HCA / CSA rows
+//    into registers and decodes them through 256-entry byte tables in LDS
+//    (each entry the two bf16 values of a code byte, code * step + min
+//    rounded once) into the same swizzled bf16 tiles; everything after the
+//    loads is unchanged.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -98,6 +104,10 @@ struct AttnParams {
     int n_win_items, n_hca_items;
     int has_hca, has_csa;  // branch present (its gate column is used)
     int ncol;              // columns (query, head) per workgroup = 16 * waves
+    // 4-bit compressed caches: bit 0 HCA, bit 1 CSA hold codes (two per byte)
+    int q4;
+    const float* q4p[4];   // (min, step) of the k_hca, v_hca, k_csa, v_csa codes
+    int lds_lut;           // byte offset of the four 256-entry decode tables
 };
 
 // ---------------------------------------------------------------- per-dtype MFMA
@@ -408,6 +418,7 @@ template <int D, int NT> struct Stage<float, D, NT> {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32_t;   // decode table entries in LDS
 
 template <typename T, int D, int NW> struct TileIO;
 
@@ -545,6 +556,52 @@ template <int D, int NW> struct TileIO<bf16_t, D, NW> : TileReadBf16<D> {
     }
     // the issued loads have landed in LDS (a barrier must follow)
     __device__ void commit(char*) const { __builtin_amdgcn_s_waitcnt(0); }
+
+    // 4-bit sources: a tile's codes travel global -> registers in 16-byte
+    // pieces of 32 codes, loaded while the previous tile is computed, and are
+    // decoded at commit_q4 through the byte tables into the tile layout above.
+    static constexpr int QPR = D / 32;                          // code pieces per row
+    static constexpr int QP = 2 * KT * QPR;                     // code pieces per tile (K and V)
+    static constexpr int NQ = (QP + NW * 64 - 1) / (NW * 64);   // of them per thread
+    uint4 qc[NQ];
+    lds_cu32_t* qlut_k;
+    lds_cu32_t* qlut_v;
+    int qtid;
+    __device__ void init_q4(int tid) { qtid = tid; }
+    // rows [0, nvalid) of a tile of codes at kb / vb (row stride rsb bytes);
+    // rows past nvalid repeat row 0
+    __device__ void issue_q4(const char* kb, const char* vb, long long rsb, int nvalid, lds_cu32_t* lk,
+                             lds_cu32_t* lv) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int pid = qtid + j * NW * 64;
+            if (QP % (NW * 64) != 0 && pid >= QP) break;
+            const int mat = pid / (KT * QPR), r = pid - mat * (KT * QPR);
+            const int row = r / QPR, pc = r - row * QPR;
+            qc[j] = ld16((mat ? vb : kb) + (long long)(row < nvalid ? row : 0) * rsb + pc * 16);
+        }
+        qlut_k = lk;
+        qlut_v = lv;
+    }
+    __device__ void commit_q4(char* buf) const {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int pid = qtid + j * NW * 64;
+            if (QP % (NW * 64) != 0 && pid >= QP) break;
+            const int mat = pid / (KT * QPR), r = pid - mat * (KT * QPR);
+            const int row = r / QPR, pc = r - row * QPR;
+            lds_cu32_t* lut = mat ? qlut_v : qlut_k;
+            const int sw = mat ? swz_v(row) : swz_k(row);
+            char* rb = buf + mat * MAT_BYTES + row * ROWB;
+            const uint32_t w[4] = {qc[j].x, qc[j].y, qc[j].z, qc[j].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 o = make_uint4(lut[w[u] & 255u], lut[(w[u] >> 8) & 255u], lut[(w[u] >> 16) & 255u],
+                                           lut[w[u] >> 24]);
+                *reinterpret_cast<uint4*>(rb + (((4 * pc + u) ^ sw) * 16)) = o;
+            }
+        }
+    }
     __device__ void scores(const char* buf, int c, const bf16x8_t* qf, float* s) const {
         this->scores_at(buf, c, qf, s);
     }
@@ -646,9 +703,11 @@ enum { ITEM_WIN = 0, ITEM_HCA = 1, ITEM_CSA = 2 };
 
 // GATHER: CSA entries are gathered per wave (else: attended densely with the
 // selection bitmap, or absent); the two variants are separate kernels so that
-// each carries only its own CSA code.
-template <typename T, int D, int NW, bool GATHER>
+// each carries only its own CSA code.  Q4 (bf16 only): the HCA and / or CSA
+// caches may be 4-bit codes (p.q4).
+template <typename T, int D, int NW, bool GATHER, bool Q4>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
+    static_assert(!Q4 || std::is_same<T, bf16_t>::value, "4-bit caches decode to bf16");
     typedef Tr<T, D> TR;
     constexpr int DT = D / 16;
     constexpr int NT = NW * 64;
@@ -701,6 +760,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 
     float gate[3] = {0.f, 0.f, 0.f};
     if (valid) load_gates(p, b, qi, h, gate);
+    // decode tables of the 4-bit caches: entry x of table s holds the bf16
+    // values of codes x & 15 and x >> 4 of tensor s (code * step + min formed
+    // in float64 and rounded once, as cache_dequant4 decodes)
+    lds_cu32_t* luts = (lds_cu32_t*)(smem + p.lds_lut);
+    if constexpr (Q4) {
+        // only the tables this workgroup's key ranges read (a split item
+        // covers one branch)
+        int need = p.q4;
+        if (p.nsplit) need &= item < p.n_win_items ? 0 : (item < p.n_win_items + p.n_hca_items ? 1 : 2);
+        for (int i = tid; i < 4 * 256; i += NT) {
+            const int st = i >> 8;
+            if (!((need >> (st >> 1)) & 1)) continue;
+            const double mn = p.q4p[st][0], step = p.q4p[st][1];
+            const uint32_t lo = f64_to_bf16_rne(fma((double)(i & 15), step, mn));
+            const uint32_t hi = f64_to_bf16_rne(fma((double)((i >> 4) & 15), step, mn));
+            reinterpret_cast<uint32_t*>(smem + p.lds_lut)[i] = lo | (hi << 16);
+        }
+    }
     if (tid < 4) sflag[tid] = 0;
     if (tid == 0) emax_s = -1;
     __syncthreads();
@@ -767,18 +844,53 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     int h_hi = do_hca ? (int)n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
     if ((long long)h_hi > hca_hi) h_hi = (int)hca_hi;
     const int h_lo = do_hca ? (int)hca_lo : 0;
-    const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * rs + hoff;
-    const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * rs + hoff;
+    // a 4-bit cache row is D / 2 bytes: its pointer arithmetic runs in bf16
+    // units with row stride rs / 4 and head offset hoff / 4; lut_x is its K
+    // decode table (V: lut_x + 1), -1 for rows in the dtype
+    const bool hq = Q4 && (p.q4 & 1), cq = Q4 && (p.q4 & 2);
+    const int hrs = hq ? rs / 4 : rs, crs = cq ? rs / 4 : rs;
+    const int lut_h = hq ? 0 : -1, lut_c = cq ? 2 : -1;
+    const T* khca = reinterpret_cast<const T*>(p.k_hca) + (long long)b * p.N_hca * hrs + (hq ? hoff / 4 : hoff);
+    const T* vhca = reinterpret_cast<const T*>(p.v_hca) + (long long)b * p.N_hca * hrs + (hq ? hoff / 4 : hoff);
     TIO tio;
     tio.init(tid, rs);
+    bool q4_pending = false;   // the tile in flight is 4-bit codes (in registers)
+    if constexpr (Q4) tio.init_q4(tid);
+    // start loading rows [row0, row0 + nvalid) of a source (row stride srs, in T units)
+    // row stride (T units) and decode table of each key source
+    auto src_rs = [&](int type) { return type == ITEM_HCA ? hrs : (type == ITEM_CSA ? crs : rs); };
+    auto src_lut = [&](int type) { return type == ITEM_HCA ? lut_h : (type == ITEM_CSA ? lut_c : -1); };
+    auto issue_src = [&](const T* kb, const T* vb, int type, int row0, int nvalid,
+                         char* buf) __attribute__((always_inline)) {
+        const int srs = src_rs(type), lut = src_lut(type);
+        if constexpr (Q4) {
+            q4_pending = lut >= 0;
+            if (lut >= 0) {
+                tio.issue_q4(reinterpret_cast<const char*>(kb + (long long)row0 * srs),
+                             reinterpret_cast<const char*>(vb + (long long)row0 * srs), (long long)srs * 2, nvalid,
+                             luts + lut * 256, luts + (lut + 1) * 256);
+                return;
+            }
+        }
+        tio.issue(kb + (long long)row0 * srs, vb + (long long)row0 * srs, nvalid, buf);
+    };
+    auto commit_src = [&](char* buf) __attribute__((always_inline)) {
+        if constexpr (Q4) {
+            if (q4_pending) {
+                tio.commit_q4(buf);
+                return;
+            }
+        }
+        tio.commit(buf);
+    };
     int parity = 0;
     bool pf = false;  // the first tile of the next stream is already on its way into tbuf(parity)
     // the first stream is the HCA one when it has entries, else the window
     if (do_hca && h_hi > h_lo) {
-        tio.issue(khca + (long long)h_lo * rs, vhca + (long long)h_lo * rs, min(KT, h_hi - h_lo), tbuf(0));
+        issue_src(khca, vhca, ITEM_HCA, h_lo, min(KT, h_hi - h_lo), tbuf(0));
         pf = true;
     } else if (do_win && wlen > 0) {
-        tio.issue(kraw, vraw, min(KT, wlen1), tbuf(0));
+        issue_src(kraw, vraw, ITEM_WIN, 0, min(KT, wlen1), tbuf(0));
         pf = true;
     }
 
@@ -844,8 +956,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const int wv_hi = valid ? (int)(t - w_lo) : 0;
     int hv = (valid && do_hca) ? (int)n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
     if (hv > h_hi) hv = h_hi;
-    const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * rs + hoff;
-    const T* vcsa = reinterpret_cast<const T*>(p.v_csa) + (long long)b * p.N_csa * rs + hoff;
+    const T* kcsa = reinterpret_cast<const T*>(p.k_csa) + (long long)b * p.N_csa * crs + (cq ? hoff / 4 : hoff);
+    const T* vcsa = reinterpret_cast<const T*>(p.v_csa) + (long long)b * p.N_csa * crs + (cq ? hoff / 4 : hoff);
 
     // ---- wave-uniform key ranges attended by every valid column of the wave:
     // chunks inside them need no per-key mask
@@ -868,24 +980,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // (nkb, nvb, [nk_begin, nk_end)), so the pipeline does not drain between
     // branches
     auto stream = [&](const T* kb, const T* vb, int k_begin, int k_end, int type, const T* nkb, const T* nvb,
-                      int nk_begin, int nk_end) {
+                      int nk_begin, int nk_end, int ntype) __attribute__((always_inline)) {
         const int n = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
         if (n == 0) return;
-        if (!pf)
-            tio.issue(kb + (long long)k_begin * rs, vb + (long long)k_begin * rs, min(KT, k_end - k_begin),
-                      tbuf(parity));
+        if (!pf) issue_src(kb, vb, type, k_begin, min(KT, k_end - k_begin), tbuf(parity));
         pf = false;
-        tio.commit(tbuf(parity));
+        commit_src(tbuf(parity));
         __syncthreads();
         for (int i = 0; i < n; ++i) {
             const int k0 = k_begin + i * KT;
             const char* buf = tbuf(parity);
             if (i + 1 < n) {
                 const int k1 = k0 + KT;
-                tio.issue(kb + (long long)k1 * rs, vb + (long long)k1 * rs, min(KT, k_end - k1), tbuf(parity ^ 1));
+                issue_src(kb, vb, type, k1, min(KT, k_end - k1), tbuf(parity ^ 1));
             } else if (nk_end > nk_begin) {
-                tio.issue(nkb + (long long)nk_begin * rs, nvb + (long long)nk_begin * rs,
-                          min(KT, nk_end - nk_begin), tbuf(parity ^ 1));
+                issue_src(nkb, nvb, ntype, nk_begin, min(KT, nk_end - nk_begin), tbuf(parity ^ 1));
                 pf = true;
             }
             auto pvf = [&](int ch, const float* pp, f32x4_t* acc) { tio.pv(buf, ch * KC, pp, acc); };
@@ -929,19 +1038,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 softmax_pv<D, NCH, false>(S, sc, mb, p.scale_log2, pvf);
             }
             parity ^= 1;
-            if (i + 1 < n) tio.commit(tbuf(parity));
+            if (i + 1 < n) commit_src(tbuf(parity));
             __syncthreads();
         }
     };
 
     // ---- the window, in one run of raw rows or two (ring wrap-around), then
     // the stream that follows it
-    auto window = [&](const T* nkb, const T* nvb, int nk_begin, int nk_end) {
+    auto window = [&](const T* nkb, const T* nvb, int nk_begin, int nk_end,
+                      int ntype) __attribute__((always_inline)) {
         if (wlen1 < wlen) {
-            stream(kraw, vraw, 0, wlen1, ITEM_WIN, kraw2, vraw2, wlen1, wlen);
-            stream(kraw2, vraw2, wlen1, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end);
+            stream(kraw, vraw, 0, wlen1, ITEM_WIN, kraw2, vraw2, wlen1, wlen, ITEM_WIN);
+            stream(kraw2, vraw2, wlen1, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end, ntype);
         } else {
-            stream(kraw, vraw, 0, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end);
+            stream(kraw, vraw, 0, wlen, ITEM_WIN, nkb, nvb, nk_begin, nk_end, ntype);
         }
     };
 
@@ -1007,6 +1117,102 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
       }
     };
 
+    // ---- CSA gather of 4-bit rows: the same per-wave tiles and entry walk as
+    // gather_dma, but the rows' codes travel global -> registers (loaded one
+    // chunk ahead, during this chunk's scores, softmax and PV) and are decoded
+    // through the CSA tables into the bf16 tile layout at the top of the chunk.
+    auto gather_q4 = [&]() {
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        typedef GatherBf16<D> GB;
+        char* gk = smem + p.lds_gather + wave * p.lds_gather_stride;
+        char* gv = gk + GB::MAT_BYTES;
+        GB gio;
+        gio.init(lane);
+        constexpr int QPR = D / 32;            // 16-byte code pieces per row
+        constexpr int NLQ = KC * QPR / 64;     // pieces per lane per matrix
+        static_assert(NLQ * 64 == KC * QPR, "chunk split");
+        const long long ers = (long long)p.Hkv * (D / 2);   // bytes between entries
+        const char* kc = reinterpret_cast<const char*>(kcsa);
+        const char* vc = reinterpret_cast<const char*>(vcsa);
+        lds_cu32_t* lk = luts + 2 * 256;
+        lds_cu32_t* lv = luts + 3 * 256;
+        const int ql_a = (wave * 16) / p.G;
+        const int ql_b = min((wave * 16 + 15) / p.G, nq - 1);
+        int j_lo = 0, j_hi = p.k;
+        if (p.nsplit) {
+            j_lo = (int)csa_lo;
+            j_hi = csa_hi < p.k ? (int)csa_hi : p.k;
+        }
+        const int nj = j_hi > j_lo ? (j_hi - j_lo + KC - 1) / KC : 0;
+        const int nchunks = ql_b >= ql_a ? (ql_b - ql_a + 1) * nj : 0;
+        if (nchunks == 0 || p.N_csa == 0) return;
+        auto entry = [&](int ci) -> int {
+            const int qq = ql_a + ci / nj;
+            const int j = j_lo + (ci - (qq - ql_a) * nj) * KC + lane;
+            int e = -1;
+            if (lane < KC && j < j_hi) {
+                e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
+                if (e < 0 || e >= p.N_csa) e = -1;
+            }
+            return e;
+        };
+        uint4 ck[NLQ], cv[NLQ];
+        // codes of the chunk whose entries lanes < KC hold (e >= 0)
+        auto load = [&](int e) {
+#pragma unroll
+            for (int j = 0; j < NLQ; ++j) {
+                const int pid = j * 64 + lane;
+                const int row = pid / QPR, pc = pid - row * QPR;
+                const long long off = (long long)__shfl(e, row) * ers + pc * 16;
+                ck[j] = ld16(kc + off);
+                cv[j] = ld16(vc + off);
+            }
+        };
+        auto expand = [&]() {
+#pragma unroll
+            for (int j = 0; j < NLQ; ++j) {
+                const int pid = j * 64 + lane;
+                const int row = pid / QPR, pc = pid - row * QPR;
+#pragma unroll
+                for (int mat = 0; mat < 2; ++mat) {
+                    const uint4 c4 = mat ? cv[j] : ck[j];
+                    const uint32_t w[4] = {c4.x, c4.y, c4.z, c4.w};
+                    lds_cu32_t* lut = mat ? lv : lk;
+                    const int sw = mat ? GB::swz_v(row) : GB::swz_k(row);
+                    char* rb = (mat ? gv : gk) + row * GB::ROWB;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint4 o = make_uint4(lut[w[u] & 255u], lut[(w[u] >> 8) & 255u],
+                                                   lut[(w[u] >> 16) & 255u], lut[w[u] >> 24]);
+                        *reinterpret_cast<uint4*>(rb + (((4 * pc + u) ^ sw) * 16)) = o;
+                    }
+                }
+            }
+        };
+        int e_cur = entry(0);
+        load(max(e_cur, 0));
+        int e_nxt = nchunks > 1 ? entry(1) : -1;
+        for (int ci = 0; ci < nchunks; ++ci) {
+            expand();          // the previous chunk's LDS reads ended at the sync below
+            wave_lds_sync();
+            const int qq = ql_a + ci / nj;
+            const unsigned long long vrows = __ballot(lane < KC && e_cur >= 0);
+            const bool more = ci + 1 < nchunks;
+            if (more) load(max(e_nxt, 0));
+            float sc[8];
+            gio.scores_at(gk, 0, qf, sc);
+            const uint32_t mb = (valid && ql == qq) ? (uint32_t)(vrows >> (8 * q4)) & 0xFFu : 0u;
+            softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2,
+                                    [&](int, const float* pp, f32x4_t* acc) { gio.pv_at(gv, 0, pp, acc); });
+            wave_lds_sync();   // this wave's K and V reads are complete
+            if (more) {
+                e_cur = e_nxt;
+                e_nxt = ci + 2 < nchunks ? entry(ci + 2) : -1;
+            }
+        }
+      }
+    };
+
     // ---- CSA gather (per wave, private LDS tiles aliasing the stream buffers)
     auto gather = [&]() {
         char* gbase = smem + p.lds_gather + wave * p.lds_gather_stride;
@@ -1067,15 +1273,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         // the gather reuses the tile buffers).
         float m_h = -INFINITY, l_h = 0.f;
         if (do_hca) {
-            stream(khca, vhca, h_lo, h_hi, ITEM_HCA, kraw, vraw, 0, wlen1);
+            stream(khca, vhca, h_lo, h_hi, ITEM_HCA, kraw, vraw, 0, wlen1, ITEM_WIN);
             m_h = S.m;
             l_h = col_sum(S.l);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] = S.acc[dt];
             S.init();
         }
-        if (do_csa && !GATHER) window(kcsa, vcsa, 0, c_hi);
-        else window(nullptr, nullptr, 0, 0);
+        if (do_csa && !GATHER) window(kcsa, vcsa, 0, c_hi, ITEM_CSA);
+        else window(nullptr, nullptr, 0, 0, ITEM_WIN);
         {
             const float l_w = col_sum(S.l);
             float c_w = valid ? gate[2] / l_w : 0.f, c_h = 0.f;
@@ -1096,29 +1302,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         }
         if (do_csa) {
             if constexpr (!GATHER) {
-                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
+                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0, ITEM_WIN);
             } else {
                 __syncthreads();  // the stream buffers become the per-wave gather tiles
-                if constexpr (std::is_same<T, bf16_t>::value) gather_dma();
-                else gather();
+                if constexpr (Q4) {
+                    if (cq) gather_q4();
+                    else gather_dma();
+                } else if constexpr (std::is_same<T, bf16_t>::value) {
+                    gather_dma();
+                } else {
+                    gather();
+                }
                 __syncthreads();
             }
             fold(gate[1]);
         }
     } else {
         // one key range per workgroup; partial states are merged by the combine kernel
-        if (do_win) window(nullptr, nullptr, 0, 0);
+        if (do_win) window(nullptr, nullptr, 0, 0, ITEM_WIN);
         if (do_csa) {
             if constexpr (!GATHER) {
-                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0);
+                stream(kcsa, vcsa, 0, c_hi, ITEM_CSA, nullptr, nullptr, 0, 0, ITEM_WIN);
             } else {
                 __syncthreads();
-                if constexpr (std::is_same<T, bf16_t>::value) gather_dma();
-                else gather();
+                if constexpr (Q4) {
+                    if (cq) gather_q4();
+                    else gather_dma();
+                } else if constexpr (std::is_same<T, bf16_t>::value) {
+                    gather_dma();
+                } else {
+                    gather();
+                }
                 __syncthreads();
             }
         }
-        if (do_hca) stream(khca, vhca, h_lo, h_hi, ITEM_HCA, nullptr, nullptr, 0, 0);
+        if (do_hca) stream(khca, vhca, h_lo, h_hi, ITEM_HCA, nullptr, nullptr, 0, 0, ITEM_WIN);
     }
 
     // ------------------------------------------------------------ epilogue
@@ -1150,15 +1368,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
 // Merge the split partial states: one thread per (column, 4 dims).
 // Every variant the launcher can select, instantiated explicitly (the host
 // compiler otherwise dropped the stubs of some variants).
-#define SHATTN_ATTN_INST(T, D)                                               \
-    template __global__ void attn_fwd_kernel<T, D, 4, false>(AttnParams);    \
-    template __global__ void attn_fwd_kernel<T, D, 4, true>(AttnParams);     \
-    template __global__ void attn_fwd_kernel<T, D, 2, false>(AttnParams);    \
-    template __global__ void attn_fwd_kernel<T, D, 2, true>(AttnParams);
-SHATTN_ATTN_INST(bf16_t, 64)
-SHATTN_ATTN_INST(bf16_t, 128)
-SHATTN_ATTN_INST(float, 64)
-SHATTN_ATTN_INST(float, 128)
+#define SHATTN_ATTN_INST(T, D, Q)                                               \
+    template __global__ void attn_fwd_kernel<T, D, 4, false, Q>(AttnParams);    \
+    template __global__ void attn_fwd_kernel<T, D, 4, true, Q>(AttnParams);     \
+    template __global__ void attn_fwd_kernel<T, D, 2, false, Q>(AttnParams);    \
+    template __global__ void attn_fwd_kernel<T, D, 2, true, Q>(AttnParams);
+SHATTN_ATTN_INST(bf16_t, 64, false)
+SHATTN_ATTN_INST(bf16_t, 128, false)
+SHATTN_ATTN_INST(bf16_t, 64, true)
+SHATTN_ATTN_INST(bf16_t, 128, true)
+SHATTN_ATTN_INST(float, 64, false)
+SHATTN_ATTN_INST(float, 128, false)
 #undef SHATTN_ATTN_INST
 
 // Merge of the split partial states.  Eight consecutive threads share one
@@ -1305,6 +1525,20 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     if (has_csa && ((a->N_csa > 0 && (!a->k_csa || !a->v_csa)) || (a->B > 0 && a->Tq > 0 && !a->idx)))
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: CSA branch needs k_csa, v_csa and idx");
     if (has_csa && a->k > 4096) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: k=%d > 4096", a->k);
+    if (a->reserved1 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved1 must be 0");
+    if (a->cache_q4 & ~3)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: cache_q4 = %d (bits 0 and 1 only)", a->cache_q4);
+    // 4-bit caches of the branches present
+    const int q4 = (has_hca ? (a->cache_q4 & 1) : 0) | (has_csa ? (a->cache_q4 & 2) : 0);
+    if (q4 && a->dtype != SHATTN_DTYPE_BF16)
+        return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: 4-bit caches need dtype bf16");
+    const float* q4p[4] = {a->q4_k_hca, a->q4_v_hca, a->q4_k_csa, a->q4_v_csa};
+    for (int i = 0; i < 4; ++i)
+        if ((q4 >> (i >> 1)) & 1) {
+            if (!q4p[i]) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: 4-bit cache without its (min, step)");
+            if (reinterpret_cast<uintptr_t>(q4p[i]) & 3)
+                return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: (min, step) must be 4-byte aligned");
+        }
     AttnParams& p = pl.p;
     p = AttnParams{};
     p.B = a->B;
@@ -1359,6 +1593,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.N_hca = has_hca ? a->N_hca : 0;
     p.N_csa = has_csa ? a->N_csa : 0;
     p.k = has_csa ? a->k : 0;
+    p.q4 = q4;
+    for (int i = 0; i < 4; ++i) p.q4p[i] = ((q4 >> (i >> 1)) & 1) ? q4p[i] : nullptr;
     const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
     p.scale_log2 = scale * 1.4426950408889634f;
     // 4 waves (64 (query, head) columns) per workgroup, one per SIMD: three
@@ -1427,6 +1663,11 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
             lds = std::max(lds, (size_t)p.lds_gather_stride * pl.waves);
         }
     }
+    if (q4) {
+        // the four 256-entry decode tables (1 KiB each) after everything else
+        p.lds_lut = (int)((lds + 15) / 16 * 16);
+        lds = (size_t)p.lds_lut + 4 * 1024;
+    }
     if (lds > 160 * 1024) return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: LDS budget exceeded");
     pl.lds = lds;
     return SHATTN_OK;
@@ -1443,11 +1684,11 @@ extern "C" size_t hybrid_sparse_attn_fwd_workspace_size(const shattn_fwd_args* a
     return pl.ws_bytes;
 }
 
-template <typename T, int D, int NW, bool GATHER>
+template <typename T, int D, int NW, bool GATHER, bool Q4>
 static int launch_attn_nw(Plan& pl, hipStream_t s) {
     if (pl.lds > 64 * 1024) {
         // dynamic LDS beyond 64 KiB must be opted into per kernel
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D, NW, GATHER>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<T, D, NW, GATHER, Q4>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -1455,7 +1696,8 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
                         pl.lds, hipGetErrorString(e));
         }
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, GATHER>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s, pl.p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, GATHER, Q4>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s,
+                       pl.p);
     hipError_t le = hipGetLastError();
     if (le != hipSuccess)
         return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
@@ -1467,11 +1709,19 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
     return check_launch("hybrid_sparse_attn_fwd (combine)");
 }
 
+template <typename T, int D, bool Q4>
+static int launch_attn_q(Plan& pl, hipStream_t s) {
+    const bool gather = pl.p.csa_mode == CSA_GATHER;
+    if (pl.waves == 2)
+        return gather ? launch_attn_nw<T, D, 2, true, Q4>(pl, s) : launch_attn_nw<T, D, 2, false, Q4>(pl, s);
+    return gather ? launch_attn_nw<T, D, 4, true, Q4>(pl, s) : launch_attn_nw<T, D, 4, false, Q4>(pl, s);
+}
+
 template <typename T, int D>
 static int launch_attn(Plan& pl, hipStream_t s) {
-    const bool gather = pl.p.csa_mode == CSA_GATHER;
-    if (pl.waves == 2) return gather ? launch_attn_nw<T, D, 2, true>(pl, s) : launch_attn_nw<T, D, 2, false>(pl, s);
-    return gather ? launch_attn_nw<T, D, 4, true>(pl, s) : launch_attn_nw<T, D, 4, false>(pl, s);
+    if constexpr (std::is_same<T, bf16_t>::value)
+        if (pl.p.q4) return launch_attn_q<T, D, true>(pl, s);
+    return launch_attn_q<T, D, false>(pl, s);
 }
 
 extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {

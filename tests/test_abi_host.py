@@ -205,6 +205,14 @@ def test_attention_errors(lib):
     assert "ring" in err(lib)
     ring = fwd(raw_ring=1, q_pos=P.value, Tr=23, B=1, Tq=16)
     assert lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(ring)) == 0
+    # 4-bit caches: known bits only, their (min, step) given, bf16 only
+    hq = dict(m_hca=4, N_hca=2, k_hca=P.value, v_hca=P.value)
+    assert call(cache_q4=4) == binding.SHATTN_EINVAL
+    assert call(reserved1=1) == binding.SHATTN_EINVAL
+    assert call(cache_q4=1, **hq) == binding.SHATTN_EINVAL
+    assert "(min, step)" in err(lib)
+    assert call(cache_q4=1, q4_k_hca=P.value, q4_v_hca=0x7F0000000002, **hq) == binding.SHATTN_EINVAL
+    assert call(dtype=1, cache_q4=1, q4_k_hca=P.value, q4_v_hca=P.value, **hq) == binding.SHATTN_EUNSUPPORTED
     # empty problem is a no-op
     assert call(B=0) == binding.SHATTN_OK
 
