@@ -56,7 +56,7 @@ def to_dev(a):
     return torch.from_numpy(a).to("cuda:0")
 
 
-def make_pipeline(inp, q4=False):
+def make_pipeline(inp, q4=False, rope=None):
     from sparse_hybrid_attention_amd import binding
     from sparse_hybrid_attention_amd.binding import HybridPipeline
     cfg = inp["cfg"]
@@ -87,6 +87,11 @@ def make_pipeline(inp, q4=False):
                   qI=to_dev(inp["qI"]), kI=to_dev(inp["kI"]), w=to_dev(inp["w"]), k=cfg["k"])
     if cfg.get("m_hca"):
         kw.update(zk_hca=to_dev(inp["zk_hca"]), zv_hca=to_dev(inp["zv_hca"]), m_hca=cfg["m_hca"])
+    if rope is not None:
+        # RoPE of the query on its last half (the Tiny-R2 split of a rope part
+        # beside a non-rope part), base 10000
+        d = cfg["d"]
+        kw.update(rope_q=(d // 2, d // 2, 10000.0), rope_fused=rope == "fused")
     return HybridPipeline(q=to_dev(inp["q"]), gates=to_dev(inp["gates"]), W=cfg["W"],
                           k_raw=to_dev(inp["k"]), v_raw=to_dev(inp["v"]), **kw)
 
@@ -126,6 +131,10 @@ def algorithmic(inp, pipe):
         out["compress_dual"] = dict(bytes=2 * B * Tr * Hkv * d * esz + 2 * B * (N1 + N2) * Hkv * d * esz
                                     + 2 * (m1 + m2) * Hkv * d * 4, flops=0.0, units=B * (N1 + N2),
                                     unit="entries")
+    if "rope_q" in pipe.names():
+        # the rotated half of every query row read and written, one position per row
+        out["rope_q"] = dict(bytes=2 * B * Tq * H * (d // 2) * esz + B * Tq * 8, flops=0.0, units=B * Tq,
+                             unit="query rows")
     if "index_topk" in pipe.names():
         Hi, di, k = cfg["Hi"], cfg["d_idx"], cfg["k"]
         vis = np.array([n_visible(x, W, cfg["m_csa"], Nc) for x in t], dtype=np.float64)
@@ -818,6 +827,9 @@ def main():
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
     ap.add_argument("--q4", action="store_true",
                     help="decode workload: the HCA and CSA caches in 4-bit storage, decoded by the attention")
+    ap.add_argument("--rope", default=None, choices=["fused", "separate"],
+                    help="prefill workloads: RoPE of the query (last d/2 channels), inside the attention's Q load "
+                         "or as a rope_apply launch before it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm (back-to-back) timing and the measured-peak probes")
@@ -880,7 +892,7 @@ def main():
     if not pipeline_workload:
         raise SystemExit(f"unknown workload {args.workload}")
     cfg = inp["cfg"]
-    pipe = make_pipeline(inp, q4=args.q4)
+    pipe = make_pipeline(inp, q4=args.q4, rope=args.rope)
     names = pipe.names()
     log(f"[bench] kernels per step: {names}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -964,7 +976,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
         "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]")
-                   + (" [HCA and CSA caches in 4-bit storage]" if args.q4 else ""),
+                   + (" [HCA and CSA caches in 4-bit storage]" if args.q4 else "")
+                   + (f" [RoPE of q, {args.rope}]" if args.rope else ""),
                    "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],
                    "query_rows": queries, "timing": "each timed step starts from flushed L2 / MALL (cold)",
                    "gpu_ms_per_step_median": round(step_ms[len(step_ms) // 2], 5)},

@@ -228,6 +228,15 @@ typedef struct shattn_fwd_args {
     const float* q4_v_hca; /*   as cache_quant4 writes them (bits of cache_q4 set) */
     const float* q4_k_csa;
     const float* q4_v_csa;
+    int32_t rope_q;      /* 1: rotate the query's channels [rope_off, rope_off +
+                            rope_dim) by RoPE at each query row's position as
+                            the attention loads it: the values rope_apply would
+                            store, so q need not be rotated beforehand.
+                            rope_off and rope_dim even, base finite and > 0. */
+    int32_t rope_off;
+    int32_t rope_dim;
+    int32_t reserved2;   /* must be 0 */
+    double rope_base;
 } shattn_fwd_args;
 
 /* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the
@@ -398,9 +407,11 @@ SHATTN_API int hybrid_cache_append(const shattn_append_args* a, void* stream);
  * nor the base; the reading taken: channels rope_off + 2i and
  * rope_off + 2i + 1 (0 <= i < rope_dim / 2) of each head turn by the angle
  * pos * base^(-2i / rope_dim), (a, b) -> (a cos - b sin, a sin + b cos);
- * the other channels are unchanged.  Arithmetic: the angle is formed and
- * reduced modulo 2 pi in float64, its sine and cosine and the rotation are
- * float32, the result is rounded once to the storage dtype.
+ * the other channels are unchanged.  Arithmetic: the angle is formed in
+ * turns (pos * f_i / 2 pi) in float64 and its whole turns dropped there; the
+ * sine and cosine of the remaining fraction (the hardware's float32 sine and
+ * cosine, which take turns) and the rotation are float32; the result is
+ * rounded once to the storage dtype.
  *
  *   x    : [rows, heads, d]  dtype, DEVICE memory, rotated in place
  *   pos  : [rows] int64, DEVICE memory, 8-byte aligned: the position of each

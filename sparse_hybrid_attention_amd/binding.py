@@ -84,6 +84,9 @@ class FwdArgs(ctypes.Structure):
         ("reserved1", ctypes.c_int32),
         ("q4_k_hca", ctypes.c_void_p), ("q4_v_hca", ctypes.c_void_p),
         ("q4_k_csa", ctypes.c_void_p), ("q4_v_csa", ctypes.c_void_p),
+        ("rope_q", ctypes.c_int32), ("rope_off", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
     ]
 
 
@@ -300,7 +303,7 @@ def csa_index_topk(qI, kI, w, q_pos0, m: int, W: int, k: int, out=None, ws=None)
 
 
 def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
-                  sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False):
+                  sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False, rope_q=None):
     """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
 
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
@@ -312,6 +315,7 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
     with gate_logits, per-token logits the kernel softmaxes over the branches).
     q_pos: device int64 [B] per-sequence positions (needs raw_ring); raw_ring:
     k_raw / v_raw are rings, position t in row t % Tr.
+    rope_q: (rope_off, rope_dim, base) to rotate q by RoPE as it is loaded.
     Returns (FwdArgs, out, keepalive tuple)."""
     _need(q, "q")
     dev = q.device
@@ -381,6 +385,9 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
         keep += [kc, vc, idx]
     a.gates = gates.data_ptr()
     a.raw_ring = 1 if raw_ring else 0
+    if rope_q is not None:
+        a.rope_q = 1
+        a.rope_off, a.rope_dim, a.rope_base = int(rope_q[0]), int(rope_q[1]), float(rope_q[2])
     if q_pos is not None:
         _need(q_pos, "q_pos", torch.int64, dev)
         if tuple(q_pos.shape) != (B,):
@@ -396,12 +403,12 @@ def hybrid_sparse_attn_fwd_workspace_size(args: FwdArgs) -> int:
 
 def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None,
                            csa=None, sm_scale=0.0, out=None, ws=None, gate_logits=False, q_pos=None,
-                           raw_ring=False):
+                           raw_ring=False, rope_q=None):
     """Gated hybrid attention forward; returns out [B, Tq, H, d]."""
     lib = load_library()
     a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
                                   hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits,
-                                  q_pos=q_pos, raw_ring=raw_ring)
+                                  q_pos=q_pos, raw_ring=raw_ring, rope_q=rope_q)
     nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
     if ws is None and nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -411,13 +418,14 @@ def hybrid_sparse_attn_fwd(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, h
 
 
 def hybrid_sparse_attn_fwd_noalloc(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
-                                   sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False):
+                                   sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False,
+                                   rope_q=None):
     """hybrid_sparse_attn_fwd without a caller workspace (the library's own
     per-GPU scratch array); returns out [B, Tq, H, d]."""
     lib = load_library()
     a, out, _keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
                                   hca=hca, csa=csa, sm_scale=sm_scale, out=out, gate_logits=gate_logits,
-                                  q_pos=q_pos, raw_ring=raw_ring)
+                                  q_pos=q_pos, raw_ring=raw_ring, rope_q=rope_q)
     _check(lib.hybrid_sparse_attn_fwd_noalloc(ctypes.byref(a), _stream(q)))
     return out
 
@@ -647,9 +655,13 @@ class HybridPipeline:
     def __init__(self, *, q, gates, W, k_raw, v_raw, q_pos0=0, raw_pos0=0,
                  zk_csa=None, zv_csa=None, m_csa=None, zk_hca=None, zv_hca=None, m_hca=None,
                  qI=None, kI=None, w=None, k=None,
-                 k_csa=None, v_csa=None, k_hca=None, v_hca=None, q4_hca=None, q4_csa=None):
+                 k_csa=None, v_csa=None, k_hca=None, v_hca=None, q4_hca=None, q4_csa=None,
+                 rope_q=None, rope_fused=True):
         """Decode with 4-bit caches: k_hca / v_hca (k_csa / v_csa) are the
-        codes [B, N, Hkv, d/2] and q4_hca (q4_csa) their (params_k, params_v)."""
+        codes [B, N, Hkv, d/2] and q4_hca (q4_csa) their (params_k, params_v).
+        rope_q = (rope_off, rope_dim, base): RoPE of q at each row's position,
+        inside the attention's Q load (rope_fused) or as a rope_apply launch
+        on q before it (which turns q in place at every run)."""
         lib = load_library()
         self.lib = lib
         dev = q.device
@@ -701,8 +713,14 @@ class HybridPipeline:
         hca = None if k_hca is None else (k_hca, v_hca, m_hca) + (() if q4_hca is None else (q4_hca,))
         csa = None if idx is None else (k_csa, v_csa, idx) + (() if q4_csa is None else (q4_csa,))
         self.q4_hca, self.q4_csa = q4_hca is not None, q4_csa is not None
+        if rope_q is not None and not rope_fused:
+            pos = (torch.arange(Tq, dtype=torch.int64, device=dev) + int(q_pos0)).repeat(B)
+            self.keep.append(pos)
+            self.calls.append(("rope_q", lib.rope_apply,
+                               (_ptr(q), _ptr(pos), B * Tq, H, d, int(rope_q[0]), int(rope_q[1]),
+                                float(rope_q[2]), dt, s)))
         a, out, keep = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0,
-                                     hca=hca, csa=csa)
+                                     hca=hca, csa=csa, rope_q=rope_q if rope_fused else None)
         self.args = a
         self.out = out
         self.keep += list(keep)

@@ -108,6 +108,9 @@ struct AttnParams {
     int q4;
     const float* q4p[4];   // (min, step) of the k_hca, v_hca, k_csa, v_csa codes
     int lds_lut;           // byte offset of the four 256-entry decode tables
+    // RoPE of the query at load (rope_q): channels [rope_off, rope_off + rope_dim)
+    int rope_q, rope_off, rope_dim;
+    double rope_step;      // 2 log2(base) / rope_dim
 };
 
 // ---------------------------------------------------------------- per-dtype MFMA
@@ -132,6 +135,22 @@ template <int D> struct Tr<bf16_t, D> {
                 for (int j = 0; j < 8; ++j) qf[ks][j] = (__bf16)0.0f;
             }
         }
+    }
+    // RoPE of the loaded query (position pos): the lane holds dims 32 ks + 8 q4
+    // .. +7 of the row, whole channel pairs when rope_off is even
+    __device__ static void rope_q(const AttnParams& p, const bf16_t*, long long pos, int q4, QF* qf) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int ch = 32 * ks + 8 * q4 + 2 * jj;
+                if (ch < p.rope_off || ch >= p.rope_off + p.rope_dim) continue;
+                float s, c, r0, r1;
+                rope_sincos(pos, (ch - p.rope_off) >> 1, p.rope_step, &s, &c);
+                rope_turn((float)qf[ks][2 * jj], (float)qf[ks][2 * jj + 1], s, c, &r0, &r1);
+                qf[ks][2 * jj] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_rne(r0));
+                qf[ks][2 * jj + 1] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_rne(r1));
+            }
     }
     // key offset (within the 32-key chunk) of this lane's score j
     __device__ static int key_of(int q4, int j) { return 8 * q4 + j; }
@@ -230,6 +249,19 @@ template <int D> struct Tr<float, D> {
     __device__ static void load_q(const float* qrow, int q4, bool ok, QF* qf) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = ok ? qrow[4 * ks + q4] : 0.f;
+    }
+    // RoPE of the loaded query (position pos): the lane holds dim 4 ks + q4;
+    // its pair partner is read from the row
+    __device__ static void rope_q(const AttnParams& p, const float* qrow, long long pos, int q4, QF* qf) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ch = 4 * ks + q4;
+            if (ch < p.rope_off || ch >= p.rope_off + p.rope_dim) continue;
+            float s, c, r0, r1;
+            rope_sincos(pos, (ch - p.rope_off) >> 1, p.rope_step, &s, &c);
+            rope_turn(qrow[ch & ~1], qrow[ch | 1], s, c, &r0, &r1);
+            qf[ks] = (ch & 1) ? r1 : r0;
+        }
     }
     __device__ static int key_of(int q4, int j) { return 16 * (j >> 2) + 4 * (j & 3) + q4; }
     __device__ static uint32_t lane_bits(uint32_t m, int q4) {
@@ -757,6 +789,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     const T* qrow = reinterpret_cast<const T*>(p.q) + (((long long)b * p.Tq + qi) * p.H + (valid ? h : 0)) * D;
     typename TR::QF qf[TR::KS];
     TR::load_q(qrow, q4, valid, qf);
+    if (p.rope_q && valid) TR::rope_q(p, qrow, t, q4, qf);
 
     float gate[3] = {0.f, 0.f, 0.f};
     if (valid) load_gates(p, b, qi, h, gate);
@@ -1539,6 +1572,14 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
             if (reinterpret_cast<uintptr_t>(q4p[i]) & 3)
                 return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: (min, step) must be 4-byte aligned");
         }
+    if (a->reserved2 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved2 must be 0");
+    if (a->rope_q != 0 && a->rope_q != 1)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: rope_q = %d (0 or 1)", a->rope_q);
+    if (a->rope_q &&
+        (a->rope_dim < 2 || a->rope_dim % 2 || a->rope_off < 0 || a->rope_off % 2 ||
+         (long long)a->rope_off + a->rope_dim > a->d || !(a->rope_base > 0.0) || !std::isfinite(a->rope_base)))
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: RoPE of q needs even rope_off / rope_dim inside d and a "
+                    "finite base > 0 (got off %d, dim %d, base %g)", a->rope_off, a->rope_dim, a->rope_base);
     AttnParams& p = pl.p;
     p = AttnParams{};
     p.B = a->B;
@@ -1594,6 +1635,10 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     p.N_csa = has_csa ? a->N_csa : 0;
     p.k = has_csa ? a->k : 0;
     p.q4 = q4;
+    p.rope_q = a->rope_q;
+    p.rope_off = a->rope_q ? a->rope_off : 0;
+    p.rope_dim = a->rope_q ? a->rope_dim : 0;
+    p.rope_step = a->rope_q ? 2.0 * std::log2(a->rope_base) / a->rope_dim : 0.0;
     for (int i = 0; i < 4; ++i) p.q4p[i] = ((q4 >> (i >> 1)) & 1) ? q4p[i] : nullptr;
     const float scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)a->d);
     p.scale_log2 = scale * 1.4426950408889634f;

@@ -87,6 +87,26 @@ template <> struct Elem<float> {
     __device__ static __forceinline__ void store1(float* p, float f) { *p = f; }
 };
 
+// RoPE of one channel pair (the reading stated with rope_apply): pair i at
+// position p turns by p * f_i, f_i = 2^(-i * step), step = 2 log2(base) / R.
+// The angle is formed in turns (p * f_i / 2 pi) in double precision and its
+// whole turns dropped there (exact), then the hardware sine and cosine of the
+// remaining fraction of a turn (v_sin_f32 / v_cos_f32 take turns) turn
+// (a, b) -> (a c - b s, a s + b c) in explicit fused multiply-adds, so that
+// every kernel rotating a pair gets the same bits.
+__device__ __forceinline__ void rope_sincos(long long p, int i, double step, float* s, float* c) {
+    constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+    double r = (double)p * (exp2(-(double)i * step) * kInvTwoPi);
+    r -= rint(r);
+    const float rf = (float)r;
+    *s = __builtin_amdgcn_sinf(rf);
+    *c = __builtin_amdgcn_cosf(rf);
+}
+__device__ __forceinline__ void rope_turn(float a, float b, float s, float c, float* ra, float* rb) {
+    *ra = fmaf(a, c, -(b * s));
+    *rb = fmaf(a, s, b * c);
+}
+
 // Wave-level (64 lanes) LDS ordering: makes this lane's earlier LDS writes
 // visible to the other lanes of the wave before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {

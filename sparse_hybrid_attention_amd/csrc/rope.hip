@@ -29,8 +29,6 @@ namespace shattn {
 namespace {
 
 constexpr int kRopeThreads = 256;
-constexpr double kTwoPi = 6.283185307179586476925286766559;
-
 constexpr int kRopeHeadsInFlight = 8;
 
 template <typename T>
@@ -44,10 +42,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(T* __restrict__ x, c
         const long long p = pos[row];
         if (p < 0) continue;                      // inactive row: unchanged
         // f_i = base^(-2i/R) = 2^(-i * step), step = 2 log2(base) / R
-        double a = (double)p * exp2(-(double)i * step);
-        a -= kTwoPi * rint(a / kTwoPi);
         float s, c;
-        sincosf((float)a, &s, &c);
+        rope_sincos(p, i, step, &s, &c);
         T* e0 = x + row * heads * (long long)d + off + 2 * i;
         for (int h0 = 0; h0 < heads; h0 += kRopeHeadsInFlight) {
             float x0[kRopeHeadsInFlight], x1[kRopeHeadsInFlight];
@@ -63,8 +59,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(T* __restrict__ x, c
             for (int j = 0; j < kRopeHeadsInFlight; ++j) {
                 if (h0 + j < heads) {
                     T* e = e0 + (long long)(h0 + j) * d;
-                    Elem<T>::store1(e, x0[j] * c - x1[j] * s);
-                    Elem<T>::store1(e + 1, x0[j] * s + x1[j] * c);
+                    float r0, r1;
+                    rope_turn(x0[j], x1[j], s, c, &r0, &r1);
+                    Elem<T>::store1(e, r0);
+                    Elem<T>::store1(e + 1, r1);
                 }
             }
         }

@@ -213,6 +213,14 @@ def test_attention_errors(lib):
     assert "(min, step)" in err(lib)
     assert call(cache_q4=1, q4_k_hca=P.value, q4_v_hca=0x7F0000000002, **hq) == binding.SHATTN_EINVAL
     assert call(dtype=1, cache_q4=1, q4_k_hca=P.value, q4_v_hca=P.value, **hq) == binding.SHATTN_EUNSUPPORTED
+    # RoPE of q at load: even channel range inside d, finite base > 0
+    rq = dict(rope_q=1, rope_off=64, rope_dim=64, rope_base=10000.0)
+    assert call(**dict(rq, rope_q=2)) == binding.SHATTN_EINVAL
+    assert call(**dict(rq, rope_off=63)) == binding.SHATTN_EINVAL
+    assert call(**dict(rq, rope_dim=66)) == binding.SHATTN_EINVAL
+    assert call(**dict(rq, rope_base=0.0)) == binding.SHATTN_EINVAL
+    assert call(**dict(rq, rope_base=float("inf"))) == binding.SHATTN_EINVAL
+    assert call(reserved2=1) == binding.SHATTN_EINVAL
     # empty problem is a no-op
     assert call(B=0) == binding.SHATTN_OK
 
