@@ -40,6 +40,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/hybrid_attn.h"
 #include "common.h"
@@ -91,6 +92,17 @@ struct BwdParams {
     int has_hca, has_csa;
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
+    // coefficient form (bf16, small N_csa): the query side writes, per
+    // (row, head, key of its sets), (dS, sum_b w_b P_b) and the key sides
+    // read them instead of recomputing scores
+    float2* coef_w;    // [B, H, T, W]: window key at slot pos - (t - W + 1)
+    float2* coef_h;    // [B, H, T, N_hca]
+    float2* coef_c;    // [B, H, T, k]: the r-th visible selected entry of row t (ascending)
+    uint32_t* bm;      // [B, T, bmw] selection bitmap of each row (visible entries only)
+    int32_t* bmpre;    // [B, T, bmw] selected entries of the row in the words before
+    int bmw;
+    float* hpart;      // [B, Hkv, nrange, N_hca, 2, d] HCA cache-gradient partial sums per row range
+    int nrange;        // row ranges of kKeyRange rows (HCA key side)
 };
 
 // this lane's quarter of a row (D / 4 elements, from element part * D / 4)
@@ -264,6 +276,300 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdParams p) {
             make_float4(p.scale * dqv[e], p.scale * dqv[e + 1], p.scale * dqv[e + 2], p.scale * dqv[e + 3]);
 }
 
+
+// ------------------------------------------------------------ 1'. query side on MFMA
+// (bf16, N_csa small enough for a per-row selection bitmap)
+// Selection bitmap of every row (visible entries only) and, per word, the
+// number of selected entries in the words before it: the rank of an entry in
+// its row's ascending selection is pre[w] + popcount(word & bits below).
+__global__ __launch_bounds__(kThreads) void bwd_bitmap_kernel(BwdParams p) {
+    const long long row = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (row >= (long long)p.B * p.T) return;
+    const int t = (int)(row % p.T);
+    uint32_t* bm = p.bm + row * p.bmw;
+    for (int w = 0; w < p.bmw; ++w) bm[w] = 0u;
+    const int nc = n_visible(t, p.W, p.m_csa, p.N_csa);
+    const int32_t* sel = p.idx + row * p.ksel;
+    for (int j = 0; j < p.ksel; ++j) {
+        const int e = sel[j];
+        if (e >= 0 && e < nc) bm[e >> 5] |= 1u << (e & 31);
+    }
+    int run = 0;
+    for (int w = 0; w < p.bmw; ++w) {
+        p.bmpre[row * p.bmw + w] = run;
+        run += __popc(bm[w]);
+    }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kKC = 32;   // keys per MFMA chunk
+
+// Workgroup: 64 query rows of one (sequence, head), 16 per wave as the
+// columns of the transposed products S^T = K Q^T and dP^T = V dO^T (32 keys
+// x 16 columns per chunk, v_mfma_f32_16x16x32_bf16) and dQ^T += K^T dS^T.
+// K and V chunks of every key source (the union of the tile's windows, the
+// HCA entries its last row sees, every CSA entry it could select, masked per
+// row through the bitmap) are staged once per workgroup in LDS by direct
+// global->LDS loads, row-major with 16-byte pieces XOR-swizzled per row,
+// double-buffered.  Pass 1: per column and branch an online log-sum-exp and
+// D_b = sum_j P_bj dpo_j (per-lane partial states merged across the column's
+// four lanes at the end).  Pass 2: P, dS and sum_b w_b P_b per (row, key)
+// are written as coefficients for the key sides; dQ accumulates K^T dS^T on
+// MFMA with dS split into two bf16 parts (hi + lo, about 16 significant
+// bits) so that the float32 gradient keeps its precision.
+template <int D>
+__global__ __launch_bounds__(kThreads, 3) void bwd_query_mfma_kernel(BwdParams p) {
+    constexpr int PIECES = D / 8, ROWB = D * 2, RPI = 1024 / ROWB, KS = D / 32, DT = D / 16;
+    constexpr int MAT = kKC * ROWB, NL = kKC / RPI;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    auto swz = [](int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); };
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, q4 = lane >> 4;
+    const int ntile = (p.T + 63) / 64;
+    const int work = (int)xcd_work_id(blockIdx.x, gridDim.x);
+    const int tile = work % ntile;
+    const int h = (work / ntile) % p.H;
+    const int b = work / (ntile * p.H);
+    const int g = h / p.G;
+    const int t0 = tile * 64;
+    const int t_last = min(t0 + 63, p.T - 1);
+    const int t = t0 + wave * 16 + n;
+    const bool valid = t < p.T;
+    const int rs = p.Hkv * D;
+    // B operands: this column's query and incoming gradient, dims 32 ks + 8 q4 .. +7
+    bf16x8_t qf[KS], of[KS];
+    {
+        const long long off = (((long long)b * p.T + (valid ? t : t_last)) * p.H + h) * D;
+        const bf16_t* qr = reinterpret_cast<const bf16_t*>(p.q) + off;
+        const bf16_t* orw = reinterpret_cast<const bf16_t*>(p.dout) + off;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * ks + 8 * q4);
+            of[ks] = *reinterpret_cast<const bf16x8_t*>(orw + 32 * ks + 8 * q4);
+        }
+    }
+    float gw[3];
+    gate_w(p, b, valid ? t : t_last, h, gw);
+    // A-operand reads of a 32-row matrix: S^T rows (keys 8 (r >> 2) + (r & 3)
+    // and +4) and the transposing reads of K^T (rows 8 (lane >> 4) + (sl >> 2)
+    // and +4, dims 16 dt + 4 (sl & 3) .. +3)
+    int kro[KS], tro[DT];
+    {
+        const int key0 = 8 * (n >> 2) + (n & 3);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kro[ks] = key0 * ROWB + (((4 * ks + q4) ^ swz(key0)) * 16);
+        const int sl = n, trow = 8 * q4 + (sl >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            tro[dt] = trow * ROWB + (((2 * dt + ((sl & 3) >> 1)) ^ swz(trow)) * 16) + 8 * (sl & 1);
+    }
+    // key sources of the workgroup: window rows [w_lo, t_last], HCA entries
+    // [0, nh_max), CSA entries [0, nc_max)
+    const int w_lo = max(0, t0 - p.W + 1);
+    const int wn = t_last - w_lo + 1;
+    const int nh_max = p.has_hca ? n_visible(t_last, p.W, p.m_hca, p.N_hca) : 0;
+    const int nc_max = p.has_csa ? n_visible(t_last, p.W, p.m_csa, p.N_csa) : 0;
+    const int cw = (wn + kKC - 1) / kKC, ch = (nh_max + kKC - 1) / kKC, cc = (nc_max + kKC - 1) / kKC;
+    const int nchunks = cw + ch + cc;
+    const bf16_t* kraw = reinterpret_cast<const bf16_t*>(p.k) + (long long)b * p.T * rs + g * D;
+    const bf16_t* vraw = reinterpret_cast<const bf16_t*>(p.v) + (long long)b * p.T * rs + g * D;
+    const bf16_t* khca = reinterpret_cast<const bf16_t*>(p.k_hca) + (long long)b * p.N_hca * rs + g * D;
+    const bf16_t* vhca = reinterpret_cast<const bf16_t*>(p.v_hca) + (long long)b * p.N_hca * rs + g * D;
+    const bf16_t* kcsa = reinterpret_cast<const bf16_t*>(p.k_csa) + (long long)b * p.N_csa * rs + g * D;
+    const bf16_t* vcsa = reinterpret_cast<const bf16_t*>(p.v_csa) + (long long)b * p.N_csa * rs + g * D;
+    // chunk ci: its type (0 window, 1 HCA, 2 CSA), first key (position or entry), valid rows
+    auto chunk = [&](int ci, int& type, int& base, int& nv) {
+        if (ci < cw) {
+            type = 0;
+            base = w_lo + ci * kKC;
+            nv = min(kKC, wn - ci * kKC);
+        } else if (ci < cw + ch) {
+            type = 1;
+            base = (ci - cw) * kKC;
+            nv = min(kKC, nh_max - base);
+        } else {
+            type = 2;
+            base = (ci - cw - ch) * kKC;
+            nv = min(kKC, nc_max - base);
+        }
+    };
+    auto tbuf = [&](int par) { return smem + par * 2 * MAT; };
+    auto stage = [&](int ci, char* buf) {
+        int type, base, nv;
+        chunk(ci, type, base, nv);
+        const bf16_t* kb = type == 0 ? kraw : (type == 1 ? khca : kcsa);
+        const bf16_t* vb = type == 0 ? vraw : (type == 1 ? vhca : vcsa);
+        kb += (long long)base * rs;
+        vb += (long long)base * rs;
+#pragma unroll
+        for (int L = wave; L < 2 * NL; L += 4) {
+            const int mat = L / NL, li = L - mat * NL;
+            const int row = li * RPI + lane / PIECES, slot = lane % PIECES;
+            const bf16_t* src = (mat ? vb : kb) + (long long)(row < nv ? row : 0) * rs + ((slot ^ swz(row)) * 8);
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + mat * MAT + li * 1024), 16, 0, 0);
+        }
+    };
+    auto mfma_scores = [&](const char* mb, const bf16x8_t* bop, float* s) {
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(mb + kro[ks]);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(mb + kro[ks] + 4 * ROWB);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bop[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bop[ks], s1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = s0[r];
+            s[4 + r] = s1[r];
+        }
+    };
+    // membership of this column's keys 8 q4 + j of chunk (type, base): branch
+    // bits, and for CSA entries the word of the row's bitmap
+    const uint32_t win_mask = branch_mask_window(p);
+    const int nh_t = p.has_hca && valid ? n_visible(t, p.W, p.m_hca, p.N_hca) : 0;
+    const uint32_t* bmrow = p.bm + ((long long)b * p.T + (valid ? t : 0)) * p.bmw;
+    const int32_t* prerow = p.bmpre + ((long long)b * p.T + (valid ? t : 0)) * p.bmw;
+    auto members = [&](int type, int base, int nv, uint32_t* mbits, uint32_t& word) {
+        word = 0u;
+        if (type == 2 && valid) word = bmrow[base >> 5];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int kk = 8 * q4 + j;
+            uint32_t m = 0u;
+            if (valid && kk < nv) {
+                const int key = base + kk;
+                if (type == 0) m = (key >= t - p.W + 1 && key <= t) ? win_mask : 0u;
+                else if (type == 1) m = key < nh_t ? 1u : 0u;
+                else m = ((word >> (kk & 31)) & 1u) ? 2u : 0u;
+            }
+            mbits[j] = m;
+        }
+    };
+
+    // ---- pass 1: per-lane partial (max, sum, sum P dpo) per branch
+    float mx[3] = {-INFINITY, -INFINITY, -INFINITY}, sm[3] = {0.f, 0.f, 0.f}, ac[3] = {0.f, 0.f, 0.f};
+    float lse[3], Db[3];
+    f32x4_t acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the two passes as one loop body compiled twice (pass a constant in each)
+    auto run_pass = [&](auto pass_c) {
+        constexpr int pass = decltype(pass_c)::value;
+        if (nchunks > 0) stage(0, tbuf(0));
+        for (int ci = 0; ci < nchunks; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();                       // chunk ci in tbuf(ci & 1); tbuf(ci + 1 & 1) free
+            if (ci + 1 < nchunks) stage(ci + 1, tbuf((ci + 1) & 1));
+            const char* kb = tbuf(ci & 1);
+            const char* vb = kb + MAT;
+            int type, base, nv;
+            chunk(ci, type, base, nv);
+            float s[8], dpo[8];
+            mfma_scores(kb, qf, s);
+            mfma_scores(vb, of, dpo);
+            uint32_t mbits[8], word;
+            members(type, base, nv, mbits, word);
+            if constexpr (pass == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float s2 = s[j] * p.scale_log2;
+#pragma unroll
+                    for (int br = 0; br < 3; ++br) {
+                        if (!(mbits[j] & (1u << br))) continue;
+                        const float mn = fmaxf(mx[br], s2);
+                        const float a = exp2f(mx[br] - mn), e = exp2f(s2 - mn);
+                        sm[br] = fmaf(sm[br], a, e);
+                        ac[br] = fmaf(ac[br], a, e * dpo[j]);
+                        mx[br] = mn;
+                    }
+                }
+            } else {
+                float ds[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float s2 = s[j] * p.scale_log2;
+                    float d_ = 0.f, wp = 0.f;
+#pragma unroll
+                    for (int br = 0; br < 3; ++br) {
+                        if (!(mbits[j] & (1u << br))) continue;
+                        const float pw = gw[br] * exp2f(s2 - lse[br]);
+                        wp += pw;
+                        d_ = fmaf(pw, dpo[j] - Db[br], d_);
+                    }
+                    ds[j] = d_;
+                    if (mbits[j]) {
+                        const int key = base + 8 * q4 + j;
+                        const long long rowc = ((long long)b * p.H + h) * p.T + t;
+                        const float2 c2 = make_float2(d_, wp);
+                        if (type == 0) p.coef_w[rowc * p.W + (key - (t - p.W + 1))] = c2;
+                        else if (type == 1) p.coef_h[rowc * p.N_hca + key] = c2;
+                        else {
+                            const int bit = (8 * q4 + j) & 31;
+                            const int r = prerow[base >> 5] + __popc(word & ((1u << bit) - 1u));
+                            p.coef_c[rowc * p.ksel + r] = c2;
+                        }
+                    }
+                }
+                // dQ^T += K^T dS^T, dS = hi + lo in bf16
+                bf16x8_t bhi, blo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const __bf16 hi = (__bf16)ds[j];
+                    bhi[j] = hi;
+                    blo[j] = (__bf16)(ds[j] - (float)hi);
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const char* a = kb + tro[dt];
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
+                    const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
+                    const i16x4_t lohi[2] = {lo, hi4};
+                    bf16x8_t aop;
+                    __builtin_memcpy(&aop, lohi, 16);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bhi, acc[dt], 0, 0, 0);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, blo, acc[dt], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();   // every wave is done with both tiles before they are restaged
+        if constexpr (pass == 0) {
+            // merge the column's four lanes (n, n + 16, n + 32, n + 48) in a fixed order
+#pragma unroll
+            for (int br = 0; br < 3; ++br) {
+                uint32_t lo, hi;
+                xor16_pair(__float_as_uint(mx[br]), lo, hi);
+                float M = fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+                xor32_pair(__float_as_uint(M), lo, hi);
+                M = fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+                const float f = M == -INFINITY ? 0.f : exp2f(mx[br] - M);
+                const float l = sum_xrows(sm[br] * f), a = sum_xrows(ac[br] * f);
+                lse[br] = l > 0.f ? M + log2f(l) : 0.f;
+                Db[br] = l > 0.f ? a / l : 0.f;
+            }
+            if (valid && q4 == 0) {
+                float* st = p.stats + (((long long)b * p.T + t) * p.H + h) * 6;
+#pragma unroll
+                for (int br = 0; br < 3; ++br) {
+                    st[br] = lse[br];
+                    st[3 + br] = Db[br];
+                }
+            }
+        }
+    };
+    run_pass(std::integral_constant<int, 0>());
+    run_pass(std::integral_constant<int, 1>());
+    if (!valid) return;
+    float* dst = p.dq + (((long long)b * p.T + t) * p.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * q4) =
+            make_float4(p.scale * acc[dt][0], p.scale * acc[dt][1], p.scale * acc[dt][2], p.scale * acc[dt][3]);
+}
+
 // ------------------------------------------------------------ 2. block weights
 // pz[i, ch] = softmax over i < m of z[i, ch] (one thread per channel; blockIdx.y = job)
 __global__ __launch_bounds__(kThreads) void bwd_weights_kernel(BwdParams p, int nch) {
@@ -271,10 +577,13 @@ __global__ __launch_bounds__(kThreads) void bwd_weights_kernel(BwdParams p, int 
     const int c = blockIdx.x * kThreads + threadIdx.x;
     if (c >= nch) return;
     float mx = -INFINITY;
+#pragma unroll 16
     for (int i = 0; i < J.m; ++i) mx = fmaxf(mx, J.z[(long long)i * nch + c]);
     float s = 0.f;
+#pragma unroll 16
     for (int i = 0; i < J.m; ++i) s += expf(J.z[(long long)i * nch + c] - mx);
     const float inv = 1.0f / s;
+#pragma unroll 16
     for (int i = 0; i < J.m; ++i) J.pz[(long long)i * nch + c] = expf(J.z[(long long)i * nch + c] - mx) * inv;
 }
 
@@ -285,7 +594,10 @@ __global__ __launch_bounds__(kThreads) void bwd_weights_kernel(BwdParams p, int 
 // 2: CSA entries (CSA branch; the visible queries whose selection holds c).
 // Workgroup: 64 consecutive keys of one (sequence, KV head); a wave takes 16,
 // walking the union of their query ranges in lockstep, G heads per row.
-template <typename T, int D, int KIND>
+// COEF: (dS, sum_b w_b P_b) of each (row, head, key) come from the query
+// side's coefficients (and CSA membership from the row bitmaps) instead of
+// being recomputed from the scores.
+template <typename T, int D, int KIND, bool COEF>
 __global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdParams p) {
     constexpr int NP = D / 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -323,7 +635,11 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdParams p) {
     }
     for (int t = t_lo; t <= t_hi; ++t) {
         bool in = valid && t >= my_first && t <= my_last;
-        if (KIND == 2) {
+        uint32_t word = 0u;
+        if (KIND == 2 && COEF) {
+            word = p.bm[((long long)b * p.T + t) * p.bmw + (j >> 5)];
+            in = in && ((word >> (j & 31)) & 1u);
+        } else if (KIND == 2) {
             // which of the wave's 16 entries row t selects: one selection
             // element per lane, OR over the wave
             const int32_t* sel = p.idx + ((long long)b * p.T + t) * p.ksel;
@@ -342,22 +658,35 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdParams p) {
             float qv[NP], ov[NP];
             load_part<T, D>(reinterpret_cast<const T*>(p.q) + qoff, part, qv);
             load_part<T, D>(reinterpret_cast<const T*>(p.dout) + qoff, part, ov);
-            const float* st = p.stats + (((long long)b * p.T + t) * p.H + h) * 6;
-            float gw[3];
-            gate_w(p, b, t, h, gw);
-            const float s2 = quad_sum(dot_part<NP>(qv, kv)) * p.scale_log2;
-            const float dpo = quad_sum(dot_part<NP>(ov, vv));
             float wsum = 0.f, ds = 0.f;
+            if constexpr (COEF) {
+                if (in) {
+                    const long long rowc = ((long long)b * p.H + h) * p.T + t;
+                    float2 c2;
+                    if (KIND == 0) c2 = p.coef_w[rowc * p.W + (j - t + p.W - 1)];
+                    else if (KIND == 1) c2 = p.coef_h[rowc * p.N_hca + j];
+                    else c2 = p.coef_c[rowc * p.ksel + p.bmpre[((long long)b * p.T + t) * p.bmw + (j >> 5)] +
+                                       __popc(word & ((1u << (j & 31)) - 1u))];
+                    ds = c2.x;
+                    wsum = c2.y;
+                }
+            } else {
+                const float* st = p.stats + (((long long)b * p.T + t) * p.H + h) * 6;
+                float gw[3];
+                gate_w(p, b, t, h, gw);
+                const float s2 = quad_sum(dot_part<NP>(qv, kv)) * p.scale_log2;
+                const float dpo = quad_sum(dot_part<NP>(ov, vv));
 #pragma unroll
-            for (int br = 0; br < 3; ++br) {
-                if (!(bmask & (1u << br))) continue;
-                const float pw = gw[br] * exp2f(s2 - st[br]);
-                wsum += pw;
-                ds = fmaf(pw, dpo - st[3 + br], ds);
-            }
-            if (!in) {
-                wsum = 0.f;
-                ds = 0.f;
+                for (int br = 0; br < 3; ++br) {
+                    if (!(bmask & (1u << br))) continue;
+                    const float pw = gw[br] * exp2f(s2 - st[br]);
+                    wsum += pw;
+                    ds = fmaf(pw, dpo - st[3 + br], ds);
+                }
+                if (!in) {
+                    wsum = 0.f;
+                    ds = 0.f;
+                }
             }
 #pragma unroll
             for (int e = 0; e < NP; ++e) {
@@ -405,6 +734,257 @@ __global__ __launch_bounds__(kThreads) void bwd_key_kernel(BwdParams p) {
     }
 }
 
+
+// ------------------------------------------------------------ 3'./4'. key sides on MFMA
+// dK^T (d x keys) = Q^T (d x rows) dS (rows x keys) and dV^T = dO^T (w P),
+// 32 rows per chunk (v_mfma_f32_16x16x32_bf16; the coefficient operand split
+// into two bf16 parts, hi + lo).  Q and dO rows of the chunk are staged in
+// LDS (row-major, swizzled, direct global->LDS loads, double-buffered) and
+// read transposed; the coefficient operand of a lane is its key's
+// coefficients at the chunk's rows 8 (lane >> 4) .. +7 (zero outside the
+// key's row set).
+//   KIND 0: raw rows; workgroup = 64 consecutive keys (16 per wave), rows
+//           [j0, j0 + 63 + W - 1]; epilogue: the cache gradients routed
+//           through the block merge.
+//   KIND 1: HCA entries; workgroup = a range of kKeyRange rows, its four
+//           waves one 32-row chunk each, every entry tile of 16; partial sums
+//           per range (combined in a fixed order by bwd_hca_reduce_kernel).
+//   KIND 2: CSA entries; workgroup = 64 consecutive entries, rows from the
+//           first one that sees its first entry.
+constexpr int kKeyRange = 128;
+
+template <int D> struct QTile {
+    static constexpr int PIECES = D / 8, ROWB = D * 2, RPI = 1024 / ROWB, DT = D / 16;
+    static constexpr int MAT = 32 * ROWB, NL = 32 / RPI;
+    __device__ static int swz(int row) { return ((row & 3) | (((row >> 3) & 3) << 2)) & (PIECES - 1); }
+};
+
+template <int D, int KIND>
+__global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) {
+    typedef QTile<D> QT;
+    constexpr int ROWB = QT::ROWB, DT = QT::DT, MAT = QT::MAT, NL = QT::NL, RPI = QT::RPI, PIECES = QT::PIECES;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, q4 = lane >> 4;
+    const int rs = p.Hkv * D;            // K/V row stride
+    const int qs = p.H * D;              // Q / dO row stride
+    const int work = (int)xcd_work_id(blockIdx.x, gridDim.x);
+    int b, g, j0 = 0, r_lo, r_hi;       // rows [r_lo, r_hi] of the workgroup
+    if (KIND == 1) {
+        const int rg = work % p.nrange;
+        g = (work / p.nrange) % p.Hkv;
+        b = work / (p.nrange * p.Hkv);
+        r_lo = rg * kKeyRange + wave * 32;            // this wave's chunk
+        r_hi = min(r_lo + 31, p.T - 1);
+    } else {
+        const int nkeys = KIND == 0 ? p.T : p.N_csa;
+        const int ntile = (nkeys + 63) / 64;
+        const int tile = work % ntile;
+        g = (work / ntile) % p.Hkv;
+        b = work / (ntile * p.Hkv);
+        j0 = tile * 64;
+        r_lo = KIND == 0 ? j0 : (j0 + 1) * p.m_csa + p.W - 1;
+        r_hi = KIND == 0 ? min(j0 + 63 + p.W - 1, p.T - 1) : p.T - 1;
+    }
+    const int j = j0 + wave * 16 + n;    // this lane's key (KIND 0, 2)
+    const int nkeys = KIND == 0 ? p.T : (KIND == 1 ? p.N_hca : p.N_csa);
+    // transposing-read offsets of a 32-row matrix (rows 8 q4 + (n >> 2) and +4)
+    int tro[DT];
+    {
+        const int trow = 8 * q4 + (n >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            tro[dt] = trow * ROWB + (((2 * dt + ((n & 3) >> 1)) ^ QT::swz(trow)) * 16) + 8 * (n & 1);
+    }
+    // KIND 1: one buffer per wave; else two shared by the workgroup
+    auto tbuf = [&](int par) { return smem + (KIND == 1 ? wave * 2 * MAT : par * 2 * MAT); };
+    // stage rows [r0, r0 + 32) of head h's Q and dO (rows past r_hi repeat r0)
+    auto stage = [&](int h, int r0, char* buf, int nw, int w0) {
+        const bf16_t* qb = reinterpret_cast<const bf16_t*>(p.q) + ((long long)b * p.T * p.H + h) * D;
+        const bf16_t* ob = reinterpret_cast<const bf16_t*>(p.dout) + ((long long)b * p.T * p.H + h) * D;
+#pragma unroll
+        for (int L = w0; L < 2 * NL; L += nw) {
+            const int mat = L / NL, li = L - mat * NL;
+            const int row = li * RPI + lane / PIECES, slot = lane % PIECES;
+            const int t = r0 + row <= r_hi ? r0 + row : r0;
+            const bf16_t* src = (mat ? ob : qb) + (long long)t * qs + ((slot ^ QT::swz(row)) * 8);
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + mat * MAT + li * 1024), 16, 0, 0);
+        }
+    };
+    auto aop_at = [&](const char* mb, int dt) {
+        const char* a = mb + tro[dt];
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a + 4 * ROWB));
+        const i16x4_t lohi[2] = {lo, hi};
+        bf16x8_t aop;
+        __builtin_memcpy(&aop, lohi, 16);
+        return aop;
+    };
+    // coefficient of key `key` (or entry) at row t of head h: (dS, w P), zero outside its row set
+    auto coef = [&](int h, int t, int key) -> float2 {
+        if (t > r_hi || key >= nkeys) return make_float2(0.f, 0.f);
+        const long long rowc = ((long long)b * p.H + h) * p.T + t;
+        if (KIND == 0) {
+            if (t < key || t > key + p.W - 1) return make_float2(0.f, 0.f);
+            return p.coef_w[rowc * p.W + (key - t + p.W - 1)];
+        } else if (KIND == 1) {
+            if (key >= n_visible(t, p.W, p.m_hca, p.N_hca)) return make_float2(0.f, 0.f);
+            return p.coef_h[rowc * p.N_hca + key];
+        } else {
+            const long long bw = ((long long)b * p.T + t) * p.bmw + (key >> 5);
+            const uint32_t word = p.bm[bw];
+            if (!((word >> (key & 31)) & 1u)) return make_float2(0.f, 0.f);
+            return p.coef_c[rowc * p.ksel + p.bmpre[bw] + __popc(word & ((1u << (key & 31)) - 1u))];
+        }
+    };
+    auto split = [](const float* v, bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const __bf16 h_ = (__bf16)v[i];
+            hi[i] = h_;
+            lo[i] = (__bf16)(v[i] - (float)h_);
+        }
+    };
+    // accumulate one staged chunk (rows r0 ..) for keys key0 + n into ak / av
+    auto chunk = [&](const char* buf, int h, int r0, int key, f32x4_t* ak, f32x4_t* av) {
+        float ds[8], wp[8];
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float2 c2 = coef(h, r0 + 8 * q4 + i, key);
+            ds[i] = c2.x;
+            wp[i] = c2.y;
+            any |= c2.x != 0.f || c2.y != 0.f;
+        }
+        if (!__any(any)) return;
+        bf16x8_t dh, dl, wh, wl;
+        split(ds, dh, dl);
+        split(wp, wh, wl);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8_t aq = aop_at(buf, dt), ao = aop_at(buf + MAT, dt);
+            ak[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, dh, ak[dt], 0, 0, 0);
+            ak[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, dl, ak[dt], 0, 0, 0);
+            av[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wh, av[dt], 0, 0, 0);
+            av[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wl, av[dt], 0, 0, 0);
+        }
+    };
+    const int ch0 = g * D + 4 * q4;   // channel of acc[dt][0] within a K/V row: + 16 dt
+    if (KIND == 1) {
+        // this wave: one chunk of 32 rows, every entry tile of 16 (a chunk
+        // past the end still writes its zero partials)
+        const bool active = r_lo < p.T;
+        char* buf = tbuf(0);
+        const int rg = work % p.nrange;
+        for (int ct = 0; ct * 16 < p.N_hca; ++ct) {
+            f32x4_t ak[DT], av[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) ak[dt] = av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int hh = 0; hh < p.G && active; ++hh) {
+                const int h = g * p.G + hh;
+                stage(h, r_lo, buf, 1, 0);
+                __builtin_amdgcn_s_waitcnt(0);
+                wave_lds_sync();
+                chunk(buf, h, r_lo, ct * 16 + n, ak, av);
+                wave_lds_sync();
+            }
+            // partial of this wave's chunk; the four waves' partials of a range
+            // are added in wave order by the reduce kernel
+            const int c = ct * 16 + n;
+            if (c < p.N_hca) {
+                float* dst = p.hpart + ((((long long)b * p.Hkv + g) * p.nrange + rg) * 4 + wave) * (long long)p.N_hca * 2 * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    *reinterpret_cast<float4*>(dst + ((long long)c * 2) * D + 16 * dt + 4 * q4) =
+                        make_float4(ak[dt][0], ak[dt][1], ak[dt][2], ak[dt][3]);
+                    *reinterpret_cast<float4*>(dst + ((long long)c * 2 + 1) * D + 16 * dt + 4 * q4) =
+                        make_float4(av[dt][0], av[dt][1], av[dt][2], av[dt][3]);
+                }
+            }
+        }
+        return;
+    }
+    if (j0 >= nkeys) return;
+    f32x4_t ak[DT], av[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) ak[dt] = av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nch = r_hi >= r_lo ? (r_hi - r_lo + 32) / 32 : 0;
+    for (int hh = 0; hh < p.G; ++hh) {
+        const int h = g * p.G + hh;
+        if (nch > 0) stage(h, r_lo, tbuf(0), 4, wave);
+        for (int ci = 0; ci < nch; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (ci + 1 < nch) stage(h, r_lo + 32 * (ci + 1), tbuf((ci + 1) & 1), 4, wave);
+            chunk(tbuf(ci & 1), h, r_lo + 32 * ci, j, ak, av);
+        }
+        __syncthreads();
+    }
+    if (j >= nkeys) return;
+    float dk[DT][4], dv[DT][4];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dk[dt][r] = p.scale * ak[dt][r];
+            dv[dt][r] = av[dt][r];
+        }
+    if (KIND == 0) {
+        // raw row j also feeds block j / m of each compression (full blocks only)
+        const int nchn = p.Hkv * D;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const bool present = which == 0 ? p.has_hca : p.has_csa;
+            if (!present) continue;
+            const int mm = which == 0 ? p.m_hca : p.m_csa;
+            const int N = which == 0 ? p.N_hca : p.N_csa;
+            const int blk = j / mm;
+            if (blk >= N) continue;
+            const int i = j - blk * mm;
+            const int zk = which == 0 ? 0 : (p.has_hca ? 2 : 0);
+            const ZJob& Jk = p.z[zk];
+            const ZJob& Jv = p.z[zk + 1];
+            const long long co = ((long long)b * N + blk) * nchn;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int chn = ch0 + 16 * dt + r;
+                    dk[dt][r] = fmaf(Jk.pz[(long long)i * nchn + chn], Jk.dxc[co + chn], dk[dt][r]);
+                    dv[dt][r] = fmaf(Jv.pz[(long long)i * nchn + chn], Jv.dxc[co + chn], dv[dt][r]);
+                }
+        }
+    }
+    float* dko = KIND == 0 ? p.dk : p.dkc_csa;
+    float* dvo = KIND == 0 ? p.dv : p.dvc_csa;
+    const long long o = ((long long)b * nkeys + j) * rs + ch0;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        *reinterpret_cast<float4*>(dko + o + 16 * dt) = make_float4(dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]);
+        *reinterpret_cast<float4*>(dvo + o + 16 * dt) = make_float4(dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
+    }
+}
+
+// HCA cache gradients: the partial sums of every (range, wave) chunk added in
+// order (one thread per (b, entry, channel))
+__global__ __launch_bounds__(kThreads) void bwd_hca_reduce_kernel(BwdParams p, int D) {
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long nchn = (long long)p.Hkv * D;
+    if (gid >= (long long)p.B * p.N_hca * nchn) return;
+    const int b = (int)(gid / (p.N_hca * nchn));
+    const long long r = gid - (long long)b * p.N_hca * nchn;
+    const int c = (int)(r / nchn), chn = (int)(r - (long long)c * nchn);
+    const int g = chn / D, e = chn - g * D;
+    float sk = 0.f, sv = 0.f;
+    for (int rc = 0; rc < p.nrange * 4; ++rc) {
+        const float* src = p.hpart + ((((long long)b * p.Hkv + g) * p.nrange) * 4 + rc) * (long long)p.N_hca * 2 * D;
+        sk += src[((long long)c * 2) * D + e];
+        sv += src[((long long)c * 2 + 1) * D + e];
+    }
+    p.dkc_hca[gid] = p.scale * sk;
+    p.dvc_hca[gid] = sv;
+}
+
 // ------------------------------------------------------------ 5. logit gradients
 // dp[b, chunk, i, ch] = sum over the chunk's blocks c of dxc[b, c, ch] x[b, c m + i, ch]
 // (one thread per (b, chunk, i, ch); blockIdx.y = job)
@@ -422,28 +1002,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dp_kernel(BwdParams p, int nch) 
     const T* x = reinterpret_cast<const T*>(J.x);
     const int c_end = min(J.N, (chunk + 1) * kDpChunk);
     float s = 0.f;
+#pragma unroll 8
     for (int blk = chunk * kDpChunk; blk < c_end; ++blk)
         s = fmaf(J.dxc[((long long)b * J.N + blk) * nch + c],
                  Elem<T>::load1(x + ((long long)b * p.T + (long long)blk * J.m + i) * nch + c), s);
     J.dp[gid] = s;
 }
 
-// dz[i, ch] = P_i (dP_i - sum_l P_l dP_l); dP_i = sum over (b, chunk) in
-// order (one thread per channel; blockIdx.y = job).  dz holds dP_i between
-// the two loops.
+// dP_i = sum over (b, chunk) of the partials, in order, stored in dz (one
+// thread per (i, ch); blockIdx.y = job)
+__global__ __launch_bounds__(kThreads) void bwd_dpsum_kernel(BwdParams p, int nch) {
+    const ZJob& J = p.z[blockIdx.y];
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long per_chunk = (long long)J.m * nch;
+    if (gid >= per_chunk) return;
+    const int nbc = p.B * J.nchunk;
+    float dp = 0.f;
+#pragma unroll 8
+    for (int bc = 0; bc < nbc; ++bc) dp += J.dp[bc * per_chunk + gid];
+    J.dz[gid] = dp;
+}
+
+// dz[i, ch] = P_i (dP_i - sum_l P_l dP_l) (one thread per channel; blockIdx.y = job)
 __global__ __launch_bounds__(kThreads) void bwd_dz_kernel(BwdParams p, int nch) {
     const ZJob& J = p.z[blockIdx.y];
     const int c = blockIdx.x * kThreads + threadIdx.x;
     if (c >= nch) return;
-    const long long per_chunk = (long long)J.m * nch;
-    const int nbc = p.B * J.nchunk;
     float cen = 0.f;
-    for (int i = 0; i < J.m; ++i) {
-        float dp = 0.f;
-        for (int bc = 0; bc < nbc; ++bc) dp += J.dp[bc * per_chunk + (long long)i * nch + c];
-        J.dz[(long long)i * nch + c] = dp;
-        cen = fmaf(J.pz[(long long)i * nch + c], dp, cen);
-    }
+#pragma unroll 16
+    for (int i = 0; i < J.m; ++i) cen = fmaf(J.pz[(long long)i * nch + c], J.dz[(long long)i * nch + c], cen);
+#pragma unroll 16
     for (int i = 0; i < J.m; ++i) {
         const long long o = (long long)i * nch + c;
         J.dz[o] = J.pz[o] * (J.dz[o] - cen);
@@ -495,9 +1083,19 @@ __global__ __launch_bounds__(kThreads) void bwd_gate_token_kernel(BwdParams p) {
 // ------------------------------------------------------------ host side
 struct BwdPlan {
     size_t off_stats, off_dkc_hca, off_dvc_hca, off_dkc_csa, off_dvc_csa, off_pz[4], off_dp[4];
+    size_t off_coef_w, off_coef_h, off_coef_c, off_bm, off_bmpre, off_hpart;
+    int nrange;
     size_t bytes;
     int N_hca, N_csa;
+    bool coef;   // MFMA query side and coefficient key sides
+    int bmw;
 };
+
+// The coefficient form holds (dS, sum w P) of every (row, head, key of its
+// sets): 8 bytes per pair, at most this much workspace for them.
+constexpr size_t kCoefMaxBytes = (size_t)8 << 30;
+// largest CSA entry count attended through the row bitmaps (masked chunks)
+constexpr int kCoefMaxNcsa = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -579,6 +1177,25 @@ BwdPlan bwd_plan(const shattn_bwd_args* a) {
         pl.off_pz[jb] = take(present ? (size_t)m * nch : 0);
         pl.off_dp[jb] = take(present ? (size_t)a->B * nchunk * m * nch : 0);
     }
+    // coefficient form: bf16, CSA entries few enough to attend masked
+    const size_t rows = (size_t)a->B * a->T;
+    const size_t coef_b = rows * a->H * 8 * ((size_t)a->W + pl.N_hca + (csa ? a->k : 0));
+    pl.coef = a->dtype == SHATTN_DTYPE_BF16 && pl.N_csa <= kCoefMaxNcsa && coef_b <= kCoefMaxBytes;
+    if (pl.coef) {
+        pl.bmw = csa ? (pl.N_csa + 31) / 32 : 0;
+        auto takeb = [&](size_t bytes) {
+            const size_t o = off;
+            off += align256(bytes);
+            return o;
+        };
+        pl.off_coef_w = takeb(rows * a->H * (size_t)a->W * 8);
+        pl.off_coef_h = takeb(rows * a->H * (size_t)pl.N_hca * 8);
+        pl.off_coef_c = takeb(csa ? rows * a->H * (size_t)a->k * 8 : 0);
+        pl.off_bm = takeb(rows * (size_t)pl.bmw * 4);
+        pl.off_bmpre = takeb(rows * (size_t)pl.bmw * 4);
+        pl.nrange = (a->T + kKeyRange - 1) / kKeyRange;
+        pl.off_hpart = takeb((size_t)a->B * a->Hkv * pl.nrange * 4 * pl.N_hca * 2 * a->d * 4);
+    }
     pl.bytes = off;
     return pl;
 }
@@ -639,15 +1256,50 @@ template <typename T, int D> int bwd_launch(const shattn_bwd_args* a, const BwdP
     const dim3 blk(kThreads);
     auto tiles = [](int n) { return (long long)((n + kRowsPerGroup - 1) / kRowsPerGroup); };
     const long long qgrid = (long long)a->B * a->H * tiles(a->T);
-    if (qgrid > 0) hipLaunchKernelGGL((bwd_query_kernel<T, D>), dim3((unsigned)qgrid), blk, 0, s, p);
-    if (p.nz > 0)
-        hipLaunchKernelGGL(bwd_weights_kernel, dim3((nch + kThreads - 1) / kThreads, p.nz), blk, 0, s, p, nch);
     const long long hgrid = (long long)a->B * a->Hkv * tiles(pl.N_hca);
-    if (hca && hgrid > 0) hipLaunchKernelGGL((bwd_key_kernel<T, D, 1>), dim3((unsigned)hgrid), blk, 0, s, p);
     const long long cgrid = (long long)a->B * a->Hkv * tiles(pl.N_csa);
-    if (csa && cgrid > 0) hipLaunchKernelGGL((bwd_key_kernel<T, D, 2>), dim3((unsigned)cgrid), blk, 0, s, p);
     const long long rgrid = (long long)a->B * a->Hkv * tiles(a->T);
-    if (rgrid > 0) hipLaunchKernelGGL((bwd_key_kernel<T, D, 0>), dim3((unsigned)rgrid), blk, 0, s, p);
+    bool coef = false;
+    if constexpr (std::is_same<T, bf16_t>::value) coef = pl.coef;
+    if (coef) {
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            p.coef_w = reinterpret_cast<float2*>(ws + pl.off_coef_w);
+            p.coef_h = reinterpret_cast<float2*>(ws + pl.off_coef_h);
+            p.coef_c = reinterpret_cast<float2*>(ws + pl.off_coef_c);
+            p.bm = reinterpret_cast<uint32_t*>(ws + pl.off_bm);
+            p.bmpre = reinterpret_cast<int32_t*>(ws + pl.off_bmpre);
+            p.bmw = pl.bmw;
+            p.hpart = reinterpret_cast<float*>(ws + pl.off_hpart);
+            p.nrange = pl.nrange;
+            const long long rows = (long long)a->B * a->T;
+            if (csa && rows > 0)
+                hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)), blk, 0, s, p);
+            const size_t lds = 4 * (size_t)32 * D * 2;   // K and V chunks, double-buffered
+            if (qgrid > 0) hipLaunchKernelGGL((bwd_query_mfma_kernel<D>), dim3((unsigned)qgrid), blk, lds, s, p);
+            if (p.nz > 0)
+                hipLaunchKernelGGL(bwd_weights_kernel, dim3((nch + kThreads - 1) / kThreads, p.nz), blk, 0, s, p, nch);
+            const size_t mat = (size_t)32 * D * 2;
+            if (hca && pl.N_hca > 0 && rows > 0) {
+                hipLaunchKernelGGL((bwd_key_mfma_kernel<D, 1>), dim3((unsigned)((long long)a->B * a->Hkv * pl.nrange)),
+                                   blk, 8 * mat, s, p);
+                const long long n = (long long)a->B * pl.N_hca * nch;
+                hipLaunchKernelGGL(bwd_hca_reduce_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), blk, 0, s,
+                                   p, D);
+            }
+            if (csa && cgrid > 0)
+                hipLaunchKernelGGL((bwd_key_mfma_kernel<D, 2>), dim3((unsigned)cgrid), blk, 4 * mat, s, p);
+            if (rgrid > 0) hipLaunchKernelGGL((bwd_key_mfma_kernel<D, 0>), dim3((unsigned)rgrid), blk, 4 * mat, s, p);
+        }
+    } else {
+        if (qgrid > 0) hipLaunchKernelGGL((bwd_query_kernel<T, D>), dim3((unsigned)qgrid), blk, 0, s, p);
+        if (p.nz > 0)
+            hipLaunchKernelGGL(bwd_weights_kernel, dim3((nch + kThreads - 1) / kThreads, p.nz), blk, 0, s, p, nch);
+        if (hca && hgrid > 0)
+            hipLaunchKernelGGL((bwd_key_kernel<T, D, 1, false>), dim3((unsigned)hgrid), blk, 0, s, p);
+        if (csa && cgrid > 0)
+            hipLaunchKernelGGL((bwd_key_kernel<T, D, 2, false>), dim3((unsigned)cgrid), blk, 0, s, p);
+        if (rgrid > 0) hipLaunchKernelGGL((bwd_key_kernel<T, D, 0, false>), dim3((unsigned)rgrid), blk, 0, s, p);
+    }
     if (p.nz > 0) {
         long long most = 0;
         for (int z = 0; z < p.nz; ++z) {
@@ -657,6 +1309,11 @@ template <typename T, int D> int bwd_launch(const shattn_bwd_args* a, const BwdP
         if (most > 0)
             hipLaunchKernelGGL((bwd_dp_kernel<T>), dim3((unsigned)((most + kThreads - 1) / kThreads), p.nz), blk, 0,
                                s, p, nch);
+        int mmax = 0;
+        for (int z = 0; z < p.nz; ++z) mmax = p.z[z].m > mmax ? p.z[z].m : mmax;
+        const long long nsum = (long long)mmax * nch;
+        hipLaunchKernelGGL(bwd_dpsum_kernel, dim3((unsigned)((nsum + kThreads - 1) / kThreads), p.nz), blk, 0, s, p,
+                           nch);
         hipLaunchKernelGGL(bwd_dz_kernel, dim3((nch + kThreads - 1) / kThreads, p.nz), blk, 0, s, p, nch);
     }
     if (a->gate_mode == 0) {
