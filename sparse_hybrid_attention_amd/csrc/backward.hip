@@ -282,22 +282,38 @@ __global__ __launch_bounds__(kThreads) void bwd_query_kernel(BwdParams p) {
 // Selection bitmap of every row (visible entries only) and, per word, the
 // number of selected entries in the words before it: the rank of an entry in
 // its row's ascending selection is pre[w] + popcount(word & bits below).
+constexpr int kMaxBmw = 128;   // bitmap words of a row (entries up to 4096)
+
 __global__ __launch_bounds__(kThreads) void bwd_bitmap_kernel(BwdParams p) {
-    const long long row = (long long)blockIdx.x * kThreads + threadIdx.x;
+    // one wave per row: the row's words are built in LDS (selections OR their
+    // bits in, one entry per lane per step), then written out with a
+    // wave-wide prefix count
+    __shared__ uint32_t words[kThreads / 64][kMaxBmw];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * (kThreads / 64) + wv;
     if (row >= (long long)p.B * p.T) return;
     const int t = (int)(row % p.T);
-    uint32_t* bm = p.bm + row * p.bmw;
-    for (int w = 0; w < p.bmw; ++w) bm[w] = 0u;
+    uint32_t* wd = words[wv];
+    for (int w = lane; w < p.bmw; w += 64) wd[w] = 0u;
+    wave_lds_sync();
     const int nc = n_visible(t, p.W, p.m_csa, p.N_csa);
     const int32_t* sel = p.idx + row * p.ksel;
-    for (int j = 0; j < p.ksel; ++j) {
+    for (int j = lane; j < p.ksel; j += 64) {
         const int e = sel[j];
-        if (e >= 0 && e < nc) bm[e >> 5] |= 1u << (e & 31);
+        if (e >= 0 && e < nc) atomicOr(&wd[e >> 5], 1u << (e & 31));
     }
-    int run = 0;
-    for (int w = 0; w < p.bmw; ++w) {
-        p.bmpre[row * p.bmw + w] = run;
-        run += __popc(bm[w]);
+    wave_lds_sync();
+    int run = 0;   // selected entries in the earlier 64-word groups
+    for (int w0 = 0; w0 < p.bmw; w0 += 64) {
+        const int w = w0 + lane;
+        const uint32_t x = w < p.bmw ? wd[w] : 0u;
+        const int c = __popc(x);
+        const int incl = wave_incl_scan(c);
+        if (w < p.bmw) {
+            p.bm[row * p.bmw + w] = x;
+            p.bmpre[row * p.bmw + w] = run + incl - c;
+        }
+        run += __shfl(incl, 63);
     }
 }
 
@@ -837,6 +853,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) 
             return p.coef_c[rowc * p.ksel + p.bmpre[bw] + __popc(word & ((1u << (key & 31)) - 1u))];
         }
     };
+    // pipelined form (KIND 0, 2): the bitmap words and prefix counts of this
+    // lane's rows (KIND 2) and then its coefficients, loaded ahead of use
+    auto load_w = [&](int r0, int key, uint32_t* word, int* pre) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = r0 + 8 * q4 + i;
+            word[i] = 0u;
+            pre[i] = 0;
+            if (KIND == 2 && t <= r_hi && key < nkeys) {
+                const long long bw = ((long long)b * p.T + t) * p.bmw + (key >> 5);
+                word[i] = p.bm[bw];
+                pre[i] = p.bmpre[bw];
+            }
+        }
+    };
+    auto load_c = [&](int h, int r0, int key, const uint32_t* word, const int* pre, float2* c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = r0 + 8 * q4 + i;
+            c[i] = make_float2(0.f, 0.f);
+            if (t > r_hi || key >= nkeys) continue;
+            const long long rowc = ((long long)b * p.H + h) * p.T + t;
+            if (KIND == 0) {
+                if (t >= key && t <= key + p.W - 1) c[i] = p.coef_w[rowc * p.W + (key - t + p.W - 1)];
+            } else if (KIND == 2) {
+                if ((word[i] >> (key & 31)) & 1u)
+                    c[i] = p.coef_c[rowc * p.ksel + pre[i] + __popc(word[i] & ((1u << (key & 31)) - 1u))];
+            }
+        }
+    };
     auto split = [](const float* v, bf16x8_t& hi, bf16x8_t& lo) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -845,16 +891,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) 
             lo[i] = (__bf16)(v[i] - (float)h_);
         }
     };
-    // accumulate one staged chunk (rows r0 ..) for keys key0 + n into ak / av
-    auto chunk = [&](const char* buf, int h, int r0, int key, f32x4_t* ak, f32x4_t* av) {
+    // accumulate one staged chunk given this lane's coefficients c[0..7]
+    auto mfma_chunk = [&](const char* buf, const float2* c, f32x4_t* ak, f32x4_t* av) {
         float ds[8], wp[8];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float2 c2 = coef(h, r0 + 8 * q4 + i, key);
-            ds[i] = c2.x;
-            wp[i] = c2.y;
-            any |= c2.x != 0.f || c2.y != 0.f;
+            ds[i] = c[i].x;
+            wp[i] = c[i].y;
+            any |= c[i].x != 0.f || c[i].y != 0.f;
         }
         if (!__any(any)) return;
         bf16x8_t dh, dl, wh, wl;
@@ -868,6 +913,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) 
             av[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wh, av[dt], 0, 0, 0);
             av[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, wl, av[dt], 0, 0, 0);
         }
+    };
+    // one staged chunk (rows r0 ..) for key `key`, coefficients loaded on the spot
+    auto chunk = [&](const char* buf, int h, int r0, int key, f32x4_t* ak, f32x4_t* av) {
+        float2 c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = coef(h, r0 + 8 * q4 + i, key);
+        mfma_chunk(buf, c, ak, av);
     };
     const int ch0 = g * D + 4 * q4;   // channel of acc[dt][0] within a K/V row: + 16 dt
     if (KIND == 1) {
@@ -909,7 +961,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) ak[dt] = av[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int nch = r_hi >= r_lo ? (r_hi - r_lo + 32) / 32 : 0;
-    for (int hh = 0; hh < p.G; ++hh) {
+    for (int hh = 0; hh < p.G && KIND == 0; ++hh) {
+        // raw rows: coefficients loaded on the spot (the window's single load
+        // per row; holding the next chunk's would cost a wave per SIMD)
         const int h = g * p.G + hh;
         if (nch > 0) stage(h, r_lo, tbuf(0), 4, wave);
         for (int ci = 0; ci < nch; ++ci) {
@@ -917,6 +971,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_key_mfma_kernel(BwdParams p) 
             __syncthreads();
             if (ci + 1 < nch) stage(h, r_lo + 32 * (ci + 1), tbuf((ci + 1) & 1), 4, wave);
             chunk(tbuf(ci & 1), h, r_lo + 32 * ci, j, ak, av);
+        }
+        __syncthreads();
+    }
+    for (int hh = 0; hh < p.G && KIND == 2; ++hh) {
+        const int h = g * p.G + hh;
+        // chunk ci + 1's coefficients (and chunk ci + 2's bitmap words) load
+        // while chunk ci is computed
+        uint32_t w1[8], w2[8];
+        int p1[8], p2[8];
+        float2 c0[8];
+        if (nch > 0) {
+            stage(h, r_lo, tbuf(0), 4, wave);
+            load_w(r_lo, j, w1, p1);
+            load_c(h, r_lo, j, w1, p1, c0);
+            load_w(r_lo + 32, j, w1, p1);
+        }
+        for (int ci = 0; ci < nch; ++ci) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int r1 = r_lo + 32 * (ci + 1);
+            float2 c1[8];
+            if (ci + 1 < nch) {
+                stage(h, r1, tbuf((ci + 1) & 1), 4, wave);
+                load_c(h, r1, j, w1, p1, c1);
+                load_w(r1 + 32, j, w2, p2);
+            }
+            mfma_chunk(tbuf(ci & 1), c0, ak, av);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                c0[i] = c1[i];
+                w1[i] = w2[i];
+                p1[i] = p2[i];
+            }
         }
         __syncthreads();
     }
@@ -1095,7 +1182,7 @@ struct BwdPlan {
 // sets): 8 bytes per pair, at most this much workspace for them.
 constexpr size_t kCoefMaxBytes = (size_t)8 << 30;
 // largest CSA entry count attended through the row bitmaps (masked chunks)
-constexpr int kCoefMaxNcsa = 4096;
+constexpr int kCoefMaxNcsa = 4096;   // = 32 * kMaxBmw
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1273,7 +1360,7 @@ template <typename T, int D> int bwd_launch(const shattn_bwd_args* a, const BwdP
             p.nrange = pl.nrange;
             const long long rows = (long long)a->B * a->T;
             if (csa && rows > 0)
-                hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)), blk, 0, s, p);
+                hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((rows + 3) / 4)), blk, 0, s, p);
             const size_t lds = 4 * (size_t)32 * D * 2;   // K and V chunks, double-buffered
             if (qgrid > 0) hipLaunchKernelGGL((bwd_query_mfma_kernel<D>), dim3((unsigned)qgrid), blk, lds, s, p);
             if (p.nz > 0)
