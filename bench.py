@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense, published
 KERNEL_SOURCES = {
     "compress_csa": "compress.hip", "compress_hca": "compress.hip", "compress_dual": "compress.hip",
-    "index_topk": "indexer.hip", "attention": "attention.hip",
+    "index_topk": "indexer.hip", "attention": "attention.hip", "backward": "backward.hip",
 }
 
 
@@ -56,7 +56,7 @@ def to_dev(a):
     return torch.from_numpy(a).to("cuda:0")
 
 
-def make_pipeline(inp, q4=False, rope=None):
+def make_pipeline(inp, q4=False, rope=None, overlap=False):
     from sparse_hybrid_attention_amd import binding
     from sparse_hybrid_attention_amd.binding import HybridPipeline
     cfg = inp["cfg"]
@@ -78,7 +78,8 @@ def make_pipeline(inp, q4=False, rope=None):
                               k_raw=to_dev(inp["k_win"]), v_raw=to_dev(inp["v_win"]),
                               q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
                               qI=to_dev(inp["qI"]), kI=to_dev(inp["kI"]), w=to_dev(inp["w"]),
-                              k=cfg["k"], m_csa=cfg["m_csa"], m_hca=cfg["m_hca"], **caches, **extra)
+                              k=cfg["k"], m_csa=cfg["m_csa"], m_hca=cfg["m_hca"], overlap=overlap, **caches,
+                              **extra)
     if q4:
         raise SystemExit("--q4 applies to the decode workload (caches given up front)")
     kw = {}
@@ -752,7 +753,8 @@ def bench_backward(args, torch, binding):
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 6)}
     roof.update(kernel="hybrid_sparse_attn_bwd (all launches of a step)", kernel_ms=round(kms, 5),
-                alg_bytes_per_launch=nbytes_alg, alg_flops_per_launch=flops, traffic=None,
+                alg_bytes_per_launch=nbytes_alg, alg_flops_per_launch=flops,
+                traffic=traffic_for("backward", "tinyr2_bwd"),
                 TFLOPs_achieved=round(flops / (kms * 1e-3) / 1e12, 3))
     line = {
         "metric": "hybrid sparse attn backward query rows/s",
@@ -830,6 +832,9 @@ def main():
     ap.add_argument("--rope", default=None, choices=["fused", "separate"],
                     help="prefill workloads: RoPE of the query (last d/2 channels), inside the attention's Q load "
                          "or as a rope_apply launch before it")
+    ap.add_argument("--overlap", action="store_true",
+                    help="decode: run the attention's window and HCA items on a second stream beside the indexer "
+                         "(measured slower at decode_1m: the indexer already fills the chip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the warm (back-to-back) timing and the measured-peak probes")
@@ -892,7 +897,7 @@ def main():
     if not pipeline_workload:
         raise SystemExit(f"unknown workload {args.workload}")
     cfg = inp["cfg"]
-    pipe = make_pipeline(inp, q4=args.q4, rope=args.rope)
+    pipe = make_pipeline(inp, q4=args.q4, rope=args.rope, overlap=args.overlap)
     names = pipe.names()
     log(f"[bench] kernels per step: {names}; warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -977,7 +982,8 @@ def main():
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
         "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]")
                    + (" [HCA and CSA caches in 4-bit storage]" if args.q4 else "")
-                   + (f" [RoPE of q, {args.rope}]" if args.rope else ""),
+                   + (f" [RoPE of q, {args.rope}]" if args.rope else "")
+                   + (" [window / HCA attention items beside the indexer]" if args.overlap else ""),
                    "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],
                    "query_rows": queries, "timing": "each timed step starts from flushed L2 / MALL (cold)",
                    "gpu_ms_per_step_median": round(step_ms[len(step_ms) // 2], 5)},

@@ -237,6 +237,16 @@ typedef struct shattn_fwd_args {
     int32_t rope_dim;
     int32_t reserved2;   /* must be 0 */
     double rope_base;
+    int32_t split_part;  /* 0: the whole attention.  A launch that splits the
+                            key list (hybrid_sparse_attn_fwd_workspace_size() >
+                            0: decode) can run as two calls on one workspace:
+                            1 = the window and HCA items, which do not read
+                            idx (so they may run while the indexer writes it,
+                            on another stream); 2 = the CSA items and the merge
+                            of every item's partial state, ordered after call
+                            1 by the caller.  Without a split, call 1 does
+                            nothing and call 2 the whole attention. */
+    int32_t reserved3;   /* must be 0 */
 } shattn_fwd_args;
 
 /* Workspace bytes hybrid_sparse_attn_fwd needs for these arguments (0 when the

@@ -87,6 +87,8 @@ class FwdArgs(ctypes.Structure):
         ("rope_q", ctypes.c_int32), ("rope_off", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
         ("reserved2", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("split_part", ctypes.c_int32),
+        ("reserved3", ctypes.c_int32),
     ]
 
 
@@ -303,7 +305,8 @@ def csa_index_topk(qI, kI, w, q_pos0, m: int, W: int, k: int, out=None, ws=None)
 
 
 def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, csa=None,
-                  sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False, rope_q=None):
+                  sm_scale=0.0, out=None, gate_logits=False, q_pos=None, raw_ring=False, rope_q=None,
+                  split_part=0):
     """Build the argument struct (and the output tensor) for hybrid_sparse_attn_fwd.
 
     hca = (k_hca, v_hca, m_hca) or None; csa = (k_csa, v_csa, idx) or None.
@@ -316,6 +319,7 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
     q_pos: device int64 [B] per-sequence positions (needs raw_ring); raw_ring:
     k_raw / v_raw are rings, position t in row t % Tr.
     rope_q: (rope_off, rope_dim, base) to rotate q by RoPE as it is loaded.
+    split_part: 0 whole attention; 1 / 2 the two calls of a split launch.
     Returns (FwdArgs, out, keepalive tuple)."""
     _need(q, "q")
     dev = q.device
@@ -385,6 +389,7 @@ def make_fwd_args(q, k_raw, v_raw, gates, W, *, q_pos0=0, raw_pos0=0, hca=None, 
         keep += [kc, vc, idx]
     a.gates = gates.data_ptr()
     a.raw_ring = 1 if raw_ring else 0
+    a.split_part = int(split_part)
     if rope_q is not None:
         a.rope_q = 1
         a.rope_off, a.rope_dim, a.rope_base = int(rope_q[0]), int(rope_q[1]), float(rope_q[2])
@@ -656,12 +661,17 @@ class HybridPipeline:
                  zk_csa=None, zv_csa=None, m_csa=None, zk_hca=None, zv_hca=None, m_hca=None,
                  qI=None, kI=None, w=None, k=None,
                  k_csa=None, v_csa=None, k_hca=None, v_hca=None, q4_hca=None, q4_csa=None,
-                 rope_q=None, rope_fused=True):
+                 rope_q=None, rope_fused=True, overlap=False):
         """Decode with 4-bit caches: k_hca / v_hca (k_csa / v_csa) are the
         codes [B, N, Hkv, d/2] and q4_hca (q4_csa) their (params_k, params_v).
         rope_q = (rope_off, rope_dim, base): RoPE of q at each row's position,
         inside the attention's Q load (rope_fused) or as a rope_apply launch
-        on q before it (which turns q in place at every run)."""
+        on q before it (which turns q in place at every run).
+        overlap: when the attention splits its key list (decode), its window
+        and HCA items run on a second stream while the indexer runs, and the
+        CSA items and the merge follow on this stream.  Off by default: at the
+        1M-token decode shape the indexer fills the chip, and the items run
+        beside it slow it by more than they save."""
         lib = load_library()
         self.lib = lib
         dev = q.device
@@ -726,8 +736,22 @@ class HybridPipeline:
         self.keep += list(keep)
         nbytes = int(lib.hybrid_sparse_attn_fwd_workspace_size(ctypes.byref(a)))
         self.attn_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        self.calls.append(("attention", lib.hybrid_sparse_attn_fwd,
-                           (ctypes.byref(a), _ptr(self.attn_ws) if nbytes else None, nbytes, s)))
+        wsp = _ptr(self.attn_ws) if nbytes else None
+        self.part1 = None
+        if overlap and nbytes > 0:
+            # the same launch in two calls on one workspace: window and HCA
+            # items on a second stream (they do not read idx), CSA items and
+            # the merge here after the indexer and after the first call
+            a1, _o1, k1 = make_fwd_args(q, k_raw, v_raw, gates, W, q_pos0=q_pos0, raw_pos0=raw_pos0, hca=hca,
+                                        csa=csa, rope_q=rope_q if rope_fused else None, out=out, split_part=1)
+            a.split_part = 2
+            self.stream2 = torch.cuda.Stream(device=dev)
+            self.ev_start = torch.cuda.Event()
+            self.ev_part1 = torch.cuda.Event()
+            self.part1 = (lib.hybrid_sparse_attn_fwd,
+                          (ctypes.byref(a1), wsp, nbytes, ctypes.c_void_p(self.stream2.cuda_stream)))
+            self.keep += [a1] + list(k1)
+        self.calls.append(("attention", lib.hybrid_sparse_attn_fwd, (ctypes.byref(a), wsp, nbytes, s)))
 
     def names(self):
         return [c[0] for c in self.calls]
@@ -737,7 +761,18 @@ class HybridPipeline:
         recorded around the calls on the pipeline's stream."""
         if events is not None:
             events[0].record(self.stream)
+        if self.part1 is not None:
+            self.ev_start.record(self.stream)
+            self.stream2.wait_event(self.ev_start)
+            fn, args = self.part1
+            rc = fn(*args)
+            if rc != SHATTN_OK:
+                raise ShattnError(rc, "attention (window and HCA items): " +
+                                  self.lib.shattn_last_error().decode(errors="replace"))
+            self.ev_part1.record(self.stream2)
         for j, (name, fn, args) in enumerate(self.calls):
+            if name == "attention" and self.part1 is not None:
+                self.stream.wait_event(self.ev_part1)
             rc = fn(*args)
             if rc != SHATTN_OK:
                 raise ShattnError(rc, f"{name}: " + self.lib.shattn_last_error().decode(errors="replace"))

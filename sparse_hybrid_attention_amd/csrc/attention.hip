@@ -102,6 +102,7 @@ struct AttnParams {
     int split_keys;
     int split_csa;   // selected CSA entries per split item (gathers are slower per key)
     int n_win_items, n_hca_items;
+    int item_lo, item_n;   // the items [item_lo, item_lo + item_n) of every (b, g, query tile) this launch runs
     int has_hca, has_csa;  // branch present (its gate column is used)
     int ncol;              // columns (query, head) per workgroup = 16 * waves
     // 4-bit compressed caches: bit 0 HCA, bit 1 CSA hold codes (two per byte)
@@ -758,13 +759,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // remapped so that every XCD runs a contiguous range of work ids: the
     // query tiles of one (b, g), which share window rows and compressed
     // entries, then meet in one L2.
-    const long long wid = xcd_work_id(blockIdx.x, gridDim.x);
-    long long wg = wid;
+    // (split mode: a launch may run a range of the items; wid names the
+    // item's absolute partial-state slot)
+    const long long wl = xcd_work_id(blockIdx.x, gridDim.x);
+    long long wg = wl;
     int item = 0;
     if (p.nsplit) {
-        item = (int)(wg % p.nsplit);
-        wg /= p.nsplit;
+        item = p.item_lo + (int)(wl % p.item_n);
+        wg = wl / p.item_n;
     }
+    const long long wid = p.nsplit ? wg * p.nsplit + item : wl;
     // later query tiles first: they attend the most CSA entries, so the
     // lightest work runs last and the tail of the launch is short
     const int qt = p.nqt - 1 - (int)(wg % p.nqt);
@@ -1517,6 +1521,8 @@ struct Plan {
     size_t lds;
     long long grid;
     size_t ws_bytes;
+    bool launch_main;   // the attention kernel runs (a CSA-items call without CSA items does not)
+    bool combine;       // the split partial states are merged after it
 };
 
 int make_plan(const shattn_fwd_args* a, Plan& pl) {
@@ -1572,7 +1578,10 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
             if (reinterpret_cast<uintptr_t>(q4p[i]) & 3)
                 return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: (min, step) must be 4-byte aligned");
         }
-    if (a->reserved2 != 0) return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved2 must be 0");
+    if (a->reserved2 != 0 || a->reserved3 != 0)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: reserved2 / reserved3 must be 0");
+    if (a->split_part < 0 || a->split_part > 2)
+        return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: split_part = %d (0, 1 or 2)", a->split_part);
     if (a->rope_q != 0 && a->rope_q != 1)
         return fail(SHATTN_EINVAL, "hybrid_sparse_attn_fwd: rope_q = %d (0 or 1)", a->rope_q);
     if (a->rope_q &&
@@ -1582,6 +1591,7 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
                     "finite base > 0 (got off %d, dim %d, base %g)", a->rope_off, a->rope_dim, a->rope_base);
     AttnParams& p = pl.p;
     p = AttnParams{};
+    pl.launch_main = pl.combine = false;
     p.B = a->B;
     p.Tq = a->Tq;
     p.H = a->H;
@@ -1674,9 +1684,19 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
         const int n_csa_items = has_csa ? (a->k + p.split_csa - 1) / p.split_csa : 0;
         p.nsplit = p.n_win_items + p.n_hca_items + n_csa_items;
         pl.ws_bytes = (size_t)nwg * p.nsplit * p.ncol * (a->d + 4) * sizeof(float);
-        pl.grid = nwg * p.nsplit;
+        // the items this call runs (split_part): all, the ones that do not
+        // read idx (window, HCA), or the CSA ones (then the merge)
+        p.item_lo = a->split_part == 2 ? p.n_win_items + p.n_hca_items : 0;
+        p.item_n = a->split_part == 0 ? p.nsplit
+                 : (a->split_part == 1 ? p.n_win_items + p.n_hca_items : n_csa_items);
+        pl.grid = nwg * p.item_n;
+        pl.combine = a->split_part != 1;
+        pl.launch_main = p.item_n > 0;
     } else {
-        pl.grid = nwg;
+        // no split: the second call of a two-part call does it all
+        pl.grid = a->split_part == 1 ? 0 : nwg;
+        pl.combine = false;
+        pl.launch_main = true;
     }
 
     const bool bf = a->dtype == SHATTN_DTYPE_BF16;
@@ -1741,13 +1761,15 @@ static int launch_attn_nw(Plan& pl, hipStream_t s) {
                         pl.lds, hipGetErrorString(e));
         }
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, GATHER, Q4>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds, s,
-                       pl.p);
-    hipError_t le = hipGetLastError();
-    if (le != hipSuccess)
-        return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
-                    pl.grid, NW * 64, pl.lds, hipGetErrorString(le));
-    if (!pl.p.nsplit) return SHATTN_OK;
+    if (pl.launch_main) {
+        hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, GATHER, Q4>), dim3((unsigned)pl.grid), dim3(NW * 64), pl.lds,
+                           s, pl.p);
+        hipError_t le = hipGetLastError();
+        if (le != hipSuccess)
+            return fail(SHATTN_EHIP, "hybrid_sparse_attn_fwd: launch failed (grid %lld, block %d, lds %zu): %s",
+                        pl.grid, NW * 64, pl.lds, hipGetErrorString(le));
+    }
+    if (!pl.p.nsplit || !pl.combine) return SHATTN_OK;
     const long long n = (long long)pl.p.B * pl.p.Hkv * pl.p.nqt * pl.p.ncol * (D / 4) * kCombineSub;
     hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        pl.p);
@@ -1773,7 +1795,7 @@ extern "C" int hybrid_sparse_attn_fwd(const shattn_fwd_args* a, void* ws, size_t
     Plan pl;
     int rc = make_plan(a, pl);
     if (rc != SHATTN_OK) return rc;
-    if (pl.grid == 0) return SHATTN_OK;
+    if (pl.grid == 0 && !(pl.p.nsplit && pl.combine)) return SHATTN_OK;
     if (pl.ws_bytes > 0) {
         if (!ws || ws_bytes < pl.ws_bytes)
             return fail(SHATTN_EWORKSPACE, "hybrid_sparse_attn_fwd: workspace of %zu bytes needed, %zu given",
@@ -1827,7 +1849,7 @@ extern "C" int hybrid_sparse_attn_fwd_noalloc(const shattn_fwd_args* a, void* st
     Plan pl;
     int rc = make_plan(a, pl);
     if (rc != SHATTN_OK) return rc;
-    if (pl.grid == 0) return SHATTN_OK;
+    if (pl.grid == 0 && !(pl.p.nsplit && pl.combine)) return SHATTN_OK;
     if (pl.ws_bytes > kScratchBytes)
         return fail(SHATTN_EUNSUPPORTED,
                     "hybrid_sparse_attn_fwd_noalloc: these arguments need %zu bytes of scratch, the library holds %zu",

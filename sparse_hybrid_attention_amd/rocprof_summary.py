@@ -42,6 +42,7 @@ KERNELS = {
     "compress_hca": (("compress_kernel",), "compress.hip"),
     "index_topk": (("index_",), "indexer.hip"),
     "attention": (("attn_fwd_kernel", "attn_combine_kernel"), "attention.hip"),
+    "backward": (("bwd_",), "backward.hip"),
 }
 COPY_BYTES = 1 << 30  # bench.py --copy-probe copies 1 GiB per launch
 

@@ -221,6 +221,9 @@ def test_attention_errors(lib):
     assert call(**dict(rq, rope_base=0.0)) == binding.SHATTN_EINVAL
     assert call(**dict(rq, rope_base=float("inf"))) == binding.SHATTN_EINVAL
     assert call(reserved2=1) == binding.SHATTN_EINVAL
+    assert call(reserved3=1) == binding.SHATTN_EINVAL
+    assert call(split_part=3) == binding.SHATTN_EINVAL
+    assert call(split_part=1) == binding.SHATTN_OK        # no split: the first call does nothing
     # empty problem is a no-op
     assert call(B=0) == binding.SHATTN_OK
 
