@@ -670,14 +670,13 @@ template <int D> struct GatherBf16 : TileReadBf16<D> {
         }
         this->init_read(lane);
     }
-    // load the rows of entries e (lane r < KC holds row r's entry, >= 0) of one
-    // matrix: row r of entry e starts at base + e * rsb bytes
-    __device__ void issue(const char* base, long long rsb, int e, const uint32_t* poff, char* dst) const {
+    // load one matrix's chunk rows: this lane's piece of load j comes from
+    // base + rowoff[j] + poff[j] (rowoff[j]: byte offset of chunk row lrow[j]'s
+    // entry; a wave-uniform base plus 32-bit lane offsets)
+    __device__ void issue(const char* base, const uint32_t* rowoff, const uint32_t* poff, char* dst) const {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int er = __shfl(e, lrow[j]);
-            __builtin_amdgcn_global_load_lds(base + er * rsb + poff[j], (lds_void_t*)(dst + j * 1024), 16, 0, 0);
-        }
+        for (int j = 0; j < NL; ++j)
+            __builtin_amdgcn_global_load_lds(base + (rowoff[j] + poff[j]), (lds_void_t*)(dst + j * 1024), 16, 0, 0);
     }
 };
 
@@ -1093,16 +1092,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     };
 
     // ---- CSA gather, bf16: per-wave K/V chunk tiles in LDS (aliasing the
-    // stream buffers), loaded by DMA; the next chunk's K rows load during this
-    // chunk's softmax and PV and its V rows after the PV, and the entry list
-    // is read one chunk ahead.
+    // stream buffers) and a two-slot ring of entry lists, all loaded by DMA,
+    // so that every vector-memory operation of the loop is a direct-to-LDS
+    // load and the waits below can count them.  Chunk ci: scores from the K
+    // tile; the entries of chunk ci + 1 (read from the ring) give the next
+    // K rows, which go out with the entry list of chunk ci + 2; softmax; PV
+    // from the V tile, then the next V rows go out.  V(ci) is in flight
+    // during the scores and softmax, K(ci + 1) during the PV.  The tiles are
+    // restrict pointers: the compiler then knows that loads into one never
+    // write another and adds no waits of its own beyond these.
     auto gather_dma = [&]() {
       if constexpr (std::is_same<T, bf16_t>::value) {
-        char* gk = smem + p.lds_gather + wave * p.lds_gather_stride;
-        char* gv = gk + GatherBf16<D>::MAT_BYTES;
-        GatherBf16<D> gio;
+        typedef GatherBf16<D> GB;
+        constexpr int NL = GB::NL;   // loads per K or V chunk tile
+        GB gio;
         gio.init(lane);
-        const long long rsb = (long long)p.Hkv * D * 2;   // bytes between entries
+        const uint32_t rsb = (uint32_t)p.Hkv * D * 2;   // bytes between entries (host: N_csa * rsb < 2^32)
         const char* kc = reinterpret_cast<const char*>(p.k_csa) + (long long)b * p.N_csa * rsb + hoff * 2;
         const char* vc = reinterpret_cast<const char*>(p.v_csa) + (long long)b * p.N_csa * rsb + hoff * 2;
         const int ql_a = (wave * 16) / p.G;
@@ -1115,42 +1120,84 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
         const int nj = j_hi > j_lo ? (j_hi - j_lo + KC - 1) / KC : 0;
         const int nchunks = ql_b >= ql_a ? (ql_b - ql_a + 1) * nj : 0;
         if (nchunks == 0 || p.N_csa == 0) return;   // no entries: nothing to attend (or to load)
-        // lanes < KC: entry of row `lane` of chunk ci (-1: none)
-        auto entry = [&](int ci) -> int {
-            const int qq = ql_a + ci / nj;
-            const int j = j_lo + (ci - (qq - ql_a) * nj) * KC + lane;
-            int e = -1;
-            if (lane < KC && j < j_hi) {
-                e = p.idx[((long long)b * p.Tq + i0 + qq) * p.k + j];
-                if (e < 0 || e >= p.N_csa) e = -1;
-            }
-            return e;
+        // chunk c (clamped to the last) -> its query and first list position
+        auto chunk_at = [&](int c, int& qq, int& jb) {
+            c = min(c, nchunks - 1);
+            qq = ql_a + c / nj;
+            jb = j_lo + (c - (qq - ql_a) * nj) * KC;
         };
-        int e_cur = entry(0);
-        gio.issue(kc, rsb, max(e_cur, 0), gio.poff_k, gk);
-        gio.issue(vc, rsb, max(e_cur, 0), gio.poff_v, gv);
-        int e_nxt = nchunks > 1 ? entry(1) : -1;
-        for (int ci = 0; ci < nchunks; ++ci) {
-            __builtin_amdgcn_s_waitcnt(0);   // chunk ci in LDS, entries of ci + 1 loaded
+        auto run = [&](char* __restrict__ tk, char* __restrict__ tv, char* __restrict__ te)
+                       __attribute__((always_inline)) {
+            // the entry list of chunk c into ring slot c & 1 (256 bytes: lane l
+            // writes the 4 bytes at 4 l; lanes >= KC repeat lanes < KC, and
+            // positions past the list repeat its last entry)
+            auto issue_entries = [&](int c) {
+                int qq, jb;
+                chunk_at(c, qq, jb);
+                const int pos = min(jb + (lane & (KC - 1)), j_hi - 1);
+                const int* src = p.idx + ((long long)b * p.Tq + i0 + qq) * p.k + pos;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src), (lds_void_t*)(te + (c & 1) * 256),
+                                                 4, 0, 0);
+            };
+            // row offsets of chunk c's loads for this lane (entries past the
+            // list, negative or beyond the cache read row 0 and are masked)
+            // and the chunk's valid-row bits (bit r: row r)
+            auto read_entries = [&](int c, uint32_t* ro, unsigned long long& vr) {
+                int qq, jb;
+                chunk_at(c, qq, jb);
+                const int nv = j_hi - jb;   // rows below nv hold list positions
+                const int* ent = reinterpret_cast<const int*>(te + (c & 1) * 256);
+#pragma unroll
+                for (int j = 0; j < NL; ++j) {
+                    const int r = gio.lrow[j];
+                    const int e = ent[r];
+                    ro[j] = (r < nv && e >= 0 && e < p.N_csa) ? (uint32_t)e * rsb : 0u;
+                }
+                const int r = lane & (KC - 1);
+                const int e = ent[r];
+                vr = __ballot(lane < KC && r < nv && e >= 0 && e < p.N_csa);
+            };
+            __builtin_amdgcn_s_waitcnt(0);
+            issue_entries(0);
+            issue_entries(1);
+            wait_vmcnt<1>();   // the entries of chunk 0
             wave_lds_sync();
-            const int qq = ql_a + ci / nj;
-            const unsigned long long vrows = __ballot(lane < KC && e_cur >= 0);
-            float sc[8];
-            gio.scores_at(gk, 0, qf, sc);
-            const bool more = ci + 1 < nchunks;
-            wave_lds_sync();   // this wave's K reads are complete
-            if (more) gio.issue(kc, rsb, max(e_nxt, 0), gio.poff_k, gk);   // K tile is free again
-            const uint32_t mb = (valid && ql == qq) ? (uint32_t)(vrows >> (8 * q4)) & 0xFFu : 0u;
-            softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2,
-                                    [&](int, const float* pp, f32x4_t* acc) { gio.pv_at(gv, 0, pp, acc); });
-            wave_lds_sync();   // this wave's V reads are complete
-            if (more) {
-                gio.issue(vc, rsb, max(e_nxt, 0), gio.poff_v, gv);        // V tile is free again
-                e_cur = e_nxt;
-                e_nxt = ci + 2 < nchunks ? entry(ci + 2) : -1;
+            uint32_t ro[NL];
+            unsigned long long vrows;
+            read_entries(0, ro, vrows);
+            gio.issue(kc, ro, gio.poff_k, tk);
+            gio.issue(vc, ro, gio.poff_v, tv);
+            for (int ci = 0; ci < nchunks; ++ci) {
+                // in flight, oldest first: K(ci) [NL], entries(ci + 1) [1], V(ci) [NL]
+                wait_vmcnt<NL>();
+                wave_lds_sync();
+                const int qq = ql_a + ci / nj;
+                float sc[8];
+                gio.scores_at(tk, 0, qf, sc);
+                wave_lds_sync();   // this wave's K reads are complete
+                // past the last chunk the next loads read row 0 into tiles no one reads
+                unsigned long long vr_n = 0ull;
+#pragma unroll
+                for (int j = 0; j < NL; ++j) ro[j] = 0u;
+                if (ci + 1 < nchunks) read_entries(ci + 1, ro, vr_n);
+                gio.issue(kc, ro, gio.poff_k, tk);   // K tile is free again
+                issue_entries(ci + 2);
+                const uint32_t mb = (valid && ql == qq) ? (uint32_t)(vrows >> (8 * q4)) & 0xFFu : 0u;
+                softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2, [&](int, const float* pp, f32x4_t* acc) {
+                    // in flight, oldest first: V(ci) [NL], then K(ci + 1) [NL]
+                    // and entries(ci + 2) [1]
+                    wait_vmcnt<NL + 1>();
+                    wave_lds_sync();
+                    gio.pv_at(tv, 0, pp, acc);
+                });
+                wave_lds_sync();   // this wave's V reads are complete
+                gio.issue(vc, ro, gio.poff_v, tv);   // V tile is free again
+                vrows = vr_n;
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(0);
+        };
+        char* gk = smem + p.lds_gather + wave * p.lds_gather_stride;
+        run(gk, gk + GB::MAT_BYTES, gk + 2 * GB::MAT_BYTES);
       }
     };
 
@@ -1708,7 +1755,8 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
     const size_t shared_b = 2 * tile_b;
     // per-wave gather tiles: bf16 K and V [KC][d] (DMA-loaded, swizzled); fp32
     // padded K and V rows plus the row list
-    const size_t gather_b = bf ? (size_t)(2 * KC * a->d) * esz : (size_t)(2 * KC * kpad) * esz + KC * 8;
+    // (bf16: then a two-slot ring of 256-byte entry lists)
+    const size_t gather_b = bf ? (size_t)(2 * KC * a->d) * esz + 512 : (size_t)(2 * KC * kpad) * esz + KC * 8;
     p.csa_mode = CSA_NONE;
     size_t lds = shared_b;
     if (has_csa) {
@@ -1723,6 +1771,9 @@ int make_plan(const shattn_fwd_args* a, Plan& pl) {
             lds = shared_b + (size_t)p.QW * p.bm_words * 4;
         } else {
             p.csa_mode = CSA_GATHER;
+            // the bf16 gather addresses a sequence's CSA rows with 32-bit offsets
+            if (bf && !(q4 & 2) && (unsigned long long)a->N_csa * a->Hkv * a->d * esz >= (1ull << 32))
+                return fail(SHATTN_EUNSUPPORTED, "hybrid_sparse_attn_fwd: CSA cache of one sequence >= 4 GiB");
             p.lds_gather = 0;
             p.lds_gather_stride = (int)((gather_b + 15) / 16 * 16);
             lds = std::max(lds, (size_t)p.lds_gather_stride * pl.waves);

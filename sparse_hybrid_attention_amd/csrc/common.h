@@ -115,6 +115,16 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (vmcnt only).  Loads, direct-to-LDS loads included, complete in the order
+// they were issued, so this also waits for every load older than the N
+// youngest.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
