@@ -1098,7 +1098,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
     // tile; the entries of chunk ci + 1 (read from the ring) give the next
     // K rows, which go out with the entry list of chunk ci + 2; softmax; PV
     // from the V tile, then the next V rows go out.  V(ci) is in flight
-    // during the scores and softmax, K(ci + 1) during the PV.  The tiles are
+    // during the scores and softmax, K(ci + 1) during the PV; the last chunk
+    // issues nothing more and waits for everything.  The tiles are
     // restrict pointers: the compiler then knows that loads into one never
     // write another and adds no waits of its own beyond these.
     auto gather_dma = [&]() {
@@ -1175,23 +1176,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnParams p) {
                 float sc[8];
                 gio.scores_at(tk, 0, qf, sc);
                 wave_lds_sync();   // this wave's K reads are complete
-                // past the last chunk the next loads read row 0 into tiles no one reads
+                const bool more = ci + 1 < nchunks;
                 unsigned long long vr_n = 0ull;
-#pragma unroll
-                for (int j = 0; j < NL; ++j) ro[j] = 0u;
-                if (ci + 1 < nchunks) read_entries(ci + 1, ro, vr_n);
-                gio.issue(kc, ro, gio.poff_k, tk);   // K tile is free again
-                issue_entries(ci + 2);
+                if (more) {
+                    read_entries(ci + 1, ro, vr_n);
+                    gio.issue(kc, ro, gio.poff_k, tk);   // K tile is free again
+                    issue_entries(ci + 2);
+                }
                 const uint32_t mb = (valid && ql == qq) ? (uint32_t)(vrows >> (8 * q4)) & 0xFFu : 0u;
                 softmax_pv<D, 1, false>(S, sc, mb, p.scale_log2, [&](int, const float* pp, f32x4_t* acc) {
-                    // in flight, oldest first: V(ci) [NL], then K(ci + 1) [NL]
-                    // and entries(ci + 2) [1]
-                    wait_vmcnt<NL + 1>();
+                    // in flight, oldest first: V(ci) [NL], then (more) K(ci + 1)
+                    // [NL] and entries(ci + 2) [1]
+                    if (more) wait_vmcnt<NL + 1>();
+                    else wait_vmcnt<0>();
                     wave_lds_sync();
                     gio.pv_at(tv, 0, pp, acc);
                 });
                 wave_lds_sync();   // this wave's V reads are complete
-                gio.issue(vc, ro, gio.poff_v, tv);   // V tile is free again
+                if (more) gio.issue(vc, ro, gio.poff_v, tv);   // V tile is free again
                 vrows = vr_n;
             }
             __builtin_amdgcn_s_waitcnt(0);
