@@ -76,7 +76,7 @@ struct IdxParams {
     uint32_t* row_tau;  // [rows] key of the sampled threshold (0: every visible entry is listed)
     float* row_delta;   // [rows] bound of |float32 score - exact score| for the row
     int32_t* row_fail;  // [rows] 1: the list cannot decide the row (the streaming kernel does)
-    uint2* row_lists;   // [rows, list_cap] (key, entry) pairs in entry order
+    uint2* row_lists;   // [rows, list_cap] (float32 score bits, entry) pairs in entry order
     int kblk;           // entry blocks per sequence for kmax_part
     int sample_stride;  // sampled entries are 0, S, 2S, ... (S = sample_stride)
     int sample_j;       // the threshold is the sample_j-th largest sampled score
@@ -1105,11 +1105,20 @@ __host__ __device__ constexpr int filter_row_tiles(bool f32, int hi, int di) {
     return f32 ? 1 : 4;
 }
 
+// Workgroups per CU the filter pass is compiled for.  Four (a 128-register
+// budget) where the kernel fits it without spills in its loop: its MFMAs then
+// write ordinary registers (no accumulator-register copies) and four waves
+// share each SIMD; elsewhere the compiler's default.
+__host__ __device__ constexpr int filter_min_blocks(bool f32, int hi, int di) {
+    return (!f32 && di == 64 && (hi == 4 || hi == 8)) ? 4 : 1;
+}
+
 // L2: no LDS; each wave scores FRT row tiles of queries against all their
 // visible entries (MFMA tiles as above) and appends the entries that pass the
 // row's threshold to the row's list in global memory.
 template <typename T, int HI, int DI>
-__global__ __launch_bounds__(WAVES * 64) void index_filter_kernel(IdxParams p) {
+__global__ __launch_bounds__(WAVES * 64, filter_min_blocks(std::is_same<T, float>::value, HI, DI))
+void index_filter_kernel(IdxParams p) {
     typedef IdxMma<T, DI> MM;
     constexpr int QPT = 16 / HI;
     constexpr int SLOTS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
@@ -1172,8 +1181,17 @@ __global__ __launch_bounds__(WAVES * 64) void index_filter_kernel(IdxParams p) {
         const int c = c0 + rho;
         MM::load_a(kI_b + (long long)(c < p.N ? c : 0) * DI, c < p.N, q4, bf);
     };
+    // every query of the wave sees at least nv_min entries: tiles below it
+    // need no visibility test
+    int nv_min = 1 << 30;
+#pragma unroll
+    for (int rt = 0; rt < FRT; ++rt)
+#pragma unroll
+        for (int sl = 0; sl < SLOTS; ++sl) nv_min = min(nv_min, nv[rt][sl]);
+    nv_min = (int)wave_allreduce((uint32_t)nv_min, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
     auto filter_tile = [&](int c0, const typename MM::F* bf) {
         const int c = c0 + rho;
+        const bool full = c0 + TILE <= nv_min;
         f32x4_t acc[FRT];
 #pragma unroll
         for (int rt = 0; rt < FRT; ++rt) acc[rt] = MM::mma(a[rt], bf);
@@ -1186,13 +1204,14 @@ __global__ __launch_bounds__(WAVES * 64) void index_filter_kernel(IdxParams p) {
 #pragma unroll
             for (int sl = 0; sl < SLOTS; ++sl) {
                 if (sl >= ns) break;
-                const bool ins = own[sl] && c < nv[rt][sl] && sc[sl] >= thr_f[rt][sl];
+                const bool ins = own[sl] && (full || c < nv[rt][sl]) && sc[sl] >= thr_f[rt][sl];
                 const unsigned long long msk = __ballot(ins);
                 if (msk == 0ull) continue;
                 const uint32_t gb = (uint32_t)(msk >> (16 * q4)) & 0xFFFFu;
                 if (ins) {
                     const int pos = cnt[rt][sl] + __popc(gb & below);
-                    if (pos < lcap) lst[rt][sl][pos] = make_uint2(fkey(sc[sl]), (uint32_t)c);
+                    // the raw float bits: the list pass turns them into keys
+                    if (pos < lcap) lst[rt][sl][pos] = make_uint2(__float_as_uint(sc[sl]), (uint32_t)c);
                 }
                 cnt[rt][sl] += __popc(gb);
             }
@@ -1271,8 +1290,9 @@ __global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
             for (int u = 0; u < 8; ++u) {
                 const int e = base + 128 * u + 2 * lane;
                 if (e < cnt) {
-                    *reinterpret_cast<uint2*>(wb.keys + e) = make_uint2(v[u].x, v[u].z);
-                    n_ge += (v[u].x >= tau) + (e + 1 < cnt && v[u].z >= tau);
+                    const uint32_t k0 = fkey(__uint_as_float(v[u].x)), k1 = fkey(__uint_as_float(v[u].z));
+                    *reinterpret_cast<uint2*>(wb.keys + e) = make_uint2(k0, k1);
+                    n_ge += (k0 >= tau) + (e + 1 < cnt && k1 >= tau);
                 }
             }
         }
