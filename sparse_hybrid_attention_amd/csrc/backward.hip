@@ -18,18 +18,35 @@
 // Window keys belong to every branch present; HCA entries to the HCA branch;
 // selected CSA entries to the CSA branch.
 //
-// Kernels (float32 arithmetic; four lanes per row, each holding a quarter of
-// the head dim, so a dot product is four partial sums and two in-register
-// exchanges; a wave holds 16 rows and walks the union of their key or query
-// sets in lockstep, masking per row):
+// Two forms of the query and key sides.
+//
+// Coefficient form (bf16 inputs, CSA caches up to 4096 entries, workspace for
+// 8 bytes per (row, head, key) pair): the contractions run on MFMA.
+//   1'. selection bitmaps of every row with per-word prefix counts (the rank
+//       of an entry in its row's selection);
+//   1'. query side: per 64 rows of a (sequence, head), K / V chunks of every
+//       key source staged in LDS; pass 1 takes each branch's LSE and D_b,
+//       pass 2 computes S, dP and dS^T on MFMA, accumulates dQ^T += K^T dS^T
+//       (dS split into two bf16 parts) and writes (dS, sum_b w_b P_b) of every
+//       (row, head, key) as the key sides' coefficients;
+//   3'./4'. key sides: dK^T = Q^T dS and dV^T = dO^T (w P) on MFMA from LDS-
+//       staged Q / dO chunks, per raw row, HCA entry (row ranges with fixed-
+//       order partial sums) and CSA entry.
+// VALU form (every other case; also the reference the coefficient form is
+// checked against): four lanes per row, each holding a quarter of the head
+// dim, a dot product being four partial sums and two in-register exchanges;
+// a wave holds 16 rows and walks the union of their key or query sets in
+// lockstep, masking per row:
 //   1. query side: per (row, head) one pass for LSE_b and D_b (an online
 //      softmax carrying a scalar accumulator of dpo), a second for dq;
-//   2. block weights P = softmax(z) of every compression logit tensor;
 //   3. key side, compressed entries: HCA entries over the query rows that see
 //      them, CSA entries over the rows whose selection holds them (found with
 //      one coalesced read of the row's selection and a wave-wide OR);
-//   4. key side, raw rows over their window band, plus the compressed-cache
-//      gradients routed back through the block merge (dx = P_i dxc);
+//   4. key side, raw rows over their window band.
+// Both forms share:
+//   2. block weights P = softmax(z) of every compression logit tensor;
+//   the compressed-cache gradients routed back through the block merge
+//      (dx = P_i dxc) in the raw-row key side's epilogue;
 //   5. logit gradients: dP_i = sum over blocks of dxc . x_i as per-chunk
 //      partials, then dz_i = P_i (dP_i - sum_l P_l dP_l) summing the partials
 //      in a fixed order;
