@@ -170,6 +170,53 @@ def test_gather_with_no_cache_entries():
     check(inp, hca, csa, got, what="empty CSA cache")
 
 
+def with_holes(idx, N, seed):
+    """The selection with entries knocked out mid-row: -1 (padding), other
+    negative values and values >= N, all of which the kernel ignores (the
+    attention's contract: only entries with 0 <= idx < N_csa are attended).
+    Returns (what the kernel gets, what the oracle gets: the same rows with
+    every ignored entry as -1)."""
+    rng = np.random.default_rng(seed)
+    bad = idx.copy()
+    u = rng.random(idx.shape)
+    bad[u < 0.2] = -1
+    bad[(u >= 0.2) & (u < 0.25)] = -7
+    bad[(u >= 0.25) & (u < 0.3)] = N + 3
+    bad[(u >= 0.3) & (u < 0.32)] = np.iinfo(np.int32).max
+    clean = bad.copy()
+    clean[(clean < 0) | (clean >= N)] = -1
+    return bad, clean
+
+
+@pytest.mark.parametrize("case", ["gather", "dense_masked", "gather_d64"])
+def test_csa_entries_outside_the_cache_are_ignored(case):
+    # prefill: the per-wave gather (G = 8) and the selection bitmap of the
+    # dense-masked stream (G = 1, small cache)
+    lib()
+    if case == "gather":
+        inp, hca, csa = prefill_case("csa_prefill_128k", seed=14, T=1536, k=72)
+    elif case == "gather_d64":
+        inp, hca, csa = prefill_case("csa_prefill_128k", seed=16, T=1024, d=64, k=40)
+    else:
+        inp, hca, csa = prefill_case("tinyr2_bf16", seed=15, B=1, T=700, k=24)
+    kc, vc, idx = csa
+    bad, clean = with_holes(idx, kc.shape[1], seed=20)
+    got = gpu_attn(inp, hca, (kc, vc, bad))
+    rows = sample_rows(1, inp["cfg"]["T"], inp["cfg"]["W"], n=48) if case != "dense_masked" else None
+    check(inp, hca, (kc, vc, clean), got, rows=rows, what=f"holes {case}")
+
+
+def test_decode_split_entries_outside_the_cache_are_ignored():
+    lib()
+    inp, hca, csa = decode_case(seed=17, B=3, N_csa=4096, N_hca=512, k=200)
+    kc, vc, idx = csa
+    bad, clean = with_holes(idx, kc.shape[1], seed=21)
+    got = gpu_attn(inp, hca, (kc, vc, bad), q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"],
+                   k_raw="k_win", v_raw="v_win")
+    check(inp, hca, (kc, vc, clean), got, q_pos0=inp["q_pos0"], raw_pos0=inp["raw_pos0"], k_raw="k_win",
+          v_raw="v_win", what="decode split holes")
+
+
 def decode_case(seed=0, **over):
     inp = synth.make_inputs("decode_1m", seed=seed, **over)
     cfg = inp["cfg"]
