@@ -966,6 +966,14 @@ def main():
             ceil = max(peaks["gather_256B_rows_GBps"].values())
             roof["gather"].update(ceiling_GBps=ceil, frac=round(g / ceil, 4),
                                   ceiling="best measured rate of random 256-byte row gathers (measured_peaks)")
+            if roof.get("traffic"):
+                # the part of the gather L2 does not serve: the measured bytes
+                # past L2 per launch against the probe's rate on a 64 MiB
+                # table read by every XCD (whose reads almost never hit L2)
+                t = roof["traffic"] / (ms * 1e-3) / 1e9
+                c64 = peaks["gather_256B_rows_GBps"]["llc_64MiB"]
+                roof["gather"].update(past_l2_GBps=round(t, 1), past_l2_ceiling_GBps=c64,
+                                      frac_past_l2=round(t / c64, 4))
 
     line = {
         "metric": METRIC,
