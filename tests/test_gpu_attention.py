@@ -152,6 +152,17 @@ def test_csa_gather_many_heads_per_group():
     check(inp, hca, csa, got, rows=sample_rows(1, 1024, 128, n=48), what="G=16 gather")
 
 
+@pytest.mark.parametrize("H,Hkv,T,k", [(16, 4, 2048, 37), (8, 4, 2048, 30), (4, 4, 1024, 13)])
+def test_csa_gather_several_queries_per_wave(H, Hkv, T, k):
+    # G = 4, 2, 1: a wave's 16 columns hold 4, 8 or 16 queries, and it walks
+    # each query's selection in turn (k not a multiple of 4 takes the gather
+    # instead of the dense-masked stream; ragged last chunks)
+    lib()
+    inp, hca, csa = prefill_case("csa_prefill_128k", seed=18, T=T, H=H, Hkv=Hkv, k=k)
+    got = gpu_attn(inp, hca, csa)
+    check(inp, hca, csa, got, rows=sample_rows(1, T, 128, n=48), what=f"gather G={H // Hkv}")
+
+
 def test_csa_gather_d64():
     # the direct-to-LDS gather tiles at d = 64 (8 rows per wave load)
     lib()
