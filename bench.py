@@ -190,7 +190,8 @@ def load_probes():
 
 def measure_peaks(torch):
     """Measured device ceilings to read the roofline fractions against: a
-    1 GiB device-to-device copy (bytes read + written per second), the bf16
+    1 GiB device-to-device copy (bytes read + written per second), a 1 GiB
+    streaming read (torch's float32 sum), the bf16
     MFMA issue rate of a loop of independent MFMAs, and the rate of random
     256-byte row gathers from a table that fits the last-level cache (64 MiB,
     the size of the 128K prefill's CSA cache) and from one that does not
@@ -212,6 +213,9 @@ def measure_peaks(torch):
         return best
     copy_gbs = 2.0 * n / (best_of(lambda: b.copy_(a)) * 1e-3) / 1e9
     del b
+    # a streaming read of the same 1 GiB (a float32 sum: 4 bytes read per 4
+    # bytes, a few kilobytes written), the ceiling of read-bound passes
+    read_gbs = n / (best_of(lambda: a.view(torch.float32).sum()) * 1e-3) / 1e9
     probes = load_probes()
     wgs, iters = 2048, 2048
     sink = torch.empty(16384 * 256, dtype=torch.float32, device="cuda:0")
@@ -236,10 +240,12 @@ def measure_peaks(torch):
                                                             stream)), 3)
         gather[name] = round(reads * 256 / (ms * 1e-3) / 1e9, 1)
     del a
-    return {"copy_GBps": round(copy_gbs, 1), "mfma_bf16_TFLOPs": max(rates.values()),
+    return {"copy_GBps": round(copy_gbs, 1), "read_GBps": round(read_gbs, 1),
+            "mfma_bf16_TFLOPs": max(rates.values()),
             "mfma_bf16_TFLOPs_by_shape": rates,
             "gather_256B_rows_GBps": gather,
-            "method": "best of 4 (gathers: 3): 1 GiB device copy (read + write bytes); 2048 workgroups x 2048 "
+            "method": "best of 4 (gathers: 3): 1 GiB device copy (read + write bytes); 1 GiB streaming read "
+                      "(torch's float32 sum); 2048 workgroups x 2048 "
                       "rounds of independent bf16 MFMAs per wave (8 x 16x16x32 or 4 x 32x32x16); 2^26 reads of "
                       "random 256-byte rows from a 64 MiB or 1 GiB table (4slices: each XCD reads one quarter, "
                       "as one KV head per pair of XCDs does in the attention), 8192 workgroups, 8 (or 16) reads "
@@ -957,6 +963,11 @@ def main():
     if peaks is not None and (roof["unit"] == "GB/s" or dtype == "bf16"):
         roof["measured_peak"] = peaks["copy_GBps"] if roof["unit"] == "GB/s" else peaks["mfma_bf16_TFLOPs"]
         roof["frac_of_measured"] = round(roof["achieved"] / roof["measured_peak"], 4)
+        if roof["unit"] == "GB/s":
+            # read-dominated passes (the decode indexer streams its keys) against
+            # the measured streaming-read rate
+            roof["measured_read_peak"] = peaks["read_GBps"]
+            roof["frac_of_measured_read"] = round(roof["achieved"] / peaks["read_GBps"], 4)
     if "gathered_bytes" in a:
         # the gathered CSA rows: bytes the kernel reads from L2 / MALL per launch
         # against the measured random-row gather rate of a cache-resident table
