@@ -451,8 +451,11 @@ SHATTN_API int rope_apply(void* x, const int64_t* pos, int64_t rows, int32_t hea
  *   codes  : [ceil(n / 2)] uint8, DEVICE memory, written: element 2j in the low
  *            nibble of byte j, element 2j + 1 in the high nibble (0 past n)
  *   params : [2] float32, DEVICE memory, 4-byte aligned, written: (min, step);
- *            it doubles as the scratch of the min / max reduction, so a second
- *            call must not use the same params while one is in flight
+ *            it doubles as the scratch of the min / max reduction, and the
+ *            first four bytes of codes (when codes is 4-byte aligned and holds
+ *            at least four bytes) hold a workgroup counter until the codes are
+ *            written, so a second call must not use the same params or codes
+ *            while one is in flight
  * cache_dequant4:
  *   out[i] = code_i * step + min, the product exact and the sum rounded to
  *   float64, then rounded once (nearest even) to dtype; codes / params as

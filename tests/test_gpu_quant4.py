@@ -19,6 +19,10 @@ pytestmark = pytest.mark.gpu
     (binding.DTYPE_F32, 1001, None),
     (binding.DTYPE_F32, 1, None),
     (binding.DTYPE_BF16, 77, 1.5),
+    (binding.DTYPE_BF16, 9, None),                   # one vector and a ragged element
+    (binding.DTYPE_BF16, 7, None),                   # four code bytes, no whole vector
+    (binding.DTYPE_F32, 4 * 4099, None),              # whole vectors only
+    (binding.DTYPE_F32, 6, None),                     # three code bytes: no counter word
 ])
 def test_quant4_matches_oracle(dtype, n, constant):
     lib()
@@ -68,3 +72,27 @@ def test_dequant4_rounds_once():
         want = O.dequant4(packed, mn, st, 16, dtype)
         assert np.array_equal(host(out).view(np.uint8), want.view(np.uint8)), (dtype, host(out), want)
     assert O.dequant4(packed, mn, st, 16, binding.DTYPE_BF16)[1] == 0x3F81   # 1 + 2^-7
+
+
+@pytest.mark.parametrize("dtype", [binding.DTYPE_BF16, binding.DTYPE_F32])
+def test_quant4_unaligned_buffers(dtype):
+    # x one element past a 16-byte boundary and codes / out one byte or one
+    # element off their vector alignment: the element-wise paths and the
+    # separate (min, step) launch, bit-exact with the oracle all the same
+    lib()
+    n = 3001
+    x = synth.make_quant(n=n + 1, dtype=dtype, seed=5)
+    xd = dev(x)[1:]
+    want_codes, mn, st = O.quant4(x[1:], dtype)
+    nb = (n + 1) // 2
+    cbuf = torch.zeros(nb + 1, dtype=torch.uint8, device=xd.device)
+    codes = cbuf[1:]
+    params = torch.empty(2, dtype=torch.float32, device=xd.device)
+    binding.cache_quant4(xd, codes=codes, params=params)
+    assert tuple(host(params)) == (mn, st)
+    assert np.array_equal(host(codes), want_codes)
+    outbuf = torch.empty(n + 1, dtype=xd.dtype, device=xd.device)
+    out = outbuf[1:]
+    binding.cache_dequant4(codes, params, out)
+    want = O.dequant4(want_codes, mn, st, n, dtype)
+    assert np.array_equal(host(out).view(np.uint8), want.view(np.uint8))
