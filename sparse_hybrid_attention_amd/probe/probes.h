@@ -51,6 +51,19 @@ SHATTN_PROBE_API int shattn_probe_gather(const void* table, int64_t nrows, int32
                                          int32_t slices, int64_t n, int32_t depth, int32_t workgroups,
                                          uint32_t* sink, void* stream);
 
+/*
+ * Streaming read throughput over `bytes` bytes (a multiple of 2048) in 2 KB
+ * tiles of 16 rows of 128 bytes, each lane keeping `depth` tiles' two 16-byte
+ * loads in flight.  mode bit 0: lane pattern of an MFMA operand load (lane l
+ * reads row l % 16, piece l / 16 of the row's first and second 64 bytes, so
+ * one load touches 16 rows) instead of 1 KB of consecutive bytes per load;
+ * mode bit 1: each wave reads one contiguous run of tiles instead of every
+ * W-th tile (W waves in the grid).  sink: uint32 [workgroups * 256], written.
+ * Supported: mode 0..3, depth in {1, 2, 4, 8}, 1 <= workgroups <= 65536.
+ */
+SHATTN_PROBE_API int shattn_probe_stream(const void* buf, int64_t bytes, int32_t mode, int32_t depth,
+                                         int32_t workgroups, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,6 +107,56 @@ __global__ __launch_bounds__(kProbeThreads) void gather_probe_kernel(const char*
     sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
 }
 
+// Streaming read of whole 2 KB tiles (16 rows of 128 bytes).  A wave reads a
+// tile with two 16-byte loads per lane, in one of two lane patterns: `mfma`
+// false, each load covers 1 KB of consecutive bytes; `mfma` true, the pattern
+// of an MFMA operand load of 16 rows of 64 bf16 (lane l reads row l % 16,
+// 16-byte piece l / 16 of the row's first and then second 64 bytes), so each
+// load touches all 16 rows.  `segments` false: wave w reads tiles w, w + W,
+// w + 2W, ... (W waves in the grid); true: each wave reads one contiguous run
+// of tiles, as a pass that gives each wave its own range of rows does.  A lane
+// keeps DEPTH tiles' loads in flight.
+template <int DEPTH, bool MFMA, bool SEG>
+__global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const char* __restrict__ buf, long long ntiles,
+                                                                     uint32_t* sink) {
+    const int lane = threadIdx.x & 63;
+    const long long wave = ((long long)blockIdx.x * kProbeThreads + threadIdx.x) >> 6;
+    const long long nwaves = ((long long)gridDim.x * kProbeThreads) >> 6;
+    int off0, off1;
+    if (MFMA) {
+        off0 = (lane & 15) * 128 + 16 * (lane >> 4);
+        off1 = off0 + 64;
+    } else {
+        off0 = 16 * lane;
+        off1 = 1024 + 16 * lane;
+    }
+    long long t0, tend, tstep;
+    if (SEG) {
+        const long long per = (ntiles + nwaves - 1) / nwaves;
+        t0 = wave * per;
+        tend = t0 + per < ntiles ? t0 + per : ntiles;
+        tstep = 1;
+    } else {
+        t0 = wave;
+        tend = ntiles;
+        tstep = nwaves;
+    }
+    uint32_t acc = 0u;
+    for (long long t = t0; t < tend; t += tstep * DEPTH) {
+        uint4 v[DEPTH][2];
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+            const long long tt = t + (long long)u * tstep;
+            const char* base = buf + (tt < tend ? tt : t0) * 2048ll;
+            v[u][0] = *reinterpret_cast<const uint4*>(base + off0);
+            v[u][1] = *reinterpret_cast<const uint4*>(base + off1);
+        }
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) acc ^= v[u][0].x ^ v[u][0].w ^ v[u][1].y ^ v[u][1].z;
+    }
+    sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? 0 : -4; }
 
 }  // namespace
@@ -143,5 +193,34 @@ extern "C" int shattn_probe_gather(const void* table, int64_t nrows, int32_t row
         case 16: hipLaunchKernelGGL(gather_probe_kernel<16>, g, b, 0, s, t, srows, row_bytes, row_stride, slices, n, sink); break;
         default: return -1;
     }
+    return launched();
+}
+
+extern "C" int shattn_probe_stream(const void* buf, int64_t bytes, int32_t mode, int32_t depth, int32_t workgroups,
+                                   uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes < 2048 || (bytes % 2048) || mode < 0 || mode > 3 || workgroups < 1 ||
+        workgroups > 65536 || (reinterpret_cast<uintptr_t>(buf) & 15))
+        return -1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const char* b = reinterpret_cast<const char*>(buf);
+    const long long nt = bytes / 2048;
+    const dim3 g((unsigned)workgroups), bl(kProbeThreads);
+#define SHATTN_STREAM_CASE(D)                                                                         \
+    case D:                                                                                           \
+        switch (mode) {                                                                               \
+            case 0: hipLaunchKernelGGL((stream_probe_kernel<D, false, false>), g, bl, 0, s, b, nt, sink); break; \
+            case 1: hipLaunchKernelGGL((stream_probe_kernel<D, true, false>), g, bl, 0, s, b, nt, sink); break;  \
+            case 2: hipLaunchKernelGGL((stream_probe_kernel<D, false, true>), g, bl, 0, s, b, nt, sink); break;  \
+            default: hipLaunchKernelGGL((stream_probe_kernel<D, true, true>), g, bl, 0, s, b, nt, sink); break;  \
+        }                                                                                             \
+        break;
+    switch (depth) {
+        SHATTN_STREAM_CASE(1)
+        SHATTN_STREAM_CASE(2)
+        SHATTN_STREAM_CASE(4)
+        SHATTN_STREAM_CASE(8)
+        default: return -1;
+    }
+#undef SHATTN_STREAM_CASE
     return launched();
 }
