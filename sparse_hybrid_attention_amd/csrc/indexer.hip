@@ -1822,10 +1822,17 @@ int launch_idx(IdxPlan& pl, hipStream_t s) {
         return check_launch("csa_index_topk (empty)");
     }
     if (pl.dense) {
-        if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, false>), pl.lds))) return rc;
-        hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, false>), dim3((unsigned)pl.grid), dim3(WAVES * 64), pl.lds,
-                           s, pl.p);
-        return check_launch("csa_index_topk");
+        // the plan never gives Hi = 16 the dense form, and it is not compiled
+        // for it (no passing GPU test covers it)
+        if constexpr (HI == 16) {
+            return fail(SHATTN_EUNSUPPORTED, "csa_index_topk: no dense selection form at Hi=16");
+        } else {
+            if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, false>), pl.lds)))
+                return rc;
+            hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, false>), dim3((unsigned)pl.grid), dim3(WAVES * 64),
+                               pl.lds, s, pl.p);
+            return check_launch("csa_index_topk");
+        }
     }
     if (pl.longp) {
         hipLaunchKernelGGL((index_kmax_kernel<T, DI>), dim3((unsigned)pl.grid_kmax), dim3(256), 0, s, pl.p);
