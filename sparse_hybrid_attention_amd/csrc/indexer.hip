@@ -80,6 +80,8 @@ struct IdxParams {
     int kblk;           // entry blocks per sequence for kmax_part
     int sample_stride;  // sampled entries are 0, S, 2S, ... (S = sample_stride)
     int sample_j;       // the threshold is the sample_j-th largest sampled score
+    int list_mcap;      // band list capacity of the list selection pass
+    int list_lds_cap;   // list entries the list selection pass holds in LDS (<= list_cap)
 };
 
 // ----------------------------------------------------------- key encoding
@@ -1031,7 +1033,8 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             const int ns = (n + S - 1) / S;
             const float delta = p.err_c * qn[qw] * kmax_all;
             uint32_t thr = 0u, tau = 0u;   // 0: list every visible entry
-            if (n > p.list_cap && ns >= p.sample_j) {
+            // (a query whose whole visible set fits the list pass's LDS)
+            if (n > p.list_lds_cap && ns >= p.sample_j) {
                 int n_gt;
                 tau = radix_kth(keys_all + qw * np, ns, p.sample_j, hist, &n_gt);
                 thr = fkey(key_f(tau) - 2.0f * delta);
@@ -1262,18 +1265,19 @@ __global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
     const long long row = blockIdx.x;
     const long long b = row / p.Tq, i = row % p.Tq;
     const int lcap = p.list_cap;
-    // LDS: keys[lcap] hist[256] mex[mcap] mpos[mcap] mid[mcap]; entries stay in the list
+    const int kcap = p.list_lds_cap;   // <= lcap: longer lists fail over to the streaming kernel
+    // LDS: keys[kcap] hist[256] mex[list_mcap] mpos[list_mcap] mid[list_mcap]; entries stay in the list
     WaveBuf wb;
     wb.keys = reinterpret_cast<uint32_t*>(smem);
     wb.ids = nullptr;
-    wb.hist = reinterpret_cast<uint32_t*>(smem + 4ull * lcap);
-    wb.mex = reinterpret_cast<double*>(smem + 4ull * lcap + 1024);
-    wb.mpos = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 8ull * p.mcap);
-    wb.mid = reinterpret_cast<int32_t*>(smem + 4ull * lcap + 1024 + 12ull * p.mcap);
+    wb.hist = reinterpret_cast<uint32_t*>(smem + 4ull * kcap);
+    wb.mex = reinterpret_cast<double*>(smem + 4ull * kcap + 1024);
+    wb.mpos = reinterpret_cast<int32_t*>(smem + 4ull * kcap + 1024 + 8ull * p.list_mcap);
+    wb.mid = reinterpret_cast<int32_t*>(smem + 4ull * kcap + 1024 + 12ull * p.list_mcap);
     const long long nvq = n_visible(row_pos0(p, b) + i, p.W, p.m, p.N);
     const int k_eff = (int)std::min<long long>(p.k, nvq);
     const int cnt = p.list_cnt[row];
-    bool ok = cnt <= lcap;
+    bool ok = cnt <= kcap;
     if (ok) {
         // two (key, entry) pairs per lane and 16-byte load, eight loads in flight
         const uint32_t tau = p.row_tau[row];
@@ -1304,7 +1308,7 @@ __global__ __launch_bounds__(64) void index_list_final_kernel(IdxParams p) {
     wave_lds_sync();
     const T* qI = reinterpret_cast<const T*>(p.qI);
     const T* kI_b = reinterpret_cast<const T*>(p.kI) + b * (long long)p.N * DI;
-    final_select<T, HI, DI>(wb, ListIds{p.row_lists + row * lcap}, cnt, k_eff, p.k, p.row_delta[row], p.mcap,
+    final_select<T, HI, DI>(wb, ListIds{p.row_lists + row * lcap}, cnt, k_eff, p.k, p.row_delta[row], p.list_mcap,
                             qI + row * HI * DI, kI_b,
                             p.w + row * HI, p.idx + row * p.k);
 }
@@ -1762,7 +1766,10 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     const double r = (double)k / S;
     const int j = (int)std::ceil(r) + (int)std::ceil(5.0 * std::sqrt(r)) + 2;
     long long lcap = (long long)std::ceil(j * (double)S + 7.0 * std::sqrt((double)j) * S) + 64;
-    const long long lcap_fit = (kMaxLds - 1024 - 16ll * p.mcap - 16) / 4 / 64 * 64;
+    // the list pass keeps a short band list (an overflowing band is decided
+    // on float32 scores), so more of its one-wave workgroups share a CU
+    p.list_mcap = std::min(p.mcap, 64);
+    const long long lcap_fit = (kMaxLds - 1024 - 16ll * p.list_mcap - 16) / 4 / 64 * 64;
     lcap = std::min((lcap + 63) / 64 * 64, lcap_fit);
     p.sample_stride = S;
     p.sample_j = j;
@@ -1774,7 +1781,16 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     pl.grid_filter = (long long)B * p.nqt;
     pl.grid_kmax = (long long)B * p.kblk;
     pl.grid = rows;
-    pl.lds = (4ull * lcap + 1024 + 16ull * p.mcap + 15) / 16 * 16;
+    // the list pass holds lists of up to j S + 5.5 sqrt(j) S + 64 entries (the
+    // mean length plus 5.5 standard deviations) in LDS; a longer list takes the
+    // streaming kernel, whose one wave per such query then costs about a
+    // millisecond, so the margin keeps that out of unstructured inputs.  At
+    // the 128K CSA prefill (k 512, S 32, j 38) that is 2368 instead of 2688
+    // entries, and 14 instead of 12 of the pass's one-wave workgroups fit a CU.
+    long long kcap = (long long)std::ceil(j * (double)S + 5.5 * std::sqrt((double)j) * S) + 64;
+    kcap = std::min((kcap + 63) / 64 * 64, lcap);
+    p.list_lds_cap = (int)kcap;
+    pl.lds = (4ull * kcap + 1024 + 16ull * p.list_mcap + 15) / 16 * 16;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
     const size_t o_km = take((size_t)B * p.kblk * 4);
