@@ -131,7 +131,7 @@ def test_probe_library_is_separate(lib):
     probe_lib = os.path.join(os.path.dirname(binding.LIB_PATH), "libshattn_probe.so")
     header = os.path.join(ROOT, "sparse_hybrid_attention_amd", "probe", "probes.h")
     declared = set(re.findall(r"SHATTN_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(header).read()))
-    assert declared == {"shattn_probe_mfma", "shattn_probe_gather"}
+    assert declared == {"shattn_probe_mfma", "shattn_probe_gather", "shattn_probe_stream"}
     out = subprocess.run(["nm", "-D", "--defined-only", probe_lib], capture_output=True, text=True,
                          check=True).stdout
     assert {l.split()[-1] for l in out.splitlines() if " T " in l} == declared
@@ -235,6 +235,16 @@ def test_index_varlen_errors(lib):
     assert "q_pos" in err(lib)
     assert f(*args(ctypes.c_void_p(0x7F0000000004))) == binding.SHATTN_EINVAL
     assert f(*args(None, B=0)) == binding.SHATTN_OK     # nothing to do
+
+
+def test_index_part_errors(lib):
+    f = lib.csa_index_topk_part
+    args = lambda part, **kw: (P, P, P, P, kw.get("B", 2), 1, 64, 4, 64, 0, None, 4, 8, 8, 0, part, None, 0, None)
+    for part in (-1, 3):
+        assert f(*args(part)) == binding.SHATTN_EINVAL
+        assert "part" in err(lib)
+    assert f(*args(2, B=0)) == binding.SHATTN_OK       # nothing to do
+    assert f(*args(1, B=0)) == binding.SHATTN_OK
 
 
 def bwd(**kw):
