@@ -237,16 +237,6 @@ def test_index_varlen_errors(lib):
     assert f(*args(None, B=0)) == binding.SHATTN_OK     # nothing to do
 
 
-def test_index_part_errors(lib):
-    f = lib.csa_index_topk_part
-    args = lambda part, **kw: (P, P, P, P, kw.get("B", 2), 1, 64, 4, 64, 0, None, 4, 8, 8, 0, part, None, 0, None)
-    for part in (-1, 3):
-        assert f(*args(part)) == binding.SHATTN_EINVAL
-        assert "part" in err(lib)
-    assert f(*args(2, B=0)) == binding.SHATTN_OK       # nothing to do
-    assert f(*args(1, B=0)) == binding.SHATTN_OK
-
-
 def bwd(**kw):
     a = binding.BwdArgs()
     a.struct_size = ctypes.sizeof(binding.BwdArgs)
