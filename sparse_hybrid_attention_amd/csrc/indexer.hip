@@ -1738,18 +1738,21 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     }
     // sampling pass: stride S (a power of two) with at most kSampleMax sampled
     // entries per query whose keys fit the dense kernel's LDS
-    auto sample_wave = [&](int q, int np) { return (4ull * q * np + 1024 + 12ull * p.mcap + 4ull * q + 15) / 16 * 16; };
+    // (the sampling pass keeps no band list: its LDS is keys, histogram and
+    // query norms, and its launch runs with mcap = 0)
+    auto sample_wave = [&](int q, int np) { return (4ull * q * np + 1024 + 4ull * q + 15) / 16 * 16; };
     int S = 1, np = 0;
     for (;; S *= 2) {
         np = ((N + S - 1) / S + TILE - 1) / TILE * TILE;
         if (np <= kSampleMax && WAVES * sample_wave(qpt, np) <= (size_t)kMaxLds) break;
     }
     {
-        int qpw = 4 * qpt;
+        // one row tile per wave (the cooperative form: each key tile feeds the
+        // four waves' row tiles) keeps the most workgroups per CU: at the 128K
+        // CSA prefill two instead of one.  Hi = 16 keeps four row tiles per
+        // wave (the form its tests cover).
+        int qpw = Hi == 16 ? 4 * qpt : qpt;
         while (qpw > qpt && WAVES * sample_wave(qpw, np) > (size_t)kMaxLds) qpw -= qpt;
-        // Hi = 16 keeps four row tiles per wave (the form its tests cover)
-        while (Hi != 16 && qpw > qpt && rows > 0 && (rows + (long long)WAVES * qpw - 1) / (WAVES * qpw) < 1024)
-            qpw -= qpt;
         pl.ls.qpw = qpw;
         pl.ls.cap = np;
         pl.ls.wave_stride = (int)sample_wave(qpw, np);
@@ -1855,8 +1858,10 @@ int launch_idx(IdxPlan& pl, hipStream_t s) {
         if ((rc = check_launch("csa_index_topk (kmax)"))) return rc;
         if ((rc = allow_lds(reinterpret_cast<const void*>(&index_dense_kernel<T, HI, DI, true>), pl.ls.lds)))
             return rc;
+        IdxParams ps = with_launch(pl.p, pl.ls);
+        ps.mcap = 0;   // no band list in the sampling pass's LDS
         hipLaunchKernelGGL((index_dense_kernel<T, HI, DI, true>), dim3((unsigned)pl.ls.grid), dim3(WAVES * 64),
-                           pl.ls.lds, s, with_launch(pl.p, pl.ls));
+                           pl.ls.lds, s, ps);
         if ((rc = check_launch("csa_index_topk (sample)"))) return rc;
         hipLaunchKernelGGL((index_filter_kernel<T, HI, DI>), dim3((unsigned)pl.grid_filter), dim3(WAVES * 64), 0, s,
                            pl.p);
