@@ -1513,17 +1513,40 @@ __global__ __launch_bounds__(kFinalThreads) void index_split_final_kernel(IdxPar
     __syncthreads();
     const int total = s_total;
     if (!s_over && total <= cap) {
-        // ---- parallel gather: entry t belongs to the chunk whose offset range holds it
-        for (int t = tid; t < total; t += kFinalThreads) {
-            int lo = 0, hi = p.nchunks - 1;   // last chunk with offs[j] <= t
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (offs[mid] <= t) lo = mid;
-                else hi = mid - 1;
+        // ---- parallel gather: entry t belongs to the chunk whose offset range
+        // holds it; each thread places four entries per round, their eight
+        // loads in flight together
+        constexpr int GU = 4;
+        for (int t0 = tid; t0 < total; t0 += GU * kFinalThreads) {
+            long long src[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int t = t0 + u * kFinalThreads;
+                int lo = 0, hi = p.nchunks - 1;   // last chunk with offs[j] <= t
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (offs[mid] <= t) lo = mid;
+                    else hi = mid - 1;
+                }
+                src[u] = t < total ? (row * p.nchunks + lo) * (long long)p.list_cap + (t - offs[lo]) : -1;
             }
-            const long long src = (row * p.nchunks + lo) * (long long)p.list_cap + (t - offs[lo]);
-            wb.keys[t] = p.lists[src];
-            wb.ids[t] = p.list_idx[src];
+            uint32_t kv[GU];
+            int32_t iv[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                if (src[u] >= 0) {
+                    kv[u] = p.lists[src[u]];
+                    iv[u] = p.list_idx[src[u]];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int t = t0 + u * kFinalThreads;
+                if (src[u] >= 0) {
+                    wb.keys[t] = kv[u];
+                    wb.ids[t] = iv[u];
+                }
+            }
         }
         __syncthreads();
         if (wave == 0)
