@@ -286,6 +286,61 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int cnt, int
     return prefix;
 }
 
+// k-th largest (1 <= kk <= cnt) of the 16-bit keys keys[0..cnt): two passes of
+// 8-bit digits.  keys is 16-byte aligned and readable up to cnt rounded up to
+// a multiple of 8.
+__device__ __forceinline__ uint32_t radix_kth16(const uint16_t* keys, int cnt, int kk, uint32_t* hist) {
+    const int lane = __lane_id();
+    uint32_t prefix = 0u;
+    int want = kk;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 8 : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+        wave_lds_sync();
+        for (int e0 = 8 * lane; e0 < cnt; e0 += 512) {
+            const uint4 v = *reinterpret_cast<const uint4*>(keys + e0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t key = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+                if (e0 + j < cnt && (pass == 0 || (key >> 8) == prefix)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+        }
+        wave_lds_sync();
+        // the bin holding the want-th largest key, bins scanned from the top
+        const uint32_t c0 = hist[lane * 4 + 0], c1 = hist[lane * 4 + 1];
+        const uint32_t c2 = hist[lane * 4 + 2], c3 = hist[lane * 4 + 3];
+        const int mine = (int)(c0 + c1 + c2 + c3);
+        const int incl = wave_incl_scan(mine);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        const int suf = total - incl + mine;   // bins of this lane and above
+        const int above = suf - mine;
+        int bin = -1, cnt_above = 0;
+        if (above < want && want <= suf) {
+            int acc = above;
+            if (acc + (int)c3 >= want) { bin = lane * 4 + 3; cnt_above = acc; }
+            else {
+                acc += c3;
+                if (acc + (int)c2 >= want) { bin = lane * 4 + 2; cnt_above = acc; }
+                else {
+                    acc += c2;
+                    if (acc + (int)c1 >= want) { bin = lane * 4 + 1; cnt_above = acc; }
+                    else { acc += c1; bin = lane * 4 + 0; cnt_above = acc; }
+                }
+            }
+        }
+        const unsigned long long who = __ballot(bin >= 0);
+        const int src = __ffsll((long long)who) - 1;
+        prefix = pass == 0 ? (uint32_t)__builtin_amdgcn_readlane(bin, src)
+                           : (prefix << 8) | (uint32_t)__builtin_amdgcn_readlane(bin, src);
+        want -= __builtin_amdgcn_readlane(cnt_above, src);
+        wave_lds_sync();
+    }
+    return prefix;
+}
+
 // Stable in-place compaction: keep entries with key >= lo.  Returns new count.
 __device__ __noinline__ int compact_ge(uint32_t* keys, int32_t* ids, int cnt, uint32_t lo) {
     const int lane = __lane_id();
@@ -886,12 +941,16 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4;
     const int qpw = p.qpw, np = p.cap, mcap = p.mcap;   // cap = keys per query (>= N)
     const int RT = qpw / QPT;
+    // sampled scores only estimate a threshold (any value is valid there, it
+    // only sets the list lengths), so the sampling pass keeps the upper 16
+    // bits of each order-preserving key: half the LDS per sample
+    constexpr int KB = SAMPLE ? 2 : 4;   // LDS bytes per key
     char* base = smem + (size_t)wave * p.wave_stride;
     uint32_t* keys_all = reinterpret_cast<uint32_t*>(base);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(base + 4ull * qpw * np);
-    double* mex = reinterpret_cast<double*>(base + 4ull * qpw * np + 1024);
-    int32_t* mpos = reinterpret_cast<int32_t*>(base + 4ull * qpw * np + 1024 + 8ull * mcap);
-    float* qn = reinterpret_cast<float*>(base + 4ull * qpw * np + 1024 + 12ull * mcap);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(base + (size_t)KB * qpw * np);
+    double* mex = reinterpret_cast<double*>(base + (size_t)KB * qpw * np + 1024);
+    int32_t* mpos = reinterpret_cast<int32_t*>(base + (size_t)KB * qpw * np + 1024 + 8ull * mcap);
+    float* qn = reinterpret_cast<float*>(base + (size_t)KB * qpw * np + 1024 + 12ull * mcap);
 
     // later queries (more visible entries) first: the light work runs last
     const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
@@ -909,8 +968,9 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
     const int NRT = coop ? WAVES : RT;   // row tiles this wave scores
     auto rt_q0 = [&](int rt) { return coop ? (qt * WAVES + rt) * qpw : q0 + rt * QPT; };
     auto rt_has = [&](int rt, int ql) { return rt < NRT && (coop ? ql < qpw : rt * QPT + ql < qpw); };
-    auto rt_keys = [&](int rt) {
-        return coop ? reinterpret_cast<uint32_t*>(smem + (size_t)rt * p.wave_stride) : keys_all + rt * QPT * np;
+    auto rt_keys = [&](int rt) {   // (in key units of KB bytes)
+        return coop ? reinterpret_cast<char*>(smem + (size_t)rt * p.wave_stride)
+                    : reinterpret_cast<char*>(base) + (size_t)KB * rt * QPT * np;
     };
 
     typename MM::F a[MAX_RT][MM::KS];
@@ -969,11 +1029,16 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             int qs[4];
             bool own[4];
             const int ns = tile_scores<HI>(acc, wr[rt], q4, sc, qs, own);
-            uint32_t* kd = rt_keys(rt);
+            char* kd = rt_keys(rt);
 #pragma unroll
             for (int sl = 0; sl < SLOTS; ++sl) {
                 if (sl >= ns) break;
-                if (own[sl] && rt_has(rt, qs[sl]) && c < np) kd[qs[sl] * np + c] = fkey(sc[sl]);
+                if (own[sl] && rt_has(rt, qs[sl]) && c < np) {
+                    if constexpr (SAMPLE)
+                        reinterpret_cast<uint16_t*>(kd)[qs[sl] * np + c] = (uint16_t)(fkey(sc[sl]) >> 16);
+                    else
+                        reinterpret_cast<uint32_t*>(kd)[qs[sl] * np + c] = fkey(sc[sl]);
+                }
             }
         }
     };
@@ -1013,7 +1078,7 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
         float km = 0.f;
         for (int w = 0; w < WAVES; ++w)
             km = fmaxf(km, __uint_as_float(*reinterpret_cast<const uint32_t*>(smem + (size_t)w * p.wave_stride +
-                                                                             4ull * qpw * np)));
+                                                                             (size_t)KB * qpw * np)));
         kmax2 = km;
         __syncthreads();
     } else {
@@ -1035,8 +1100,9 @@ __global__ __launch_bounds__(WAVES * 64, (HI <= 4 && DI == 64) ? 4 : 1) void ind
             uint32_t thr = 0u, tau = 0u;   // 0: list every visible entry
             // (a query whose whole visible set fits the list pass's LDS)
             if (n > p.list_lds_cap && ns >= p.sample_j) {
-                int n_gt;
-                tau = radix_kth(keys_all + qw * np, ns, p.sample_j, hist, &n_gt);
+                // the sample_j-th largest truncated key, as a full key with
+                // its low 16 bits zero: at most the sampled score itself
+                tau = radix_kth16(reinterpret_cast<const uint16_t*>(base) + qw * np, ns, p.sample_j, hist) << 16;
                 thr = fkey(key_f(tau) - 2.0f * delta);
             }
             if (lane == 0) {
@@ -1761,9 +1827,9 @@ int make_idx_plan(int B, int Tq, int N, int Hi, int d_idx, int64_t q_pos0, int m
     }
     // sampling pass: stride S (a power of two) with at most kSampleMax sampled
     // entries per query whose keys fit the dense kernel's LDS
-    // (the sampling pass keeps no band list: its LDS is keys, histogram and
-    // query norms, and its launch runs with mcap = 0)
-    auto sample_wave = [&](int q, int np) { return (4ull * q * np + 1024 + 4ull * q + 15) / 16 * 16; };
+    // (the sampling pass keeps no band list: its LDS is 16-bit keys,
+    // histogram and query norms, and its launch runs with mcap = 0)
+    auto sample_wave = [&](int q, int np) { return (2ull * q * np + 1024 + 4ull * q + 15) / 16 * 16; };
     int S = 1, np = 0;
     for (;; S *= 2) {
         np = ((N + S - 1) / S + TILE - 1) / TILE * TILE;
