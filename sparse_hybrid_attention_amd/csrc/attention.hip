@@ -1518,11 +1518,28 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     // merge items [it0, it1) into (m, l, a): strided over the group, then across it
     auto merge = [&](int it0, int it1, float& m, float& l, float* a) {
         float pm = -INFINITY, pl = 0.f, pa[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int it = it0 + sub; it < it1; it += kCombineSub) {
-            const float* s = part(it);
-            const float4 ai = *reinterpret_cast<const float4*>(s + 4 + 4 * dq);
-            const float av[4] = {ai.x, ai.y, ai.z, ai.w};
-            fold_in(pm, pl, pa, s[0], s[1], av);
+        // four of this lane's items per round: their loads go out together,
+        // then they fold in item order
+        constexpr int U = 4;
+        for (int it = it0 + sub; it < it1; it += U * kCombineSub) {
+            float2 ml[U];
+            float4 ai[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int iu = it + u * kCombineSub;
+                if (iu < it1) {
+                    const float* s = part(iu);
+                    ml[u] = *reinterpret_cast<const float2*>(s);
+                    ai[u] = *reinterpret_cast<const float4*>(s + 4 + 4 * dq);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (it + u * kCombineSub < it1) {
+                    const float av[4] = {ai[u].x, ai[u].y, ai[u].z, ai[u].w};
+                    fold_in(pm, pl, pa, ml[u].x, ml[u].y, av);
+                }
+            }
         }
 #pragma unroll
         for (int off = 1; off < kCombineSub; off <<= 1) {
