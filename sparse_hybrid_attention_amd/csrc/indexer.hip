@@ -1182,9 +1182,19 @@ __host__ __device__ constexpr int filter_min_blocks(bool f32, int hi, int di) {
     return (!f32 && di == 64 && (hi == 4 || hi == 8)) ? 4 : 1;
 }
 
-// L2: no LDS; each wave scores FRT row tiles of queries against all their
-// visible entries (MFMA tiles as above) and appends the entries that pass the
-// row's threshold to the row's list in global memory.
+// L2: each wave scores FRT row tiles of queries against all their visible
+// entries (MFMA tiles as above) and appends the entries that pass the row's
+// threshold to the row's list in global memory.  For bf16 keys of 64
+// dimensions the four waves of a workgroup (consecutive queries) share each
+// key tile: groups of four tiles are staged in LDS (double-buffered, the next
+// group's global loads in flight while the current one is scored), so each
+// key row is read from L2 once per 64 queries instead of once per 16.  Other
+// forms load their key tiles per wave into registers.
+template <typename T, int DI>
+__host__ __device__ constexpr bool filter_shared_tiles() {
+    return std::is_same<T, bf16_t>::value && DI == 64;
+}
+
 template <typename T, int HI, int DI>
 __global__ __launch_bounds__(WAVES * 64, filter_min_blocks(std::is_same<T, float>::value, HI, DI))
 void index_filter_kernel(IdxParams p) {
@@ -1197,7 +1207,10 @@ void index_filter_kernel(IdxParams p) {
     const int qt = p.nqt - 1 - (int)(blockIdx.x % p.nqt);
     const int b = blockIdx.x / p.nqt;
     const int q0 = (qt * WAVES + wave) * QPW;
-    if (q0 >= p.Tq) return;
+    constexpr bool SHARED = filter_shared_tiles<T, DI>();
+    // with shared key tiles every wave takes part in the loads and barriers
+    // (a wave past the last query has no visible entries and scores nothing)
+    if (!SHARED && q0 >= p.Tq) return;
     const T* qI = reinterpret_cast<const T*>(p.qI);
     const T* kI_b = reinterpret_cast<const T*>(p.kI) + (long long)b * p.N * DI;
     const int lcap = p.list_cap;
@@ -1286,25 +1299,82 @@ void index_filter_kernel(IdxParams p) {
             }
         }
     };
-    constexpr int PF = 2;
-    typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
-    auto group = [&](int g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
-        const int g1 = g0 + PF * TILE;
-        if (g1 < nv_max) {
+    if constexpr (SHARED) {
+        // LDS groups of GT key tiles, rows of DI bf16 (8 pieces of 16 bytes);
+        // piece j of row r sits at slot j ^ (r & 7), so the 8 lanes of one
+        // operand read (rows rho, one piece) hit distinct banks
+        constexpr int GT = 4, GROWS = GT * TILE, PIECES = DI / 8;
+        constexpr int LPT = GROWS * PIECES / (WAVES * 64);   // 16-byte loads per thread per group
+        static_assert(PIECES == 8 && LPT * WAVES * 64 == GROWS * PIECES, "shared key tiles: bf16, d_idx 64");
+        __shared__ __attribute__((aligned(16))) uint4 kt[2][GROWS * PIECES];
+        __shared__ int wg_nv[WAVES];
+        if (lane == 0) wg_nv[wave] = nv_max;
+        __syncthreads();
+        const int nv_wg = max(max(wg_nv[0], wg_nv[1]), max(wg_nv[2], wg_nv[3]));
+        const int ngroups = (nv_wg + GROWS - 1) / GROWS;
+        uint4 pre[LPT];
+        auto load_group = [&](int g) {
 #pragma unroll
-            for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+            for (int u = 0; u < LPT; ++u) {
+                const int e = u * WAVES * 64 + tid, r = e / PIECES, j = e % PIECES;
+                const int c = g * GROWS + r;
+                pre[u] = ld16(kI_b + (long long)(c < p.N ? c : 0) * DI + 8 * j);
+            }
+        };
+        auto store_group = [&](int slot) {
+#pragma unroll
+            for (int u = 0; u < LPT; ++u) {
+                const int e = u * WAVES * 64 + tid, r = e / PIECES, j = e % PIECES;
+                kt[slot][r * PIECES + (j ^ (r & 7))] = pre[u];
+            }
+        };
+        if (ngroups > 0) {
+            load_group(0);
+            store_group(0);
         }
+        __syncthreads();
+        for (int g = 0; g < ngroups; ++g) {
+            if (g + 1 < ngroups) load_group(g + 1);
+            const uint4* buf = kt[g & 1];
 #pragma unroll
-        for (int t = 0; t < PF; ++t)
-            if (g0 + t * TILE < nv_max) filter_tile(g0 + t * TILE, cur[t]);
-    };
-    if (nv_max > 0) {
+            for (int t = 0; t < GT; ++t) {
+                const int c0 = g * GROWS + t * TILE;
+                if (c0 < nv_max) {
+                    const int r = t * TILE + rho;
+                    typename MM::F bf[MM::KS];
 #pragma unroll
-        for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
-    }
-    for (int g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
-        group(g0, bq0, bq1);
-        if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
+                    for (int ks = 0; ks < MM::KS; ++ks) {
+                        const int j = 4 * ks + q4;
+                        bf[ks] = *reinterpret_cast<const bf16x8_t*>(&buf[r * PIECES + (j ^ (r & 7))]);
+                    }
+                    filter_tile(c0, bf);
+                }
+            }
+            // the other slot was last read before the previous barrier
+            if (g + 1 < ngroups) store_group((g + 1) & 1);
+            __syncthreads();
+        }
+    } else {
+        constexpr int PF = 2;
+        typename MM::F bq0[PF][MM::KS], bq1[PF][MM::KS];
+        auto group = [&](int g0, typename MM::F (&cur)[PF][MM::KS], typename MM::F (&nxt)[PF][MM::KS]) {
+            const int g1 = g0 + PF * TILE;
+            if (g1 < nv_max) {
+#pragma unroll
+                for (int t = 0; t < PF; ++t) load_b(g1 + t * TILE, nxt[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < PF; ++t)
+                if (g0 + t * TILE < nv_max) filter_tile(g0 + t * TILE, cur[t]);
+        };
+        if (nv_max > 0) {
+#pragma unroll
+            for (int t = 0; t < PF; ++t) load_b(t * TILE, bq0[t]);
+        }
+        for (int g0 = 0; g0 < nv_max; g0 += 2 * PF * TILE) {
+            group(g0, bq0, bq1);
+            if (g0 + PF * TILE < nv_max) group(g0 + PF * TILE, bq1, bq0);
+        }
     }
     // counts (a count above list_cap marks an overflowed list)
     const bool owner = (HI <= 4) || (HI == 8 ? (q4 & 1) == 0 : q4 == 0);
