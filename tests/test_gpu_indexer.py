@@ -52,7 +52,9 @@ def test_tinyr2_full_all_rows():
 # Hi=16, d_idx=128 on the dense (N <= 2048) kernel: one build of that kernel
 # took a GPU memory fault on this case; the cause is not identified, the
 # kernel is back to its earlier form, and the case stays skipped until the
-# cause is shown.
+# cause is shown.  The dense kernel is no longer built for Hi = 16: such
+# inputs take the list pipeline, which test_hi16_short_candidate_sets covers
+# at N <= 2048 for d_idx 64 and 128.
 DENSE_16_128_FAULT = "dense kernel Hi=16 d_idx=128: memory fault with one build, cause not identified"
 
 
