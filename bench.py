@@ -42,9 +42,11 @@ def log(msg):
 
 
 # ------------------------------------------------------------------ workload
-def build_inputs(name, seed=0, gates=None):
+def build_inputs(name, seed=0, gates=None, d_idx=None):
     from sparse_hybrid_attention_amd import synth
     over = {} if gates is None else {"gates": gates}
+    if d_idx is not None:
+        over["d_idx"] = d_idx
     return synth.make_inputs(name, seed=seed, **over)
 
 
@@ -869,6 +871,9 @@ def main():
                          "Tiny-R2 training-shape prefill)")
     ap.add_argument("--gates", default=None, choices=["mix", "hca", "csa", "swa"],
                     help="override the workload's gate setting (one-hot modes or the U(0,1) mix)")
+    ap.add_argument("--d-idx", type=int, default=None, choices=[64, 128],
+                    help="override the indexer key width of a workload with an indexer (CSA prefill, "
+                         "Tiny-R2, decode)")
     ap.add_argument("--q4", action="store_true",
                     help="decode workload: the HCA and CSA caches in 4-bit storage, decoded by the attention")
     ap.add_argument("--rope", default=None, choices=["fused", "separate"],
@@ -898,7 +903,7 @@ def main():
     inp = cpu = None
     if pipeline_workload and not args.copy_probe:
         log(f"[bench] building inputs for {args.workload}")
-        inp = build_inputs(args.workload, gates=args.gates)
+        inp = build_inputs(args.workload, gates=args.gates, d_idx=args.d_idx)
         if not args.no_cpu_baseline:
             # before the GPU is touched: the oracle's worker processes are forked
             log("[bench] timing the CPU oracle on a bounded sample")
@@ -1046,6 +1051,7 @@ def main():
         "data": "synthetic (seeded N(0,1) / U(0,1) draws, resident in HBM)",
         "config": {"workload": WORKLOADS[args.workload] + ("" if args.gates is None else f" [gates: {args.gates}]")
                    + (" [HCA and CSA caches in 4-bit storage]" if args.q4 else "")
+                   + (f" [indexer d_idx {args.d_idx}]" if args.d_idx else "")
                    + (f" [RoPE of q, {args.rope}]" if args.rope else "")
                    + (" [window / HCA attention items beside the indexer]" if args.overlap else ""),
                    "name": args.workload, "gates": cfg.get("gates"), "batch": cfg["B"],

@@ -1184,15 +1184,15 @@ __host__ __device__ constexpr int filter_min_blocks(bool f32, int hi, int di) {
 
 // L2: each wave scores FRT row tiles of queries against all their visible
 // entries (MFMA tiles as above) and appends the entries that pass the row's
-// threshold to the row's list in global memory.  For bf16 keys of 64
-// dimensions the four waves of a workgroup (consecutive queries) share each
+// threshold to the row's list in global memory.  For bf16 keys (64 or 128
+// dimensions) the four waves of a workgroup (consecutive queries) share each
 // key tile: groups of four tiles are staged in LDS (double-buffered, the next
 // group's global loads in flight while the current one is scored), so each
 // key row is read from L2 once per 64 queries instead of once per 16.  Other
 // forms load their key tiles per wave into registers.
 template <typename T, int DI>
 __host__ __device__ constexpr bool filter_shared_tiles() {
-    return std::is_same<T, bf16_t>::value && DI == 64;
+    return std::is_same<T, bf16_t>::value && (DI == 64 || DI == 128);
 }
 
 template <typename T, int HI, int DI>
@@ -1300,12 +1300,13 @@ void index_filter_kernel(IdxParams p) {
         }
     };
     if constexpr (SHARED) {
-        // LDS groups of GT key tiles, rows of DI bf16 (8 pieces of 16 bytes);
-        // piece j of row r sits at slot j ^ (r & 7), so the 8 lanes of one
-        // operand read (rows rho, one piece) hit distinct banks
+        // LDS groups of GT key tiles, rows of DI bf16 (DI / 8 pieces of 16
+        // bytes); piece j of row r sits at slot j ^ (r & 7), so the 8 lanes of
+        // one operand read (rows rho, one piece) hit distinct banks
         constexpr int GT = 4, GROWS = GT * TILE, PIECES = DI / 8;
         constexpr int LPT = GROWS * PIECES / (WAVES * 64);   // 16-byte loads per thread per group
-        static_assert(PIECES == 8 && LPT * WAVES * 64 == GROWS * PIECES, "shared key tiles: bf16, d_idx 64");
+        static_assert(PIECES % 8 == 0 && LPT * WAVES * 64 == GROWS * PIECES,
+                      "shared key tiles: bf16, d_idx 64 or 128");
         __shared__ __attribute__((aligned(16))) uint4 kt[2][GROWS * PIECES];
         __shared__ int wg_nv[WAVES];
         if (lane == 0) wg_nv[wave] = nv_max;
