@@ -153,7 +153,7 @@ def sampled_rows(B, T, n, seed):
 # each list, and the streaming kernel (bounded per-query buffers with
 # compactions) for the queries whose list cannot decide.  The cases below
 # repeat the small-N checks on that path (N = T / 4 > 2048).
-@pytest.mark.parametrize("Hi,d_idx", [(1, 64), (2, 128), (4, 64), (8, 64), (16, 128)])
+@pytest.mark.parametrize("Hi,d_idx", [(1, 64), (2, 128), (4, 64), (4, 128), (8, 64), (8, 128), (16, 128)])
 def test_streaming_head_counts(Hi, d_idx):
     lib()
     inp = synth.make_inputs("tinyr2_bf16", seed=30 + Hi, B=2, T=8500, Hi=Hi, d_idx=d_idx, k=64)
